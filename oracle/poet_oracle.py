@@ -1,0 +1,278 @@
+"""Plain float64 CPU oracle for the POET-X linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the library path
+never does.  It shares no code with the HIP kernels: it imports numpy only.
+
+What it computes (sources are the pages' titles and sections):
+  * "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+    Transformation", SAI replication review, Summary: every weight is trained
+    through an orthogonal equivalence W_RP = R W0 P with W0 frozen; R and P are
+    block-diagonal orthogonal matrices in a random permuted basis, built by the
+    Cayley-Neumann parameterization (CNP) from a skew-symmetric Q stored as its
+    upper triangle; two of the four permutations are absorbed into W0.
+  * same review, Weaknesses ("Cayley approximation ..."): the first-order
+    expansion of the Cayley map is I + 2Q, which fixes R = (I+Q)(I-Q)^-1.
+  * same review, Reproducibility ("Partial coverage ..."): the fused kernel
+    follows the paper's Eq. 8/9 with k = 3 and stores b(b-1)/2 elements per block.
+  * agidaily.cc article (the W_RP = R W0 P formula and merge-then-reinitialize).
+
+Everything is the dense definition written out: dense R and P are formed, the
+layer is y_t = R W0 P x_t, and gradients are those of L = <dY, Y>.  Readings
+taken where the pages are silent (all listed in the design notes):
+  * Q[r, c] = q[idx(r, c)] for r < c in row-major order of the strict upper
+    triangle, Q[c, r] = -Q[r, c], zero diagonal;
+  * k is the highest power kept: G = (I + Q) * sum_{i=0..k} Q^i;
+  * a permutation pi acts by gather, (Pi v)[i] = v[pi[i]], i.e. Pi[i, pi[i]] = 1,
+    and R = Pi_R^T D_R Pi_R with D_R = blockdiag(G_R,0, G_R,1, ...);
+  * the absorbed permutations are the two next to W0:  Wt = Pi_R W0 Pi_P^T;
+  * merge folds R W0 P into the weight, resamples both permutations and sets
+    q to zero.
+
+All functions take and return numpy float64 arrays (float32 inputs are widened
+losslessly); permutations are integer arrays.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "triangle_pairs", "skew_from_params", "params_grad_from_skew_grad",
+    "neumann_cayley", "exact_cayley", "block_diag", "gather_matrix",
+    "orthogonal_from_blocks", "prepermute", "blocks_from_params",
+    "forward", "forward_from_blocks", "backward", "backward_from_blocks",
+    "cnp_vjp", "merge", "effective_weight",
+]
+
+
+# --------------------------------------------------------------- skew storage
+def triangle_pairs(b: int):
+    """Storage order of the b(b-1)/2 upper-triangle parameters: row-major over
+    the strict upper triangle, i.e. (0,1), (0,2), ..., (0,b-1), (1,2), ..."""
+    return [(r, c) for r in range(b) for c in range(r + 1, b)]
+
+
+def skew_from_params(q: np.ndarray, b: int) -> np.ndarray:
+    """Compact parameters [nblk, b(b-1)/2] -> skew blocks Q [nblk, b, b].
+
+    Compact skew-symmetric storage (review Summary; b(b-1)/2 elements per block
+    in the Reproducibility section)."""
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim == 1:
+        q = q[None, :]
+    nblk = q.shape[0]
+    assert q.shape[1] == b * (b - 1) // 2
+    Q = np.zeros((nblk, b, b), dtype=np.float64)
+    for i, (r, c) in enumerate(triangle_pairs(b)):
+        Q[:, r, c] = q[:, i]
+        Q[:, c, r] = -q[:, i]
+    return Q
+
+
+def params_grad_from_skew_grad(dQ: np.ndarray) -> np.ndarray:
+    """Adjoint of skew_from_params: dL/dq[idx(r,c)] = dL/dQ[r,c] - dL/dQ[c,r]."""
+    dQ = np.asarray(dQ, dtype=np.float64)
+    if dQ.ndim == 2:
+        dQ = dQ[None]
+    b = dQ.shape[1]
+    pairs = triangle_pairs(b)
+    dq = np.zeros((dQ.shape[0], len(pairs)), dtype=np.float64)
+    for i, (r, c) in enumerate(pairs):
+        dq[:, i] = dQ[:, r, c] - dQ[:, c, r]
+    return dq
+
+
+# ------------------------------------------------------ Cayley-Neumann blocks
+def neumann_cayley(Q: np.ndarray, k: int) -> np.ndarray:
+    """Truncated Cayley map G = (I + Q) * sum_{i=0..k} Q^i, with explicit powers.
+
+    The Cayley transform (I+Q)(I-Q)^-1 with (I-Q)^-1 replaced by its Neumann
+    series cut after Q^k (review Summary, "Cayley-Neumann orthogonalization";
+    k = 3 in the Reproducibility section).  Works on [b, b] or [nblk, b, b]."""
+    Q = np.asarray(Q, dtype=np.float64)
+    single = Q.ndim == 2
+    if single:
+        Q = Q[None]
+    b = Q.shape[-1]
+    eye = np.eye(b)
+    out = np.empty_like(Q)
+    for j in range(Q.shape[0]):
+        series = np.zeros((b, b))
+        for i in range(k + 1):
+            series = series + np.linalg.matrix_power(Q[j], i)
+        out[j] = (eye + Q[j]) @ series
+    return out[0] if single else out
+
+
+def exact_cayley(Q: np.ndarray) -> np.ndarray:
+    """Exact Cayley transform (I + Q)(I - Q)^-1 by a linear solve (pins only)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    single = Q.ndim == 2
+    if single:
+        Q = Q[None]
+    b = Q.shape[-1]
+    eye = np.eye(b)
+    # X (I - Q) = (I + Q)  <=>  (I - Q)^T X^T = (I + Q)^T
+    out = np.stack([np.linalg.solve((eye - Qj).T, (eye + Qj).T).T for Qj in Q])
+    return out[0] if single else out
+
+
+def blocks_from_params(q: np.ndarray, b: int, k: int, cayley: str = "neumann") -> np.ndarray:
+    Q = skew_from_params(q, b)
+    if cayley == "exact":
+        return exact_cayley(Q)
+    return neumann_cayley(Q, k)
+
+
+# ------------------------------------------------------- dense R, P and Wt
+def block_diag(G: np.ndarray) -> np.ndarray:
+    """D = diag(G_0, G_1, ...) as a dense matrix."""
+    G = np.asarray(G, dtype=np.float64)
+    nblk, b, _ = G.shape
+    D = np.zeros((nblk * b, nblk * b))
+    for j in range(nblk):
+        D[j * b:(j + 1) * b, j * b:(j + 1) * b] = G[j]
+    return D
+
+
+def gather_matrix(pi: np.ndarray) -> np.ndarray:
+    """Permutation matrix Pi with Pi[i, pi[i]] = 1, so (Pi v)[i] = v[pi[i]]."""
+    pi = np.asarray(pi, dtype=np.int64)
+    d = pi.shape[0]
+    Pm = np.zeros((d, d))
+    Pm[np.arange(d), pi] = 1.0
+    return Pm
+
+
+def orthogonal_from_blocks(G: np.ndarray, pi: np.ndarray) -> np.ndarray:
+    """R = Pi^T D Pi: block-diagonal in the basis permuted by pi.
+
+    Entry-wise this is R[pi[i], pi[j]] = D[i, j]; the tests check it against
+    the product with explicit permutation matrices."""
+    D = block_diag(G)
+    pi = np.asarray(pi, dtype=np.int64)
+    R = np.empty_like(D)
+    R[np.ix_(pi, pi)] = D
+    return R
+
+
+def prepermute(W0: np.ndarray, pi_R: np.ndarray, pi_P: np.ndarray) -> np.ndarray:
+    """Weight with the two inner permutations absorbed: Wt = Pi_R W0 Pi_P^T,
+    i.e. Wt[i, j] = W0[pi_R[i], pi_P[j]] (review Summary, "permutation reduction")."""
+    W0 = np.asarray(W0, dtype=np.float64)
+    return W0[np.asarray(pi_R, dtype=np.int64)][:, np.asarray(pi_P, dtype=np.int64)]
+
+
+def effective_weight(W0, G_R, G_P, pi_R, pi_P) -> np.ndarray:
+    """W_RP = R W0 P (dense)."""
+    R = orthogonal_from_blocks(G_R, pi_R)
+    P = orthogonal_from_blocks(G_P, pi_P)
+    return R @ np.asarray(W0, dtype=np.float64) @ P
+
+
+# ------------------------------------------------------------- the layer
+def forward_from_blocks(x, W0, G_R, G_P, pi_R, pi_P) -> np.ndarray:
+    """Y = X P^T W0^T R^T, i.e. y_t = R W0 P x_t for every token row x_t."""
+    R = orthogonal_from_blocks(G_R, pi_R)
+    P = orthogonal_from_blocks(G_P, pi_P)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    return x @ P.T @ W0.T @ R.T
+
+
+def forward(x, W0, q_R, q_P, pi_R, pi_P, b: int, k: int, cayley: str = "neumann"):
+    G_R = blocks_from_params(q_R, b, k, cayley)
+    G_P = blocks_from_params(q_P, b, k, cayley)
+    return forward_from_blocks(x, W0, G_R, G_P, pi_R, pi_P)
+
+
+def _diag_blocks(M: np.ndarray, b: int) -> np.ndarray:
+    nblk = M.shape[0] // b
+    return np.stack([M[j * b:(j + 1) * b, j * b:(j + 1) * b] for j in range(nblk)])
+
+
+def backward_from_blocks(dy, x, W0, G_R, G_P, pi_R, pi_P):
+    """Gradients of L = <dY, Y> for Y = X P^T W0^T R^T.  W0 is frozen: no dW0.
+
+    Returns (dx, dG_R, dG_P) with
+      dX = dY R W0 P,
+      dR = dY^T X P^T W0^T,   dP = W0^T R^T dY^T X,
+      dD_R = Pi_R dR Pi_R^T and dG_R,j its j-th diagonal block (P likewise)."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    b = G_R.shape[-1]
+    R = orthogonal_from_blocks(G_R, pi_R)
+    P = orthogonal_from_blocks(G_P, pi_P)
+    dx = dy @ R @ W0 @ P
+    dR = (dy.T @ x) @ P.T @ W0.T
+    dP = (W0.T @ R.T) @ (dy.T @ x)
+    PiR = np.asarray(pi_R, dtype=np.int64)
+    PiP = np.asarray(pi_P, dtype=np.int64)
+    dD_R = dR[np.ix_(PiR, PiR)]          # = Pi_R dR Pi_R^T
+    dD_P = dP[np.ix_(PiP, PiP)]
+    return dx, _diag_blocks(dD_R, b), _diag_blocks(dD_P, b)
+
+
+def _poly_cnp(X: np.ndarray, k: int) -> np.ndarray:
+    """f(X) = (I + X) sum_{i=0..k} X^i for a square (possibly 2b x 2b) matrix."""
+    eye = np.eye(X.shape[0])
+    series = np.zeros_like(X)
+    for i in range(k + 1):
+        series = series + np.linalg.matrix_power(X, i)
+    return (eye + X) @ series
+
+
+def cnp_vjp(Q: np.ndarray, dG: np.ndarray, k: int) -> np.ndarray:
+    """Adjoint of the truncated Cayley map: dQ = L_f(Q^T, dG).
+
+    The Frechet derivative of a polynomial f at A in direction E is the
+    upper-right block of f([[A, E], [0, A]]) (block-triangular formula,
+    Higham, Functions of Matrices, 2008, sec. 3.2); for a real polynomial the
+    Frobenius adjoint of L_f(A, .) is L_f(A^T, .)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    dG = np.asarray(dG, dtype=np.float64)
+    single = Q.ndim == 2
+    if single:
+        Q, dG = Q[None], dG[None]
+    b = Q.shape[-1]
+    out = np.empty_like(Q)
+    for j in range(Q.shape[0]):
+        big = np.zeros((2 * b, 2 * b))
+        big[:b, :b] = Q[j].T
+        big[b:, b:] = Q[j].T
+        big[:b, b:] = dG[j]
+        out[j] = _poly_cnp(big, k)[:b, b:]
+    return out[0] if single else out
+
+
+def backward(dy, x, W0, q_R, q_P, pi_R, pi_P, b: int, k: int):
+    """Full backward to the compact parameters: (dx, dq_R, dq_P, dG_R, dG_P)."""
+    Q_R = skew_from_params(q_R, b)
+    Q_P = skew_from_params(q_P, b)
+    G_R = neumann_cayley(Q_R, k)
+    G_P = neumann_cayley(Q_P, k)
+    dx, dG_R, dG_P = backward_from_blocks(dy, x, W0, G_R, G_P, pi_R, pi_P)
+    dq_R = params_grad_from_skew_grad(cnp_vjp(Q_R, dG_R, k))
+    dq_P = params_grad_from_skew_grad(cnp_vjp(Q_P, dG_P, k))
+    return dx, dq_R, dq_P, dG_R, dG_P
+
+
+# ------------------------------------------------------------------- merge
+def merge(Wt, q_R, q_P, pi_R_old, pi_P_old, pi_R_new, pi_P_new, b: int, k: int):
+    """Merge-then-reinitialize: fold R W0 P into the weight, resample the
+    permutations and reset q (agidaily.cc article; review "merge_then_reinitialize").
+
+    The stored weight is Wt = Pi_R W0 Pi_P^T, so W0 = Pi_R^T Wt Pi_P.  After the
+    merge, W0' = R W0 P and the stored weight for the new permutations is
+    Wt' = Pi_R' W0' Pi_P'^T.  Returns (Wt', q_R', q_P') with q' = 0."""
+    Wt = np.asarray(Wt, dtype=np.float64)
+    PR = gather_matrix(pi_R_old)
+    PP = gather_matrix(pi_P_old)
+    W0 = PR.T @ Wt @ PP
+    G_R = blocks_from_params(q_R, b, k)
+    G_P = blocks_from_params(q_P, b, k)
+    W_eff = effective_weight(W0, G_R, G_P, pi_R_old, pi_P_old)
+    Wt_new = gather_matrix(pi_R_new) @ W_eff @ gather_matrix(pi_P_new).T
+    return Wt_new, np.zeros_like(np.asarray(q_R, dtype=np.float64)), \
+        np.zeros_like(np.asarray(q_P, dtype=np.float64))
