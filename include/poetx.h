@@ -1,0 +1,194 @@
+/*
+ * libpoetx: the POET-X linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer trains a frozen weight W0 (m x n, d_out x d_in) through an
+ * orthogonal equivalence  W_RP = R W0 P  ("POET-X: Memory-efficient LLM
+ * Training by Scaling Orthogonal Transformation", SAI replication review,
+ * Summary; agidaily.cc article, formula W_RP = R . W0 . P).  R (m x m) and
+ * P (n x n) are block-diagonal orthogonal matrices in a random permuted basis;
+ * every b x b block G is the Cayley map of a skew-symmetric Q truncated after
+ * the k-th Neumann term, and Q is stored as its b(b-1)/2 upper-triangle values
+ * (review Summary; Reproducibility, "Partial coverage ...").
+ *
+ * Conventions fixed by this library (readings of points the pages leave open):
+ *   - compact layout: q[idx(r,c)] = Q[r,c] for r < c with
+ *     idx(r,c) = r*b - r*(r+1)/2 + (c - r - 1)  (row-major strict upper
+ *     triangle), Q[c,r] = -Q[r,c], Q[r,r] = 0;
+ *   - G = (I + Q) * sum_{i=0..k} Q^i  (first-order term I + 2Q, as the
+ *     review's "Cayley approximation" weakness states);
+ *   - a permutation pi (int32, length d) gathers: (Pi v)[i] = v[pi[i]];
+ *     R = Pi_R^T diag(G_R,0, G_R,1, ...) Pi_R, P likewise; block j covers the
+ *     permuted indices [j*b, (j+1)*b);
+ *   - the two permutations next to W0 are absorbed into the stored weight
+ *     Wt = Pi_R W0 Pi_P^T, Wt[i][j] = W0[pi_R[i]][pi_P[j]] (review Summary,
+ *     "permutation reduction");
+ *   - activations are row-major [T, features] (one token per row); the layer
+ *     computes y_t = R W0 P x_t for every row.
+ *
+ * Memory and execution model (all entry points):
+ *   - every tensor pointer is a caller-owned DEVICE pointer, contiguous
+ *     row-major, 16-byte aligned; the library never allocates or frees device
+ *     memory and keeps no pointer after the call returns;
+ *   - work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream); results are ready when the stream is;
+ *   - scratch memory comes from the caller's workspace `ws` of `ws_bytes`
+ *     bytes (256-byte aligned); the matching *_workspace_bytes() query returns
+ *     the size needed (0 means ws may be NULL);
+ *   - all arguments are validated on the host BEFORE any HIP call: a bad
+ *     argument returns an error code and enqueues nothing;
+ *   - nothing aborts and no C++ exception crosses this interface.
+ *   - calls on different streams that share output or workspace memory race.
+ *
+ * Data types: POETX_F32 or POETX_BF16 for activations, Wt and G blocks (bf16
+ * is stored as the upper 16 bits of an IEEE float, round-to-nearest-even on
+ * every conversion); the compact parameters q, dq and the block gradients dG
+ * are always float32.  Every product accumulates in float32 (MFMA).
+ *
+ * Supported sizes: 16 <= b <= 1024 with b % 16 == 0, b | m, b | n,
+ * 1 <= k <= 8, T >= 0 (T == 0 is an empty batch), every extent below 2^31.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+    POETX_OK = 0,
+    POETX_ERR_INVALID_ARG = 1, /* null pointer, unknown enum value */
+    POETX_ERR_SHAPE = 2,       /* b does not divide m/n, T < 0, b % 16 != 0, ... */
+    POETX_ERR_UNSUPPORTED = 3, /* b or k outside the supported range */
+    POETX_ERR_WORKSPACE = 4,   /* ws_bytes below the *_workspace_bytes() value */
+    POETX_ERR_HIP = 5          /* a HIP call failed; see poetx_last_hip_error() */
+};
+
+enum { POETX_F32 = 0, POETX_BF16 = 1 };
+
+/* fast saves h2 = Wt P-side output for the backward; mem keeps only x and
+ * recomputes (review Summary: POET-X_fast / checkpointed POET-X_mem). */
+enum { POETX_FAST = 0, POETX_MEM = 1 };
+
+typedef struct poetx_linear_desc {
+    int64_t T;       /* tokens (rows of x and y), >= 0 */
+    int64_t m;       /* d_out: rows of W0, size of R */
+    int64_t n;       /* d_in: columns of W0, size of P */
+    int64_t b;       /* block size of R and P */
+    int32_t k;       /* Neumann order (highest power of Q kept) */
+    int32_t dtype;   /* POETX_F32 or POETX_BF16 */
+    int32_t variant; /* POETX_FAST or POETX_MEM */
+    int32_t reserved;/* must be 0 */
+} poetx_linear_desc;
+
+/* Library version string, e.g. "libpoetx 0.1.0 gfx950". */
+const char* poetx_version(void);
+/* Static text for a status code. */
+const char* poetx_status_string(int status);
+/* Text of the last HIP failure seen by the calling thread ("" if none). */
+const char* poetx_last_hip_error(void);
+
+/* ------------------------------------------------ compact skew parameters */
+/* Q[j] = unpack(q[j]) for nblk blocks (compact skew storage, review Summary).
+ * q: float32 [nblk, b(b-1)/2]; Q: dtype [nblk, b, b].  Bit-exact. */
+int poetx_skew_unpack(const float* q, void* Q, int dtype, int64_t nblk, int64_t b,
+                      void* stream);
+
+/* Adjoint of unpack: dq[j][idx(r,c)] = dQ[j][r][c] - dQ[j][c][r].
+ * dQ: float32 [nblk, b, b]; dq: float32 [nblk, b(b-1)/2]. */
+int poetx_skew_pack(const float* dQ, float* dq, int64_t nblk, int64_t b, void* stream);
+
+/* ----------------------------------------------- Cayley-Neumann transform */
+/* G[j] = (I + Q_j) sum_{i<=k} Q_j^i for a flat batch of nblk blocks (the
+ * review's fused Cayley-Neumann kernel, Summary and Reproducibility).
+ * q: float32 [nblk, b(b-1)/2]; G: G_dtype [nblk, b, b].  With G_dtype
+ * POETX_BF16 the powers of Q are multiplied in bf16 with float32
+ * accumulation and the terms I + 2Q are added in float32; POETX_F32 keeps
+ * every operand in float32.  One call may cover the blocks of many layers. */
+size_t poetx_cnp_fwd_workspace_bytes(int64_t nblk, int64_t b, int k, int G_dtype);
+int poetx_cnp_fwd(const float* q, int64_t nblk, int64_t b, int k, void* G, int G_dtype,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Adjoint of poetx_cnp_fwd followed by the skew pack:
+ * dq = pack(L_f(Q^T)[dG]).  dG: float32 [nblk, b, b]; dq: float32
+ * [nblk, b(b-1)/2].  `dtype` selects the operand precision of the products
+ * as for poetx_cnp_fwd. */
+size_t poetx_cnp_bwd_workspace_bytes(int64_t nblk, int64_t b, int k, int dtype);
+int poetx_cnp_bwd(const float* q, const float* dG, int64_t nblk, int64_t b, int k,
+                  float* dq, int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ permutations */
+/* dst[i][j] = src[row_idx[i]][col_idx[j]] (row_idx / col_idx may be NULL for
+ * the identity).  src, dst: dtype [rows, cols] with leading dimension cols.
+ * With scatter_cols != 0 the columns are scattered instead:
+ * dst[i][col_idx[j]] = src[row_idx[i]][j].  Bit-exact.  The index arrays
+ * must be permutations (see poetx_check_perm); src and dst must not overlap. */
+int poetx_permute(const void* src, void* dst, int dtype, int64_t rows, int64_t cols,
+                  const int32_t* row_idx, const int32_t* col_idx, int scatter_cols,
+                  void* stream);
+
+/* Wt = Pi_R W0 Pi_P^T, i.e. Wt[i][j] = W0[pi_R[i]][pi_P[j]] (the review's
+ * permutation reduction).  W0, Wt: dtype [m, n].  Bit-exact. */
+int poetx_prepermute(const void* W0, void* Wt, int dtype, int64_t m, int64_t n,
+                     const int32_t* pi_R, const int32_t* pi_P, void* stream);
+
+/* Debug check that pi is a bijection of [0, len): writes 1 (yes) or 0 to the
+ * device int32 *ok.  Needs poetx_check_perm_workspace_bytes(len) of ws. */
+size_t poetx_check_perm_workspace_bytes(int64_t len);
+int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------- the layer */
+/* Forward of the input-centric chain (review Summary):
+ *   a  = x gathered by pi_P          [T, n]
+ *   h1 = a . blockdiag(G_P)^T        [T, n]
+ *   h2 = h1 . Wt^T                   [T, m]
+ *   z  = h2 . blockdiag(G_R)^T       [T, m]
+ *   y  = z scattered by pi_R         [T, m]   (y = x P^T W0^T R^T)
+ * x: dtype [T, n]; Wt: dtype [m, n]; G_R: dtype [m/b, b, b]; G_P: dtype
+ * [n/b, b, b]; y: dtype [T, m].  FAST writes h2 (dtype [T, m]) to `saved`,
+ * which must hold poetx_linear_saved_bytes(d) bytes; MEM writes nothing there
+ * (saved may be NULL). */
+size_t poetx_linear_saved_bytes(const poetx_linear_desc* d);
+size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d);
+int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
+                     const void* G_R, const void* G_P, const int32_t* pi_R,
+                     const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Backward of the chain for L = <dy, y>; W0 is frozen, so there is no dW0.
+ *   dx  = dy R W0 P                              dtype [T, n]
+ *   dG_R[j] = (Pi_R dR Pi_R^T) block j, dR = dy^T x P^T W0^T     float32 [m/b, b, b]
+ *   dG_P[j] = (Pi_P dP Pi_P^T) block j, dP = W0^T R^T dy^T x     float32 [n/b, b, b]
+ * FAST reads h2 from `saved` (written by poetx_linear_fwd with the same
+ * inputs); MEM recomputes it from x.  Feed dG_R / dG_P to poetx_cnp_bwd to
+ * obtain dq_R / dq_P.  T == 0 writes zero block gradients. */
+size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d);
+int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,
+                     const void* Wt, const void* G_R, const void* G_P, const int32_t* pi_R,
+                     const int32_t* pi_P, const void* saved, void* dx, float* dG_R,
+                     float* dG_P, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ merge */
+/* Merge-then-reinitialize (agidaily.cc article; review "merge_then_reinitialize"):
+ * with G from q_R / q_P (k = d->k, products in d->dtype),
+ *   M   = diag(G_R) . Wt . diag(G_P)      (Wt in the old permuted bases)
+ *   Wt' [i][j] = M[s_R[i]][s_P[j]],  s = pi_old^-1 o pi_new
+ * so that Wt' = Pi_R' (R W0 P) Pi_P'^T; then q_R and q_P are set to zero.
+ * Wt is updated in place (dtype [m, n]); the caller draws pi_new (no RNG in
+ * the library) and uses it from then on.  Passing pi_new == pi_old gives a
+ * pure fold; with q == 0 as well the call leaves Wt bit-identical.
+ * d->T and d->variant are ignored. */
+size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d);
+int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P,
+                const int32_t* pi_R_old, const int32_t* pi_P_old, const int32_t* pi_R_new,
+                const int32_t* pi_P_new, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

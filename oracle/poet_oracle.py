@@ -276,3 +276,62 @@ def merge(Wt, q_R, q_P, pi_R_old, pi_P_old, pi_R_new, pi_P_new, b: int, k: int):
     Wt_new = gather_matrix(pi_R_new) @ W_eff @ gather_matrix(pi_P_new).T
     return Wt_new, np.zeros_like(np.asarray(q_R, dtype=np.float64)), \
         np.zeros_like(np.asarray(q_P, dtype=np.float64))
+
+
+# ------------------------------------------ outputs the oracle computes one by one
+# For full-size workloads the tests compare sampled outputs; each one is the
+# same dense definition as above, restricted to the requested entries.
+def input_grad(dy, W0, G_R, G_P, pi_R, pi_P) -> np.ndarray:
+    """dX = dY R W0 P for the given rows of dY (rows are independent)."""
+    R = orthogonal_from_blocks(G_R, pi_R)
+    P = orthogonal_from_blocks(G_P, pi_P)
+    return ((np.asarray(dy, dtype=np.float64) @ R) @ np.asarray(W0, dtype=np.float64)) @ P
+
+
+def block_grad_entries(dy, x, W0, G_R, G_P, pi_R, pi_P, side: str, entries):
+    """Selected entries (j, r, c) of dG_R or dG_P (see backward_from_blocks).
+
+    dG_R,j[r, c] = dR[pi_R[jb+r], pi_R[jb+c]] with dR = dY^T X P^T W0^T, so
+    dR[a, e] = dY[:, a] . (X P^T W0[e, :]^T);
+    dG_P,j[r, c] = dP[pi_P[jb+r], pi_P[jb+c]] with dP = W0^T R^T dY^T X, so
+    dP[a, e] = (dY R W0[:, a]) . X[:, e]."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    b = G_R.shape[-1]
+    out = np.empty(len(entries))
+    if side == "R":
+        P = orthogonal_from_blocks(G_P, pi_P)
+        pi = np.asarray(pi_R, dtype=np.int64)
+        cache = {}
+        for i, (j, r, c) in enumerate(entries):
+            a, e = pi[j * b + r], pi[j * b + c]
+            if e not in cache:
+                cache[e] = x @ (P.T @ W0[e, :])
+            out[i] = dy[:, a] @ cache[e]
+    else:
+        R = orthogonal_from_blocks(G_R, pi_R)
+        pi = np.asarray(pi_P, dtype=np.int64)
+        cache = {}
+        for i, (j, r, c) in enumerate(entries):
+            a, e = pi[j * b + r], pi[j * b + c]
+            if a not in cache:
+                cache[a] = dy @ (R @ W0[:, a])
+            out[i] = cache[a] @ x[:, e]
+    return out
+
+
+def merge_entries(Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_new, pi_P_new, entries):
+    """Selected entries (i, j) of the merged stored weight
+    Wt'[i, j] = (R W0 P)[pi_R_new[i], pi_P_new[j]] with W0 = Pi_R^T Wt Pi_P."""
+    Wt = np.asarray(Wt, dtype=np.float64)
+    R = orthogonal_from_blocks(G_R, pi_R_old)
+    P = orthogonal_from_blocks(G_P, pi_P_old)
+    inv_R = np.argsort(np.asarray(pi_R_old))   # W0[a, :] = Wt[inv_R[a], :] permuted
+    inv_P = np.argsort(np.asarray(pi_P_old))
+    W0 = Wt[inv_R][:, inv_P]
+    out = np.empty(len(entries))
+    for t, (i, j) in enumerate(entries):
+        a, e = pi_R_new[i], pi_P_new[j]
+        out[t] = R[a, :] @ W0 @ P[:, e]
+    return out

@@ -1,0 +1,673 @@
+// libpoetx C ABI: argument validation, workspace planning and the stream-ordered
+// kernel sequences of the POET-X layer.  No device memory is allocated here:
+// every scratch buffer is carved from the caller's workspace.
+#include <stdint.h>
+
+#include <algorithm>
+#include <string>
+
+#include "elementwise.h"
+#include "gemm.h"
+#include "poetx.h"
+
+using namespace poetx;
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return POETX_ERR_HIP;
+}
+
+#define HIP_TRY(expr)                                   \
+    do {                                                \
+        const hipError_t e_ = (expr);                   \
+        if (e_ != hipSuccess) return hip_fail(e_);      \
+    } while (0)
+
+#define POETX_TRY(expr)                                 \
+    do {                                                \
+        const int s_ = (expr);                          \
+        if (s_ != POETX_OK) return s_;                  \
+    } while (0)
+
+constexpr int64_t kMaxExtent = (int64_t(1) << 31) - 1;
+
+// Bump allocator over the caller's workspace; with a null base it only measures.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    void* take(size_t bytes) {
+        off = (off + 255) & ~size_t(255);
+        void* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    }
+    template <typename T> T* take_n(int64_t n) { return static_cast<T*>(take(sizeof(T) * (size_t)std::max<int64_t>(n, 0))); }
+};
+
+inline bool dtype_ok(int d) { return d == POETX_F32 || d == POETX_BF16; }
+inline size_t esize(int d) { return d == POETX_BF16 ? 2 : 4; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_block(int64_t b) {
+    if (b <= 0) return POETX_ERR_SHAPE;
+    if (b < 16 || b > 1024 || b % 16 != 0) return POETX_ERR_UNSUPPORTED;
+    return POETX_OK;
+}
+
+int check_k(int k) { return (k >= 1 && k <= 8) ? POETX_OK : POETX_ERR_UNSUPPORTED; }
+
+int check_nblk(int64_t nblk, int64_t b) {
+    if (nblk < 0) return POETX_ERR_SHAPE;
+    if (nblk > 0 && nblk > kMaxExtent / (b * b)) return POETX_ERR_SHAPE;
+    return POETX_OK;
+}
+
+int check_desc(const poetx_linear_desc* d) {
+    if (!d) return POETX_ERR_INVALID_ARG;
+    if (!dtype_ok(d->dtype) || (d->variant != POETX_FAST && d->variant != POETX_MEM) || d->reserved != 0)
+        return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(d->b));
+    POETX_TRY(check_k(d->k));
+    if (d->T < 0 || d->m <= 0 || d->n <= 0) return POETX_ERR_SHAPE;
+    if (d->m % d->b != 0 || d->n % d->b != 0) return POETX_ERR_SHAPE;
+    if (d->T > kMaxExtent || d->m > kMaxExtent || d->n > kMaxExtent) return POETX_ERR_SHAPE;
+    return POETX_OK;
+}
+
+// ------------------------------------------------------------- GEMM helpers
+GemmTile pick_tile(bool bf16, int64_t M, int64_t N, int64_t batch_tiles_hint) {
+    (void)batch_tiles_hint;
+    if (bf16) {
+        if (M >= 256 && N >= 128) return GemmTile::Large;
+        if (M >= 128 && N >= 128) return GemmTile::Medium;
+        return GemmTile::Small;
+    }
+    if (M >= 128 && N >= 128) return GemmTile::Medium;
+    return GemmTile::Small;
+}
+
+struct Mat {
+    const void* p;
+    int64_t ld;
+    int64_t stride;
+};
+
+hipError_t gemm(GemmLayout layout, bool cbf16, bool obf16, int64_t M, int64_t N, int64_t K, int64_t batch, Mat A,
+                Mat B, void* C, int64_t ldc, int64_t sC, hipStream_t s, float alpha = 1.f,
+                const float* cin1 = nullptr, float beta1 = 0.f, const float* cin2 = nullptr, float beta2 = 0.f,
+                float gamma = 0.f, void* C2 = nullptr) {
+    GemmArgs g;
+    g.A = A.p; g.lda = A.ld; g.strideA = A.stride;
+    g.B = B.p; g.ldb = B.ld; g.strideB = B.stride;
+    g.C = C; g.ldc = ldc; g.strideC = sC;
+    g.C2 = C2; g.ldc2 = ldc; g.strideC2 = sC;
+    g.Cin1 = cin1; g.ldcin1 = ldc; g.strideCin1 = sC; g.beta1 = beta1;
+    g.Cin2 = cin2; g.ldcin2 = ldc; g.strideCin2 = sC; g.beta2 = beta2;
+    g.alpha = alpha; g.gamma = gamma;
+    g.M = (int)M; g.N = (int)N; g.K = (int)K;
+    g.batch = (int)batch;
+    g.splits = 1;
+    g.k_per_split = (int)std::max<int64_t>(K, 1);
+    return gemm_launch(g, layout, pick_tile(cbf16, M, N, batch), cbf16, obf16, s);
+}
+
+// Square b x b block products over nblk blocks stored back to back.
+struct BlkMat {
+    const void* p;
+};
+inline Mat sq(const void* p, int64_t b) { return Mat{p, b, b * b}; }
+
+// --------------------------------------------------- Cayley-Neumann planning
+struct CnpBufs {
+    float* Q32 = nullptr; void* Qc = nullptr;
+    float* S32 = nullptr; void* Sc = nullptr;
+    float* U32 = nullptr; void* Uc = nullptr;   // T = 2Q+S (k=3) / P1 = Q+S (k=4)
+    float* V32 = nullptr; void* Vc = nullptr;   // U = 2Q+2S (k=3) / E (k=4)
+    float* W32 = nullptr;                       // Q + E (k=4)
+    // Horner (other k): D_1..D_k, two rolling gradient buffers
+    float* D32[9] = {}; void* Dc[9] = {};
+    // backward
+    void* dGc = nullptr;
+    float* a32 = nullptr; float* b32 = nullptr; void* c_c = nullptr; void* d_c = nullptr;
+    float* e32 = nullptr; float* f32 = nullptr; float* g32 = nullptr;
+};
+
+// The compute-dtype copy of a float32 buffer: its own buffer for bf16, the
+// float32 buffer itself otherwise.
+void* ctake(Carver& cv, bool cbf16, int64_t elems, float* alias32) {
+    return cbf16 ? cv.take(2 * (size_t)elems) : static_cast<void*>(alias32);
+}
+
+void plan_cnp(Carver& cv, int64_t nblk, int64_t b, int k, bool cbf16, bool backward, CnpBufs& B) {
+    const int64_t e = nblk * b * b;
+    B.Q32 = cv.take_n<float>(e);
+    B.Qc = ctake(cv, cbf16, e, B.Q32);
+    if (k == 3 || k == 4) {
+        B.S32 = cv.take_n<float>(e);
+        B.Sc = ctake(cv, cbf16, e, B.S32);
+        B.U32 = cv.take_n<float>(e);
+        B.Uc = ctake(cv, cbf16, e, B.U32);
+        B.V32 = cv.take_n<float>(e);
+        B.Vc = ctake(cv, cbf16, e, B.V32);
+        if (k == 4) B.W32 = cv.take_n<float>(e);
+    } else {
+        B.D32[1] = B.Q32;
+        B.Dc[1] = B.Qc;
+        const int keep = backward ? k : std::min(k, 3);
+        for (int i = 2; i <= keep; ++i) {
+            B.D32[i] = cv.take_n<float>(e);
+            B.Dc[i] = ctake(cv, cbf16, e, B.D32[i]);
+        }
+    }
+    if (backward) {
+        B.a32 = cv.take_n<float>(e);
+        B.b32 = cv.take_n<float>(e);
+        B.c_c = cbf16 ? cv.take(2 * (size_t)e) : static_cast<void*>(cv.take_n<float>(e));
+        B.d_c = cbf16 ? cv.take(2 * (size_t)e) : static_cast<void*>(cv.take_n<float>(e));
+        B.e32 = cv.take_n<float>(e);
+        B.f32 = cv.take_n<float>(e);
+        B.g32 = cv.take_n<float>(e);
+        B.dGc = cbf16 ? cv.take(2 * (size_t)e) : nullptr;
+    }
+}
+
+// Shared front part: Q (float32 and compute copy) and, for k = 3 / 4, S = Q^2.
+int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, CnpBufs& B, hipStream_t s) {
+    HIP_TRY(skew_unpack(q, B.Q32, false, nblk, (int)b, s));
+    if (cbf16) HIP_TRY(combine(nblk, (int)b, B.Q32, 1.f, nullptr, 0, nullptr, 0, 0, nullptr, B.Qc, true, s));
+    if (k == 3 || k == 4) {
+        // S = Q Q = -Q Q^T
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Qc, b), B.S32, b, b * b, s,
+                     -1.f, nullptr, 0, nullptr, 0, 0, cbf16 ? B.Sc : nullptr));
+    }
+    return POETX_OK;
+}
+
+// Forward Cayley-Neumann schedules.  k = 3: G = I + 2Q + 2S + (2Q + S) S.
+// k = 4: E = (Q + S) + (Q + S) S, G = I + Q + E + Q E.  Other k: Horner,
+// D_1 = Q, D_{i+1} = Q + Q D_i, G = I + Q + D_k + Q D_k.  Every product is a
+// correction term; the leading terms are added in float32 by the epilogue.
+int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void* G, bool gbf16, CnpBufs& B,
+                hipStream_t s) {
+    POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
+    const int ib = (int)b;
+    const int64_t bb = b * b;
+    if (k == 3) {
+        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 1.f, nullptr, 0, 0, nullptr, B.Uc, cbf16, s));
+        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 2.f, nullptr, 0, 0, B.V32, nullptr, false, s));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, gbf16, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), G, b, bb, s, 1.f,
+                     B.V32, 1.f, nullptr, 0, 1.f));
+    } else if (k == 4) {
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.U32, cbf16 ? B.Uc : nullptr, cbf16, s));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), B.V32, b, bb, s, 1.f,
+                     B.U32, 1.f, nullptr, 0, 0, cbf16 ? B.Vc : nullptr));
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.V32, 1.f, nullptr, 0, 0, B.W32, nullptr, false, s));
+        HIP_TRY(gemm(GemmLayout::NN, cbf16, gbf16, b, b, b, nblk, sq(B.Qc, b), sq(B.Vc, b), G, b, bb, s, 1.f,
+                     B.W32, 1.f, nullptr, 0, 1.f));
+    } else {
+        // rolling D buffers: slots 1 (= Q), 2, 3
+        int cur = 1;
+        for (int i = 1; i < k; ++i) {
+            const int nxt = (cur == 2) ? 3 : 2;
+            HIP_TRY(gemm(GemmLayout::NN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Dc[cur], b), B.D32[nxt], b,
+                         bb, s, 1.f, B.Q32, 1.f, nullptr, 0, 0, cbf16 ? B.Dc[nxt] : nullptr));
+            cur = nxt;
+        }
+        HIP_TRY(gemm(GemmLayout::NN, cbf16, gbf16, b, b, b, nblk, sq(B.Qc, b), sq(B.Dc[cur], b), G, b, bb, s, 1.f,
+                     B.Q32, 1.f, B.D32[cur], 1.f, 1.f));
+    }
+    return POETX_OK;
+}
+
+// Adjoint schedules (reverse of the forward ones), ending with the skew pack.
+int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k, bool cbf16, float* dq,
+                 CnpBufs& B, hipStream_t s) {
+    POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
+    const int ib = (int)b;
+    const int64_t bb = b * b;
+    const void* dGc = dG;
+    if (cbf16) {
+        HIP_TRY(combine(nblk, ib, dG, 1.f, nullptr, 0, nullptr, 0, 0, nullptr, B.dGc, true, s));
+        dGc = B.dGc;
+    }
+    float* dQ = B.g32;
+    if (k == 3) {
+        // T = 2Q + S (compute copy only)
+        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 1.f, nullptr, 0, 0, nullptr, B.Uc, cbf16, s));
+        // dA = dG + dG S,  dB = dG + T^T dG
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Sc, b), B.a32, b, bb, s, 1.f, dG,
+                     1.f));
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(dGc, b), B.b32, b, bb, s, 1.f, dG,
+                     1.f));
+        // dS = dA + dB (compute copy)
+        HIP_TRY(combine(nblk, ib, B.a32, 1.f, B.b32, 1.f, nullptr, 0, 0, nullptr, B.c_c, cbf16, s));
+        // dQ = 2 dA + dS Q^T + Q^T dS
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.c_c, b), sq(B.Qc, b), B.e32, b, bb, s, 1.f,
+                     B.a32, 2.f));
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.c_c, b), dQ, b, bb, s, 1.f,
+                     B.e32, 1.f));
+    } else if (k == 4) {
+        // recompute P1 = Q + S and E = P1 + P1 S
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.U32, cbf16 ? B.Uc : nullptr, cbf16, s));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), B.V32, b, bb, s, 1.f,
+                     B.U32, 1.f, nullptr, 0, 0, cbf16 ? B.Vc : nullptr));
+        // X1 = dG + dG E^T ; dE = dG + Q^T dG
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Vc, b), B.a32, b, bb, s, 1.f, dG,
+                     1.f));
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dGc, b), B.b32, b, bb, s, 1.f, dG,
+                     1.f, nullptr, 0, 0, cbf16 ? B.c_c : nullptr));
+        const void* dEc = cbf16 ? B.c_c : static_cast<void*>(B.b32);
+        // dP1 = dE + dE S ; dS = P1^T dE + dP1
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dEc, b), sq(B.Sc, b), B.e32, b, bb, s, 1.f,
+                     B.b32, 1.f));
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(dEc, b), cbf16 ? nullptr : B.f32,
+                     b, bb, s, 1.f, B.e32, 1.f, nullptr, 0, 0, cbf16 ? B.d_c : nullptr));
+        const void* dSc = cbf16 ? B.d_c : static_cast<void*>(B.f32);
+        // dQ = X1 + dP1 + dS Q^T + Q^T dS
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dSc, b), sq(B.Qc, b), B.W32, b, bb, s, 1.f,
+                     B.a32, 1.f, B.e32, 1.f));
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dSc, b), dQ, b, bb, s, 1.f, B.W32,
+                     1.f));
+    } else {
+        // recompute D_2..D_k (D_1 = Q)
+        for (int i = 1; i < k; ++i)
+            HIP_TRY(gemm(GemmLayout::NN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Dc[i], b), B.D32[i + 1], b,
+                         bb, s, 1.f, B.Q32, 1.f, nullptr, 0, 0, cbf16 ? B.Dc[i + 1] : nullptr));
+        // G = I + Q + D_k + Q D_k:  acc = dG + dG D_k^T,  dD_k = dG + Q^T dG
+        float* acc = B.e32;
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Dc[k], b), acc, b, bb, s, 1.f,
+                     dG, 1.f));
+        float* dD32[2] = {B.a32, B.b32};
+        void* dDc[2] = {B.c_c, B.d_c};
+        int cur = 0;
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dGc, b), dD32[cur], b, bb, s, 1.f,
+                     dG, 1.f, nullptr, 0, 0, cbf16 ? dDc[cur] : nullptr));
+        for (int i = k - 1; i >= 1; --i) {
+            const void* cur_c = cbf16 ? dDc[cur] : static_cast<void*>(dD32[cur]);
+            // D_{i+1} = Q + Q D_i:  acc += dD_{i+1} + dD_{i+1} D_i^T ;  dD_i = Q^T dD_{i+1}
+            HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(cur_c, b), sq(B.Dc[i], b), B.f32, b, bb, s,
+                         1.f, acc, 1.f, dD32[cur], 1.f));
+            std::swap(acc, B.f32);
+            const int nxt = cur ^ 1;
+            HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(cur_c, b), dD32[nxt], b, bb, s,
+                         1.f, nullptr, 0, nullptr, 0, 0, cbf16 ? dDc[nxt] : nullptr));
+            cur = nxt;
+        }
+        // D_1 = Q: acc += dD_1
+        HIP_TRY(combine(nblk, ib, acc, 1.f, dD32[cur], 1.f, nullptr, 0, 0, dQ, nullptr, false, s));
+    }
+    HIP_TRY(skew_pack(dQ, dq, nblk, ib, s));
+    return POETX_OK;
+}
+
+size_t cnp_ws(int64_t nblk, int64_t b, int k, bool cbf16, bool backward) {
+    Carver cv(nullptr);
+    CnpBufs B;
+    plan_cnp(cv, nblk, b, k, cbf16, backward, B);
+    return cv.off;
+}
+
+// -------------------------------------------------------------- the layer
+struct LinearBufs {
+    void* buf[3] = {};
+    float* part = nullptr;
+    int splits_R = 1, splits_P = 1;
+    int64_t kps_R = 0, kps_P = 0;
+};
+
+// Split-K plan for dG = A^T B with K = T: enough workgroups to cover the chip.
+void plan_splits(int64_t T, int64_t b, int64_t nblk, bool bf16, int& splits, int64_t& kps) {
+    const GemmTile tile = pick_tile(bf16, b, b, 0);
+    const int64_t tr = gemm_tile_rows(tile, bf16), tc = gemm_tile_cols(tile, bf16);
+    const int64_t tiles = ((b + tr - 1) / tr) * ((b + tc - 1) / tc) * nblk;
+    int64_t want = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
+    want = std::min<int64_t>(want, std::max<int64_t>(1, T / 256));
+    int64_t k = (T + want - 1) / want;
+    k = std::max<int64_t>(64, (k + 63) / 64 * 64);
+    kps = k;
+    splits = (int)std::max<int64_t>(1, (T + k - 1) / k);
+}
+
+void plan_linear(Carver& cv, const poetx_linear_desc* d, bool backward, LinearBufs& L) {
+    const int64_t wide = std::max(d->m, d->n);
+    const size_t es = esize(d->dtype);
+    const int nb = backward ? 3 : 2;
+    for (int i = 0; i < nb; ++i) L.buf[i] = cv.take(es * (size_t)(d->T * wide));
+    if (backward) {
+        const bool bf = d->dtype == POETX_BF16;
+        plan_splits(d->T, d->b, d->m / d->b, bf, L.splits_R, L.kps_R);
+        plan_splits(d->T, d->b, d->n / d->b, bf, L.splits_P, L.kps_P);
+        const int64_t pr = L.splits_R > 1 ? L.splits_R * d->m * d->b : 0;
+        const int64_t pp = L.splits_P > 1 ? L.splits_P * d->n * d->b : 0;
+        L.part = cv.take_n<float>(std::max(pr, pp));
+    }
+}
+
+// Batched block product over the feature axis of a [T, d] activation:
+// out[:, jb:(j+1)b] = in[:, jb:(j+1)b] . G_j^T (NT) or . G_j (NN).
+hipError_t block_apply(GemmLayout layout, bool bf16, int64_t T, int64_t d, int64_t b, const void* in,
+                       const void* G, void* out, hipStream_t s) {
+    return gemm(layout, bf16, bf16, T, b, b, d / b, Mat{in, d, b}, Mat{G, b, b * b}, out, d, b, s);
+}
+
+// dG_j = A_j^T B_j over the T rows, split along T; partials reduced in order.
+int block_grad(bool bf16, int64_t T, int64_t d, int64_t b, const void* A, const void* B, float* dG, int splits,
+               int64_t kps, float* part, hipStream_t s) {
+    GemmArgs g;
+    g.A = A; g.lda = d; g.strideA = b;
+    g.B = B; g.ldb = d; g.strideB = b;
+    g.ldc = b; g.strideC = b * b;
+    g.M = (int)b; g.N = (int)b; g.K = (int)T;
+    g.batch = (int)(d / b);
+    g.splits = splits;
+    g.k_per_split = (int)kps;
+    if (splits > 1) {
+        g.C = part;
+        g.strideSplit = d * b;  // nblk * b * b
+    } else {
+        g.C = dG;
+    }
+    HIP_TRY(gemm_launch(g, GemmLayout::TN, pick_tile(bf16, b, b, 0), bf16, false, s));
+    if (splits > 1) HIP_TRY(splitk_reduce(part, dG, d * b, splits, s));
+    return POETX_OK;
+}
+
+int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                   const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
+                   hipStream_t s) {
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, m = d->m, n = d->n, b = d->b;
+    // a = x gathered by pi_P;  h1 = a . blockdiag(G_P)^T
+    HIP_TRY(permute_2d(x, buf_a, bf, T, n, nullptr, pi_P, false, s));
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, buf_a, G_P, buf_b, s));
+    // h2 = h1 . Wt^T
+    HIP_TRY(gemm(GemmLayout::NT, bf, bf, T, m, n, 1, Mat{buf_b, n, 0}, Mat{Wt, n, 0}, h2_out, m, 0, s));
+    // z = h2 . blockdiag(G_R)^T ; y = z scattered by pi_R
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, m, b, h2_out, G_R, buf_b, s));
+    HIP_TRY(permute_2d(buf_b, y, bf, T, m, nullptr, pi_R, true, s));
+    return POETX_OK;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* poetx_version(void) { return "libpoetx 0.1.0 gfx950"; }
+
+const char* poetx_status_string(int status) {
+    switch (status) {
+        case POETX_OK: return "ok";
+        case POETX_ERR_INVALID_ARG: return "invalid argument";
+        case POETX_ERR_SHAPE: return "invalid shape";
+        case POETX_ERR_UNSUPPORTED: return "unsupported block size, order or dtype";
+        case POETX_ERR_WORKSPACE: return "workspace too small";
+        case POETX_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* poetx_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int poetx_skew_unpack(const float* q, void* Q, int dtype, int64_t nblk, int64_t b, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    if (b <= 1 || b > 1024) return b <= 0 ? POETX_ERR_SHAPE : POETX_ERR_UNSUPPORTED;
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!q || !Q) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(skew_unpack(q, Q, dtype == POETX_BF16, nblk, (int)b, as_stream(stream)));
+    return POETX_OK;
+}
+
+int poetx_skew_pack(const float* dQ, float* dq, int64_t nblk, int64_t b, void* stream) {
+    if (b <= 1 || b > 1024) return b <= 0 ? POETX_ERR_SHAPE : POETX_ERR_UNSUPPORTED;
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!dQ || !dq) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(skew_pack(dQ, dq, nblk, (int)b, as_stream(stream)));
+    return POETX_OK;
+}
+
+size_t poetx_cnp_fwd_workspace_bytes(int64_t nblk, int64_t b, int k, int G_dtype) {
+    if (check_block(b) != POETX_OK || check_k(k) != POETX_OK || check_nblk(nblk, b) != POETX_OK ||
+        !dtype_ok(G_dtype))
+        return 0;
+    return cnp_ws(nblk, b, k, G_dtype == POETX_BF16, false);
+}
+
+int poetx_cnp_fwd(const float* q, int64_t nblk, int64_t b, int k, void* G, int G_dtype, void* ws, size_t ws_bytes,
+                  void* stream) {
+    if (!dtype_ok(G_dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    POETX_TRY(check_k(k));
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!q || !G) return POETX_ERR_INVALID_ARG;
+    const bool cbf = G_dtype == POETX_BF16;
+    const size_t need = cnp_ws(nblk, b, k, cbf, false);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (need && !ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws);
+    CnpBufs B;
+    plan_cnp(cv, nblk, b, k, cbf, false, B);
+    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, as_stream(stream));
+}
+
+size_t poetx_cnp_bwd_workspace_bytes(int64_t nblk, int64_t b, int k, int dtype) {
+    if (check_block(b) != POETX_OK || check_k(k) != POETX_OK || check_nblk(nblk, b) != POETX_OK ||
+        !dtype_ok(dtype))
+        return 0;
+    return cnp_ws(nblk, b, k, dtype == POETX_BF16, true);
+}
+
+int poetx_cnp_bwd(const float* q, const float* dG, int64_t nblk, int64_t b, int k, float* dq, int dtype, void* ws,
+                  size_t ws_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    POETX_TRY(check_k(k));
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!q || !dG || !dq) return POETX_ERR_INVALID_ARG;
+    const bool cbf = dtype == POETX_BF16;
+    const size_t need = cnp_ws(nblk, b, k, cbf, true);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (need && !ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws);
+    CnpBufs B;
+    plan_cnp(cv, nblk, b, k, cbf, true, B);
+    return cnp_backward(q, dG, nblk, b, k, cbf, dq, B, as_stream(stream));
+}
+
+int poetx_permute(const void* src, void* dst, int dtype, int64_t rows, int64_t cols, const int32_t* row_idx,
+                  const int32_t* col_idx, int scatter_cols, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || rows > kMaxExtent || cols > kMaxExtent) return POETX_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return POETX_OK;
+    if (!src || !dst) return POETX_ERR_INVALID_ARG;
+    if (cols % (16 / (int64_t)esize(dtype)) != 0) return POETX_ERR_SHAPE;
+    HIP_TRY(permute_2d(src, dst, dtype == POETX_BF16, rows, cols, row_idx, col_idx, scatter_cols != 0,
+                       as_stream(stream)));
+    return POETX_OK;
+}
+
+int poetx_prepermute(const void* W0, void* Wt, int dtype, int64_t m, int64_t n, const int32_t* pi_R,
+                     const int32_t* pi_P, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    if (m <= 0 || n <= 0 || m > kMaxExtent || n > kMaxExtent) return POETX_ERR_SHAPE;
+    if (!W0 || !Wt || !pi_R || !pi_P) return POETX_ERR_INVALID_ARG;
+    if (n % (16 / (int64_t)esize(dtype)) != 0) return POETX_ERR_SHAPE;
+    HIP_TRY(permute_2d(W0, Wt, dtype == POETX_BF16, m, n, pi_R, pi_P, false, as_stream(stream)));
+    return POETX_OK;
+}
+
+size_t poetx_check_perm_workspace_bytes(int64_t len) {
+    if (len < 0 || len > kMaxExtent) return 0;
+    return (size_t)(len + 1) * sizeof(int32_t);
+}
+
+int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size_t ws_bytes, void* stream) {
+    if (len < 0 || len > kMaxExtent) return POETX_ERR_SHAPE;
+    if (!ok || (len > 0 && !pi)) return POETX_ERR_INVALID_ARG;
+    if (ws_bytes < poetx_check_perm_workspace_bytes(len)) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    int* counts = static_cast<int*>(ws);
+    HIP_TRY(check_perm(pi, len, ok, counts, counts + len, as_stream(stream)));
+    return POETX_OK;
+}
+
+size_t poetx_linear_saved_bytes(const poetx_linear_desc* d) {
+    if (check_desc(d) != POETX_OK || d->variant != POETX_FAST) return 0;
+    return esize(d->dtype) * (size_t)(d->T * d->m);
+}
+
+size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
+    if (check_desc(d) != POETX_OK) return 0;
+    Carver cv(nullptr);
+    LinearBufs L;
+    plan_linear(cv, d, false, L);
+    if (d->variant == POETX_MEM) cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
+    return cv.off;
+}
+
+int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                     const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
+                     void* stream) {
+    POETX_TRY(check_desc(d));
+    if (d->T == 0) return POETX_OK;
+    if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
+    if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    const size_t need = poetx_linear_fwd_workspace_bytes(d);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws);
+    LinearBufs L;
+    plan_linear(cv, d, false, L);
+    void* h2 = saved;
+    if (d->variant == POETX_MEM) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
+    return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, L.buf[0], L.buf[1], as_stream(stream));
+}
+
+size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {
+    if (check_desc(d) != POETX_OK) return 0;
+    Carver cv(nullptr);
+    LinearBufs L;
+    plan_linear(cv, d, true, L);
+    return cv.off;
+}
+
+int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, const void* Wt, const void* G_R,
+                     const void* G_P, const int32_t* pi_R, const int32_t* pi_P, const void* saved, void* dx,
+                     float* dG_R, float* dG_P, void* ws, size_t ws_bytes, void* stream) {
+    POETX_TRY(check_desc(d));
+    if (!dG_R || !dG_P) return POETX_ERR_INVALID_ARG;
+    const hipStream_t s = as_stream(stream);
+    const int64_t T = d->T, m = d->m, n = d->n, b = d->b;
+    if (T == 0) {
+        HIP_TRY(fill_zero(dG_R, sizeof(float) * (size_t)(m * b), s));
+        HIP_TRY(fill_zero(dG_P, sizeof(float) * (size_t)(n * b), s));
+        return POETX_OK;
+    }
+    if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
+    if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    const size_t need = poetx_linear_bwd_workspace_bytes(d);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws);
+    LinearBufs L;
+    plan_linear(cv, d, true, L);
+    const bool bf = d->dtype == POETX_BF16;
+    void* bufA = L.buf[0];
+    void* bufB = L.buf[1];
+    void* bufC = L.buf[2];
+    // a = x gathered by pi_P (kept for dG_P)
+    HIP_TRY(permute_2d(x, bufA, bf, T, n, nullptr, pi_P, false, s));
+    const void* h2 = saved;
+    if (d->variant == POETX_MEM) {
+        // recompute h1 and h2 from x
+        HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, bufA, G_P, bufB, s));
+        HIP_TRY(gemm(GemmLayout::NT, bf, bf, T, m, n, 1, Mat{bufB, n, 0}, Mat{Wt, n, 0}, bufC, m, 0, s));
+        h2 = bufC;
+    }
+    // dz = dy gathered by pi_R
+    HIP_TRY(permute_2d(dy, bufB, bf, T, m, nullptr, pi_R, false, s));
+    // dG_R[j] = dz_j^T h2_j
+    POETX_TRY(block_grad(bf, T, m, b, bufB, h2, dG_R, L.splits_R, L.kps_R, L.part, s));
+    // dh2 = dz . blockdiag(G_R)
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, m, b, bufB, G_R, bufC, s));
+    // dh1 = dh2 . Wt
+    HIP_TRY(gemm(GemmLayout::NN, bf, bf, T, n, m, 1, Mat{bufC, m, 0}, Mat{Wt, n, 0}, bufB, n, 0, s));
+    // dG_P[j] = dh1_j^T a_j
+    POETX_TRY(block_grad(bf, T, n, b, bufB, bufA, dG_P, L.splits_P, L.kps_P, L.part, s));
+    // da = dh1 . blockdiag(G_P) ; dx = da scattered by pi_P
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, n, b, bufB, G_P, bufC, s));
+    HIP_TRY(permute_2d(bufC, dx, bf, T, n, nullptr, pi_P, true, s));
+    return POETX_OK;
+}
+
+size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d) {
+    if (check_desc(d) != POETX_OK) return 0;
+    const bool bf = d->dtype == POETX_BF16;
+    Carver cv(nullptr);
+    const size_t es = esize(d->dtype);
+    cv.take(es * (size_t)(d->m * d->b));  // G_R
+    cv.take(es * (size_t)(d->n * d->b));  // G_P
+    cv.take(es * (size_t)(d->m * d->n));  // D_R Wt
+    cv.take(es * (size_t)(d->m * d->n));  // D_R Wt D_P
+    cv.take_n<int32_t>(d->m);             // sigma_R
+    cv.take_n<int32_t>(d->n);             // sigma_P
+    cv.take_n<int32_t>(std::max(d->m, d->n));  // inverse scratch
+    cv.take(std::max(cnp_ws(d->m / d->b, d->b, d->k, bf, false), cnp_ws(d->n / d->b, d->b, d->k, bf, false)));
+    return cv.off;
+}
+
+int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, const int32_t* pi_R_old,
+                const int32_t* pi_P_old, const int32_t* pi_R_new, const int32_t* pi_P_new, void* ws,
+                size_t ws_bytes, void* stream) {
+    POETX_TRY(check_desc(d));
+    if (!Wt || !q_R || !q_P || !pi_R_old || !pi_P_old || !pi_R_new || !pi_P_new) return POETX_ERR_INVALID_ARG;
+    const size_t need = poetx_merge_workspace_bytes(d);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    const hipStream_t s = as_stream(stream);
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t m = d->m, n = d->n, b = d->b;
+    const size_t es = esize(d->dtype);
+    Carver cv(ws);
+    void* G_R = cv.take(es * (size_t)(m * b));
+    void* G_P = cv.take(es * (size_t)(n * b));
+    void* W1 = cv.take(es * (size_t)(m * n));
+    void* W2 = cv.take(es * (size_t)(m * n));
+    int32_t* sig_R = cv.take_n<int32_t>(m);
+    int32_t* sig_P = cv.take_n<int32_t>(n);
+    int32_t* inv = cv.take_n<int32_t>(std::max(m, n));
+    char* cnp_base = static_cast<char*>(cv.take(0));
+    {
+        Carver c1(cnp_base);
+        CnpBufs B;
+        plan_cnp(c1, m / b, b, d->k, bf, false, B);
+        POETX_TRY(cnp_forward(q_R, m / b, b, d->k, bf, G_R, bf, B, s));
+    }
+    {
+        Carver c2(cnp_base);
+        CnpBufs B;
+        plan_cnp(c2, n / b, b, d->k, bf, false, B);
+        POETX_TRY(cnp_forward(q_P, n / b, b, d->k, bf, G_P, bf, B, s));
+    }
+    // W1 = diag(G_R) . Wt  (row blocks);  W2 = W1 . diag(G_P)  (column blocks)
+    HIP_TRY(gemm(GemmLayout::NN, bf, bf, b, n, b, m / b, Mat{G_R, b, b * b}, Mat{Wt, n, b * n}, W1, n, b * n, s));
+    HIP_TRY(gemm(GemmLayout::NN, bf, bf, m, b, b, n / b, Mat{W1, n, b}, Mat{G_P, b, b * b}, W2, n, b, s));
+    // Wt'[i][j] = W2[sigma_R[i]][sigma_P[j]], sigma = pi_old^-1 o pi_new
+    HIP_TRY(compose_perm(pi_R_old, pi_R_new, inv, sig_R, m, s));
+    HIP_TRY(compose_perm(pi_P_old, pi_P_new, inv, sig_P, n, s));
+    HIP_TRY(permute_2d(W2, Wt, bf, m, n, sig_R, sig_P, false, s));
+    HIP_TRY(fill_zero(q_R, sizeof(float) * (size_t)(m / b) * (size_t)(b * (b - 1) / 2), s));
+    HIP_TRY(fill_zero(q_P, sizeof(float) * (size_t)(n / b) * (size_t)(b * (b - 1) / 2), s));
+    return POETX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,379 @@
+// Memory-bound kernels of libpoetx: compact skew unpack / pack, the 2-D
+// permutation (gather or scatter of columns, optional row gather), the
+// split-K reduction, the float32 combine used between Cayley-Neumann
+// products, fills and permutation helpers.
+#include <algorithm>
+
+#include "device_common.h"
+#include "elementwise.h"
+
+namespace poetx {
+
+namespace {
+
+// Storage position of Q[r][c], r < c, in the row-major strict upper triangle.
+__device__ __forceinline__ int64_t tri_index(int64_t r, int64_t c, int64_t b) {
+    return r * b - (r * (r + 1)) / 2 + (c - r - 1);
+}
+
+constexpr int kSkewTile = 32;
+
+// Q[j] = unpack(q[j]).  One workgroup per (block, 32 x 32 output tile).  Tiles
+// below the diagonal are produced from the mirrored upper tile staged in LDS,
+// so global reads are contiguous row segments of the triangle and writes are
+// contiguous row segments of Q.
+template <typename T>
+__global__ void __launch_bounds__(256) skew_unpack_kernel(const float* __restrict__ q, T* __restrict__ Q,
+                                                          int b) {
+    __shared__ float tile[kSkewTile][kSkewTile + 1];
+    const int tiles = b / kSkewTile;
+    const int ti = blockIdx.x / tiles;
+    const int tj = blockIdx.x % tiles;
+    const int64_t blk = blockIdx.y;
+    const int64_t ntri = (int64_t)b * (b - 1) / 2;
+    const float* qb = q + blk * ntri;
+    T* Qb = Q + blk * (int64_t)b * b;
+    const int tx = threadIdx.x & 31;
+    const int ty = threadIdx.x >> 5;  // 0..7
+    // the upper tile (min(ti,tj), max(ti,tj)) staged as tile[row][col]
+    const int ui = min(ti, tj), uj = max(ti, tj);
+    for (int rr = ty; rr < kSkewTile; rr += 8) {
+        const int r = ui * kSkewTile + rr;
+        const int c = uj * kSkewTile + tx;
+        tile[rr][tx] = (r < c) ? qb[tri_index(r, c, b)] : 0.f;
+    }
+    __syncthreads();
+    for (int rr = ty; rr < kSkewTile; rr += 8) {
+        const int r = ti * kSkewTile + rr;
+        const int c = tj * kSkewTile + tx;
+        float v;
+        if (ti < tj) v = tile[rr][tx];
+        else if (ti > tj) v = -tile[tx][rr];
+        else v = (rr < tx) ? tile[rr][tx] : (rr > tx ? -tile[tx][rr] : 0.f);
+        store_f32(Qb + (int64_t)r * b + c, v);
+    }
+}
+
+// dq[j][idx(r,c)] = dQ[j][r][c] - dQ[j][c][r] for r < c.  One workgroup per
+// (block, upper 32 x 32 tile); the mirrored tile is staged in LDS.
+__global__ void __launch_bounds__(256) skew_pack_kernel(const float* __restrict__ dQ, float* __restrict__ dq,
+                                                        int b) {
+    __shared__ float up[kSkewTile][kSkewTile + 1];
+    __shared__ float lo[kSkewTile][kSkewTile + 1];
+    const int tiles = b / kSkewTile;
+    const int ti = blockIdx.x / tiles;
+    const int tj = blockIdx.x % tiles;
+    if (ti > tj) return;
+    const int64_t blk = blockIdx.y;
+    const int64_t ntri = (int64_t)b * (b - 1) / 2;
+    const float* G = dQ + blk * (int64_t)b * b;
+    float* out = dq + blk * ntri;
+    const int tx = threadIdx.x & 31;
+    const int ty = threadIdx.x >> 5;
+    for (int rr = ty; rr < kSkewTile; rr += 8) {
+        up[rr][tx] = G[(int64_t)(ti * kSkewTile + rr) * b + tj * kSkewTile + tx];
+        lo[rr][tx] = G[(int64_t)(tj * kSkewTile + rr) * b + ti * kSkewTile + tx];
+    }
+    __syncthreads();
+    for (int rr = ty; rr < kSkewTile; rr += 8) {
+        const int r = ti * kSkewTile + rr;
+        const int c = tj * kSkewTile + tx;
+        if (r < c) out[tri_index(r, c, b)] = up[rr][tx] - lo[tx][rr];
+    }
+}
+
+// Small-block variants (b not a multiple of 32): one thread per element.
+template <typename T>
+__global__ void skew_unpack_simple(const float* __restrict__ q, T* __restrict__ Q, int b, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t bb = (int64_t)b * b;
+    const int64_t blk = i / bb;
+    const int r = (int)((i % bb) / b);
+    const int c = (int)(i % b);
+    const float* qb = q + blk * ((int64_t)b * (b - 1) / 2);
+    float v = 0.f;
+    if (r < c) v = qb[tri_index(r, c, b)];
+    else if (r > c) v = -qb[tri_index(c, r, b)];
+    store_f32(Q + i, v);
+}
+
+__global__ void skew_pack_simple(const float* __restrict__ dQ, float* __restrict__ dq, int b, int64_t nblk) {
+    const int64_t ntri = (int64_t)b * (b - 1) / 2;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nblk * ntri) return;
+    const int64_t blk = i / ntri;
+    int64_t t = i % ntri;
+    // invert idx(r, c): row r holds b - 1 - r entries
+    int r = 0;
+    while (t >= b - 1 - r) { t -= b - 1 - r; ++r; }
+    const int c = r + 1 + (int)t;
+    const float* G = dQ + blk * (int64_t)b * b;
+    dq[i] = G[(int64_t)r * b + c] - G[(int64_t)c * b + r];
+}
+
+// ------------------------------------------------------------- permutation
+// A workgroup owns `rows_per_wg` full rows, staged in LDS: gathers read the
+// row contiguously and pick from LDS; scatters place into LDS and write the
+// row contiguously.  Both global streams are 16-byte vectors.
+template <typename T>
+__global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ src, T* __restrict__ dst,
+                                                        int64_t rows, int cols, const int* __restrict__ row_idx,
+                                                        const int* __restrict__ col_idx, int scatter,
+                                                        int rows_per_wg) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T* buf = reinterpret_cast<T*>(smem_raw);
+    constexpr int V = ElemTraits<T>::kVec;
+    const int chunks = cols / V;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)min<int64_t>(rows_per_wg, rows - row0);
+    const int total = nrows * chunks;
+    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+        const int r = u / chunks;
+        const int c = (u % chunks) * V;
+        const int64_t gr = row0 + r;
+        const int64_t sr = row_idx ? row_idx[gr] : gr;
+        const uint4 v = *reinterpret_cast<const uint4*>(src + sr * cols + c);
+        if (scatter && col_idx) {
+            const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+            for (int i = 0; i < V; ++i) buf[r * cols + col_idx[c + i]] = e[i];
+        } else {
+            *reinterpret_cast<uint4*>(buf + r * cols + c) = v;
+        }
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+        const int r = u / chunks;
+        const int c = (u % chunks) * V;
+        uint4 v;
+        if (scatter || !col_idx) {
+            v = *reinterpret_cast<const uint4*>(buf + r * cols + c);
+        } else {
+            T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+            for (int i = 0; i < V; ++i) e[i] = buf[r * cols + col_idx[c + i]];
+        }
+        *reinterpret_cast<uint4*>(dst + (row0 + r) * cols + c) = v;
+    }
+}
+
+// Rows too long for LDS: element-wise gather / scatter straight from memory.
+template <typename T>
+__global__ void permute_direct(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int64_t cols,
+                               const int* __restrict__ row_idx, const int* __restrict__ col_idx, int scatter) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * cols) return;
+    const int64_t r = i / cols;
+    const int64_t c = i % cols;
+    const int64_t sr = row_idx ? row_idx[r] : r;
+    if (!col_idx) {
+        dst[i] = src[sr * cols + c];
+    } else if (scatter) {
+        dst[r * cols + col_idx[c]] = src[sr * cols + c];
+    } else {
+        dst[i] = src[sr * cols + col_idx[c]];
+    }
+}
+
+// -------------------------------------------------------------- reductions
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, float* __restrict__ out, int64_t count,
+                                     int splits) {
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 >= count) return;
+    if (i4 + 4 <= count && (count & 3) == 0) {
+        float4 s = *reinterpret_cast<const float4*>(part + i4);
+        for (int k = 1; k < splits; ++k) {
+            const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * count + i4);
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        *reinterpret_cast<float4*>(out + i4) = s;
+    } else {
+        for (int64_t i = i4; i < min(count, i4 + 4); ++i) {
+            float s = part[i];
+            for (int k = 1; k < splits; ++k) s += part[(int64_t)k * count + i];
+            out[i] = s;
+        }
+    }
+}
+
+// out = c0*in0 + c1*in1 + c2*in2 + gamma*I over nblk b x b blocks (absent
+// inputs are skipped); written as float32 and/or in the compute dtype.
+template <typename CT>
+__global__ void combine_kernel(int64_t total, int b, const float* __restrict__ in0, float c0,
+                               const float* __restrict__ in1, float c1, const float* __restrict__ in2, float c2,
+                               float gamma, float* __restrict__ out32, CT* __restrict__ outc) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    float v = 0.f;
+    if (in0) v += c0 * in0[i];
+    if (in1) v += c1 * in1[i];
+    if (in2) v += c2 * in2[i];
+    if (gamma != 0.f) {
+        const int64_t e = i % ((int64_t)b * b);
+        if (e / b == e % b) v += gamma;
+    }
+    if (out32) out32[i] = v;
+    if (outc) store_f32(outc + i, v);
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < words) p[i] = 0u;
+}
+
+// sigma[i] = inv_old[pi_new[i]] with inv_old the inverse of pi_old.
+__global__ void invert_perm_kernel(const int* __restrict__ pi, int* __restrict__ inv, int64_t len) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < len) inv[pi[i]] = (int)i;
+}
+
+__global__ void compose_perm_kernel(const int* __restrict__ inv_old, const int* __restrict__ pi_new,
+                                    int* __restrict__ sigma, int64_t len) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < len) sigma[i] = inv_old[pi_new[i]];
+}
+
+__global__ void count_perm_kernel(const int* __restrict__ pi, int* __restrict__ counts, int64_t len,
+                                  int* __restrict__ bad) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= len) return;
+    const int v = pi[i];
+    if (v < 0 || v >= len) { atomicOr(bad, 1); return; }
+    atomicAdd(&counts[v], 1);
+}
+
+__global__ void check_counts_kernel(const int* __restrict__ counts, int64_t len, int* __restrict__ bad) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < len && counts[i] != 1) atomicOr(bad, 1);
+}
+
+__global__ void finish_check_kernel(const int* __restrict__ bad, int* __restrict__ ok) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) ok[0] = bad[0] ? 0 : 1;
+}
+
+constexpr int64_t kMaxGridY = 65535;
+
+inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+}  // namespace
+
+hipError_t skew_unpack(const float* q, void* Q, bool bf16, int64_t nblk, int b, hipStream_t s) {
+    if (nblk <= 0) return hipSuccess;
+    if (b % kSkewTile == 0) {
+        const int64_t ntri = (int64_t)b * (b - 1) / 2, bb = (int64_t)b * b;
+        for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGridY) {
+            const unsigned nz = (unsigned)std::min<int64_t>(kMaxGridY, nblk - z0);
+            dim3 grid((b / kSkewTile) * (b / kSkewTile), nz);
+            if (bf16)
+                hipLaunchKernelGGL(skew_unpack_kernel<bf16_t>, grid, dim3(256), 0, s, q + z0 * ntri,
+                                   (bf16_t*)Q + z0 * bb, b);
+            else
+                hipLaunchKernelGGL(skew_unpack_kernel<float>, grid, dim3(256), 0, s, q + z0 * ntri,
+                                   (float*)Q + z0 * bb, b);
+        }
+    } else {
+        const int64_t total = nblk * (int64_t)b * b;
+        if (bf16) hipLaunchKernelGGL(skew_unpack_simple<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s, q,
+                                     (bf16_t*)Q, b, total);
+        else hipLaunchKernelGGL(skew_unpack_simple<float>, dim3(blocks_for(total, 256)), dim3(256), 0, s, q,
+                                (float*)Q, b, total);
+    }
+    return hipGetLastError();
+}
+
+hipError_t skew_pack(const float* dQ, float* dq, int64_t nblk, int b, hipStream_t s) {
+    if (nblk <= 0) return hipSuccess;
+    if (b % kSkewTile == 0) {
+        const int64_t ntri = (int64_t)b * (b - 1) / 2, bb = (int64_t)b * b;
+        for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGridY) {
+            const unsigned nz = (unsigned)std::min<int64_t>(kMaxGridY, nblk - z0);
+            dim3 grid((b / kSkewTile) * (b / kSkewTile), nz);
+            hipLaunchKernelGGL(skew_pack_kernel, grid, dim3(256), 0, s, dQ + z0 * bb, dq + z0 * ntri, b);
+        }
+    } else {
+        const int64_t total = nblk * ((int64_t)b * (b - 1) / 2);
+        hipLaunchKernelGGL(skew_pack_simple, dim3(blocks_for(total, 256)), dim3(256), 0, s, dQ, dq, b, nblk);
+    }
+    return hipGetLastError();
+}
+
+size_t permute_lds_row_limit_bytes() { return 64 * 1024; }
+
+hipError_t permute_2d(const void* src, void* dst, bool bf16, int64_t rows, int64_t cols, const int* row_idx,
+                      const int* col_idx, bool scatter, hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    const int esz = bf16 ? 2 : 4;
+    const int64_t row_bytes = cols * esz;
+    if (row_bytes <= (int64_t)permute_lds_row_limit_bytes() && (cols % (16 / esz)) == 0) {
+        // ~32 KB of rows per workgroup (at least one row).
+        int rpw = (int)std::max<int64_t>(1, (32 * 1024) / row_bytes);
+        rpw = (int)std::min<int64_t>(rpw, rows);
+        const size_t smem = (size_t)rpw * row_bytes;
+        const unsigned grid = (unsigned)((rows + rpw - 1) / rpw);
+        if (bf16)
+            hipLaunchKernelGGL(permute_rows_lds<bf16_t>, dim3(grid), dim3(256), smem, s, (const bf16_t*)src,
+                               (bf16_t*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
+        else
+            hipLaunchKernelGGL(permute_rows_lds<float>, dim3(grid), dim3(256), smem, s, (const float*)src,
+                               (float*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
+    } else {
+        const int64_t total = rows * cols;
+        if (bf16)
+            hipLaunchKernelGGL(permute_direct<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s,
+                               (const bf16_t*)src, (bf16_t*)dst, rows, cols, row_idx, col_idx, scatter ? 1 : 0);
+        else
+            hipLaunchKernelGGL(permute_direct<float>, dim3(blocks_for(total, 256)), dim3(256), 0, s,
+                               (const float*)src, (float*)dst, rows, cols, row_idx, col_idx, scatter ? 1 : 0);
+    }
+    return hipGetLastError();
+}
+
+hipError_t splitk_reduce(const float* part, float* out, int64_t count, int splits, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks_for((count + 3) / 4, 256)), dim3(256), 0, s, part, out,
+                       count, splits);
+    return hipGetLastError();
+}
+
+hipError_t combine(int64_t nblk, int b, const float* in0, float c0, const float* in1, float c1, const float* in2,
+                   float c2, float gamma, float* out32, void* outc, bool outc_bf16, hipStream_t s) {
+    const int64_t total = nblk * (int64_t)b * b;
+    if (total <= 0) return hipSuccess;
+    if (outc_bf16)
+        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s, total, b, in0, c0,
+                           in1, c1, in2, c2, gamma, out32, (bf16_t*)outc);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks_for(total, 256)), dim3(256), 0, s, total, b, in0, c0,
+                           in1, c1, in2, c2, gamma, out32, (float*)outc);
+    return hipGetLastError();
+}
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
+    const int64_t words = (int64_t)(bytes / 4);
+    if (words <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(words, 256)), dim3(256), 0, s, (uint32_t*)p, words);
+    return hipGetLastError();
+}
+
+hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int* sigma, int64_t len,
+                        hipStream_t s) {
+    if (len <= 0) return hipSuccess;
+    hipLaunchKernelGGL(invert_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi_old, inv_tmp, len);
+    hipLaunchKernelGGL(compose_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, inv_tmp, pi_new, sigma,
+                       len);
+    return hipGetLastError();
+}
+
+hipError_t check_perm(const int* pi, int64_t len, int* ok, int* counts, int* bad, hipStream_t s) {
+    hipError_t e = fill_zero(counts, (size_t)(len + 1) * sizeof(int), s);
+    if (e != hipSuccess) return e;
+    if (len > 0) {
+        hipLaunchKernelGGL(count_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi, counts, len, bad);
+        hipLaunchKernelGGL(check_counts_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, counts, len, bad);
+    }
+    hipLaunchKernelGGL(finish_check_kernel, dim3(1), dim3(64), 0, s, bad, ok);
+    return hipGetLastError();
+}
+
+}  // namespace poetx

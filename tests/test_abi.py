@@ -1,0 +1,122 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching HIP (no GPU needed)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "poetx.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(poetx_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from orthogonal_equivalence_poet_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from orthogonal_equivalence_poet_amd import build
+        build.build(verbose=False)
+    binding.load()
+    return binding
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = _declared()
+    assert len(names) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (poetx_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(B.EXPORTS) == set(names)
+    lib = B.load()
+    for n in names:
+        getattr(lib, n)
+
+
+def test_version_and_status_strings(B):
+    assert "gfx950" in B.poetx_version()
+    lib = B.load()
+    assert lib.poetx_status_string(0) == b"ok"
+    assert lib.poetx_status_string(4) == b"workspace too small"
+    assert lib.poetx_status_string(99) == b"unknown status"
+
+
+def _d(B, **kw):
+    base = dict(T=32, m=64, n=64, b=16, k=3, dtype=B.POETX_F32, variant=B.POETX_FAST)
+    base.update(kw)
+    return B.desc(**base)
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b=24), 3), (dict(b=8), 3), (dict(b=2048), 3), (dict(b=0), 2),
+    (dict(m=72), 2), (dict(n=40), 2), (dict(T=-1), 2),
+    (dict(k=0), 3), (dict(k=9), 3), (dict(dtype=7), 1), (dict(variant=5), 1),
+])
+def test_linear_fwd_rejects_bad_desc(B, kw, status):
+    lib = B.load()
+    d = _d(B, **kw)
+    st = lib.poetx_linear_fwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+    assert lib.poetx_linear_fwd_workspace_bytes(C.byref(d)) == 0
+
+
+def test_null_pointers_and_small_workspace(B):
+    lib = B.load()
+    d = _d(B)
+    need = lib.poetx_linear_fwd_workspace_bytes(C.byref(d))
+    assert need > 0
+    assert lib.poetx_linear_fwd(C.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+    # fast needs the saved buffer
+    assert lib.poetx_linear_fwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None) == 1
+    assert lib.poetx_linear_fwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                None) == 4
+    nb = lib.poetx_linear_bwd_workspace_bytes(C.byref(d))
+    assert lib.poetx_linear_bwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                FAKE, nb, None) == 1
+    assert lib.poetx_linear_bwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, nb - 1, None) == 4
+    assert lib.poetx_linear_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+
+
+def test_empty_batch_forward_is_a_no_op(B):
+    lib = B.load()
+    d = _d(B, T=0)
+    # returns before any HIP call: nothing to compute
+    assert lib.poetx_linear_fwd(C.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_cnp_and_skew_validation(B):
+    lib = B.load()
+    assert lib.poetx_cnp_fwd(FAKE, 4, 24, 3, FAKE, 0, FAKE, 1 << 30, None) == 3
+    assert lib.poetx_cnp_fwd(FAKE, 4, 16, 0, FAKE, 0, FAKE, 1 << 30, None) == 3
+    assert lib.poetx_cnp_fwd(FAKE, -1, 16, 3, FAKE, 0, FAKE, 1 << 30, None) == 2
+    assert lib.poetx_cnp_fwd(FAKE, 4, 16, 3, FAKE, 5, FAKE, 1 << 30, None) == 1
+    need = lib.poetx_cnp_fwd_workspace_bytes(4, 16, 3, 0)
+    assert need > 0
+    assert lib.poetx_cnp_fwd(FAKE, 4, 16, 3, FAKE, 0, FAKE, need - 1, None) == 4
+    assert lib.poetx_cnp_fwd(None, 4, 16, 3, FAKE, 0, FAKE, need, None) == 1
+    assert lib.poetx_cnp_fwd(None, 0, 16, 3, None, 0, None, 0, None) == 0  # empty batch
+    assert lib.poetx_cnp_bwd(FAKE, FAKE, 4, 16, 3, None, 0, FAKE, 1 << 30, None) == 1
+    assert lib.poetx_skew_unpack(FAKE, FAKE, 3, 4, 16, None) == 1
+    assert lib.poetx_skew_pack(FAKE, FAKE, 4, 0, None) == 2
+    assert lib.poetx_permute(FAKE, FAKE, 0, 4, 6, None, None, 0, None) == 2  # 6 f32 columns: not 16-byte rows
+    assert lib.poetx_check_perm(FAKE, 10, FAKE, FAKE, 3, None) == 4
+
+
+def test_workspace_sizes_scale(B):
+    lib = B.load()
+    d = B.desc(2048, 4096, 4096, 256, 3, B.POETX_BF16, B.POETX_FAST)
+    assert lib.poetx_linear_saved_bytes(C.byref(d)) == 2048 * 4096 * 2
+    dm = B.desc(2048, 4096, 4096, 256, 3, B.POETX_BF16, B.POETX_MEM)
+    assert lib.poetx_linear_saved_bytes(C.byref(dm)) == 0
+    assert lib.poetx_linear_bwd_workspace_bytes(C.byref(dm)) >= 3 * 2048 * 4096 * 2
+    assert lib.poetx_cnp_fwd_workspace_bytes(64, 256, 3, 1) == 2 * lib.poetx_cnp_fwd_workspace_bytes(32, 256, 3, 1)
