@@ -187,6 +187,32 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P,
                 const int32_t* pi_R_old, const int32_t* pi_P_old, const int32_t* pi_R_new,
                 const int32_t* pi_P_new, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- building blocks (stages) */
+/* The MFMA GEMM every stage of the layer runs on, exposed for composition and
+ * per-stage measurement.  C[z] = op(A[z]) op(B[z]) for z < batch, with
+ *   POETX_GEMM_NT:  A [M][K] (lda), B [N][K] (ldb)      C = A B^T
+ *   POETX_GEMM_NN:  A [M][K] (lda), B [K][N] (ldb)      C = A B
+ *   POETX_GEMM_TN:  A [K][M] (lda), B [K][N] (ldb)      C = A^T B
+ * C [M][N] (ldc), all of `dtype`, float32 accumulation; strides are the
+ * element offsets between batch entries.  The contiguous extent of every
+ * operand, every leading dimension and every stride must be a multiple of
+ * 16 bytes.  With dense != 0 the call uses the tile schedule of the layer's
+ * dense Wt products (batch must be 1), otherwise that of the block products. */
+enum { POETX_GEMM_NT = 0, POETX_GEMM_NN = 1, POETX_GEMM_TN = 2 };
+int poetx_gemm(int layout, int dtype, int dense, int64_t M, int64_t N, int64_t K, int64_t batch,
+               const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
+               void* C, int64_t ldc, int64_t strideC, void* stream);
+
+/* Block gradients of the batch-wise block products (the backward of the
+ * review's "batch-wise block-diagonal matmul"): for j < d/b
+ *   dG[j] = A[:, jb:(j+1)b]^T B[:, jb:(j+1)b]      (sum over the T rows)
+ * A, B: dtype [T, d]; dG: float32 [d/b, b, b].  The token axis is split over
+ * workgroups and the partial sums are added in a fixed order (deterministic).
+ * T == 0 writes zeros. */
+size_t poetx_block_grad_workspace_bytes(int64_t T, int64_t d, int64_t b, int dtype);
+int poetx_block_grad(int dtype, int64_t T, int64_t d, int64_t b, const void* A, const void* B, float* dG,
+                     void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libpoetx.so")
 POETX_OK, POETX_ERR_INVALID_ARG, POETX_ERR_SHAPE, POETX_ERR_UNSUPPORTED, POETX_ERR_WORKSPACE, POETX_ERR_HIP = range(6)
 POETX_F32, POETX_BF16 = 0, 1
 POETX_FAST, POETX_MEM = 0, 1
+POETX_GEMM_NT, POETX_GEMM_NN, POETX_GEMM_TN = 0, 1, 2
 
 EXPORTS = [
     "poetx_version", "poetx_status_string", "poetx_last_hip_error",
@@ -29,6 +30,7 @@ EXPORTS = [
     "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd",
     "poetx_linear_bwd_workspace_bytes", "poetx_linear_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
+    "poetx_gemm", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
 ]
 
 
@@ -68,6 +70,10 @@ _SIGS = {
     "poetx_linear_bwd": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_merge_workspace_bytes": ([_DP], _SZ),
     "poetx_merge": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
+    "poetx_gemm": ([_I32, _I32, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64,
+                    _VP], _I32),
+    "poetx_block_grad_workspace_bytes": ([_I64, _I64, _I64, _I32], _SZ),
+    "poetx_block_grad": ([_I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
 }
 
 
@@ -220,3 +226,22 @@ def poetx_merge(d: LinearDesc, Wt, q_R, q_P, pi_R_old, pi_P_old, pi_R_new, pi_P_
     _check("poetx_merge", load().poetx_merge(C.byref(d), _ptr(Wt), _ptr(q_R), _ptr(q_P), _ptr(pi_R_old),
                                              _ptr(pi_P_old), _ptr(pi_R_new), _ptr(pi_P_new), p, nbytes,
                                              _stream(stream)))
+
+
+def poetx_gemm(layout, A, B, C, M, N, K, batch=1, lda=None, ldb=None, ldc=None, strideA=0, strideB=0, strideC=0,
+               dense=False, stream=None):
+    lda = lda if lda is not None else (K if layout != POETX_GEMM_TN else M)
+    ldb = ldb if ldb is not None else (K if layout == POETX_GEMM_NT else N)
+    ldc = ldc if ldc is not None else N
+    _check("poetx_gemm", load().poetx_gemm(layout, _dtype_code(C), int(bool(dense)), M, N, K, batch, _ptr(A), lda,
+                                           strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC, _stream(stream)))
+
+
+def poetx_block_grad_workspace_bytes(T, d, b, dtype) -> int:
+    return load().poetx_block_grad_workspace_bytes(T, d, b, dtype)
+
+
+def poetx_block_grad(A, B, dG, T, d, b, ws=None, stream=None):
+    p, nbytes = _ws(ws)
+    _check("poetx_block_grad", load().poetx_block_grad(_dtype_code(A), T, d, b, _ptr(A), _ptr(B), _ptr(dG), p,
+                                                       nbytes, _stream(stream)))

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <string>
 
+#include "dense_gemm.h"
 #include "elementwise.h"
 #include "gemm.h"
 #include "poetx.h"
@@ -100,7 +101,7 @@ struct Mat {
 hipError_t gemm(GemmLayout layout, bool cbf16, bool obf16, int64_t M, int64_t N, int64_t K, int64_t batch, Mat A,
                 Mat B, void* C, int64_t ldc, int64_t sC, hipStream_t s, float alpha = 1.f,
                 const float* cin1 = nullptr, float beta1 = 0.f, const float* cin2 = nullptr, float beta2 = 0.f,
-                float gamma = 0.f, void* C2 = nullptr) {
+                float gamma = 0.f, void* C2 = nullptr, bool dense = false) {
     GemmArgs g;
     g.A = A.p; g.lda = A.ld; g.strideA = A.stride;
     g.B = B.p; g.ldb = B.ld; g.strideB = B.stride;
@@ -113,7 +114,17 @@ hipError_t gemm(GemmLayout layout, bool cbf16, bool obf16, int64_t M, int64_t N,
     g.batch = (int)batch;
     g.splits = 1;
     g.k_per_split = (int)std::max<int64_t>(K, 1);
+    (void)dense;
     return gemm_launch(g, layout, pick_tile(cbf16, M, N, batch), cbf16, obf16, s);
+}
+
+// The dense Wt products of the chain: [T, K] x Wt (NT forward, NN backward).
+hipError_t dense_gemm(GemmLayout layout, bool bf, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, void* C, int64_t ldc, hipStream_t s) {
+    if (bf && layout != GemmLayout::TN && dense_gemm_supported(M, N, K, lda, ldb) && ldc % 8 == 0)
+        return dense_gemm_bf16(layout == GemmLayout::NN, A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, s);
+    return gemm(layout, bf, bf, M, N, K, 1, Mat{A, lda, 0}, Mat{B, ldb, 0}, C, ldc, 0, s, 1.f, nullptr, 0, nullptr,
+                0, 0, nullptr, true);
 }
 
 // Square b x b block products over nblk blocks stored back to back.
@@ -386,7 +397,7 @@ int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, co
     HIP_TRY(permute_2d(x, buf_a, bf, T, n, nullptr, pi_P, false, s));
     HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, buf_a, G_P, buf_b, s));
     // h2 = h1 . Wt^T
-    HIP_TRY(gemm(GemmLayout::NT, bf, bf, T, m, n, 1, Mat{buf_b, n, 0}, Mat{Wt, n, 0}, h2_out, m, 0, s));
+    HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, buf_b, n, Wt, n, h2_out, m, s));
     // z = h2 . blockdiag(G_R)^T ; y = z scattered by pi_R
     HIP_TRY(block_apply(GemmLayout::NT, bf, T, m, b, h2_out, G_R, buf_b, s));
     HIP_TRY(permute_2d(buf_b, y, bf, T, m, nullptr, pi_R, true, s));
@@ -590,7 +601,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     if (d->variant == POETX_MEM) {
         // recompute h1 and h2 from x
         HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, bufA, G_P, bufB, s));
-        HIP_TRY(gemm(GemmLayout::NT, bf, bf, T, m, n, 1, Mat{bufB, n, 0}, Mat{Wt, n, 0}, bufC, m, 0, s));
+        HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, bufB, n, Wt, n, bufC, m, s));
         h2 = bufC;
     }
     // dz = dy gathered by pi_R
@@ -600,7 +611,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     // dh2 = dz . blockdiag(G_R)
     HIP_TRY(block_apply(GemmLayout::NN, bf, T, m, b, bufB, G_R, bufC, s));
     // dh1 = dh2 . Wt
-    HIP_TRY(gemm(GemmLayout::NN, bf, bf, T, n, m, 1, Mat{bufC, m, 0}, Mat{Wt, n, 0}, bufB, n, 0, s));
+    HIP_TRY(dense_gemm(GemmLayout::NN, bf, T, n, m, bufC, m, Wt, n, bufB, n, s));
     // dG_P[j] = dh1_j^T a_j
     POETX_TRY(block_grad(bf, T, n, b, bufB, bufA, dG_P, L.splits_P, L.kps_P, L.part, s));
     // da = dh1 . blockdiag(G_P) ; dx = da scattered by pi_P
@@ -668,6 +679,67 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
     HIP_TRY(fill_zero(q_R, sizeof(float) * (size_t)(m / b) * (size_t)(b * (b - 1) / 2), s));
     HIP_TRY(fill_zero(q_P, sizeof(float) * (size_t)(n / b) * (size_t)(b * (b - 1) / 2), s));
     return POETX_OK;
+}
+
+int poetx_gemm(int layout, int dtype, int dense, int64_t M, int64_t N, int64_t K, int64_t batch, const void* A,
+               int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB, void* C, int64_t ldc,
+               int64_t strideC, void* stream) {
+    if (!dtype_ok(dtype) || layout < POETX_GEMM_NT || layout > POETX_GEMM_TN) return POETX_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent ||
+        batch > kMaxExtent)
+        return POETX_ERR_SHAPE;
+    if (dense && batch > 1) return POETX_ERR_SHAPE;
+    if (M == 0 || N == 0 || batch == 0) return POETX_OK;
+    if (!A || !B || !C) return POETX_ERR_INVALID_ARG;
+    const int64_t vec = 16 / (int64_t)esize(dtype);
+    const bool a_kmajor = layout != POETX_GEMM_TN;
+    const bool b_kmajor = layout == POETX_GEMM_NT;
+    const int64_t a_contig = a_kmajor ? K : M, b_contig = b_kmajor ? K : N;
+    if (a_contig % vec || b_contig % vec || lda % vec || ldb % vec || strideA % vec || strideB % vec)
+        return POETX_ERR_SHAPE;
+    if (lda < a_contig || ldb < b_contig || ldc < N) return POETX_ERR_SHAPE;
+    if (((uintptr_t)A | (uintptr_t)B) & 15) return POETX_ERR_INVALID_ARG;
+    const GemmLayout L = layout == POETX_GEMM_NT ? GemmLayout::NT : layout == POETX_GEMM_NN ? GemmLayout::NN
+                                                                                          : GemmLayout::TN;
+    const bool bf = dtype == POETX_BF16;
+    if (dense) {
+        HIP_TRY(dense_gemm(L, bf, M, N, K, A, lda, B, ldb, C, ldc, as_stream(stream)));
+    } else {
+        HIP_TRY(gemm(L, bf, bf, M, N, K, batch, Mat{A, lda, strideA}, Mat{B, ldb, strideB}, C, ldc, strideC,
+                     as_stream(stream)));
+    }
+    return POETX_OK;
+}
+
+size_t poetx_block_grad_workspace_bytes(int64_t T, int64_t d, int64_t b, int dtype) {
+    if (!dtype_ok(dtype) || check_block(b) != POETX_OK || T < 0 || d <= 0 || d % b || T > kMaxExtent ||
+        d > kMaxExtent)
+        return 0;
+    int splits;
+    int64_t kps;
+    plan_splits(T, b, d / b, dtype == POETX_BF16, splits, kps);
+    return splits > 1 ? sizeof(float) * (size_t)(splits * d * b) : 0;
+}
+
+int poetx_block_grad(int dtype, int64_t T, int64_t d, int64_t b, const void* A, const void* B, float* dG, void* ws,
+                     size_t ws_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    if (T < 0 || d <= 0 || d % b || T > kMaxExtent || d > kMaxExtent) return POETX_ERR_SHAPE;
+    if (!dG) return POETX_ERR_INVALID_ARG;
+    const hipStream_t s = as_stream(stream);
+    if (T == 0) {
+        HIP_TRY(fill_zero(dG, sizeof(float) * (size_t)(d * b), s));
+        return POETX_OK;
+    }
+    if (!A || !B) return POETX_ERR_INVALID_ARG;
+    const size_t need = poetx_block_grad_workspace_bytes(T, d, b, dtype);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (need && !ws) return POETX_ERR_INVALID_ARG;
+    int splits;
+    int64_t kps;
+    plan_splits(T, b, d / b, dtype == POETX_BF16, splits, kps);
+    return block_grad(dtype == POETX_BF16, T, d, b, A, B, dG, splits, kps, static_cast<float*>(ws), s);
 }
 
 }  // extern "C"

@@ -60,27 +60,38 @@ struct Stager {
     // the tile; k0 = first k; rows_total / K bound the valid region.
     __device__ __forceinline__ void load(const CT* __restrict__ src, int64_t ld, int row0,
                                          int rows_total, int k0, int K, int tid) {
+        // Rows past rows_total read the last valid row (their results are never
+        // stored); k past K must contribute zero, so only a ragged k-tile is
+        // predicated (a uniform branch).
+        if (k0 + BK <= K) load_impl<false>(src, ld, row0, rows_total, k0, K, tid);
+        else load_impl<true>(src, ld, row0, rows_total, k0, K, tid);
+    }
+
+    template <bool RAGGED_K>
+    __device__ __forceinline__ void load_impl(const CT* __restrict__ src, int64_t ld, int row0,
+                                              int rows_total, int k0, int K, int tid) {
 #pragma unroll
         for (int u = 0; u < kPerThread; ++u) {
             const int unit = tid + u * THREADS;
+            const bool live = (kUnits % THREADS == 0) || unit < kUnits;
             if (KMAJOR) {
                 const int row = unit / (BK / kVec);
                 const int kc = unit % (BK / kVec);
-                const int gr = row0 + row;
+                const int gr = min(row0 + row, rows_total - 1);
                 const int gk = k0 + kc * kVec;
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if ((kUnits % THREADS == 0 || unit < kUnits) && gr < rows_total && gk < K)
+                if (live && (!RAGGED_K || gk < K))
                     v = *reinterpret_cast<const uint4*>(src + (int64_t)gr * ld + gk);
                 r[u] = v;
             } else {
                 const int mg = unit % (ROWS / kVec);
                 const int kg = unit / (ROWS / kVec);
-                const int gm = row0 + mg * kVec;
+                const int gm = min(row0 + mg * kVec, rows_total - kVec);
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) {
                     const int gk = k0 + kg * kVec + e;
                     uint4 v = make_uint4(0, 0, 0, 0);
-                    if ((kUnits % THREADS == 0 || unit < kUnits) && gm < rows_total && gk < K)
+                    if (live && (!RAGGED_K || gk < K))
                         v = *reinterpret_cast<const uint4*>(src + (int64_t)gk * ld + gm);
                     r[u * kVec + e] = v;
                 }
@@ -154,8 +165,16 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
     tn = in_group / gm;
 }
 
+// Register budget: the Large tile's 110.6 KB of LDS allows one workgroup (one
+// wave per SIMD) per CU, so it may use the whole register file; the others run
+// two or more workgroups per CU.
+template <int BM, int BN> struct WavesPerEu {
+    static constexpr int lo = (BM * BN >= 256 * 128) ? 1 : 2;
+    static constexpr int hi = (BM * BN >= 256 * 128) ? 1 : 4;
+};
+
 template <typename CT, typename OutT, bool A_KMAJOR, bool B_KMAJOR, int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(WM* WN * 64)
+__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WavesPerEu<BM, BN>::lo, WavesPerEu<BM, BN>::hi)))
 gemm_kernel(const GemmArgs p) {
     using Cfg = TileCfg<CT, BM, BN, WM, WN>;
     constexpr int BK = Cfg::BK;
@@ -196,11 +215,18 @@ gemm_kernel(const GemmArgs p) {
 
     constexpr int kBufElems = (BM + BN) * RE;   // one stage: A tile then B tile
 
+    // One register stage, two LDS stages: after the MFMAs of k-tile kt the
+    // registers holding tile kt+1 go to LDS and the loads of tile kt+2 are
+    // issued at once, so every load has a whole k-tile of MFMA work to land.
     if (ntiles_k > 0) {
         sa.load(A, p.lda, tm * BM, p.M, k_begin, k_end, tid);
         sb.load(B, p.ldb, tn * BN, p.N, k_begin, k_end, tid);
         sa.store(lds, tid);
         sb.store(lds + BM * RE, tid);
+        if (ntiles_k > 1) {
+            sa.load(A, p.lda, tm * BM, p.M, k_begin + BK, k_end, tid);
+            sb.load(B, p.ldb, tn * BN, p.N, k_begin + BK, k_end, tid);
+        }
     }
     __syncthreads();
 
@@ -208,12 +234,6 @@ gemm_kernel(const GemmArgs p) {
     const int frag_k = (lane >> 5) * Cfg::kVec;
     for (int kt = 0; kt < ntiles_k; ++kt) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < ntiles_k;
-        if (more) {
-            const int k0 = k_begin + (kt + 1) * BK;
-            sa.load(A, p.lda, tm * BM, p.M, k0, k_end, tid);
-            sb.load(B, p.ldb, tn * BN, p.N, k0, k_end, tid);
-        }
         const CT* as = lds + cur * kBufElems + (wm * Cfg::WTM + frag_row) * RE + frag_k;
         const CT* bs = lds + cur * kBufElems + BM * RE + (wn * Cfg::WTN + frag_row) * RE + frag_k;
 #pragma unroll
@@ -230,9 +250,14 @@ gemm_kernel(const GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < Cfg::NJ; ++j) Mfma32<CT>::run(af[i], bfr[j], acc[i][j]);
         }
-        if (more) {
+        if (kt + 1 < ntiles_k) {
             sa.store(lds + (cur ^ 1) * kBufElems, tid);
             sb.store(lds + (cur ^ 1) * kBufElems + BM * RE, tid);
+            if (kt + 2 < ntiles_k) {
+                const int k0 = k_begin + (kt + 2) * BK;
+                sa.load(A, p.lda, tm * BM, p.M, k0, k_end, tid);
+                sb.load(B, p.ldb, tn * BN, p.N, k0, k_end, tid);
+            }
         }
         __syncthreads();
     }
@@ -246,22 +271,39 @@ gemm_kernel(const GemmArgs p) {
     const int64_t zi2 = (int64_t)z * p.strideCin2;
     const int col_base = tn * BN + wn * Cfg::WTN + (lane & 31);
     const int row_base = tm * BM + wm * Cfg::WTM + (lane >> 5) * 4;
-#pragma unroll
-    for (int i = 0; i < Cfg::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
+    const bool plain = !p.Cin1 && !p.Cin2 && !C2 && p.gamma == 0.f && p.alpha == 1.f;
+    if (plain) {
+        OutT* Cz = C + zc;
+#pragma clang loop unroll(full)
+        for (int i = 0; i < Cfg::MI; ++i)
+#pragma clang loop unroll(full)
+            for (int j = 0; j < Cfg::NJ; ++j) {
                 const int col = col_base + j * 32;
-                if (row >= p.M || col >= p.N) continue;
-                float v = p.alpha * acc[i][j][r];
-                if (p.Cin1) v += p.beta1 * p.Cin1[zi1 + (int64_t)row * p.ldcin1 + col];
-                if (p.Cin2) v += p.beta2 * p.Cin2[zi2 + (int64_t)row * p.ldcin2 + col];
-                if (row == col) v += p.gamma;
-                if (C) store_f32(C + zc + (int64_t)row * p.ldc + col, v);
-                if (C2) store_f32(C2 + zc2 + (int64_t)row * p.ldc2 + col, v);
+#pragma clang loop unroll(full)
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
+                    if (row < p.M && col < p.N) store_f32(Cz + (int64_t)row * p.ldc + col, acc[i][j][r]);
+                }
             }
+    } else {
+#pragma clang loop unroll(full)
+        for (int i = 0; i < Cfg::MI; ++i)
+#pragma clang loop unroll(full)
+            for (int j = 0; j < Cfg::NJ; ++j) {
+                const int col = col_base + j * 32;
+#pragma clang loop unroll(full)
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
+                    if (row >= p.M || col >= p.N) continue;
+                    float v = p.alpha * acc[i][j][r];
+                    if (p.Cin1) v += p.beta1 * p.Cin1[zi1 + (int64_t)row * p.ldcin1 + col];
+                    if (p.Cin2) v += p.beta2 * p.Cin2[zi2 + (int64_t)row * p.ldcin2 + col];
+                    if (row == col) v += p.gamma;
+                    if (C) store_f32(C + zc + (int64_t)row * p.ldc + col, v);
+                    if (C2) store_f32(C2 + zc2 + (int64_t)row * p.ldc2 + col, v);
+                }
+            }
+    }
 }
 
 template <typename CT, typename OutT, bool AK, bool BKM, int BM, int BN, int WM, int WN>

@@ -276,3 +276,49 @@ def test_merge_preserves_layer_output():
     g.pi_P = dev_i32(inp["pi_P_new"])
     y1 = host(g.forward())
     assert rel_fro(y1, y0) <= 1e-5
+
+
+# --------------------------------------------------------- building blocks
+GEMM_CASES = [
+    # layout, dense, M, N, K, dtype
+    ("NT", True, 2048, 4096, 4096, "bf16"),
+    ("NN", True, 2048, 4096, 4096, "bf16"),
+    ("NT", True, 300, 1024, 512, "bf16"),     # ragged M, several tiles
+    ("NN", True, 77, 136, 320, "bf16"),       # ragged M and N
+    ("NT", False, 333, 256, 256, "bf16"),
+    ("NN", False, 333, 256, 256, "bf16"),
+    ("TN", False, 256, 256, 999, "bf16"),     # ragged K (token axis)
+    ("NT", False, 100, 96, 80, "f32"),
+    ("TN", False, 64, 48, 37, "f32"),
+]
+
+
+@pytest.mark.parametrize("layout,dense,M,N,K,dtype", GEMM_CASES)
+def test_gemm_parity(layout, dense, M, N, K, dtype):
+    ash = (M, K) if layout != "TN" else (K, M)
+    bsh = (N, K) if layout == "NT" else (K, N)
+    A = I.gaussian(ash, 1.0, dtype, 400, M, K)
+    Bm = I.gaussian(bsh, 1.0, dtype, 401, N, K)
+    C = torch.empty((M, N), dtype=tdtype(dtype), device=DEV)
+    code_l = {"NT": B.POETX_GEMM_NT, "NN": B.POETX_GEMM_NN, "TN": B.POETX_GEMM_TN}[layout]
+    B.poetx_gemm(code_l, dev(A, dtype), dev(Bm, dtype), C, M, N, K, dense=dense)
+    a64, b64 = A.astype(np.float64), Bm.astype(np.float64)
+    ref = {"NT": lambda: a64 @ b64.T, "NN": lambda: a64 @ b64, "TN": lambda: a64.T @ b64}[layout]()
+    # bf16 output rounding (2^-9) on top of float32 accumulation
+    assert rel_fro(host(C), ref) <= (4e-3 if dtype == "bf16" else 1e-6)
+
+
+@pytest.mark.parametrize("T,d,b,dtype", [(2048, 4096, 256, "bf16"), (777, 512, 128, "bf16"), (50, 96, 32, "f32"),
+                                         (0, 256, 64, "bf16")])
+def test_block_grad_parity(T, d, b, dtype):
+    A = I.gaussian((T, d), 1.0, dtype, 402, T, d)
+    Bm = I.gaussian((T, d), 1.0, dtype, 403, T, d)
+    dG = torch.full((d // b, b, b), 3.0, dtype=torch.float32, device=DEV)
+    ws = B.workspace(B.poetx_block_grad_workspace_bytes(T, d, b, code(dtype)))
+    B.poetx_block_grad(dev(A, dtype), dev(Bm, dtype), dG, T, d, b, ws)
+    a64, b64 = A.astype(np.float64), Bm.astype(np.float64)
+    ref = np.stack([a64[:, j * b:(j + 1) * b].T @ b64[:, j * b:(j + 1) * b] for j in range(d // b)])
+    if T == 0:
+        assert not dG.any()
+    else:
+        assert rel_fro(host(dG), ref) <= (1e-5 if dtype == "f32" else 1e-5)
