@@ -81,14 +81,16 @@ int check_desc(const poetx_linear_desc* d) {
 }
 
 // ------------------------------------------------------------- GEMM helpers
-GemmTile pick_tile(bool bf16, int64_t M, int64_t N, int64_t batch_tiles_hint) {
-    (void)batch_tiles_hint;
+// Largest workgroup tile that still gives about one workgroup per CU (256 CUs);
+// small problems fall through to the 64 x 64 tile.
+GemmTile pick_tile(bool bf16, int64_t M, int64_t N, int64_t batch) {
+    auto wgs = [&](int64_t tm, int64_t tn) { return ((M + tm - 1) / tm) * ((N + tn - 1) / tn) * std::max<int64_t>(batch, 1); };
     if (bf16) {
-        if (M >= 256 && N >= 128) return GemmTile::Large;
-        if (M >= 128 && N >= 128) return GemmTile::Medium;
+        if (M >= 256 && N >= 128 && wgs(256, 128) >= 240) return GemmTile::Large;
+        if (M >= 128 && N >= 128 && wgs(128, 128) >= 240) return GemmTile::Medium;
         return GemmTile::Small;
     }
-    if (M >= 128 && N >= 128) return GemmTile::Medium;
+    if (M >= 128 && N >= 128 && wgs(128, 128) >= 240) return GemmTile::Medium;
     return GemmTile::Small;
 }
 
@@ -134,15 +136,20 @@ struct BlkMat {
 inline Mat sq(const void* p, int64_t b) { return Mat{p, b, b * b}; }
 
 // --------------------------------------------------- Cayley-Neumann planning
+// Buffers of one Cayley-Neumann call ([nblk, b, b] each).  "32" buffers are
+// float32; "c" buffers hold the operand copy in the compute dtype (bf16 on the
+// bf16 path; on the float32 path a c buffer is its own float32 buffer or an
+// alias of the matching 32 buffer).
 struct CnpBufs {
     float* Q32 = nullptr; void* Qc = nullptr;
-    float* S32 = nullptr; void* Sc = nullptr;
-    float* U32 = nullptr; void* Uc = nullptr;   // T = 2Q+S (k=3) / P1 = Q+S (k=4)
-    float* V32 = nullptr; void* Vc = nullptr;   // U = 2Q+2S (k=3) / E (k=4)
-    float* W32 = nullptr;                       // Q + E (k=4)
-    // Horner (other k): D_1..D_k, two rolling gradient buffers
+    // k = 3: U32 = 2Q + 2S, Sc = S, Tc = 2Q + S (one fused epilogue)
+    float* U32 = nullptr; void* Sc = nullptr; void* Tc = nullptr;
+    // k = 4: S, P1 = Q + S, E = P1 + P1 S, W = Q + E
+    float* S32 = nullptr; float* P32 = nullptr; void* Pc = nullptr; float* E32 = nullptr; void* Ec = nullptr;
+    float* W32 = nullptr;
+    // Horner (other k): D_1..D_k
     float* D32[9] = {}; void* Dc[9] = {};
-    // backward
+    // backward scratch
     void* dGc = nullptr;
     float* a32 = nullptr; float* b32 = nullptr; void* c_c = nullptr; void* d_c = nullptr;
     float* e32 = nullptr; float* f32 = nullptr; float* g32 = nullptr;
@@ -153,19 +160,25 @@ struct CnpBufs {
 void* ctake(Carver& cv, bool cbf16, int64_t elems, float* alias32) {
     return cbf16 ? cv.take(2 * (size_t)elems) : static_cast<void*>(alias32);
 }
+// A compute-dtype buffer of its own.
+void* cown(Carver& cv, bool cbf16, int64_t elems) { return cv.take((cbf16 ? 2 : 4) * (size_t)elems); }
 
 void plan_cnp(Carver& cv, int64_t nblk, int64_t b, int k, bool cbf16, bool backward, CnpBufs& B) {
     const int64_t e = nblk * b * b;
     B.Q32 = cv.take_n<float>(e);
     B.Qc = ctake(cv, cbf16, e, B.Q32);
-    if (k == 3 || k == 4) {
+    if (k == 3) {
+        B.U32 = cv.take_n<float>(e);
+        B.Sc = cown(cv, cbf16, e);
+        B.Tc = cown(cv, cbf16, e);
+    } else if (k == 4) {
         B.S32 = cv.take_n<float>(e);
         B.Sc = ctake(cv, cbf16, e, B.S32);
-        B.U32 = cv.take_n<float>(e);
-        B.Uc = ctake(cv, cbf16, e, B.U32);
-        B.V32 = cv.take_n<float>(e);
-        B.Vc = ctake(cv, cbf16, e, B.V32);
-        if (k == 4) B.W32 = cv.take_n<float>(e);
+        B.P32 = cv.take_n<float>(e);
+        B.Pc = ctake(cv, cbf16, e, B.P32);
+        B.E32 = cv.take_n<float>(e);
+        B.Ec = ctake(cv, cbf16, e, B.E32);
+        B.W32 = cv.take_n<float>(e);
     } else {
         B.D32[1] = B.Q32;
         B.Dc[1] = B.Qc;
@@ -178,8 +191,8 @@ void plan_cnp(Carver& cv, int64_t nblk, int64_t b, int k, bool cbf16, bool backw
     if (backward) {
         B.a32 = cv.take_n<float>(e);
         B.b32 = cv.take_n<float>(e);
-        B.c_c = cbf16 ? cv.take(2 * (size_t)e) : static_cast<void*>(cv.take_n<float>(e));
-        B.d_c = cbf16 ? cv.take(2 * (size_t)e) : static_cast<void*>(cv.take_n<float>(e));
+        B.c_c = cown(cv, cbf16, e);
+        B.d_c = cown(cv, cbf16, e);
         B.e32 = cv.take_n<float>(e);
         B.f32 = cv.take_n<float>(e);
         B.g32 = cv.take_n<float>(e);
@@ -187,12 +200,26 @@ void plan_cnp(Carver& cv, int64_t nblk, int64_t b, int k, bool cbf16, bool backw
     }
 }
 
-// Shared front part: Q (float32 and compute copy) and, for k = 3 / 4, S = Q^2.
+// Shared front part: Q in float32 and in the compute dtype (one pass), and the
+// square S = Q Q = -Q Q^T.  For k = 3 the square's epilogue also emits
+// Tc = 2Q + S and U = 2Q + 2S; for k = 4 it emits S (float32 and compute).
 int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, CnpBufs& B, hipStream_t s) {
-    HIP_TRY(skew_unpack(q, B.Q32, false, nblk, (int)b, s));
-    if (cbf16) HIP_TRY(combine(nblk, (int)b, B.Q32, 1.f, nullptr, 0, nullptr, 0, 0, nullptr, B.Qc, true, s));
-    if (k == 3 || k == 4) {
-        // S = Q Q = -Q Q^T
+    HIP_TRY(skew_unpack(q, B.Q32, false, nblk, (int)b, s, cbf16 ? B.Qc : nullptr));
+    if (k == 3) {
+        GemmArgs g;
+        g.A = B.Qc; g.lda = b; g.strideA = b * b;
+        g.B = B.Qc; g.ldb = b; g.strideB = b * b;
+        g.C = B.U32; g.ldc = b; g.strideC = b * b;
+        g.C2 = B.Sc; g.ldc2 = b; g.strideC2 = b * b;
+        g.C3 = B.Tc;
+        g.Cin1 = B.Q32; g.ldcin1 = b; g.strideCin1 = b * b;
+        g.alpha = -1.f;
+        g.mode = 1;
+        g.M = g.N = g.K = (int)b;
+        g.batch = (int)nblk;
+        g.k_per_split = (int)b;
+        HIP_TRY(gemm_launch(g, GemmLayout::NT, pick_tile(cbf16, b, b, nblk), cbf16, false, s));
+    } else if (k == 4) {
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Qc, b), B.S32, b, b * b, s,
                      -1.f, nullptr, 0, nullptr, 0, 0, cbf16 ? B.Sc : nullptr));
     }
@@ -209,16 +236,14 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
     const int ib = (int)b;
     const int64_t bb = b * b;
     if (k == 3) {
-        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 1.f, nullptr, 0, 0, nullptr, B.Uc, cbf16, s));
-        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 2.f, nullptr, 0, 0, B.V32, nullptr, false, s));
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, gbf16, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), G, b, bb, s, 1.f,
-                     B.V32, 1.f, nullptr, 0, 1.f));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, gbf16, b, b, b, nblk, sq(B.Tc, b), sq(B.Sc, b), G, b, bb, s, 1.f,
+                     B.U32, 1.f, nullptr, 0, 1.f));
     } else if (k == 4) {
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.U32, cbf16 ? B.Uc : nullptr, cbf16, s));
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), B.V32, b, bb, s, 1.f,
-                     B.U32, 1.f, nullptr, 0, 0, cbf16 ? B.Vc : nullptr));
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.V32, 1.f, nullptr, 0, 0, B.W32, nullptr, false, s));
-        HIP_TRY(gemm(GemmLayout::NN, cbf16, gbf16, b, b, b, nblk, sq(B.Qc, b), sq(B.Vc, b), G, b, bb, s, 1.f,
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, cbf16 ? B.Pc : nullptr, cbf16, s));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(B.Sc, b), B.E32, b, bb, s, 1.f,
+                     B.P32, 1.f, nullptr, 0, 0, cbf16 ? B.Ec : nullptr));
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.E32, 1.f, nullptr, 0, 0, B.W32, nullptr, false, s));
+        HIP_TRY(gemm(GemmLayout::NN, cbf16, gbf16, b, b, b, nblk, sq(B.Qc, b), sq(B.Ec, b), G, b, bb, s, 1.f,
                      B.W32, 1.f, nullptr, 0, 1.f));
     } else {
         // rolling D buffers: slots 1 (= Q), 2, 3
@@ -248,27 +273,23 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
     }
     float* dQ = B.g32;
     if (k == 3) {
-        // T = 2Q + S (compute copy only)
-        HIP_TRY(combine(nblk, ib, B.Q32, 2.f, B.S32, 1.f, nullptr, 0, 0, nullptr, B.Uc, cbf16, s));
-        // dA = dG + dG S,  dB = dG + T^T dG
+        // G = A B with A = I + T, B = I + S (T = 2Q + S, S symmetric):
+        // dA = dG + dG S ;  dS = dA + dB with dB = dG + T^T dG ;  dQ = 2 dA + dS Q^T + Q^T dS
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Sc, b), B.a32, b, bb, s, 1.f, dG,
                      1.f));
-        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(dGc, b), B.b32, b, bb, s, 1.f, dG,
-                     1.f));
-        // dS = dA + dB (compute copy)
-        HIP_TRY(combine(nblk, ib, B.a32, 1.f, B.b32, 1.f, nullptr, 0, 0, nullptr, B.c_c, cbf16, s));
-        // dQ = 2 dA + dS Q^T + Q^T dS
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Tc, b), sq(dGc, b), nullptr, b, bb, s, 1.f,
+                     dG, 1.f, B.a32, 1.f, 0.f, B.c_c));
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.c_c, b), sq(B.Qc, b), B.e32, b, bb, s, 1.f,
                      B.a32, 2.f));
         HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.c_c, b), dQ, b, bb, s, 1.f,
                      B.e32, 1.f));
     } else if (k == 4) {
         // recompute P1 = Q + S and E = P1 + P1 S
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.U32, cbf16 ? B.Uc : nullptr, cbf16, s));
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(B.Sc, b), B.V32, b, bb, s, 1.f,
-                     B.U32, 1.f, nullptr, 0, 0, cbf16 ? B.Vc : nullptr));
+        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, cbf16 ? B.Pc : nullptr, cbf16, s));
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(B.Sc, b), B.E32, b, bb, s, 1.f,
+                     B.P32, 1.f, nullptr, 0, 0, cbf16 ? B.Ec : nullptr));
         // X1 = dG + dG E^T ; dE = dG + Q^T dG
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Vc, b), B.a32, b, bb, s, 1.f, dG,
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Ec, b), B.a32, b, bb, s, 1.f, dG,
                      1.f));
         HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dGc, b), B.b32, b, bb, s, 1.f, dG,
                      1.f, nullptr, 0, 0, cbf16 ? B.c_c : nullptr));
@@ -276,13 +297,12 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         // dP1 = dE + dE S ; dS = P1^T dE + dP1
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dEc, b), sq(B.Sc, b), B.e32, b, bb, s, 1.f,
                      B.b32, 1.f));
-        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Uc, b), sq(dEc, b), cbf16 ? nullptr : B.f32,
-                     b, bb, s, 1.f, B.e32, 1.f, nullptr, 0, 0, cbf16 ? B.d_c : nullptr));
-        const void* dSc = cbf16 ? B.d_c : static_cast<void*>(B.f32);
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(dEc, b), nullptr, b, bb, s, 1.f,
+                     B.e32, 1.f, nullptr, 0, 0, B.d_c));
         // dQ = X1 + dP1 + dS Q^T + Q^T dS
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dSc, b), sq(B.Qc, b), B.W32, b, bb, s, 1.f,
+        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.d_c, b), sq(B.Qc, b), B.W32, b, bb, s, 1.f,
                      B.a32, 1.f, B.e32, 1.f));
-        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dSc, b), dQ, b, bb, s, 1.f, B.W32,
+        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.d_c, b), dQ, b, bb, s, 1.f, B.W32,
                      1.f));
     } else {
         // recompute D_2..D_k (D_1 = Q)
@@ -332,8 +352,15 @@ struct LinearBufs {
 };
 
 // Split-K plan for dG = A^T B with K = T: enough workgroups to cover the chip.
+// Tile of the block-gradient products (M = N = b, K = tokens, split along K).
+GemmTile grad_tile(bool bf16, int64_t b) {
+    if (bf16 && b >= 256) return GemmTile::Large;
+    if (b >= 128) return GemmTile::Medium;
+    return GemmTile::Small;
+}
+
 void plan_splits(int64_t T, int64_t b, int64_t nblk, bool bf16, int& splits, int64_t& kps) {
-    const GemmTile tile = pick_tile(bf16, b, b, 0);
+    const GemmTile tile = grad_tile(bf16, b);
     const int64_t tr = gemm_tile_rows(tile, bf16), tc = gemm_tile_cols(tile, bf16);
     const int64_t tiles = ((b + tr - 1) / tr) * ((b + tc - 1) / tc) * nblk;
     int64_t want = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
@@ -383,7 +410,7 @@ int block_grad(bool bf16, int64_t T, int64_t d, int64_t b, const void* A, const 
     } else {
         g.C = dG;
     }
-    HIP_TRY(gemm_launch(g, GemmLayout::TN, pick_tile(bf16, b, b, 0), bf16, false, s));
+    HIP_TRY(gemm_launch(g, GemmLayout::TN, grad_tile(bf16, b), bf16, false, s));
     if (splits > 1) HIP_TRY(splitk_reduce(part, dG, d * b, splits, s));
     return POETX_OK;
 }

@@ -7,7 +7,9 @@
 
 namespace poetx {
 
-hipError_t skew_unpack(const float* q, void* Q, bool bf16, int64_t nblk, int b, hipStream_t s);
+// Q = unpack(q) in float32 or bf16; with Q2_bf16 set, a bf16 copy is written too.
+hipError_t skew_unpack(const float* q, void* Q, bool bf16, int64_t nblk, int b, hipStream_t s,
+                       void* Q2_bf16 = nullptr);
 hipError_t skew_pack(const float* dQ, float* dq, int64_t nblk, int b, hipStream_t s);
 hipError_t permute_2d(const void* src, void* dst, bool bf16, int64_t rows, int64_t cols, const int* row_idx,
                       const int* col_idx, bool scatter, hipStream_t s);

@@ -24,7 +24,7 @@ constexpr int kSkewTile = 32;
 // contiguous row segments of Q.
 template <typename T>
 __global__ void __launch_bounds__(256) skew_unpack_kernel(const float* __restrict__ q, T* __restrict__ Q,
-                                                          int b) {
+                                                          int b, bf16_t* __restrict__ Q2) {
     __shared__ float tile[kSkewTile][kSkewTile + 1];
     const int tiles = b / kSkewTile;
     const int ti = blockIdx.x / tiles;
@@ -51,6 +51,7 @@ __global__ void __launch_bounds__(256) skew_unpack_kernel(const float* __restric
         else if (ti > tj) v = -tile[tx][rr];
         else v = (rr < tx) ? tile[rr][tx] : (rr > tx ? -tile[tx][rr] : 0.f);
         store_f32(Qb + (int64_t)r * b + c, v);
+        if (Q2) Q2[blk * (int64_t)b * b + (int64_t)r * b + c] = ElemTraits<bf16_t>::from_f32(v);
     }
 }
 
@@ -84,7 +85,8 @@ __global__ void __launch_bounds__(256) skew_pack_kernel(const float* __restrict_
 
 // Small-block variants (b not a multiple of 32): one thread per element.
 template <typename T>
-__global__ void skew_unpack_simple(const float* __restrict__ q, T* __restrict__ Q, int b, int64_t total) {
+__global__ void skew_unpack_simple(const float* __restrict__ q, T* __restrict__ Q, int b, int64_t total,
+                                   bf16_t* __restrict__ Q2) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const int64_t bb = (int64_t)b * b;
@@ -96,6 +98,7 @@ __global__ void skew_unpack_simple(const float* __restrict__ q, T* __restrict__ 
     if (r < c) v = qb[tri_index(r, c, b)];
     else if (r > c) v = -qb[tri_index(c, r, b)];
     store_f32(Q + i, v);
+    if (Q2) Q2[i] = ElemTraits<bf16_t>::from_f32(v);
 }
 
 __global__ void skew_pack_simple(const float* __restrict__ dQ, float* __restrict__ dq, int b, int64_t nblk) {
@@ -258,26 +261,28 @@ inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + thre
 
 }  // namespace
 
-hipError_t skew_unpack(const float* q, void* Q, bool bf16, int64_t nblk, int b, hipStream_t s) {
+hipError_t skew_unpack(const float* q, void* Q, bool bf16, int64_t nblk, int b, hipStream_t s, void* Q2_bf16) {
     if (nblk <= 0) return hipSuccess;
+    bf16_t* Q2 = static_cast<bf16_t*>(Q2_bf16);
     if (b % kSkewTile == 0) {
         const int64_t ntri = (int64_t)b * (b - 1) / 2, bb = (int64_t)b * b;
         for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGridY) {
             const unsigned nz = (unsigned)std::min<int64_t>(kMaxGridY, nblk - z0);
             dim3 grid((b / kSkewTile) * (b / kSkewTile), nz);
+            bf16_t* q2 = Q2 ? Q2 + z0 * bb : nullptr;
             if (bf16)
                 hipLaunchKernelGGL(skew_unpack_kernel<bf16_t>, grid, dim3(256), 0, s, q + z0 * ntri,
-                                   (bf16_t*)Q + z0 * bb, b);
+                                   (bf16_t*)Q + z0 * bb, b, q2);
             else
                 hipLaunchKernelGGL(skew_unpack_kernel<float>, grid, dim3(256), 0, s, q + z0 * ntri,
-                                   (float*)Q + z0 * bb, b);
+                                   (float*)Q + z0 * bb, b, q2);
         }
     } else {
         const int64_t total = nblk * (int64_t)b * b;
         if (bf16) hipLaunchKernelGGL(skew_unpack_simple<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s, q,
-                                     (bf16_t*)Q, b, total);
+                                     (bf16_t*)Q, b, total, Q2);
         else hipLaunchKernelGGL(skew_unpack_simple<float>, dim3(blocks_for(total, 256)), dim3(256), 0, s, q,
-                                (float*)Q, b, total);
+                                (float*)Q, b, total, Q2);
     }
     return hipGetLastError();
 }

@@ -27,6 +27,10 @@ struct GemmArgs {
     const float* Cin2 = nullptr;
     int64_t ldcin2 = 0, strideCin2 = 0;
     float alpha = 1.f, beta1 = 0.f, beta2 = 0.f, gamma = 0.f;
+    // Epilogue mode 1 (Cayley-Neumann square): with v = alpha * acc and
+    // Q = Cin1, writes C = 2Q + 2v (float32), C2 = v and C3 = 2Q + v (compute dtype).
+    int mode = 0;
+    void* C3 = nullptr;
     int M = 0, N = 0, K = 0;
     int batch = 1;
     int splits = 1;

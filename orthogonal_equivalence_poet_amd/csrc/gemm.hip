@@ -271,7 +271,7 @@ gemm_kernel(const GemmArgs p) {
     const int64_t zi2 = (int64_t)z * p.strideCin2;
     const int col_base = tn * BN + wn * Cfg::WTN + (lane & 31);
     const int row_base = tm * BM + wm * Cfg::WTM + (lane >> 5) * 4;
-    const bool plain = !p.Cin1 && !p.Cin2 && !C2 && p.gamma == 0.f && p.alpha == 1.f;
+    const bool plain = !p.Cin1 && !p.Cin2 && !C2 && p.gamma == 0.f && p.alpha == 1.f && p.mode == 0;
     if (plain) {
         OutT* Cz = C + zc;
 #pragma clang loop unroll(full)
@@ -286,21 +286,42 @@ gemm_kernel(const GemmArgs p) {
                 }
             }
     } else {
+        // General epilogue: the float32 addends of a 32 x 32 tile are fetched
+        // first (16 independent loads per lane), then combined and stored.
+        const float* __restrict__ cin1 = p.Cin1 ? p.Cin1 + zi1 : nullptr;
+        const float* __restrict__ cin2 = p.Cin2 ? p.Cin2 + zi2 : nullptr;
+        OutT* __restrict__ c1 = C ? C + zc : nullptr;
+        CT* __restrict__ c2 = C2 ? C2 + zc2 : nullptr;
+        CT* __restrict__ c3 = p.C3 ? reinterpret_cast<CT*>(p.C3) + zc2 : nullptr;
 #pragma clang loop unroll(full)
         for (int i = 0; i < Cfg::MI; ++i)
 #pragma clang loop unroll(full)
             for (int j = 0; j < Cfg::NJ; ++j) {
                 const int col = col_base + j * 32;
+                float a1[16], a2[16];
+#pragma clang loop unroll(full)
+                for (int r = 0; r < 16; ++r) {
+                    const int row = min(row_base + i * 32 + (r >> 2) * 8 + (r & 3), p.M - 1);
+                    const int cc = min(col, p.N - 1);
+                    a1[r] = cin1 ? cin1[(int64_t)row * p.ldcin1 + cc] : 0.f;
+                    a2[r] = cin2 ? cin2[(int64_t)row * p.ldcin2 + cc] : 0.f;
+                }
 #pragma clang loop unroll(full)
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
                     if (row >= p.M || col >= p.N) continue;
-                    float v = p.alpha * acc[i][j][r];
-                    if (p.Cin1) v += p.beta1 * p.Cin1[zi1 + (int64_t)row * p.ldcin1 + col];
-                    if (p.Cin2) v += p.beta2 * p.Cin2[zi2 + (int64_t)row * p.ldcin2 + col];
-                    if (row == col) v += p.gamma;
-                    if (C) store_f32(C + zc + (int64_t)row * p.ldc + col, v);
-                    if (C2) store_f32(C2 + zc2 + (int64_t)row * p.ldc2 + col, v);
+                    const float v = p.alpha * acc[i][j][r];
+                    if (p.mode == 1) {
+                        const float q2 = 2.f * a1[r];
+                        c1[(int64_t)row * p.ldc + col] = ElemTraits<OutT>::from_f32(q2 + 2.f * v);
+                        store_f32(c2 + (int64_t)row * p.ldc2 + col, v);
+                        store_f32(c3 + (int64_t)row * p.ldc2 + col, q2 + v);
+                        continue;
+                    }
+                    float o = v + p.beta1 * a1[r] + p.beta2 * a2[r];
+                    if (row == col) o += p.gamma;
+                    if (c1) store_f32(c1 + (int64_t)row * p.ldc + col, o);
+                    if (c2) store_f32(c2 + (int64_t)row * p.ldc2 + col, o);
                 }
             }
     }
@@ -317,6 +338,7 @@ hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream) {
         q.B = reinterpret_cast<const CT*>(p.B) + (int64_t)z0 * p.strideB;
         if (p.C) q.C = reinterpret_cast<OutT*>(p.C) + (int64_t)z0 * p.strideC;
         if (p.C2) q.C2 = reinterpret_cast<CT*>(p.C2) + (int64_t)z0 * p.strideC2;
+        if (p.C3) q.C3 = reinterpret_cast<CT*>(p.C3) + (int64_t)z0 * p.strideC2;
         if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)z0 * p.strideCin1;
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)z0 * p.strideCin2;
         dim3 grid(tiles, p.splits, q.batch);
