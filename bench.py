@@ -137,8 +137,7 @@ def stage_timings(spec, S, reps):
     NT, NN = B.POETX_GEMM_NT, B.POETX_GEMM_NN
 
     def blk(layout, A, G, C, d):
-        return lambda: B.poetx_gemm(layout, A, G, C, T, b, b, batch=d // b, lda=d, ldb=b, ldc=d, strideA=b,
-                                    strideB=b * b, strideC=b)
+        return lambda: B.poetx_block_apply(A, G, C, T, d, b, transpose_G=(layout == NT))
 
     st = {}
     # (name, fn, algorithmic flops, algorithmic HBM bytes)

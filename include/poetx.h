@@ -203,6 +203,14 @@ int poetx_gemm(int layout, int dtype, int dense, int64_t M, int64_t N, int64_t K
                const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
                void* C, int64_t ldc, int64_t strideC, void* stream);
 
+/* Batch-wise block-diagonal product (review Summary: the block-diagonal matmul
+ * done per block, never building the sparse matrix): for j < d/b
+ *   transpose_G == 1:  out[:, jb:(j+1)b] = in[:, jb:(j+1)b] . G[j]^T
+ *   transpose_G == 0:  out[:, jb:(j+1)b] = in[:, jb:(j+1)b] . G[j]
+ * in, out: dtype [T, d]; G: dtype [d/b, b, b].  out must not overlap in. */
+int poetx_block_apply(int dtype, int transpose_G, int64_t T, int64_t d, int64_t b, const void* in, const void* G,
+                      void* out, void* stream);
+
 /* Block gradients of the batch-wise block products (the backward of the
  * review's "batch-wise block-diagonal matmul"): for j < d/b
  *   dG[j] = A[:, jb:(j+1)b]^T B[:, jb:(j+1)b]      (sum over the T rows)

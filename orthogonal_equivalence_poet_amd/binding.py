@@ -30,7 +30,7 @@ EXPORTS = [
     "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd",
     "poetx_linear_bwd_workspace_bytes", "poetx_linear_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
-    "poetx_gemm", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
+    "poetx_gemm", "poetx_block_apply", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
 ]
 
 
@@ -72,6 +72,7 @@ _SIGS = {
     "poetx_merge": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_gemm": ([_I32, _I32, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64,
                     _VP], _I32),
+    "poetx_block_apply": ([_I32, _I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP], _I32),
     "poetx_block_grad_workspace_bytes": ([_I64, _I64, _I64, _I32], _SZ),
     "poetx_block_grad": ([_I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
 }
@@ -235,6 +236,11 @@ def poetx_gemm(layout, A, B, C, M, N, K, batch=1, lda=None, ldb=None, ldc=None, 
     ldc = ldc if ldc is not None else N
     _check("poetx_gemm", load().poetx_gemm(layout, _dtype_code(C), int(bool(dense)), M, N, K, batch, _ptr(A), lda,
                                            strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC, _stream(stream)))
+
+
+def poetx_block_apply(inp, G, out, T, d, b, transpose_G=True, stream=None):
+    _check("poetx_block_apply", load().poetx_block_apply(_dtype_code(out), int(bool(transpose_G)), T, d, b, _ptr(inp),
+                                                         _ptr(G), _ptr(out), _stream(stream)))
 
 
 def poetx_block_grad_workspace_bytes(T, d, b, dtype) -> int:

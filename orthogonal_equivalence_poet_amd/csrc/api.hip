@@ -359,9 +359,14 @@ GemmTile grad_tile(bool bf16, int64_t b) {
     return GemmTile::Small;
 }
 
+// Block gradients of bf16 blocks of b >= 64 run on the pipelined kernel
+// (256 x 128 tiles, transposed LDS reads for both operands).
+bool grad_pipe(bool bf16, int64_t b) { return bf16 && b >= 64 && b % 8 == 0; }
+
 void plan_splits(int64_t T, int64_t b, int64_t nblk, bool bf16, int& splits, int64_t& kps) {
     const GemmTile tile = grad_tile(bf16, b);
-    const int64_t tr = gemm_tile_rows(tile, bf16), tc = gemm_tile_cols(tile, bf16);
+    const int64_t tr = grad_pipe(bf16, b) ? pipe_tile_rows(PipeTile::Tall) : gemm_tile_rows(tile, bf16);
+    const int64_t tc = grad_pipe(bf16, b) ? pipe_tile_cols(PipeTile::Tall) : gemm_tile_cols(tile, bf16);
     const int64_t tiles = ((b + tr - 1) / tr) * ((b + tc - 1) / tc) * nblk;
     int64_t want = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
     want = std::min<int64_t>(want, std::max<int64_t>(1, T / 256));
@@ -390,12 +395,38 @@ void plan_linear(Carver& cv, const poetx_linear_desc* d, bool backward, LinearBu
 // out[:, jb:(j+1)b] = in[:, jb:(j+1)b] . G_j^T (NT) or . G_j (NN).
 hipError_t block_apply(GemmLayout layout, bool bf16, int64_t T, int64_t d, int64_t b, const void* in,
                        const void* G, void* out, hipStream_t s) {
+    const bool nn = layout == GemmLayout::NN;
+    if (bf16 && pipe_gemm_supported(false, nn, T, b, b, d, b, b, b * b)) {
+        PipeArgs p;
+        p.A = in; p.lda = d; p.strideA = b;
+        p.B = G; p.ldb = b; p.strideB = b * b;
+        p.C = out; p.ldc = d; p.strideC = b;
+        p.M = (int)T; p.N = (int)b; p.K = (int)b;
+        p.batch = (int)(d / b);
+        p.k_per_split = (int)b;
+        return pipe_gemm(false, nn, false, p, s, b >= 256 ? PipeTile::Wide : PipeTile::Tall);
+    }
     return gemm(layout, bf16, bf16, T, b, b, d / b, Mat{in, d, b}, Mat{G, b, b * b}, out, d, b, s);
 }
 
 // dG_j = A_j^T B_j over the T rows, split along T; partials reduced in order.
 int block_grad(bool bf16, int64_t T, int64_t d, int64_t b, const void* A, const void* B, float* dG, int splits,
                int64_t kps, float* part, hipStream_t s) {
+    if (grad_pipe(bf16, b)) {
+        PipeArgs p;
+        p.A = A; p.lda = d; p.strideA = b;
+        p.B = B; p.ldb = d; p.strideB = b;
+        p.C = splits > 1 ? static_cast<void*>(part) : static_cast<void*>(dG);
+        p.ldc = b; p.strideC = b * b;
+        p.strideSplit = d * b;  // nblk * b * b
+        p.M = (int)b; p.N = (int)b; p.K = (int)T;
+        p.batch = (int)(d / b);
+        p.splits = splits;
+        p.k_per_split = (int)kps;
+        HIP_TRY(pipe_gemm(true, true, true, p, s, PipeTile::Tall));
+        if (splits > 1) HIP_TRY(splitk_reduce(part, dG, d * b, splits, s));
+        return POETX_OK;
+    }
     GemmArgs g;
     g.A = A; g.lda = d; g.strideA = b;
     g.B = B; g.ldb = d; g.strideB = b;
@@ -735,6 +766,18 @@ int poetx_gemm(int layout, int dtype, int dense, int64_t M, int64_t N, int64_t K
         HIP_TRY(gemm(L, bf, bf, M, N, K, batch, Mat{A, lda, strideA}, Mat{B, ldb, strideB}, C, ldc, strideC,
                      as_stream(stream)));
     }
+    return POETX_OK;
+}
+
+int poetx_block_apply(int dtype, int transpose_G, int64_t T, int64_t d, int64_t b, const void* in, const void* G,
+                      void* out, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    if (T < 0 || d <= 0 || d % b || T > kMaxExtent || d > kMaxExtent) return POETX_ERR_SHAPE;
+    if (T == 0) return POETX_OK;
+    if (!in || !G || !out) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(block_apply(transpose_G ? GemmLayout::NT : GemmLayout::NN, dtype == POETX_BF16, T, d, b, in, G, out,
+                        as_stream(stream)));
     return POETX_OK;
 }
 

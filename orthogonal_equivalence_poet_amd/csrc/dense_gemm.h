@@ -1,4 +1,6 @@
-// Host-side interface of the dense Wt GEMM (bf16, 256 x 128 x 64 tiles).
+// Host-side interface of the pipelined bf16 MFMA GEMM (256 x 128 x 64 tiles,
+// direct-to-LDS loads) that runs the dense Wt products, the batched block
+// products and the block gradients of the layer.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,6 +8,36 @@
 
 namespace poetx {
 
+struct PipeArgs {
+    const void* A = nullptr;   // bf16
+    int64_t lda = 0, strideA = 0;
+    const void* B = nullptr;   // bf16
+    int64_t ldb = 0, strideB = 0;
+    void* C = nullptr;         // bf16 or float32
+    int64_t ldc = 0, strideC = 0, strideSplit = 0;
+    int M = 0, N = 0, K = 0;
+    int batch = 1;
+    int splits = 1;
+    int k_per_split = 0;       // multiple of 64
+};
+
+// a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead
+// of [N][K].  C[z] (M x N) = op(A[z]) op(B[z]) over the k range of each split;
+// with splits > 1 split s writes its partial sum at C + s * strideSplit.
+// Requirements (pipe_gemm_supported): K-contiguous operands need K % 64 == 0;
+// every leading dimension, stride and contiguous extent a multiple of 8.
+// Workgroup tile: Tall 256 x 128 (dense products), Wide 128 x 256 (block
+// products: one workgroup spans a whole block of 256 outputs), Square 128 x 128
+// (block gradients).  Instantiated: k-major A with bf16 output (Tall, Wide) and
+// m/n-major A and B with float32 output (Tall, Square).
+enum class PipeTile { Tall, Wide, Square };
+bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                         int64_t strideA, int64_t strideB);
+hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile);
+int pipe_tile_rows(PipeTile t);
+int pipe_tile_cols(PipeTile t);
+
+// Dense convenience wrappers (batch 1, no split).
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
 // C[M][N] = A[M][K] . B^T (b_nn = false, B is [N][K]) or A . B (b_nn = true, B is [K][N]).
 hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,

@@ -1,35 +1,41 @@
-// Dense Wt products of the POET-X chain on MFMA (bf16 operands, float32
-// accumulation, bf16 output):
-//   forward   h2  = h1 . Wt^T   (B = Wt is [N][K], k contiguous)      "NT"
-//   backward  dh1 = dh2 . Wt    (B = Wt is [K][N], n contiguous)      "NN"
-// These two products carry most of the layer's arithmetic (the input-centric
-// chain of the review's Summary keeps W0 frozen and never materialises R W0 P).
+// Pipelined bf16 MFMA GEMM (float32 accumulation) for the large products of the
+// POET-X chain (the input-centric, matrix-free reformulation of the review's
+// Summary keeps W0 frozen and never materialises R W0 P):
+//   dense   h2  = h1 . Wt^T  (A k-major, B k-major)   dh1 = dh2 . Wt (B n-major)
+//   blocks  h1_j = a_j . G_j^T, dh2_j = dz_j . G_j     (batched over blocks j)
+//   grads   dG_j = dz_j^T h2_j                          (A and B m/n-major, K = tokens,
+//                                                        split along K, float32 out)
 //
-// Workgroup tile 256 x 128 x 64, four waves in a 2 x 2 grid, each wave owning a
-// 128 x 64 sub-tile as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128 float32
-// accumulators per lane, in AGPRs).
+// Workgroup tile BM x BN x 64 (256 x 128 for the dense products, 128 x 256 for
+// the block products, 128 x 128 for the block gradients), four waves in a 2 x 2
+// grid, each wave owning a (BM/2) x (BN/2) sub-tile of v_mfma_f32_32x32x16_bf16
+// tiles (float32 accumulators in AGPRs).
 //
 // Operand tiles travel global -> LDS by direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so no
-// VGPRs stage them and no ds_write is issued.  Three LDS stages of 48 KB form a
-// ring: while the MFMAs consume stage kt % 3, the loads of tiles kt+1 and kt+2
-// are in flight.  The loads are issued from inline asm so that the compiler does
-// not add a conservative vmcnt(0) before every LDS read; the kernel itself waits
+// VGPRs stage them and no ds_write is issued.  Three LDS stages form a ring:
+// while the MFMAs consume stage kt % 3, the loads of tiles kt+1 and kt+2 are in
+// flight.  The loads are issued from inline asm so that the compiler does not
+// add a conservative vmcnt(0) before every LDS read; the kernel itself waits
 // (s_waitcnt vmcnt) for exactly the tile it is about to read, then barriers.
 //
 // LDS layouts (XOR-swizzled instead of padded, because a DMA writes whole
 // 1 KB runs):
 //   k-major tile [rows][64 k], 128-byte rows of eight 16-byte chunks: chunk c
 //     of row r sits in slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), which
-//     keeps the ds_read_b128 fragment reads free of bank conflicts for 32- and
-//     64-bank LDS alike;
-//   n-major tile (the NN operand) [64 k][128 n], 256-byte rows of sixteen
-//     chunks: chunk c of row k sits in slot c ^ (2 (k & 7)); fragments are read
-//     with ds_read_b64_tr_b16, which transposes 16-lane groups so that lane i
-//     receives four consecutive k of column i.
+//     keeps the ds_read_b128 fragment reads free of bank conflicts;
+//   m/n-major tile [64 k][rows], 256- or 512-byte rows: chunk c of k-row k sits
+//     in slot c ^ 4 (k & 3); fragments are read with ds_read_b64_tr_b16, which
+//     transposes 16-lane groups so that lane i receives four consecutive k of
+//     column i; the swizzle spreads the four k-rows x four chunks that 32 lanes
+//     touch over all 64 banks.
 //
-// Rows past M (tokens) or N are read from the last valid row / column chunk and
-// never stored; K must be a multiple of 64 (the host falls back otherwise).
+// Rows past M or N are read from the last valid row / column chunk and never
+// stored.  K-contiguous operands need K % 64 == 0; for m/n-major operands a
+// ragged last k-tile is loaded from clamped rows and its rows past K are zeroed
+// in LDS before use.
+#include <type_traits>
+
 #include "dense_gemm.h"
 #include "device_common.h"
 
@@ -37,14 +43,20 @@ namespace poetx {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kStages = 3;
-constexpr int kABytes = BM * BK * 2;                 // 32 KB
-constexpr int kBBytes = BN * BK * 2;                 // 16 KB
-constexpr int kStageBytes = kABytes + kBBytes;       // 48 KB
-constexpr int WTM = 128, WTN = 64, MI = 4, NJ = 2;
-constexpr int kLoadsPerTile = kABytes / (kThreads * 16) + kBBytes / (kThreads * 16);   // 12
+
+// Workgroup tile BM x BN (x 64 k), four waves in a 2 x 2 grid.
+template <int BM_, int BN_>
+struct Geo {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int kABytes = BM * BK * 2;
+    static constexpr int kBBytes = BN * BK * 2;
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int WTM = BM / 2, WTN = BN / 2, MI = WTM / 32, NJ = WTN / 32;
+    static constexpr int kLoadsPerTile = (kABytes + kBBytes) / (kThreads * 16);
+};
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -74,97 +86,110 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_mn(int k) { return 4 * (k & 3); }
 
-// Issue the loads of one k-tile (A and B) into the LDS stage at byte offset
-// `stage`.  Wave w handles the 1 KB runs g = w, w + 4, ...
-template <bool B_NN>
-__device__ __forceinline__ void dma_tile(uint32_t stage, const uint16_t* __restrict__ A, int64_t lda,
-                                         const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M,
-                                         int N, int k0, int wave, int lane) {
-    // A: 32 runs of 8 rows; lane -> row 8g + lane/8, slot lane % 8
+// Loads of one operand tile into LDS at byte offset `dst`.
+//   k-major: ROWS rows x 64 k from src[row][k] (ld = row stride), rows clamped to rows_total.
+//   m/n-major: 64 k-rows x ROWS from src[k][col] (ld = k-row stride), k clamped to k_end,
+//   columns clamped to rows_total.
+template <int ROWS, bool MN>
+__device__ __forceinline__ void dma_operand(uint32_t dst, const uint16_t* __restrict__ src, int64_t ld, int r0,
+                                            int rows_total, int k0, int k_end, int wave, int lane) {
+    if constexpr (!MN) {
+        constexpr int kRuns = ROWS / 8;            // 8 rows of 128 bytes per 1 KB run
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int g = j * 4 + wave;
-        const int r = 8 * g + (lane >> 3);
-        const int c = (lane & 7) ^ swz_k(r);
-        const int row = min(m0 + r, M - 1);
-        dma16(A + (int64_t)row * lda + k0 + c * 8, __builtin_amdgcn_readfirstlane(stage + g * 1024));
-    }
-    const uint32_t bst = stage + kABytes;
-    if constexpr (!B_NN) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kRuns / 4; ++j) {
             const int g = j * 4 + wave;
             const int r = 8 * g + (lane >> 3);
             const int c = (lane & 7) ^ swz_k(r);
-            const int row = min(n0 + r, N - 1);
-            dma16(B + (int64_t)row * ldb + k0 + c * 8, __builtin_amdgcn_readfirstlane(bst + g * 1024));
+            const int row = min(r0 + r, rows_total - 1);
+            dma16(src + (int64_t)row * ld + k0 + c * 8, __builtin_amdgcn_readfirstlane(dst + g * 1024));
         }
     } else {
-        // B [K][N]: 16 runs of 4 k-rows; lane -> k-row 4g + lane/16, slot lane % 16
+        constexpr int kRowBytes = ROWS * 2;        // one k-row
+        constexpr int kRowsPerRun = 1024 / kRowBytes;
+        constexpr int kSlots = kRowBytes / 16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 64 / kRowsPerRun / 4; ++j) {
             const int g = j * 4 + wave;
-            const int kr = 4 * g + (lane >> 4);
-            const int c = (lane & 15) ^ (2 * (kr & 7));
-            const int col = min(n0 + c * 8, N - 8);
-            dma16(B + (int64_t)(k0 + kr) * ldb + col, __builtin_amdgcn_readfirstlane(bst + g * 1024));
+            const int kr = kRowsPerRun * g + lane / kSlots;
+            const int c = (lane % kSlots) ^ swz_mn(kr);
+            const int col = min(r0 + c * 8, rows_total - 8);
+            const int k = min(k0 + kr, k_end - 1);
+            dma16(src + (int64_t)k * ld + col, __builtin_amdgcn_readfirstlane(dst + g * 1024));
         }
     }
 }
 
-template <bool B_NN>
+template <class G, bool A_MN, bool B_MN>
+__device__ __forceinline__ void dma_tile(uint32_t stage, const uint16_t* __restrict__ A, int64_t lda,
+                                         const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M,
+                                         int N, int k0, int k_end, int wave, int lane) {
+    dma_operand<G::BM, A_MN>(stage, A, lda, m0, M, k0, k_end, wave, lane);
+    dma_operand<G::BN, B_MN>(stage + G::kABytes, B, ldb, n0, N, k0, k_end, wave, lane);
+}
+
+// Fragment of 32 rows (k-major) or 32 columns (m/n-major) starting at `row0`
+// for k-step ks: lane l gets row/column row0 + l%32 and k = 16 ks + 8 (l/32) + 0..7.
+template <bool MN, int ROWS>
+__device__ __forceinline__ uint4 load_frag(const unsigned char* __restrict__ base, int row0, int ks, int lane) {
+    if constexpr (!MN) {
+        const int slot = (2 * ks + (lane >> 5)) ^ ((lane & 7) ^ ((lane >> 3) & 1));
+        return *reinterpret_cast<const uint4*>(base + (row0 + (lane & 31)) * 128 + slot * 16);
+    } else {
+        // Two transposed reads: lane 4e + q of each 16-lane group addresses k-row
+        // (kbase + e) and columns cb + 4q .. cb + 4q + 3.
+        const int i16 = lane & 15;
+        const int e = i16 >> 2, q = i16 & 3;
+        const int cb = row0 + 16 * ((lane >> 4) & 1) + 4 * q;
+        s16x4_t h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int kr = ks * 16 + 8 * (lane >> 5) + 4 * hh + e;
+            const int sl = (cb >> 3) ^ swz_mn(kr);
+            const unsigned char* p = base + kr * (ROWS * 2) + sl * 16 + (cb & 7) * 2;
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)((lds_void_t*)p));
+        }
+        return make_uint4((uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
+                          (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16),
+                          (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16),
+                          (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16));
+    }
+}
+
+template <class G, bool A_MN, bool B_MN>
 __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, int wm, int wn, int lane,
-                                             f32x16_t (&acc)[MI][NJ]) {
-    const unsigned char* as = st;
-    const unsigned char* bs = st + kABytes;
-    const int fA = (lane & 7) ^ ((lane >> 3) & 1);    // swz_k(row) for every fragment row of this lane
+                                             f32x16_t (&acc)[G::MI][G::NJ]) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-        const int slot = (2 * ks + (lane >> 5)) ^ fA;
-        uint4 af[MI], bfr[NJ];
+        uint4 af[G::MI], bfr[G::NJ];
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-            af[i] = *reinterpret_cast<const uint4*>(as + (wm * WTM + i * 32 + (lane & 31)) * 128 + slot * 16);
-        if constexpr (!B_NN) {
+        for (int i = 0; i < G::MI; ++i) af[i] = load_frag<A_MN, G::BM>(st, wm * G::WTM + i * 32, ks, lane);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(bs + (wn * WTN + j * 32 + (lane & 31)) * 128 + slot * 16);
-        } else {
-            // Two transposed reads per fragment: k = ks*16 + 8*(lane/32) + 4h + e, e = 0..3,
-            // column wn*64 + 32j + lane%32.  Lane 4e + q of each 16-lane group
-            // addresses k-row (kbase + e) and columns nb + 4q .. nb + 4q + 3.
-            const int i16 = lane & 15;
-            const int e = i16 >> 2, q = i16 & 3;
+        for (int j = 0; j < G::NJ; ++j)
+            bfr[j] = load_frag<B_MN, G::BN>(st + G::kABytes, wn * G::WTN + j * 32, ks, lane);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int nb = wn * WTN + 32 * j + 16 * ((lane >> 4) & 1) + 4 * q;
-                s16x4_t h[2];
+        for (int i = 0; i < G::MI; ++i)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int kr = ks * 16 + 8 * (lane >> 5) + 4 * hh + e;
-                    const int sl = (nb >> 3) ^ (2 * (kr & 7));
-                    const unsigned char* p = bs + kr * 256 + sl * 16 + (nb & 7) * 2;
-                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_t*)((lds_void_t*)p));
-                }
-                bfr[j] = make_uint4((uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
-                                    (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16),
-                                    (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16),
-                                    (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], acc[i][j]);
+            for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], acc[i][j]);
+    }
+}
+
+// Zero the k-rows >= valid of an m/n-major tile (ragged last k-tile).
+template <int ROWS>
+__device__ __forceinline__ void zero_rows_mn(unsigned char* __restrict__ base, int valid, int tid) {
+    constexpr int kChunks = ROWS * 2 / 16;   // 16-byte chunks per k-row
+    for (int u = tid; u < (64 - valid) * kChunks; u += kThreads) {
+        const int r = valid + u / kChunks;
+        *reinterpret_cast<uint4*>(base + r * ROWS * 2 + (u % kChunks) * 16) = make_uint4(0, 0, 0, 0);
     }
 }
 
 // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
 // launch slot id is regrouped to give each XCD a contiguous run of tiles in
 // four-M-panel-deep order; the A and B panels an XCD shares stay in its L2.
-__device__ __forceinline__ void dense_tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
     if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
     constexpr int G = 4;
@@ -176,19 +201,27 @@ __device__ __forceinline__ void dense_tile_coords(int id, int tiles_m, int tiles
     tn = r / gm;
 }
 
-template <bool B_NN>
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-dense_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-                  uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K) {
+pipe_gemm_kernel(const PipeArgs p) {
+    using G = Geo<BM, BN>;
+    constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
+    constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
+    constexpr int kLoadsPerTile = G::kLoadsPerTile;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int M = p.M, N = p.N;
     int tm, tn;
-    dense_tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = K / BK;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)blockIdx.y * p.strideA;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)blockIdx.y * p.strideB;
+    const int kb = blockIdx.z * p.k_per_split;
+    const int ke = min(p.K, kb + p.k_per_split);
+    const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const uint32_t base = lds_offset(lds);
 
     f32x16_t acc[MI][NJ];
@@ -199,23 +232,35 @@ dense_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* _
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    dma_tile<B_NN>(base, A, lda, B, ldb, m0, n0, M, N, 0, wave, lane);
-    if (nk > 1) dma_tile<B_NN>(base + kStageBytes, A, lda, B, ldb, m0, n0, M, N, BK, wave, lane);
+    if (nk > 0) dma_tile<G, A_MN, B_MN>(base, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, wave, lane);
+    if (nk > 1)
+        dma_tile<G, A_MN, B_MN>(base + kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N, kb + BK, ke, wave, lane);
     int st = 0;   // stage of tile kt
     for (int kt = 0; kt < nk; ++kt) {
         // this thread's loads of tile kt are done when at most those of tile kt+1 remain
         if (kt + 1 < nk) wait_vmcnt<kLoadsPerTile>();
         else wait_vmcnt<0>();
         block_barrier();   // everyone's tile kt has landed; stage (kt+2)%3 is no longer read
+        if constexpr (A_MN || B_MN) {
+            const int valid = ke - (kb + kt * BK);
+            if (valid < BK) {   // ragged last tile: rows past K were loaded from clamped rows
+                if constexpr (A_MN) zero_rows_mn<BM>(lds + st * kStageBytes, valid, tid);
+                if constexpr (B_MN) zero_rows_mn<BN>(lds + st * kStageBytes + kABytes, valid, tid);
+                __syncthreads();
+            }
+        }
         if (kt + 2 < nk) {
             const int st2 = st >= 1 ? st - 1 : 2;   // (kt + 2) % 3
-            dma_tile<B_NN>(base + st2 * kStageBytes, A, lda, B, ldb, m0, n0, M, N, (kt + 2) * BK, wave, lane);
+            dma_tile<G, A_MN, B_MN>(base + st2 * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N,
+                                    kb + (kt + 2) * BK, ke, wave, lane);
         }
-        compute_tile<B_NN>(lds + st * kStageBytes, wm, wn, lane, acc);
+        compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc);
         st = st == 2 ? 0 : st + 1;
     }
 
     // epilogue: lane holds rows 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 per tile
+    using OutT = typename std::conditional<OUT_F32, float, bf16_t>::type;
+    OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)blockIdx.y * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
     const int col0 = n0 + wn * WTN + (lane & 31);
     const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
     if (m0 + BM <= M && n0 + BN <= N) {
@@ -225,8 +270,8 @@ dense_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* _
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    C[(int64_t)(row0 + i * 32 + (r >> 2) * 8 + (r & 3)) * ldc + col0 + j * 32] =
-                        f32_to_bf16(acc[i][j][r]);
+                    store_f32(C + (int64_t)(row0 + i * 32 + (r >> 2) * 8 + (r & 3)) * p.ldc + col0 + j * 32,
+                              acc[i][j][r]);
     } else {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -236,13 +281,62 @@ dense_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* _
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = row0 + i * 32 + (r >> 2) * 8 + (r & 3);
-                    if (row < M && col < N) C[(int64_t)row * ldc + col] = f32_to_bf16(acc[i][j][r]);
+                    if (row < M && col < N) store_f32(C + (int64_t)row * p.ldc + col, acc[i][j][r]);
                 }
             }
     }
 }
 
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32>
+hipError_t launch(const PipeArgs& p, hipStream_t stream) {
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    constexpr int kMaxY = 65535;
+    for (int y0 = 0; y0 < p.batch; y0 += kMaxY) {
+        PipeArgs q = p;
+        q.batch = min(kMaxY, p.batch - y0);
+        q.A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)y0 * p.strideA;
+        q.B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)y0 * p.strideB;
+        q.C = reinterpret_cast<char*>(p.C) + (int64_t)y0 * p.strideC * (OUT_F32 ? 4 : 2);
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32>), dim3(tiles, q.batch, p.splits),
+                           dim3(kThreads), 0, stream, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
+
+bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                         int64_t strideA, int64_t strideB) {
+    if (M <= 0 || N <= 0 || K <= 0) return false;
+    if (a_mn && !b_mn) return false;
+    if (lda % 8 || ldb % 8 || strideA % 8 || strideB % 8) return false;
+    if (!a_mn && K % BK) return false;
+    if (!b_mn && K % BK) return false;
+    if (a_mn && (M % 8 || M < 8)) return false;
+    if (b_mn && (N % 8 || N < 8)) return false;
+    return true;
+}
+
+hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile) {
+    if (p.M <= 0 || p.N <= 0 || p.batch <= 0 || p.splits <= 0) return hipSuccess;
+    // instantiated combinations: dense / block products (k-major A, bf16 out) and
+    // block gradients (m/n-major A and B, float32 out)
+    if (!a_mn && !out_f32) {
+        if (tile == PipeTile::Wide)
+            return b_mn ? launch<128, 256, false, true, false>(p, stream) : launch<128, 256, false, false, false>(p, stream);
+        return b_mn ? launch<256, 128, false, true, false>(p, stream) : launch<256, 128, false, false, false>(p, stream);
+    }
+    if (a_mn && b_mn && out_f32) {
+        if (tile == PipeTile::Square) return launch<128, 128, true, true, true>(p, stream);
+        return launch<256, 128, true, true, true>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : 128; }
+int pipe_tile_cols(PipeTile t) { return t == PipeTile::Wide ? 256 : 128; }
 
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     return M > 0 && N >= 8 && K >= BK && K % BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0;
@@ -250,14 +344,13 @@ bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t 
 
 hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                            int M, int N, int K, hipStream_t stream) {
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (b_nn)
-        hipLaunchKernelGGL(dense_gemm_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, (const uint16_t*)A, lda,
-                           (const uint16_t*)B, ldb, (uint16_t*)C, ldc, M, N, K);
-    else
-        hipLaunchKernelGGL(dense_gemm_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream, (const uint16_t*)A,
-                           lda, (const uint16_t*)B, ldb, (uint16_t*)C, ldc, M, N, K);
-    return hipGetLastError();
+    PipeArgs p;
+    p.A = A; p.lda = lda;
+    p.B = B; p.ldb = ldb;
+    p.C = C; p.ldc = ldc;
+    p.M = M; p.N = N; p.K = K;
+    p.k_per_split = K;
+    return pipe_gemm(false, b_nn, false, p, stream, PipeTile::Tall);
 }
 
 }  // namespace poetx

@@ -322,3 +322,17 @@ def test_block_grad_parity(T, d, b, dtype):
         assert not dG.any()
     else:
         assert rel_fro(host(dG), ref) <= (1e-5 if dtype == "f32" else 1e-5)
+
+
+@pytest.mark.parametrize("T,d,b,dtype", [(2048, 4096, 256, "bf16"), (300, 1024, 512, "bf16"), (77, 192, 64, "bf16"),
+                                         (33, 96, 32, "f32"), (129, 128, 16, "bf16")])
+@pytest.mark.parametrize("transpose", [True, False])
+def test_block_apply_parity(T, d, b, dtype, transpose):
+    X = I.gaussian((T, d), 1.0, dtype, 404, T, d)
+    G = I.gaussian((d // b, b, b), 0.1, dtype, 405, d, b)
+    out = torch.empty((T, d), dtype=tdtype(dtype), device=DEV)
+    B.poetx_block_apply(dev(X, dtype), dev(G, dtype), out, T, d, b, transpose_G=transpose)
+    x64, g64 = X.astype(np.float64), G.astype(np.float64)
+    ref = np.concatenate([x64[:, j * b:(j + 1) * b] @ (g64[j].T if transpose else g64[j]) for j in range(d // b)],
+                         axis=1)
+    assert rel_fro(host(out), ref) <= (4e-3 if dtype == "bf16" else 1e-6)
