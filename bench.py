@@ -44,7 +44,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 256 << 20      # plain copy every run performs (counter scale reference)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.json")
 GEMM_SRC = os.path.join(ROOT, "orthogonal_equivalence_poet_amd", "csrc", "dense_gemm.hip")
-DENSE_KERNEL_TAG = "dense_gemm_kernel<false>"   # the dense NT (forward) instantiation (demangled)
+DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false>"   # dense NT (forward), demangled
+COPY_KERNEL_TAG = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 
 def gemm_source_hash() -> str:
@@ -213,7 +214,7 @@ def parse_pmc(pmc_dir):
                 v = float(row.get("Counter_Value", "nan"))
                 if DENSE_KERNEL_TAG in name:
                     key = "gemm"
-                elif "copy" in name.lower() or "elementwise_kernel" in name:
+                elif COPY_KERNEL_TAG in name:
                     key = "copy"
                 else:
                     continue
@@ -263,7 +264,7 @@ def main():
     step = make_step(spec, S)
 
     # reference copy of known size (scale for the HBM counters)
-    cs = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    cs = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
     cd = torch.empty_like(cs)
     cd.copy_(cs)
 

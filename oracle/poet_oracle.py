@@ -42,6 +42,7 @@ __all__ = [
     "orthogonal_from_blocks", "prepermute", "blocks_from_params",
     "forward", "forward_from_blocks", "backward", "backward_from_blocks",
     "cnp_vjp", "merge", "effective_weight",
+    "input_grad", "block_grad_entries", "block_grad_blocks", "merge_entries",
 ]
 
 
@@ -318,6 +319,32 @@ def block_grad_entries(dy, x, W0, G_R, G_P, pi_R, pi_P, side: str, entries):
             if a not in cache:
                 cache[a] = dy @ (R @ W0[:, a])
             out[i] = cache[a] @ x[:, e]
+    return out
+
+
+def block_grad_blocks(dy, x, W0, G_R, G_P, pi_R, pi_P, side: str, blocks):
+    """Whole blocks j of dG_R or dG_P (see backward_from_blocks).
+
+    With idx = pi[jb : (j+1)b] the basis indices of block j,
+    dG_R,j = dY[:, idx]^T (X P^T W0[idx, :]^T) and
+    dG_P,j = (dY R W0[:, idx])^T X[:, idx]."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    b = G_R.shape[-1]
+    out = np.empty((len(blocks), b, b))
+    if side == "R":
+        P = orthogonal_from_blocks(G_P, pi_P)
+        pi = np.asarray(pi_R, dtype=np.int64)
+        for t, j in enumerate(blocks):
+            idx = pi[j * b:(j + 1) * b]
+            out[t] = dy[:, idx].T @ (x @ (P.T @ W0[idx, :].T))
+    else:
+        R = orthogonal_from_blocks(G_R, pi_R)
+        pi = np.asarray(pi_P, dtype=np.int64)
+        for t, j in enumerate(blocks):
+            idx = pi[j * b:(j + 1) * b]
+            out[t] = (dy @ (R @ W0[:, idx])).T @ x[:, idx]
     return out
 
 

@@ -41,6 +41,22 @@ def _backward_block_transposed(dy, x, W0, G_R, G_P, pi_R, pi_P):
     return dx, np.swapaxes(dG_R, -1, -2), dG_P
 
 
+def _entries_transposed(dy, x, W0, G_R, G_P, pi_R, pi_P, side, entries):
+    return O.__dict__["_orig_entries"](dy, x, W0, G_R, G_P, pi_R, pi_P, side, [(j, c, r) for j, r, c in entries])
+
+
+def _blocks_transposed(dy, x, W0, G_R, G_P, pi_R, pi_P, side, blocks):
+    return np.swapaxes(O.__dict__["_orig_blocks"](dy, x, W0, G_R, G_P, pi_R, pi_P, side, blocks), -1, -2)
+
+
+def _input_grad_r_transposed(dy, W0, G_R, G_P, pi_R, pi_P):
+    return O.__dict__["_orig_igrad"](dy, W0, np.swapaxes(G_R, -1, -2), G_P, pi_R, pi_P)
+
+
+def _merge_entries_old_perms(Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_new, pi_P_new, entries):
+    return O.__dict__["_orig_merge_e"](Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_old, pi_P_new, entries)
+
+
 MUTATIONS = [
     ("params_grad_from_skew_grad", _pack_sign_flip, "_orig_pack",
      [P.test_skew_exact_and_pack_adjoint]),
@@ -56,6 +72,14 @@ MUTATIONS = [
      [P.test_cnp_vjp_matches_finite_differences, lambda: P.test_backward_matches_finite_differences(3)]),
     ("backward_from_blocks", _backward_block_transposed, "_orig_bwd",
      [lambda: P.test_backward_matches_finite_differences(3)]),
+    ("block_grad_entries", _entries_transposed, "_orig_entries",
+     [P.test_sampled_block_grads_match_finite_differences]),
+    ("block_grad_blocks", _blocks_transposed, "_orig_blocks",
+     [P.test_sampled_block_grads_match_finite_differences]),
+    ("input_grad", _input_grad_r_transposed, "_orig_igrad",
+     [P.test_sampled_input_grad_rows_brute_force]),
+    ("merge_entries", _merge_entries_old_perms, "_orig_merge_e",
+     [P.test_merge_entries_match_merged_function]),
 ]
 
 

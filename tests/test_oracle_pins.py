@@ -312,3 +312,82 @@ def test_merge_with_zero_q_and_same_perms_is_identity():
     Wt = O.prepermute(W0, pi_R, pi_P)
     Wt2, _, _ = O.merge(Wt, 0 * q_R, 0 * q_P, pi_R, pi_P, pi_R, pi_P, 4, 3)
     assert np.array_equal(Wt2, Wt)
+
+
+# ------------------------------------- outputs the oracle computes one by one
+def _blocks(rng, nblk, b, k=3, std=0.3):
+    return O.blocks_from_params(_rand_q(rng, nblk, b, std), b, k)
+
+
+def _loss_g(dy, x, W0, G_R, G_P, pi_R, pi_P):
+    return np.sum(dy * O.forward_from_blocks(x, W0, G_R, G_P, pi_R, pi_P))
+
+
+def test_sampled_block_grads_match_finite_differences():
+    # L = <dY, X P^T W0^T R^T> is linear in every entry of G_R and of G_P, so a
+    # central difference is exact up to rounding.
+    rng = np.random.default_rng(21)
+    m, n, b, T = 12, 8, 4, 6
+    W0, _, _, x, dy, pi_R, pi_P = _layer(rng, m, n, b, T)
+    G_R, G_P = _blocks(rng, m // b, b), _blocks(rng, n // b, b)
+    h = 1e-3
+    for side, G, nblk in (("R", G_R, m // b), ("P", G_P, n // b)):
+        entries = [(j, r, c) for j in range(nblk) for r in range(b) for c in range(b)]
+        got = O.block_grad_entries(dy, x, W0, G_R, G_P, pi_R, pi_P, side, entries)
+        whole = O.block_grad_blocks(dy, x, W0, G_R, G_P, pi_R, pi_P, side, list(range(nblk)))
+        fd = np.empty(len(entries))
+        for i, (j, r, c) in enumerate(entries):
+            Gp, Gm = G.copy(), G.copy()
+            Gp[j, r, c] += h
+            Gm[j, r, c] -= h
+            args_p = (Gp, G_P) if side == "R" else (G_R, Gp)
+            args_m = (Gm, G_P) if side == "R" else (G_R, Gm)
+            fd[i] = (_loss_g(dy, x, W0, *args_p, pi_R, pi_P) - _loss_g(dy, x, W0, *args_m, pi_R, pi_P)) / (2 * h)
+        assert np.allclose(got, fd, rtol=0, atol=1e-9)
+        assert np.allclose(whole.reshape(-1), fd, rtol=0, atol=1e-9)
+
+
+def test_sampled_input_grad_rows_brute_force():
+    # dx[t, i] = sum_o dy[t, o] * W_RP[o, i] with W_RP[o, i] = sum_{a, e} R[o, a] W0[a, e] P[e, i],
+    # summed term by term from the block entries: R[pi_R[u], pi_R[v]] = G_R[u // b][u % b, v % b]
+    # when u, v lie in the same block.
+    rng = np.random.default_rng(22)
+    m, n, b, T = 8, 6, 2, 3
+    W0, _, _, x, dy, pi_R, pi_P = _layer(rng, m, n, b, T)
+    G_R, G_P = _blocks(rng, m // b, b), _blocks(rng, n // b, b)
+
+    def entry(G, pi, row, col):
+        u, v = int(np.where(pi == row)[0][0]), int(np.where(pi == col)[0][0])
+        return G[u // b][u % b, v % b] if u // b == v // b else 0.0
+
+    W = np.zeros((m, n))
+    for o in range(m):
+        for i in range(n):
+            W[o, i] = sum(entry(G_R, pi_R, o, a) * W0[a, e] * entry(G_P, pi_P, e, i)
+                          for a in range(m) for e in range(n))
+    rows = [2, 0]
+    got = O.input_grad(dy[rows], W0, G_R, G_P, pi_R, pi_P)
+    for t, row in enumerate(rows):
+        for i in range(n):
+            assert abs(got[t, i] - sum(dy[row, o] * W[o, i] for o in range(m))) < 1e-12
+    y = O.forward_from_blocks(x[rows], W0, G_R, G_P, pi_R, pi_P)
+    for t, row in enumerate(rows):
+        for o in range(m):
+            assert abs(y[t, o] - sum(W[o, i] * x[row, i] for i in range(n))) < 1e-12
+
+
+def test_merge_entries_match_merged_function():
+    # Folding the layer into the weight keeps y unchanged: with the merged stored
+    # weight Wt', q = 0 and the new permutations, y = Pi_R'^T Wt' Pi_P' x.
+    rng = np.random.default_rng(23)
+    m, n, b, T, k = 12, 8, 4, 5, 3
+    W0, q_R, q_P, x, _, pi_R, pi_P = _layer(rng, m, n, b, T)
+    Wt = O.prepermute(W0, pi_R, pi_P)
+    pi_R2, pi_P2 = rng.permutation(m), rng.permutation(n)
+    G_R, G_P = O.blocks_from_params(q_R, b, k), O.blocks_from_params(q_P, b, k)
+    entries = [(i, j) for i in range(m) for j in range(n)]
+    Wt2 = O.merge_entries(Wt, G_R, G_P, pi_R, pi_P, pi_R2, pi_P2, entries).reshape(m, n)
+    W_new = np.empty((m, n))
+    W_new[np.ix_(pi_R2, pi_P2)] = Wt2
+    y_before = O.forward(x, W0, q_R, q_P, pi_R, pi_P, b, k)
+    assert np.allclose(x @ W_new.T, y_before, rtol=0, atol=1e-13)
