@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 256 << 20      # plain copy every run performs (counter scale reference)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.json")
 GEMM_SRC = os.path.join(ROOT, "orthogonal_equivalence_poet_amd", "csrc", "dense_gemm.hip")
-DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false>"   # dense NT (forward), demangled
+DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false, false, 3>"   # dense NT (forward), demangled
 COPY_KERNEL_TAG = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 

@@ -100,6 +100,31 @@ struct Mat {
     int64_t stride;
 };
 
+// Products of small matrices (the Cayley-Neumann b x b products): bf16 operands
+// that meet the direct-to-LDS load rules go to the pipelined kernel with the
+// general epilogue, everything else to the register-staged kernel.
+hipError_t small_gemm(const GemmArgs& g, GemmLayout layout, bool cbf16, bool obf16, hipStream_t s) {
+    const bool a_mn = layout == GemmLayout::TN;
+    const bool b_mn = layout != GemmLayout::NT;
+    const bool aligned = ((uintptr_t)g.A | (uintptr_t)g.B) % 16 == 0;
+    if (cbf16 && aligned && g.M <= 1024 && g.N <= 1024 && g.splits == 1 &&
+        pipe_gemm_supported(a_mn, b_mn, g.M, g.N, g.K, g.lda, g.ldb, g.strideA, g.strideB)) {
+        PipeArgs p;
+        p.A = g.A; p.lda = g.lda; p.strideA = g.strideA;
+        p.B = g.B; p.ldb = g.ldb; p.strideB = g.strideB;
+        p.C = g.C; p.ldc = g.ldc; p.strideC = g.strideC;
+        p.C2 = g.C2; p.C3 = g.C3; p.ldc2 = g.ldc2; p.strideC2 = g.strideC2;
+        p.Cin1 = g.Cin1; p.ldcin1 = g.ldcin1; p.strideCin1 = g.strideCin1;
+        p.Cin2 = g.Cin2; p.ldcin2 = g.ldcin2; p.strideCin2 = g.strideCin2;
+        p.alpha = g.alpha; p.beta1 = g.beta1; p.beta2 = g.beta2; p.gamma = g.gamma; p.mode = g.mode;
+        p.M = g.M; p.N = g.N; p.K = g.K;
+        p.batch = g.batch;
+        p.k_per_split = g.K;
+        return pipe_gemm_general(a_mn, b_mn, !obf16, p, s);
+    }
+    return gemm_launch(g, layout, pick_tile(cbf16, g.M, g.N, g.batch), cbf16, obf16, s);
+}
+
 hipError_t gemm(GemmLayout layout, bool cbf16, bool obf16, int64_t M, int64_t N, int64_t K, int64_t batch, Mat A,
                 Mat B, void* C, int64_t ldc, int64_t sC, hipStream_t s, float alpha = 1.f,
                 const float* cin1 = nullptr, float beta1 = 0.f, const float* cin2 = nullptr, float beta2 = 0.f,
@@ -116,7 +141,7 @@ hipError_t gemm(GemmLayout layout, bool cbf16, bool obf16, int64_t M, int64_t N,
     g.batch = (int)batch;
     g.splits = 1;
     g.k_per_split = (int)std::max<int64_t>(K, 1);
-    (void)dense;
+    if (!dense) return small_gemm(g, layout, cbf16, obf16, s);
     return gemm_launch(g, layout, pick_tile(cbf16, M, N, batch), cbf16, obf16, s);
 }
 
@@ -218,7 +243,7 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
         g.M = g.N = g.K = (int)b;
         g.batch = (int)nblk;
         g.k_per_split = (int)b;
-        HIP_TRY(gemm_launch(g, GemmLayout::NT, pick_tile(cbf16, b, b, nblk), cbf16, false, s));
+        HIP_TRY(small_gemm(g, GemmLayout::NT, cbf16, false, s));
     } else if (k == 4) {
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Qc, b), B.S32, b, b * b, s,
                      -1.f, nullptr, 0, nullptr, 0, 0, cbf16 ? B.Sc : nullptr));

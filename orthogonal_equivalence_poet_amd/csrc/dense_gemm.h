@@ -19,6 +19,19 @@ struct PipeArgs {
     int batch = 1;
     int splits = 1;
     int k_per_split = 0;       // multiple of 64
+    // General epilogue (pipe_gemm_general only).  With v = alpha * acc:
+    //   mode 0: o = v + beta1 Cin1 + beta2 Cin2 + gamma [row == col];
+    //           C = o (output dtype, if C), C2 = o (bf16, if C2);
+    //   mode 1 (Cayley-Neumann square): C = 2 Cin1 + 2 v, C2 = v, C3 = 2 Cin1 + v.
+    void* C2 = nullptr;        // bf16
+    void* C3 = nullptr;        // bf16, same layout as C2
+    int64_t ldc2 = 0, strideC2 = 0;
+    const float* Cin1 = nullptr;
+    int64_t ldcin1 = 0, strideCin1 = 0;
+    const float* Cin2 = nullptr;
+    int64_t ldcin2 = 0, strideCin2 = 0;
+    float alpha = 1.f, beta1 = 0.f, beta2 = 0.f, gamma = 0.f;
+    int mode = 0;
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead
@@ -35,6 +48,11 @@ bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, 
                          int64_t strideA, int64_t strideB);
 hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile);
 int pipe_tile_rows(PipeTile t);
+// Batched products of small matrices (the Cayley-Neumann b x b products) with the
+// general epilogue above: 64 x 64 workgroup tiles, or 128 x 128 when the batch is
+// large enough to fill the chip with them.  Operand layouts as in pipe_gemm
+// ((a_mn, b_mn) = (0, 0), (0, 1) or (1, 1)); no split-K.
+hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream);
 int pipe_tile_cols(PipeTile t);
 
 // Dense convenience wrappers (batch 1, no split).

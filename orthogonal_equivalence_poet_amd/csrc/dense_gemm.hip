@@ -6,16 +6,21 @@
 //   grads   dG_j = dz_j^T h2_j                          (A and B m/n-major, K = tokens,
 //                                                        split along K, float32 out)
 //
+//   small   the Cayley-Neumann b x b products (batched over blocks, general
+//           epilogue with float32 addends and several outputs)
+//
 // Workgroup tile BM x BN x 64 (256 x 128 for the dense products, 128 x 256 for
-// the block products, 128 x 128 for the block gradients), four waves in a 2 x 2
-// grid, each wave owning a (BM/2) x (BN/2) sub-tile of v_mfma_f32_32x32x16_bf16
-// tiles (float32 accumulators in AGPRs).
+// the block products, 128 x 128 for the block gradients, 64 x 64 or 128 x 128
+// for the small products), four waves in a 2 x 2 grid, each wave owning a
+// (BM/2) x (BN/2) sub-tile of v_mfma_f32_32x32x16_bf16 tiles (float32
+// accumulators in AGPRs).
 //
 // Operand tiles travel global -> LDS by direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so no
-// VGPRs stage them and no ds_write is issued.  Three LDS stages form a ring:
-// while the MFMAs consume stage kt % 3, the loads of tiles kt+1 and kt+2 are in
-// flight.  The loads are issued from inline asm so that the compiler does not
+// VGPRs stage them and no ds_write is issued.  S LDS stages form a ring (S = 3
+// for the large tiles, 4 for the 128 x 128 and 64 x 64 ones): while the MFMAs
+// consume stage kt % S, the loads of tiles kt+1 .. kt+S-1 are in flight, so a
+// short product (K = 256) waits for memory once.  The loads are issued from inline asm so that the compiler does not
 // add a conservative vmcnt(0) before every LDS read; the kernel itself waits
 // (s_waitcnt vmcnt) for exactly the tile it is about to read, then barriers.
 //
@@ -25,7 +30,7 @@
 //     of row r sits in slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), which
 //     keeps the ds_read_b128 fragment reads free of bank conflicts;
 //   m/n-major tile [64 k][rows], 256- or 512-byte rows: chunk c of k-row k sits
-//     in slot c ^ 4 (k & 3); fragments are read with ds_read_b64_tr_b16, which
+//     in slot c ^ 4 (k & 3) (128-byte rows: c ^ 4 ((k >> 1) & 1)); fragments are read with ds_read_b64_tr_b16, which
 //     transposes 16-lane groups so that lane i receives four consecutive k of
 //     column i; the swizzle spreads the four k-rows x four chunks that 32 lanes
 //     touch over all 64 banks.
@@ -45,7 +50,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStages = 3;
 
 // Workgroup tile BM x BN (x 64 k), four waves in a 2 x 2 grid.
 template <int BM_, int BN_>
@@ -86,7 +90,13 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_mn(int k) { return 4 * (k & 3); }
+// m/n-major k-rows of 16 or more chunks rotate by 4 chunks per k; 64-column
+// tiles (8 chunks, two k-rows per 256 bytes of banks) flip by 4 every other k.
+template <int ROWS>
+__device__ __forceinline__ int swz_mn(int k) {
+    if constexpr (ROWS >= 128) return 4 * (k & 3);
+    else return 4 * ((k >> 1) & 1);
+}
 
 // Loads of one operand tile into LDS at byte offset `dst`.
 //   k-major: ROWS rows x 64 k from src[row][k] (ld = row stride), rows clamped to rows_total.
@@ -113,7 +123,7 @@ __device__ __forceinline__ void dma_operand(uint32_t dst, const uint16_t* __rest
         for (int j = 0; j < 64 / kRowsPerRun / 4; ++j) {
             const int g = j * 4 + wave;
             const int kr = kRowsPerRun * g + lane / kSlots;
-            const int c = (lane % kSlots) ^ swz_mn(kr);
+            const int c = (lane % kSlots) ^ swz_mn<ROWS>(kr);
             const int col = min(r0 + c * 8, rows_total - 8);
             const int k = min(k0 + kr, k_end - 1);
             dma16(src + (int64_t)k * ld + col, __builtin_amdgcn_readfirstlane(dst + g * 1024));
@@ -146,7 +156,7 @@ __device__ __forceinline__ uint4 load_frag(const unsigned char* __restrict__ bas
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int kr = ks * 16 + 8 * (lane >> 5) + 4 * hh + e;
-            const int sl = (cb >> 3) ^ swz_mn(kr);
+            const int sl = (cb >> 3) ^ swz_mn<ROWS>(kr);
             const unsigned char* p = base + kr * (ROWS * 2) + sl * 16 + (cb & 7) * 2;
             h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t*)((lds_void_t*)p));
@@ -201,24 +211,116 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
     tn = r / gm;
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Batched launches (grid.y = batch entries): the launch slots an XCD receives
+// are regrouped so that each XCD owns whole batch entries, and every operand
+// panel of an entry is fetched into one L2 only.  Within an entry tiles run
+// down the M direction first.  A single product keeps the grouped order above.
+__device__ __forceinline__ void batch_tile_coords(int tiles_m, int tiles_n, int& z, int& tm, int& tn) {
+    if (gridDim.y == 1) {
+        z = 0;
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+        return;
+    }
+    const int tiles = tiles_m * tiles_n;
+    const int total = tiles * (int)gridDim.y;
+    int id = blockIdx.x + tiles * blockIdx.y;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+    z = id / tiles;
+    const int t = id - z * tiles;
+    tm = t % tiles_m;
+    tn = t / tiles_m;
+}
+
+// Register budget: the 256 x 128 and 128 x 256 tiles hold 128 accumulators per
+// lane and their LDS ring allows one workgroup per CU, so they take the whole
+// register file; smaller tiles leave room for several workgroups per CU.
+template <int BM, int BN> struct PipeWaves {
+    static constexpr int lo = 1;
+    static constexpr int hi = (BM * BN >= 256 * 128) ? 1 : 4;
+};
+
+// General epilogue of one wave (see PipeArgs): addends are fetched for a whole
+// 32 x 32 tile first, then combined and stored.
+template <int MI, int NJ, typename OutT>
+__device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[MI][NJ], int row0, int col0,
+                                                 int z) {
+    const float* __restrict__ cin1 = p.Cin1 ? p.Cin1 + (int64_t)z * p.strideCin1 : nullptr;
+    const float* __restrict__ cin2 = p.Cin2 ? p.Cin2 + (int64_t)z * p.strideCin2 : nullptr;
+    OutT* __restrict__ c1 = p.C ? reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC : nullptr;
+    bf16_t* __restrict__ c2 = p.C2 ? reinterpret_cast<bf16_t*>(p.C2) + (int64_t)z * p.strideC2 : nullptr;
+    bf16_t* __restrict__ c3 = p.C3 ? reinterpret_cast<bf16_t*>(p.C3) + (int64_t)z * p.strideC2 : nullptr;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = col0 + j * 32;
+            const int cc = min(col, p.N - 1);
+            float a1[16], a2[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = min(row0 + i * 32 + (r >> 2) * 8 + (r & 3), p.M - 1);
+                a1[r] = cin1 ? cin1[(int64_t)row * p.ldcin1 + cc] : 0.f;
+                a2[r] = cin2 ? cin2[(int64_t)row * p.ldcin2 + cc] : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                if (row >= p.M || col >= p.N) continue;
+                const float v = p.alpha * acc[i][j][r];
+                if (p.mode == 1) {
+                    const float q2 = 2.f * a1[r];
+                    store_f32(c1 + (int64_t)row * p.ldc + col, q2 + 2.f * v);
+                    store_f32(c2 + (int64_t)row * p.ldc2 + col, v);
+                    store_f32(c3 + (int64_t)row * p.ldc2 + col, q2 + v);
+                    continue;
+                }
+                float o = v + p.beta1 * a1[r] + p.beta2 * a2[r];
+                if (row == col) o += p.gamma;
+                if (c1) store_f32(c1 + (int64_t)row * p.ldc + col, o);
+                if (c2) store_f32(c2 + (int64_t)row * p.ldc2 + col, o);
+            }
+        }
+}
+
+// Wait until at most `tiles` k-tiles of this thread's loads are still in flight
+// (tiles is wave-uniform and at most S - 2).
+template <int LPT, int S>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+    static_assert(S >= 2 && S <= 8 && LPT * (S - 2) < 64, "vmcnt range");
+    switch (tiles) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: if constexpr (S > 2) wait_vmcnt<LPT>(); break;
+        case 2: if constexpr (S > 3) wait_vmcnt<2 * LPT>(); break;
+        case 3: if constexpr (S > 4) wait_vmcnt<3 * LPT>(); break;
+        case 4: if constexpr (S > 5) wait_vmcnt<4 * LPT>(); break;
+        case 5: if constexpr (S > 6) wait_vmcnt<5 * LPT>(); break;
+        default: if constexpr (S > 7) wait_vmcnt<6 * LPT>(); break;
+    }
+}
+
+// S-stage LDS ring: S - 1 k-tiles are requested before the first one is used,
+// so a product with K <= 64 (S - 1) waits for memory once.
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN, int S>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN>::lo, PipeWaves<BM, BN>::hi)))
 pipe_gemm_kernel(const PipeArgs p) {
     using G = Geo<BM, BN>;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     constexpr int kLoadsPerTile = G::kLoadsPerTile;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * kStageBytes];
+    static_assert(S * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int M = p.M, N = p.N;
     int tm, tn;
-    tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    int z;
+    batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)blockIdx.y * p.strideA;
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)blockIdx.y * p.strideB;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
     const int kb = blockIdx.z * p.k_per_split;
     const int ke = min(p.K, kb + p.k_per_split);
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
@@ -232,15 +334,18 @@ pipe_gemm_kernel(const PipeArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    if (nk > 0) dma_tile<G, A_MN, B_MN>(base, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, wave, lane);
-    if (nk > 1)
-        dma_tile<G, A_MN, B_MN>(base + kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N, kb + BK, ke, wave, lane);
-    int st = 0;   // stage of tile kt
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < nk)
+            dma_tile<G, A_MN, B_MN>(base + t * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N, kb + t * BK, ke, wave,
+                                    lane);
+    int st = 0;        // stage of tile kt
+    int st_load = S - 1;   // stage that receives tile kt + S - 1
     for (int kt = 0; kt < nk; ++kt) {
-        // this thread's loads of tile kt are done when at most those of tile kt+1 remain
-        if (kt + 1 < nk) wait_vmcnt<kLoadsPerTile>();
-        else wait_vmcnt<0>();
-        block_barrier();   // everyone's tile kt has landed; stage (kt+2)%3 is no longer read
+        // this thread's loads of tile kt are done when at most those of the
+        // tiles after it (up to kt + S - 2) remain
+        wait_tiles<kLoadsPerTile, S>(min(nk, kt + S - 1) - kt - 1);
+        block_barrier();   // everyone's tile kt has landed; stage st_load (tile kt-1) is no longer read
         if constexpr (A_MN || B_MN) {
             const int valid = ke - (kb + kt * BK);
             if (valid < BK) {   // ragged last tile: rows past K were loaded from clamped rows
@@ -249,20 +354,23 @@ pipe_gemm_kernel(const PipeArgs p) {
                 __syncthreads();
             }
         }
-        if (kt + 2 < nk) {
-            const int st2 = st >= 1 ? st - 1 : 2;   // (kt + 2) % 3
-            dma_tile<G, A_MN, B_MN>(base + st2 * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N,
-                                    kb + (kt + 2) * BK, ke, wave, lane);
-        }
+        if (kt + S - 1 < nk)
+            dma_tile<G, A_MN, B_MN>(base + st_load * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N,
+                                    kb + (kt + S - 1) * BK, ke, wave, lane);
         compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc);
-        st = st == 2 ? 0 : st + 1;
+        st = st == S - 1 ? 0 : st + 1;
+        st_load = st_load == S - 1 ? 0 : st_load + 1;
     }
 
     // epilogue: lane holds rows 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 per tile
     using OutT = typename std::conditional<OUT_F32, float, bf16_t>::type;
-    OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)blockIdx.y * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
     const int col0 = n0 + wn * WTN + (lane & 31);
     const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
+    if constexpr (GEN) {
+        general_epilogue<MI, NJ, OutT>(p, acc, row0, col0, z);
+        return;
+    }
+    OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -287,7 +395,7 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32>
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN = false, int S = 3>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -296,8 +404,12 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         q.batch = min(kMaxY, p.batch - y0);
         q.A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)y0 * p.strideA;
         q.B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)y0 * p.strideB;
-        q.C = reinterpret_cast<char*>(p.C) + (int64_t)y0 * p.strideC * (OUT_F32 ? 4 : 2);
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32>), dim3(tiles, q.batch, p.splits),
+        if (p.C) q.C = reinterpret_cast<char*>(p.C) + (int64_t)y0 * p.strideC * (OUT_F32 ? 4 : 2);
+        if (p.C2) q.C2 = reinterpret_cast<bf16_t*>(p.C2) + (int64_t)y0 * p.strideC2;
+        if (p.C3) q.C3 = reinterpret_cast<bf16_t*>(p.C3) + (int64_t)y0 * p.strideC2;
+        if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)y0 * p.strideCin1;
+        if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, GEN, S>), dim3(tiles, q.batch, p.splits),
                            dim3(kThreads), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -329,10 +441,30 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
         return b_mn ? launch<256, 128, false, true, false>(p, stream) : launch<256, 128, false, false, false>(p, stream);
     }
     if (a_mn && b_mn && out_f32) {
-        if (tile == PipeTile::Square) return launch<128, 128, true, true, true>(p, stream);
+        if (tile == PipeTile::Square) return launch<128, 128, true, true, true, false, 4>(p, stream);
         return launch<256, 128, true, true, true>(p, stream);
     }
     return hipErrorInvalidValue;
+}
+
+template <int T, bool OUT_F32>
+hipError_t launch_general(bool a_mn, bool b_mn, const PipeArgs& p, hipStream_t stream) {
+    if (!a_mn && !b_mn) return launch<T, T, false, false, OUT_F32, true, 4>(p, stream);
+    if (!a_mn && b_mn) return launch<T, T, false, true, OUT_F32, true, 4>(p, stream);
+    return launch<T, T, true, true, OUT_F32, true, 4>(p, stream);
+}
+
+hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream) {
+    if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+    if (a_mn && !b_mn) return hipErrorInvalidValue;
+    if (p.splits != 1) return hipErrorInvalidValue;
+    // 128 x 128 tiles only when they alone give about four workgroups per CU
+    const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    if (big >= 1024) {
+        return out_f32 ? launch_general<128, true>(a_mn, b_mn, p, stream)
+                       : launch_general<128, false>(a_mn, b_mn, p, stream);
+    }
+    return out_f32 ? launch_general<64, true>(a_mn, b_mn, p, stream) : launch_general<64, false>(a_mn, b_mn, p, stream);
 }
 
 int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : 128; }

@@ -118,7 +118,11 @@ __global__ void skew_pack_simple(const float* __restrict__ dQ, float* __restrict
 // ------------------------------------------------------------- permutation
 // A workgroup owns `rows_per_wg` full rows, staged in LDS: gathers read the
 // row contiguously and pick from LDS; scatters place into LDS and write the
-// row contiguously.  Both global streams are 16-byte vectors.
+// row contiguously.  Both global streams are 16-byte vectors.  Every thread
+// issues kBatch loads (data and indices) before it uses any of them, so a
+// workgroup waits for memory a few times, not once per vector.
+constexpr int kPermBatch = 8;
+
 template <typename T>
 __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ src, T* __restrict__ dst,
                                                         int64_t rows, int cols, const int* __restrict__ row_idx,
@@ -127,37 +131,78 @@ __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ sr
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     T* buf = reinterpret_cast<T*>(smem_raw);
     constexpr int V = ElemTraits<T>::kVec;
+    constexpr int NB = kPermBatch;
     const int chunks = cols / V;
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     const int nrows = (int)min<int64_t>(rows_per_wg, rows - row0);
     const int total = nrows * chunks;
-    for (int u = threadIdx.x; u < total; u += blockDim.x) {
-        const int r = u / chunks;
-        const int c = (u % chunks) * V;
-        const int64_t gr = row0 + r;
-        const int64_t sr = row_idx ? row_idx[gr] : gr;
-        const uint4 v = *reinterpret_cast<const uint4*>(src + sr * cols + c);
-        if (scatter && col_idx) {
-            const T* e = reinterpret_cast<const T*>(&v);
+    const bool scat = scatter && col_idx;
+    for (int u0 = threadIdx.x; u0 < total; u0 += 256 * NB) {
+        uint4 v[NB];
+        int ci[NB][V];
 #pragma unroll
-            for (int i = 0; i < V; ++i) buf[r * cols + col_idx[c + i]] = e[i];
-        } else {
-            *reinterpret_cast<uint4*>(buf + r * cols + c) = v;
+        for (int k = 0; k < NB; ++k) {
+            const int u = u0 + k * 256;
+            if (u < total) {
+                const int r = u / chunks;
+                const int c = (u % chunks) * V;
+                const int64_t gr = row0 + r;
+                const int64_t sr = row_idx ? row_idx[gr] : gr;
+                v[k] = *reinterpret_cast<const uint4*>(src + sr * cols + c);
+                if (scat) {
+#pragma unroll
+                    for (int i = 0; i < V; ++i) ci[k][i] = col_idx[c + i];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int u = u0 + k * 256;
+            if (u < total) {
+                const int r = u / chunks;
+                const int c = (u % chunks) * V;
+                if (scat) {
+                    const T* e = reinterpret_cast<const T*>(&v[k]);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) buf[r * cols + ci[k][i]] = e[i];
+                } else {
+                    *reinterpret_cast<uint4*>(buf + r * cols + c) = v[k];
+                }
+            }
         }
     }
     __syncthreads();
-    for (int u = threadIdx.x; u < total; u += blockDim.x) {
-        const int r = u / chunks;
-        const int c = (u % chunks) * V;
-        uint4 v;
-        if (scatter || !col_idx) {
-            v = *reinterpret_cast<const uint4*>(buf + r * cols + c);
-        } else {
-            T* e = reinterpret_cast<T*>(&v);
+    const bool gath = !scatter && col_idx;
+    for (int u0 = threadIdx.x; u0 < total; u0 += 256 * NB) {
+        int ci[NB][V];
+        if (gath) {
 #pragma unroll
-            for (int i = 0; i < V; ++i) e[i] = buf[r * cols + col_idx[c + i]];
+            for (int k = 0; k < NB; ++k) {
+                const int u = u0 + k * 256;
+                if (u < total) {
+                    const int c = (u % chunks) * V;
+#pragma unroll
+                    for (int i = 0; i < V; ++i) ci[k][i] = col_idx[c + i];
+                }
+            }
         }
-        *reinterpret_cast<uint4*>(dst + (row0 + r) * cols + c) = v;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int u = u0 + k * 256;
+            if (u < total) {
+                const int r = u / chunks;
+                const int c = (u % chunks) * V;
+                uint4 v;
+                if (!gath) {
+                    v = *reinterpret_cast<const uint4*>(buf + r * cols + c);
+                } else {
+                    T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) e[i] = buf[r * cols + ci[k][i]];
+                }
+                *reinterpret_cast<uint4*>(dst + (row0 + r) * cols + c) = v;
+            }
+        }
     }
 }
 
