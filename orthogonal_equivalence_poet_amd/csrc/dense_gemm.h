@@ -32,6 +32,7 @@ struct PipeArgs {
     int64_t ldcin2 = 0, strideCin2 = 0;
     float alpha = 1.f, beta1 = 0.f, beta2 = 0.f, gamma = 0.f;
     int mode = 0;
+    int epi_vec = 0;           // set by pipe_gemm_general: epilogue may use vector accesses
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead

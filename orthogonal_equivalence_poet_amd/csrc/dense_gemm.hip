@@ -49,17 +49,20 @@ namespace poetx {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 
-// Workgroup tile BM x BN (x 64 k), four waves in a 2 x 2 grid.
-template <int BM_, int BN_>
+// Workgroup tile BM x BN (x 64 k), NWM x NWN waves, each owning a WTM x WTN
+// sub-tile of MI x NJ 32 x 32 MFMA tiles.
+template <int BM_, int BN_, int NWM_ = 2, int NWN_ = 2>
 struct Geo {
-    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+    static constexpr int NW = NWM * NWN;
+    static constexpr int kThreads = 64 * NW;
     static constexpr int kABytes = BM * BK * 2;
     static constexpr int kBBytes = BN * BK * 2;
     static constexpr int kStageBytes = kABytes + kBBytes;
-    static constexpr int WTM = BM / 2, WTN = BN / 2, MI = WTM / 32, NJ = WTN / 32;
+    static constexpr int WTM = BM / NWM, WTN = BN / NWN, MI = WTM / 32, NJ = WTN / 32;
     static constexpr int kLoadsPerTile = (kABytes + kBBytes) / (kThreads * 16);
+    static_assert(MI >= 1 && NJ >= 1 && (kABytes + kBBytes) % (kThreads * 16) == 0, "tile geometry");
 };
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -102,41 +105,66 @@ __device__ __forceinline__ int swz_mn(int k) {
 //   k-major: ROWS rows x 64 k from src[row][k] (ld = row stride), rows clamped to rows_total.
 //   m/n-major: 64 k-rows x ROWS from src[k][col] (ld = k-row stride), k clamped to k_end,
 //   columns clamped to rows_total.
-template <int ROWS, bool MN>
-__device__ __forceinline__ void dma_operand(uint32_t dst, const uint16_t* __restrict__ src, int64_t ld, int r0,
-                                            int rows_total, int k0, int k_end, int wave, int lane) {
+// With NW waves each thread issues OperandLoads<ROWS, MN, NW>::n loads;
+// dma_one issues the j-th.
+template <int ROWS, bool MN, int NW>
+struct OperandLoads {
+    static constexpr int runs = ROWS * BK * 2 / 1024;   // 1 KB runs per operand tile
+    static constexpr int n = runs / NW;
+    static_assert(runs % NW == 0, "runs per wave");
+};
+
+template <int ROWS, bool MN, int NW>
+__device__ __forceinline__ void dma_one(int j, uint32_t dst, const uint16_t* __restrict__ src, int64_t ld, int r0,
+                                        int rows_total, int k0, int k_end, int wave, int lane) {
+    const int g = j * NW + wave;   // 1 KB run of this wave
     if constexpr (!MN) {
-        constexpr int kRuns = ROWS / 8;            // 8 rows of 128 bytes per 1 KB run
-#pragma unroll
-        for (int j = 0; j < kRuns / 4; ++j) {
-            const int g = j * 4 + wave;
-            const int r = 8 * g + (lane >> 3);
-            const int c = (lane & 7) ^ swz_k(r);
-            const int row = min(r0 + r, rows_total - 1);
-            dma16(src + (int64_t)row * ld + k0 + c * 8, __builtin_amdgcn_readfirstlane(dst + g * 1024));
-        }
+        const int r = 8 * g + (lane >> 3);           // 8 rows of 128 bytes per run
+        const int c = (lane & 7) ^ swz_k(r);
+        const int row = min(r0 + r, rows_total - 1);
+        dma16(src + (int64_t)row * ld + k0 + c * 8, __builtin_amdgcn_readfirstlane(dst + g * 1024));
     } else {
-        constexpr int kRowBytes = ROWS * 2;        // one k-row
+        constexpr int kRowBytes = ROWS * 2;          // one k-row
         constexpr int kRowsPerRun = 1024 / kRowBytes;
         constexpr int kSlots = kRowBytes / 16;
+        const int kr = kRowsPerRun * g + lane / kSlots;
+        const int c = (lane % kSlots) ^ swz_mn<ROWS>(kr);
+        const int col = min(r0 + c * 8, rows_total - 8);
+        const int k = min(k0 + kr, k_end - 1);
+        dma16(src + (int64_t)k * ld + col, __builtin_amdgcn_readfirstlane(dst + g * 1024));
+    }
+}
+
+// Everything needed to issue the loads of one k-tile into one LDS stage.
+struct DmaJob {
+    uint32_t stage;
+    const uint16_t* A;
+    int64_t lda;
+    const uint16_t* B;
+    int64_t ldb;
+    int m0, n0, M, N, k0, k_end, wave, lane;
+};
+
+// Part PART of NPARTS of a k-tile's loads (A's loads first, then B's), so the
+// loads can be spread over the MFMA work of the tile being computed.
+template <class G, bool A_MN, bool B_MN, int PART, int NPARTS>
+__device__ __forceinline__ void dma_part(const DmaJob& d) {
+    constexpr int NA = OperandLoads<G::BM, A_MN, G::NW>::n, NB = OperandLoads<G::BN, B_MN, G::NW>::n;
+    constexpr int L = NA + NB;
+    constexpr int lo = PART * L / NPARTS, hi = (PART + 1) * L / NPARTS;
 #pragma unroll
-        for (int j = 0; j < 64 / kRowsPerRun / 4; ++j) {
-            const int g = j * 4 + wave;
-            const int kr = kRowsPerRun * g + lane / kSlots;
-            const int c = (lane % kSlots) ^ swz_mn<ROWS>(kr);
-            const int col = min(r0 + c * 8, rows_total - 8);
-            const int k = min(k0 + kr, k_end - 1);
-            dma16(src + (int64_t)k * ld + col, __builtin_amdgcn_readfirstlane(dst + g * 1024));
-        }
+    for (int idx = lo; idx < hi; ++idx) {
+        if (idx < NA)
+            dma_one<G::BM, A_MN, G::NW>(idx, d.stage, d.A, d.lda, d.m0, d.M, d.k0, d.k_end, d.wave, d.lane);
+        else
+            dma_one<G::BN, B_MN, G::NW>(idx - NA, d.stage + G::kABytes, d.B, d.ldb, d.n0, d.N, d.k0, d.k_end,
+                                        d.wave, d.lane);
     }
 }
 
 template <class G, bool A_MN, bool B_MN>
-__device__ __forceinline__ void dma_tile(uint32_t stage, const uint16_t* __restrict__ A, int64_t lda,
-                                         const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M,
-                                         int N, int k0, int k_end, int wave, int lane) {
-    dma_operand<G::BM, A_MN>(stage, A, lda, m0, M, k0, k_end, wave, lane);
-    dma_operand<G::BN, B_MN>(stage + G::kABytes, B, ldb, n0, N, k0, k_end, wave, lane);
+__device__ __forceinline__ void dma_tile(const DmaJob& d) {
+    dma_part<G, A_MN, B_MN, 0, 1>(d);
 }
 
 // Fragment of 32 rows (k-major) or 32 columns (m/n-major) starting at `row0`
@@ -168,26 +196,49 @@ __device__ __forceinline__ uint4 load_frag(const unsigned char* __restrict__ bas
     }
 }
 
+// One k-tile (four k-steps of 16).  Fragments are double-buffered in
+// registers: the LDS reads of step ks+1 are issued before the MFMAs of step
+// ks, and scheduling barriers keep the compiler from sinking them, so each
+// wave (one per SIMD) waits for LDS once per k-tile instead of once per
+// fragment.
+template <class G, bool A_MN, bool B_MN>
+__device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st, int wm, int wn, int ks, int lane,
+                                           uint4 (&af)[G::MI], uint4 (&bfr)[G::NJ]) {
+#pragma unroll
+    for (int i = 0; i < G::MI; ++i) af[i] = load_frag<A_MN, G::BM>(st, wm * G::WTM + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < G::NJ; ++j) bfr[j] = load_frag<B_MN, G::BN>(st + G::kABytes, wn * G::WTN + j * 32, ks, lane);
+}
+
 template <class G, bool A_MN, bool B_MN>
 __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, int wm, int wn, int lane,
-                                             f32x16_t (&acc)[G::MI][G::NJ]) {
+                                             f32x16_t (&acc)[G::MI][G::NJ], const DmaJob& next, bool load_next) {
+    uint4 af[2][G::MI], bfr[2][G::NJ];
+    load_frags<G, A_MN, B_MN>(st, wm, wn, 0, lane, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-        uint4 af[G::MI], bfr[G::NJ];
-#pragma unroll
-        for (int i = 0; i < G::MI; ++i) af[i] = load_frag<A_MN, G::BM>(st, wm * G::WTM + i * 32, ks, lane);
-#pragma unroll
-        for (int j = 0; j < G::NJ; ++j)
-            bfr[j] = load_frag<B_MN, G::BN>(st + G::kABytes, wn * G::WTN + j * 32, ks, lane);
+        const int cur = ks & 1;
+        if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(st, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+        // a quarter of the next tile's loads per k-step
+        if (load_next) {
+            switch (ks) {
+                case 0: dma_part<G, A_MN, B_MN, 0, 4>(next); break;
+                case 1: dma_part<G, A_MN, B_MN, 1, 4>(next); break;
+                case 2: dma_part<G, A_MN, B_MN, 2, 4>(next); break;
+                default: dma_part<G, A_MN, B_MN, 3, 4>(next); break;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < G::MI; ++i)
 #pragma unroll
-            for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], acc[i][j]);
+            for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Zero the k-rows >= valid of an m/n-major tile (ragged last k-tile).
-template <int ROWS>
+template <int ROWS, int kThreads>
 __device__ __forceinline__ void zero_rows_mn(unsigned char* __restrict__ base, int valid, int tid) {
     constexpr int kChunks = ROWS * 2 / 16;   // 16-byte chunks per k-row
     for (int u = tid; u < (64 - valid) * kChunks; u += kThreads) {
@@ -234,52 +285,111 @@ __device__ __forceinline__ void batch_tile_coords(int tiles_m, int tiles_n, int&
 // Register budget: the 256 x 128 and 128 x 256 tiles hold 128 accumulators per
 // lane and their LDS ring allows one workgroup per CU, so they take the whole
 // register file; smaller tiles leave room for several workgroups per CU.
-template <int BM, int BN> struct PipeWaves {
+template <int BM, int BN, int NW> struct PipeWaves {
     static constexpr int lo = 1;
-    static constexpr int hi = (BM * BN >= 256 * 128) ? 1 : 4;
+    static constexpr int hi = (BM * BN >= 256 * 128) ? NW / 4 : 4;
 };
 
-// General epilogue of one wave (see PipeArgs): addends are fetched for a whole
-// 32 x 32 tile first, then combined and stored.
-template <int MI, int NJ, typename OutT>
-__device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[MI][NJ], int row0, int col0,
-                                                 int z) {
+// General epilogue (see PipeArgs), staged through LDS: the waves write their
+// accumulators into a BM x BN float32 tile (rows padded by 8 floats so that
+// the two row groups of a 32 x 32 MFMA tile land in different banks), then
+// every thread combines and stores row-contiguous 4-column chunks: 16-byte
+// float32 loads and stores, 8-byte bf16 stores, whole 256- or 512-byte rows
+// per wave instruction.  Chunks are taken element-wise when the host found
+// the addresses unsuited to vectors or the tile is clipped.
+template <int BM, int BN>
+struct EpiTile {
+    static constexpr int kLd = BN + 8;                       // floats per LDS row
+    static constexpr int kBytes = BM * kLd * 4;
+};
+
+__device__ __forceinline__ float4 load4(const float* __restrict__ p, bool vec, bool full, int valid) {
+    if (vec && full) return *reinterpret_cast<const float4*>(p);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid > 0) v.x = p[0];
+    if (valid > 1) v.y = p[1];
+    if (valid > 2) v.z = p[2];
+    if (valid > 3) v.w = p[3];
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* __restrict__ p, float4 v, bool vec, bool full, int valid) {
+    if constexpr (sizeof(T) == 4) {
+        if (vec && full) { *reinterpret_cast<float4*>(p) = v; return; }
+    } else {
+        if (vec && full) {
+            const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+            return;
+        }
+    }
+    if (valid > 0) store_f32(p, v.x);
+    if (valid > 1) store_f32(p + 1, v.y);
+    if (valid > 2) store_f32(p + 2, v.z);
+    if (valid > 3) store_f32(p + 3, v.w);
+}
+
+template <class G, typename OutT>
+__device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[G::MI][G::NJ], float* tile,
+                                                 int m0, int n0, int wm, int wn, int z, int tid) {
+    constexpr int BM = G::BM, BN = G::BN, MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
+    constexpr int kThreads = G::kThreads;
+    using E = EpiTile<BM, BN>;
+    const int lane = tid & 63;
+    block_barrier();   // every wave is done reading the operand stages
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int col = wn * WTN + j * 32 + (lane & 31);
+                tile[row * E::kLd + col] = acc[i][j][r];
+            }
+    __syncthreads();
     const float* __restrict__ cin1 = p.Cin1 ? p.Cin1 + (int64_t)z * p.strideCin1 : nullptr;
     const float* __restrict__ cin2 = p.Cin2 ? p.Cin2 + (int64_t)z * p.strideCin2 : nullptr;
     OutT* __restrict__ c1 = p.C ? reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC : nullptr;
     bf16_t* __restrict__ c2 = p.C2 ? reinterpret_cast<bf16_t*>(p.C2) + (int64_t)z * p.strideC2 : nullptr;
     bf16_t* __restrict__ c3 = p.C3 ? reinterpret_cast<bf16_t*>(p.C3) + (int64_t)z * p.strideC2 : nullptr;
+    const bool vec = p.epi_vec != 0;
+    constexpr int kChunks = BM * BN / 4;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int col = col0 + j * 32;
-            const int cc = min(col, p.N - 1);
-            float a1[16], a2[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = min(row0 + i * 32 + (r >> 2) * 8 + (r & 3), p.M - 1);
-                a1[r] = cin1 ? cin1[(int64_t)row * p.ldcin1 + cc] : 0.f;
-                a2[r] = cin2 ? cin2[(int64_t)row * p.ldcin2 + cc] : 0.f;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + i * 32 + (r >> 2) * 8 + (r & 3);
-                if (row >= p.M || col >= p.N) continue;
-                const float v = p.alpha * acc[i][j][r];
-                if (p.mode == 1) {
-                    const float q2 = 2.f * a1[r];
-                    store_f32(c1 + (int64_t)row * p.ldc + col, q2 + 2.f * v);
-                    store_f32(c2 + (int64_t)row * p.ldc2 + col, v);
-                    store_f32(c3 + (int64_t)row * p.ldc2 + col, q2 + v);
-                    continue;
-                }
-                float o = v + p.beta1 * a1[r] + p.beta2 * a2[r];
-                if (row == col) o += p.gamma;
-                if (c1) store_f32(c1 + (int64_t)row * p.ldc + col, o);
-                if (c2) store_f32(c2 + (int64_t)row * p.ldc2 + col, o);
-            }
+    for (int u0 = 0; u0 < kChunks; u0 += kThreads) {
+        const int u = u0 + tid;
+        const int row = u / (BN / 4);
+        const int c = (u % (BN / 4)) * 4;
+        const int gr = m0 + row, gc = n0 + c;
+        if (gr >= p.M || gc >= p.N) continue;
+        const int valid = min(4, p.N - gc);
+        const bool full = valid == 4;
+        float4 v = *reinterpret_cast<const float4*>(tile + row * E::kLd + c);
+        v.x *= p.alpha; v.y *= p.alpha; v.z *= p.alpha; v.w *= p.alpha;
+        const float4 a1 = cin1 ? load4(cin1 + (int64_t)gr * p.ldcin1 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.mode == 1) {
+            const float4 q2 = make_float4(2.f * a1.x, 2.f * a1.y, 2.f * a1.z, 2.f * a1.w);
+            store4(c1 + (int64_t)gr * p.ldc + gc,
+                   make_float4(q2.x + 2.f * v.x, q2.y + 2.f * v.y, q2.z + 2.f * v.z, q2.w + 2.f * v.w), vec, full, valid);
+            store4(c2 + (int64_t)gr * p.ldc2 + gc, v, vec, full, valid);
+            store4(c3 + (int64_t)gr * p.ldc2 + gc, make_float4(q2.x + v.x, q2.y + v.y, q2.z + v.z, q2.w + v.w), vec,
+                   full, valid);
+            continue;
         }
+        const float4 a2 = cin2 ? load4(cin2 + (int64_t)gr * p.ldcin2 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 o = make_float4(v.x + p.beta1 * a1.x + p.beta2 * a2.x, v.y + p.beta1 * a1.y + p.beta2 * a2.y,
+                               v.z + p.beta1 * a1.z + p.beta2 * a2.z, v.w + p.beta1 * a1.w + p.beta2 * a2.w);
+        if (p.gamma != 0.f) {
+            if (gr == gc) o.x += p.gamma;
+            if (gr == gc + 1) o.y += p.gamma;
+            if (gr == gc + 2) o.z += p.gamma;
+            if (gr == gc + 3) o.w += p.gamma;
+        }
+        if (c1) store4(c1 + (int64_t)gr * p.ldc + gc, o, vec, full, valid);
+        if (c2) store4(c2 + (int64_t)gr * p.ldc2 + gc, o, vec, full, valid);
+    }
 }
 
 // Wait until at most `tiles` k-tiles of this thread's loads are still in flight
@@ -300,11 +410,11 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
 
 // S-stage LDS ring: S - 1 k-tiles are requested before the first one is used,
 // so a product with K <= 64 (S - 1) waits for memory once.
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN, int S>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN>::lo, PipeWaves<BM, BN>::hi)))
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN, int S, int NWM = 2, int NWN = 2>
+__global__ void __launch_bounds__(64 * NWM * NWN)
+__attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
 pipe_gemm_kernel(const PipeArgs p) {
-    using G = Geo<BM, BN>;
+    using G = Geo<BM, BN, NWM, NWN>;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     constexpr int kLoadsPerTile = G::kLoadsPerTile;
@@ -313,7 +423,7 @@ pipe_gemm_kernel(const PipeArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / NWN, wn = wave % NWN;
     const int M = p.M, N = p.N;
     int tm, tn;
     int z;
@@ -334,11 +444,15 @@ pipe_gemm_kernel(const PipeArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    DmaJob job{base, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, wave, lane};
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-        if (t < nk)
-            dma_tile<G, A_MN, B_MN>(base + t * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N, kb + t * BK, ke, wave,
-                                    lane);
+    for (int t = 0; t < S - 1; ++t) {
+        if (t < nk) {
+            job.stage = base + t * kStageBytes;
+            job.k0 = kb + t * BK;
+            dma_tile<G, A_MN, B_MN>(job);
+        }
+    }
     int st = 0;        // stage of tile kt
     int st_load = S - 1;   // stage that receives tile kt + S - 1
     for (int kt = 0; kt < nk; ++kt) {
@@ -349,15 +463,14 @@ pipe_gemm_kernel(const PipeArgs p) {
         if constexpr (A_MN || B_MN) {
             const int valid = ke - (kb + kt * BK);
             if (valid < BK) {   // ragged last tile: rows past K were loaded from clamped rows
-                if constexpr (A_MN) zero_rows_mn<BM>(lds + st * kStageBytes, valid, tid);
-                if constexpr (B_MN) zero_rows_mn<BN>(lds + st * kStageBytes + kABytes, valid, tid);
+                if constexpr (A_MN) zero_rows_mn<BM, G::kThreads>(lds + st * kStageBytes, valid, tid);
+                if constexpr (B_MN) zero_rows_mn<BN, G::kThreads>(lds + st * kStageBytes + kABytes, valid, tid);
                 __syncthreads();
             }
         }
-        if (kt + S - 1 < nk)
-            dma_tile<G, A_MN, B_MN>(base + st_load * kStageBytes, A, p.lda, B, p.ldb, m0, n0, M, N,
-                                    kb + (kt + S - 1) * BK, ke, wave, lane);
-        compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc);
+        job.stage = base + st_load * kStageBytes;
+        job.k0 = kb + (kt + S - 1) * BK;
+        compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc, job, kt + S - 1 < nk);
         st = st == S - 1 ? 0 : st + 1;
         st_load = st_load == S - 1 ? 0 : st_load + 1;
     }
@@ -367,7 +480,8 @@ pipe_gemm_kernel(const PipeArgs p) {
     const int col0 = n0 + wn * WTN + (lane & 31);
     const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
     if constexpr (GEN) {
-        general_epilogue<MI, NJ, OutT>(p, acc, row0, col0, z);
+        static_assert(EpiTile<BM, BN>::kBytes <= S * kStageBytes, "epilogue tile exceeds the LDS ring");
+        general_epilogue<G, OutT>(p, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid);
         return;
     }
     OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
@@ -395,7 +509,7 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN = false, int S = 3>
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN = false, int S = 3, int NWM = 2, int NWN = 2>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -409,8 +523,8 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         if (p.C3) q.C3 = reinterpret_cast<bf16_t*>(p.C3) + (int64_t)y0 * p.strideC2;
         if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)y0 * p.strideCin1;
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, GEN, S>), dim3(tiles, q.batch, p.splits),
-                           dim3(kThreads), 0, stream, q);
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, GEN, S, NWM, NWN>),
+                           dim3(tiles, q.batch, p.splits), dim3(64 * NWM * NWN), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -437,12 +551,14 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     // block gradients (m/n-major A and B, float32 out)
     if (!a_mn && !out_f32) {
         if (tile == PipeTile::Wide)
-            return b_mn ? launch<128, 256, false, true, false>(p, stream) : launch<128, 256, false, false, false>(p, stream);
-        return b_mn ? launch<256, 128, false, true, false>(p, stream) : launch<256, 128, false, false, false>(p, stream);
+            return b_mn ? launch<128, 256, false, true, false, false, 3, 2, 4>(p, stream)
+                        : launch<128, 256, false, false, false, false, 3, 2, 4>(p, stream);
+        return b_mn ? launch<256, 128, false, true, false, false, 3, 4, 2>(p, stream)
+                    : launch<256, 128, false, false, false, false, 3, 4, 2>(p, stream);
     }
     if (a_mn && b_mn && out_f32) {
         if (tile == PipeTile::Square) return launch<128, 128, true, true, true, false, 4>(p, stream);
-        return launch<256, 128, true, true, true>(p, stream);
+        return launch<256, 128, true, true, true, false, 3, 4, 2>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -454,8 +570,16 @@ hipError_t launch_general(bool a_mn, bool b_mn, const PipeArgs& p, hipStream_t s
     return launch<T, T, true, true, OUT_F32, true, 4>(p, stream);
 }
 
-hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream) {
-    if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p_in, hipStream_t stream) {
+    if (p_in.M <= 0 || p_in.N <= 0 || p_in.batch <= 0) return hipSuccess;
+    PipeArgs p = p_in;
+    // 16-byte float32 / 8-byte bf16 epilogue accesses need every row start and
+    // every batch stride of every epilogue operand aligned to 4 elements
+    auto al = [](const void* ptr, int64_t ld, int64_t stride) {
+        return ptr == nullptr || (((uintptr_t)ptr % 16) == 0 && ld % 4 == 0 && stride % 4 == 0);
+    };
+    p.epi_vec = al(p.C, p.ldc, p.strideC) && al(p.C2, p.ldc2, p.strideC2) && al(p.C3, p.ldc2, p.strideC2) &&
+                al(p.Cin1, p.ldcin1, p.strideCin1) && al(p.Cin2, p.ldcin2, p.strideCin2);
     if (a_mn && !b_mn) return hipErrorInvalidValue;
     if (p.splits != 1) return hipErrorInvalidValue;
     // 128 x 128 tiles only when they alone give about four workgroups per CU
