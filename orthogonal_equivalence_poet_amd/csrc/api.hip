@@ -385,16 +385,21 @@ GemmTile grad_tile(bool bf16, int64_t b) {
 }
 
 // Block gradients of bf16 blocks of b >= 64 run on the pipelined kernel
-// (256 x 128 tiles, transposed LDS reads for both operands).
+// (64 x 64 tiles, transposed LDS reads for both operands).
 bool grad_pipe(bool bf16, int64_t b) { return bf16 && b >= 64 && b % 8 == 0; }
 
 void plan_splits(int64_t T, int64_t b, int64_t nblk, bool bf16, int& splits, int64_t& kps) {
     const GemmTile tile = grad_tile(bf16, b);
-    const int64_t tr = grad_pipe(bf16, b) ? pipe_tile_rows(PipeTile::Tall) : gemm_tile_rows(tile, bf16);
-    const int64_t tc = grad_pipe(bf16, b) ? pipe_tile_cols(PipeTile::Tall) : gemm_tile_cols(tile, bf16);
+    const bool pipe = grad_pipe(bf16, b);
+    const int64_t tr = pipe ? pipe_tile_rows(PipeTile::Small) : gemm_tile_rows(tile, bf16);
+    const int64_t tc = pipe ? pipe_tile_cols(PipeTile::Small) : gemm_tile_cols(tile, bf16);
     const int64_t tiles = ((b + tr - 1) / tr) * ((b + tc - 1) / tc) * nblk;
-    int64_t want = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
-    want = std::min<int64_t>(want, std::max<int64_t>(1, T / 256));
+    // pipelined 64 x 64 tiles: split the token axis only until about one
+    // workgroup per CU, keeping at least 512 tokens per split; register-staged
+    // tiles: about four workgroups per CU
+    const int64_t target = pipe ? 256 : 1024;
+    int64_t want = std::max<int64_t>(1, (target + tiles - 1) / tiles);
+    want = std::min<int64_t>(want, std::max<int64_t>(1, T / (pipe ? 512 : 256)));
     int64_t k = (T + want - 1) / want;
     k = std::max<int64_t>(64, (k + 63) / 64 * 64);
     kps = k;
@@ -448,7 +453,7 @@ int block_grad(bool bf16, int64_t T, int64_t d, int64_t b, const void* A, const 
         p.batch = (int)(d / b);
         p.splits = splits;
         p.k_per_split = (int)kps;
-        HIP_TRY(pipe_gemm(true, true, true, p, s, PipeTile::Tall));
+        HIP_TRY(pipe_gemm(true, true, true, p, s, PipeTile::Small));
         if (splits > 1) HIP_TRY(splitk_reduce(part, dG, d * b, splits, s));
         return POETX_OK;
     }

@@ -42,9 +42,10 @@ struct PipeArgs {
 // every leading dimension, stride and contiguous extent a multiple of 8.
 // Workgroup tile: Tall 256 x 128 (dense products), Wide 128 x 256 (block
 // products: one workgroup spans a whole block of 256 outputs), Square 128 x 128
-// (block gradients).  Instantiated: k-major A with bf16 output (Tall, Wide) and
-// m/n-major A and B with float32 output (Tall, Square).
-enum class PipeTile { Tall, Wide, Square };
+// and Small 64 x 64 (block gradients: enough tiles to fill the chip without
+// splitting the token axis).  Instantiated: k-major A with bf16 output (Tall,
+// Wide) and m/n-major A and B with float32 output (Tall, Square, Small).
+enum class PipeTile { Tall, Wide, Square, Small };
 bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                          int64_t strideA, int64_t strideB);
 hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile);

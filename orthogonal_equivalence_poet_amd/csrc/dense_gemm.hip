@@ -558,6 +558,7 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     }
     if (a_mn && b_mn && out_f32) {
         if (tile == PipeTile::Square) return launch<128, 128, true, true, true, false, 4>(p, stream);
+        if (tile == PipeTile::Small) return launch<64, 64, true, true, true, false, 4>(p, stream);
         return launch<256, 128, true, true, true, false, 3, 4, 2>(p, stream);
     }
     return hipErrorInvalidValue;
@@ -591,8 +592,8 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
     return out_f32 ? launch_general<64, true>(a_mn, b_mn, p, stream) : launch_general<64, false>(a_mn, b_mn, p, stream);
 }
 
-int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : 128; }
-int pipe_tile_cols(PipeTile t) { return t == PipeTile::Wide ? 256 : 128; }
+int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : t == PipeTile::Small ? 64 : 128; }
+int pipe_tile_cols(PipeTile t) { return t == PipeTile::Wide ? 256 : t == PipeTile::Small ? 64 : 128; }
 
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     return M > 0 && N >= 8 && K >= BK && K % BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0;
