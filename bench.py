@@ -5,10 +5,11 @@ Workload: W0 4096 x 4096 bf16 ~ N(0, 0.02^2), block size b = 256 (16 blocks
 per side), Neumann order k = 3, upper-triangle parameters float32 ~ N(0, 1e-3^2),
 x bf16 ~ N(0, 1) of 1 x 2048 tokens, fast variant.  One step is
 
-  poetx_cnp_fwd   (all 32 R and P blocks in one call)
+  poetx_cnp_fwd_save   (all 32 R and P blocks in one call; keeps Q and its
+                        square for the backward)
   poetx_linear_fwd
   poetx_linear_bwd
-  poetx_cnp_bwd   (all 32 blocks in one call)
+  poetx_cnp_bwd_saved  (all 32 blocks in one call, reusing what the forward kept)
 
 with every input already resident in HBM.  The timed region is bracketed by a
 device synchronisation on both sides and measured with HIP events on the
@@ -103,6 +104,8 @@ def build_state(spec):
              B.poetx_cnp_fwd_workspace_bytes(nR + nP, b, spec.k, B.POETX_BF16),
              B.poetx_cnp_bwd_workspace_bytes(nR + nP, b, spec.k, B.POETX_BF16))
     S["ws"] = B.workspace(ws)
+    # the transform's forward keeps Q, its square and companions for the backward
+    S["cnp_saved"] = B.workspace(B.poetx_cnp_saved_bytes(nR + nP, b, spec.k, B.POETX_BF16))
     return S, inp
 
 
@@ -111,12 +114,13 @@ def make_step(spec, S):
     nblk = spec.nblk_R + spec.nblk_P
 
     def step():
-        B.poetx_cnp_fwd(S["q"], nblk, spec.b, spec.k, S["G"], S["ws"])
+        B.poetx_cnp_fwd_save(S["q"], nblk, spec.b, spec.k, S["G"], S["cnp_saved"], S["ws"])
         B.poetx_linear_fwd(S["desc"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], S["y"],
                            S["saved"], S["ws"])
         B.poetx_linear_bwd(S["desc"], S["dy"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"],
                            S["saved"], S["dx"], S["dG_R"], S["dG_P"], S["ws"])
-        B.poetx_cnp_bwd(S["q"], S["dG"], nblk, spec.b, spec.k, S["dq"], B.POETX_BF16, S["ws"])
+        B.poetx_cnp_bwd_saved(S["q"], S["dG"], nblk, spec.b, spec.k, S["dq"], B.POETX_BF16, S["cnp_saved"],
+                              S["ws"])
     return step
 
 
@@ -143,7 +147,8 @@ def stage_timings(spec, S, reps):
     st = {}
     # (name, fn, algorithmic flops, algorithmic HBM bytes)
     stages = [
-        ("cnp_fwd", lambda: B.poetx_cnp_fwd(S["q"], nblk, b, k, S["G"], S["ws"]), 2 * 2 * b ** 3 * nblk,
+        ("cnp_fwd", lambda: B.poetx_cnp_fwd_save(S["q"], nblk, b, k, S["G"], S["cnp_saved"], S["ws"]),
+         2 * 2 * b ** 3 * nblk,
          4 * nblk * b * (b - 1) // 2 + 2 * nblk * b * b),
         ("perm_gather_x", lambda: B.poetx_permute(S["x"], a, T, n, None, S["pi_P"], False), 0, 2 * 2 * T * n),
         ("blk_fwd_P", blk(NT, a, S["G_P"], h1, n), 2 * T * n * b, 2 * (2 * T * n + n * b)),
@@ -159,8 +164,9 @@ def stage_timings(spec, S, reps):
         ("grad_P", lambda: B.poetx_block_grad(h1, a, dG, T, n, b, gws), 2 * T * n * b, 2 * 2 * T * n + 4 * n * b),
         ("blk_bwd_P", blk(NN, h1, S["G_P"], a, n), 2 * T * n * b, 2 * (2 * T * n + n * b)),
         ("perm_scatter_dx", lambda: B.poetx_permute(a, S["dx"], T, n, None, S["pi_P"], True), 0, 2 * 2 * T * n),
-        ("cnp_bwd", lambda: B.poetx_cnp_bwd(S["q"], S["dG"], nblk, b, k, S["dq"], B.POETX_BF16, S["ws"]),
-         5 * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
+        ("cnp_bwd", lambda: B.poetx_cnp_bwd_saved(S["q"], S["dG"], nblk, b, k, S["dq"], B.POETX_BF16,
+                                                  S["cnp_saved"], S["ws"]),
+         4 * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
     ]
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
@@ -306,7 +312,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "llama8b_q_proj: W0 4096x4096 bf16, b=256 (16+16 blocks), k=3, "
-                               "1 x 2048 tokens, fast variant; step = cnp_fwd + linear_fwd + linear_bwd + cnp_bwd",
+                               "1 x 2048 tokens, fast variant; step = cnp_fwd_save + linear_fwd + linear_bwd + "
+                               "cnp_bwd_saved",
                    "global_batch": 1, "seq_len": spec.T, "parallelism": "single GPU"},
         "gemm_pct_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(gemm_tflops, 1),

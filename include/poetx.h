@@ -120,6 +120,23 @@ size_t poetx_cnp_bwd_workspace_bytes(int64_t nblk, int64_t b, int k, int dtype);
 int poetx_cnp_bwd(const float* q, const float* dG, int64_t nblk, int64_t b, int k,
                   float* dq, int dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* Save / reuse variant of the pair above (the fast-versus-memory trade of the
+ * review's POET-X_fast / POET-X_mem, applied to the transform): the forward
+ * keeps Q and the square of Q with its companion terms in the caller's
+ * `saved` buffer (device memory of at least poetx_cnp_saved_bytes bytes,
+ * 256-byte aligned), and the backward reads them instead of recomputing.
+ * The backward's `saved` must hold what poetx_cnp_fwd_save wrote for the same
+ * q, nblk, b, k and dtype, unchanged since; results are bit-identical to
+ * poetx_cnp_fwd / poetx_cnp_bwd.  `ws` as for the plain calls (their
+ * *_workspace_bytes suffice).  Errors: a null `saved` is POETX_ERR_INVALID_ARG,
+ * saved_bytes too small is POETX_ERR_WORKSPACE. */
+size_t poetx_cnp_saved_bytes(int64_t nblk, int64_t b, int k, int dtype);
+int poetx_cnp_fwd_save(const float* q, int64_t nblk, int64_t b, int k, void* G, int G_dtype,
+                       void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+int poetx_cnp_bwd_saved(const float* q, const float* dG, int64_t nblk, int64_t b, int k,
+                        float* dq, int dtype, const void* saved, size_t saved_bytes,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ permutations */
 /* dst[i][j] = src[row_idx[i]][col_idx[j]] (row_idx / col_idx may be NULL for
  * the identity).  src, dst: dtype [rows, cols] with leading dimension cols.

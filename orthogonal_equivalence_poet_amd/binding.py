@@ -25,6 +25,7 @@ EXPORTS = [
     "poetx_skew_unpack", "poetx_skew_pack",
     "poetx_cnp_fwd_workspace_bytes", "poetx_cnp_fwd",
     "poetx_cnp_bwd_workspace_bytes", "poetx_cnp_bwd",
+    "poetx_cnp_saved_bytes", "poetx_cnp_fwd_save", "poetx_cnp_bwd_saved",
     "poetx_permute", "poetx_prepermute",
     "poetx_check_perm_workspace_bytes", "poetx_check_perm",
     "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd",
@@ -59,6 +60,9 @@ _SIGS = {
     "poetx_cnp_fwd": ([_VP, _I64, _I64, _I32, _VP, _I32, _VP, _SZ, _VP], _I32),
     "poetx_cnp_bwd_workspace_bytes": ([_I64, _I64, _I32, _I32], _SZ),
     "poetx_cnp_bwd": ([_VP, _VP, _I64, _I64, _I32, _VP, _I32, _VP, _SZ, _VP], _I32),
+    "poetx_cnp_saved_bytes": ([_I64, _I64, _I32, _I32], _SZ),
+    "poetx_cnp_fwd_save": ([_VP, _I64, _I64, _I32, _VP, _I32, _VP, _SZ, _VP, _SZ, _VP], _I32),
+    "poetx_cnp_bwd_saved": ([_VP, _VP, _I64, _I64, _I32, _VP, _I32, _VP, _SZ, _VP, _SZ, _VP], _I32),
     "poetx_permute": ([_VP, _VP, _I32, _I64, _I64, _VP, _VP, _I32, _VP], _I32),
     "poetx_prepermute": ([_VP, _VP, _I32, _I64, _I64, _VP, _VP, _VP], _I32),
     "poetx_check_perm_workspace_bytes": ([_I64], _SZ),
@@ -170,6 +174,24 @@ def poetx_cnp_bwd(q, dG, nblk, b, k, dq, dtype, ws=None, stream=None):
     p, nbytes = _ws(ws)
     _check("poetx_cnp_bwd", load().poetx_cnp_bwd(_ptr(q), _ptr(dG), nblk, b, k, _ptr(dq), dtype, p, nbytes,
                                                  _stream(stream)))
+
+
+def poetx_cnp_saved_bytes(nblk, b, k, dtype) -> int:
+    return load().poetx_cnp_saved_bytes(nblk, b, k, dtype)
+
+
+def poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws=None, stream=None):
+    p, nbytes = _ws(ws)
+    sp, sbytes = _ws(saved)
+    _check("poetx_cnp_fwd_save", load().poetx_cnp_fwd_save(_ptr(q), nblk, b, k, _ptr(G), _dtype_code(G), sp, sbytes,
+                                                           p, nbytes, _stream(stream)))
+
+
+def poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, dtype, saved, ws=None, stream=None):
+    p, nbytes = _ws(ws)
+    sp, sbytes = _ws(saved)
+    _check("poetx_cnp_bwd_saved", load().poetx_cnp_bwd_saved(_ptr(q), _ptr(dG), nblk, b, k, _ptr(dq), dtype, sp,
+                                                             sbytes, p, nbytes, _stream(stream)))
 
 
 def poetx_permute(src, dst, rows, cols, row_idx=None, col_idx=None, scatter_cols=False, stream=None):

@@ -188,17 +188,20 @@ void* ctake(Carver& cv, bool cbf16, int64_t elems, float* alias32) {
 // A compute-dtype buffer of its own.
 void* cown(Carver& cv, bool cbf16, int64_t elems) { return cv.take((cbf16 ? 2 : 4) * (size_t)elems); }
 
-void plan_cnp(Carver& cv, int64_t nblk, int64_t b, int k, bool cbf16, bool backward, CnpBufs& B) {
+// The prologue's outputs (Q, the square and its companions) come from `sv`,
+// everything else from `cv`; `sv` is the caller's saved buffer when the
+// forward keeps them for the backward, else the workspace itself.
+void plan_cnp(Carver& cv, Carver& sv, int64_t nblk, int64_t b, int k, bool cbf16, bool backward, CnpBufs& B) {
     const int64_t e = nblk * b * b;
-    B.Q32 = cv.take_n<float>(e);
-    B.Qc = ctake(cv, cbf16, e, B.Q32);
+    B.Q32 = sv.take_n<float>(e);
+    B.Qc = ctake(sv, cbf16, e, B.Q32);
     if (k == 3) {
-        B.U32 = cv.take_n<float>(e);
-        B.Sc = cown(cv, cbf16, e);
-        B.Tc = cown(cv, cbf16, e);
+        B.U32 = sv.take_n<float>(e);
+        B.Sc = cown(sv, cbf16, e);
+        B.Tc = cown(sv, cbf16, e);
     } else if (k == 4) {
-        B.S32 = cv.take_n<float>(e);
-        B.Sc = ctake(cv, cbf16, e, B.S32);
+        B.S32 = sv.take_n<float>(e);
+        B.Sc = ctake(sv, cbf16, e, B.S32);
         B.P32 = cv.take_n<float>(e);
         B.Pc = ctake(cv, cbf16, e, B.P32);
         B.E32 = cv.take_n<float>(e);
@@ -287,8 +290,8 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
 
 // Adjoint schedules (reverse of the forward ones), ending with the skew pack.
 int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k, bool cbf16, float* dq,
-                 CnpBufs& B, hipStream_t s) {
-    POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
+                 CnpBufs& B, bool saved, hipStream_t s) {
+    if (!saved) POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
     const int ib = (int)b;
     const int64_t bb = b * b;
     const void* dGc = dG;
@@ -361,11 +364,20 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
     return POETX_OK;
 }
 
-size_t cnp_ws(int64_t nblk, int64_t b, int k, bool cbf16, bool backward) {
-    Carver cv(nullptr);
+// Workspace of one Cayley-Neumann call (with_saved: the prologue outputs live
+// in a separate saved buffer) and the size of that saved buffer.
+size_t cnp_ws(int64_t nblk, int64_t b, int k, bool cbf16, bool backward, bool with_saved = false) {
+    Carver cv(nullptr), sv(nullptr);
     CnpBufs B;
-    plan_cnp(cv, nblk, b, k, cbf16, backward, B);
+    plan_cnp(cv, with_saved ? sv : cv, nblk, b, k, cbf16, backward, B);
     return cv.off;
+}
+
+size_t cnp_saved(int64_t nblk, int64_t b, int k, bool cbf16) {
+    Carver cv(nullptr), sv(nullptr);
+    CnpBufs B;
+    plan_cnp(cv, sv, nblk, b, k, cbf16, true, B);
+    return sv.off;
 }
 
 // -------------------------------------------------------------- the layer
@@ -553,7 +565,33 @@ int poetx_cnp_fwd(const float* q, int64_t nblk, int64_t b, int k, void* G, int G
     if (need && !ws) return POETX_ERR_INVALID_ARG;
     Carver cv(ws);
     CnpBufs B;
-    plan_cnp(cv, nblk, b, k, cbf, false, B);
+    plan_cnp(cv, cv, nblk, b, k, cbf, false, B);
+    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, as_stream(stream));
+}
+
+size_t poetx_cnp_saved_bytes(int64_t nblk, int64_t b, int k, int dtype) {
+    if (check_block(b) != POETX_OK || check_k(k) != POETX_OK || check_nblk(nblk, b) != POETX_OK ||
+        !dtype_ok(dtype))
+        return 0;
+    return cnp_saved(nblk, b, k, dtype == POETX_BF16);
+}
+
+int poetx_cnp_fwd_save(const float* q, int64_t nblk, int64_t b, int k, void* G, int G_dtype, void* saved,
+                       size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+    if (!dtype_ok(G_dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    POETX_TRY(check_k(k));
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!q || !G || !saved) return POETX_ERR_INVALID_ARG;
+    const bool cbf = G_dtype == POETX_BF16;
+    if (saved_bytes < cnp_saved(nblk, b, k, cbf)) return POETX_ERR_WORKSPACE;
+    const size_t need = cnp_ws(nblk, b, k, cbf, false, true);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (need && !ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws), sv(saved);
+    CnpBufs B;
+    plan_cnp(cv, sv, nblk, b, k, cbf, false, B);
     return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, as_stream(stream));
 }
 
@@ -578,8 +616,27 @@ int poetx_cnp_bwd(const float* q, const float* dG, int64_t nblk, int64_t b, int 
     if (need && !ws) return POETX_ERR_INVALID_ARG;
     Carver cv(ws);
     CnpBufs B;
-    plan_cnp(cv, nblk, b, k, cbf, true, B);
-    return cnp_backward(q, dG, nblk, b, k, cbf, dq, B, as_stream(stream));
+    plan_cnp(cv, cv, nblk, b, k, cbf, true, B);
+    return cnp_backward(q, dG, nblk, b, k, cbf, dq, B, false, as_stream(stream));
+}
+
+int poetx_cnp_bwd_saved(const float* q, const float* dG, int64_t nblk, int64_t b, int k, float* dq, int dtype,
+                        const void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    POETX_TRY(check_k(k));
+    POETX_TRY(check_nblk(nblk, b));
+    if (nblk == 0) return POETX_OK;
+    if (!q || !dG || !dq || !saved) return POETX_ERR_INVALID_ARG;
+    const bool cbf = dtype == POETX_BF16;
+    if (saved_bytes < cnp_saved(nblk, b, k, cbf)) return POETX_ERR_WORKSPACE;
+    const size_t need = cnp_ws(nblk, b, k, cbf, true, true);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (need && !ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws), sv(const_cast<void*>(saved));
+    CnpBufs B;
+    plan_cnp(cv, sv, nblk, b, k, cbf, true, B);
+    return cnp_backward(q, dG, nblk, b, k, cbf, dq, B, true, as_stream(stream));
 }
 
 int poetx_permute(const void* src, void* dst, int dtype, int64_t rows, int64_t cols, const int32_t* row_idx,
@@ -748,13 +805,13 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
     {
         Carver c1(cnp_base);
         CnpBufs B;
-        plan_cnp(c1, m / b, b, d->k, bf, false, B);
+        plan_cnp(c1, c1, m / b, b, d->k, bf, false, B);
         POETX_TRY(cnp_forward(q_R, m / b, b, d->k, bf, G_R, bf, B, s));
     }
     {
         Carver c2(cnp_base);
         CnpBufs B;
-        plan_cnp(c2, n / b, b, d->k, bf, false, B);
+        plan_cnp(c2, c2, n / b, b, d->k, bf, false, B);
         POETX_TRY(cnp_forward(q_P, n / b, b, d->k, bf, G_P, bf, B, s));
     }
     // W1 = diag(G_R) . Wt  (row blocks);  W2 = W1 . diag(G_P)  (column blocks)

@@ -410,41 +410,30 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
 
 // S-stage LDS ring: S - 1 k-tiles are requested before the first one is used,
 // so a product with K <= 64 (S - 1) waits for memory once.
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN, int S, int NWM = 2, int NWN = 2>
-__global__ void __launch_bounds__(64 * NWM * NWN)
-__attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
-pipe_gemm_kernel(const PipeArgs p) {
-    using G = Geo<BM, BN, NWM, NWN>;
+// Epilogue kinds: plain store, general (see PipeArgs).
+constexpr int kEpiPlain = 0, kEpiGeneral = 1;
+
+// The k loop of one output tile at (m0, n0) into acc (zeroed here).
+template <class G, bool A_MN, bool B_MN, int S>
+__device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __restrict__ A, int64_t lda,
+                                          const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M, int N,
+                                          int kb, int ke, int tid, f32x16_t (&acc)[G::MI][G::NJ]) {
+    constexpr int BM = G::BM, BN = G::BN;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
-    constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     constexpr int kLoadsPerTile = G::kLoadsPerTile;
-    static_assert(S * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes];
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / NWN, wn = wave % NWN;
-    const int M = p.M, N = p.N;
-    int tm, tn;
-    int z;
-    batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
-    const int kb = blockIdx.z * p.k_per_split;
-    const int ke = min(p.K, kb + p.k_per_split);
+    const int wm = wave / G::NWN, wn = wave % G::NWN;
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const uint32_t base = lds_offset(lds);
-
-    f32x16_t acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < G::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < G::NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    DmaJob job{base, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, wave, lane};
+    DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) {
         if (t < nk) {
@@ -474,12 +463,38 @@ pipe_gemm_kernel(const PipeArgs p) {
         st = st == S - 1 ? 0 : st + 1;
         st_load = st_load == S - 1 ? 0 : st_load + 1;
     }
+}
+
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2>
+__global__ void __launch_bounds__(64 * NWM * NWN)
+__attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
+pipe_gemm_kernel(const PipeArgs p) {
+    using G = Geo<BM, BN, NWM, NWN>;
+    constexpr int kStageBytes = G::kStageBytes;
+    constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
+    static_assert(S * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int M = p.M, N = p.N;
+    const int kb = blockIdx.z * p.k_per_split;
+    const int ke = min(p.K, kb + p.k_per_split);
+    int tm, tn;
+    int z;
+    batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
+    f32x16_t acc[MI][NJ];
+    main_loop<G, A_MN, B_MN, S>(lds, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, tid, acc);
 
     // epilogue: lane holds rows 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 per tile
     using OutT = typename std::conditional<OUT_F32, float, bf16_t>::type;
     const int col0 = n0 + wn * WTN + (lane & 31);
     const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
-    if constexpr (GEN) {
+    if constexpr (EPI == kEpiGeneral) {
         static_assert(EpiTile<BM, BN>::kBytes <= S * kStageBytes, "epilogue tile exceeds the LDS ring");
         general_epilogue<G, OutT>(p, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid);
         return;
@@ -509,7 +524,7 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, bool GEN = false, int S = 3, int NWM = 2, int NWN = 2>
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -523,7 +538,7 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         if (p.C3) q.C3 = reinterpret_cast<bf16_t*>(p.C3) + (int64_t)y0 * p.strideC2;
         if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)y0 * p.strideCin1;
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, GEN, S, NWM, NWN>),
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN>),
                            dim3(tiles, q.batch, p.splits), dim3(64 * NWM * NWN), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -551,24 +566,24 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     // block gradients (m/n-major A and B, float32 out)
     if (!a_mn && !out_f32) {
         if (tile == PipeTile::Wide)
-            return b_mn ? launch<128, 256, false, true, false, false, 3, 2, 4>(p, stream)
-                        : launch<128, 256, false, false, false, false, 3, 2, 4>(p, stream);
-        return b_mn ? launch<256, 128, false, true, false, false, 3, 4, 2>(p, stream)
-                    : launch<256, 128, false, false, false, false, 3, 4, 2>(p, stream);
+            return b_mn ? launch<128, 256, false, true, false, kEpiPlain, 3, 2, 4>(p, stream)
+                        : launch<128, 256, false, false, false, kEpiPlain, 3, 2, 4>(p, stream);
+        return b_mn ? launch<256, 128, false, true, false, kEpiPlain, 3, 4, 2>(p, stream)
+                    : launch<256, 128, false, false, false, kEpiPlain, 3, 4, 2>(p, stream);
     }
     if (a_mn && b_mn && out_f32) {
-        if (tile == PipeTile::Square) return launch<128, 128, true, true, true, false, 4>(p, stream);
-        if (tile == PipeTile::Small) return launch<64, 64, true, true, true, false, 4>(p, stream);
-        return launch<256, 128, true, true, true, false, 3, 4, 2>(p, stream);
+        if (tile == PipeTile::Square) return launch<128, 128, true, true, true, kEpiPlain, 4>(p, stream);
+        if (tile == PipeTile::Small) return launch<64, 64, true, true, true, kEpiPlain, 4>(p, stream);
+        return launch<256, 128, true, true, true, kEpiPlain, 3, 4, 2>(p, stream);
     }
     return hipErrorInvalidValue;
 }
 
 template <int T, bool OUT_F32>
 hipError_t launch_general(bool a_mn, bool b_mn, const PipeArgs& p, hipStream_t stream) {
-    if (!a_mn && !b_mn) return launch<T, T, false, false, OUT_F32, true, 4>(p, stream);
-    if (!a_mn && b_mn) return launch<T, T, false, true, OUT_F32, true, 4>(p, stream);
-    return launch<T, T, true, true, OUT_F32, true, 4>(p, stream);
+    if (!a_mn && !b_mn) return launch<T, T, false, false, OUT_F32, kEpiGeneral, 4>(p, stream);
+    if (!a_mn && b_mn) return launch<T, T, false, true, OUT_F32, kEpiGeneral, 4>(p, stream);
+    return launch<T, T, true, true, OUT_F32, kEpiGeneral, 4>(p, stream);
 }
 
 hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p_in, hipStream_t stream) {

@@ -120,3 +120,18 @@ def test_workspace_sizes_scale(B):
     assert lib.poetx_linear_saved_bytes(C.byref(dm)) == 0
     assert lib.poetx_linear_bwd_workspace_bytes(C.byref(dm)) >= 3 * 2048 * 4096 * 2
     assert lib.poetx_cnp_fwd_workspace_bytes(64, 256, 3, 1) == 2 * lib.poetx_cnp_fwd_workspace_bytes(32, 256, 3, 1)
+
+
+def test_cnp_saved_validation(B):
+    lib = B.load()
+    sb = lib.poetx_cnp_saved_bytes(4, 256, 3, 1)
+    # k = 3, bf16: Q (float32 and bf16), 2Q + 2S (float32), S and 2Q + S (bf16)
+    assert sb >= 4 * 256 * 256 * (4 + 2 + 4 + 2 + 2)
+    ws = lib.poetx_cnp_bwd_workspace_bytes(4, 256, 3, 1)
+    assert lib.poetx_cnp_fwd_save(FAKE, 4, 256, 3, FAKE, 1, None, sb, FAKE, ws, None) == 1
+    assert lib.poetx_cnp_fwd_save(FAKE, 4, 256, 3, FAKE, 1, FAKE, sb - 1, FAKE, ws, None) == 4
+    assert lib.poetx_cnp_bwd_saved(FAKE, FAKE, 4, 256, 3, FAKE, 1, None, sb, FAKE, ws, None) == 1
+    assert lib.poetx_cnp_bwd_saved(FAKE, FAKE, 4, 256, 3, FAKE, 1, FAKE, sb - 1, FAKE, ws, None) == 4
+    assert lib.poetx_cnp_bwd_saved(FAKE, FAKE, 4, 256, 3, FAKE, 1, FAKE, sb, FAKE, 0, None) == 4
+    assert lib.poetx_cnp_fwd_save(FAKE, 4, 24, 3, FAKE, 1, FAKE, sb, FAKE, ws, None) == 3
+    assert lib.poetx_cnp_saved_bytes(4, 24, 3, 1) == 0

@@ -149,6 +149,26 @@ def test_cnp_bwd_parity(b, k, dtype, std, norm):
     assert rel_fro(dq, ref) <= tol(dtype)
 
 
+@pytest.mark.parametrize("b,k,dtype", [(256, 3, "bf16"), (64, 3, "f32"), (128, 4, "bf16"), (64, 5, "bf16"),
+                                       (16, 2, "f32")])
+def test_cnp_saved_variant_is_bitwise_identical(b, k, dtype):
+    """Forward keeping the square and its companions, backward reusing them:
+    the same products on the same values as the recomputing pair."""
+    nblk = 6
+    q = dev(_q(nblk, b, 0.05, 400 + b + k))
+    dG = dev(I.gaussian((nblk, b, b), 1.0, "f32", 401, b, k))
+    G_ref = cnp_fwd(q, nblk, b, k, dtype)
+    dq_ref = cnp_bwd(q, dG, nblk, b, k, dtype)
+    saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code(dtype)))
+    G = torch.empty_like(G_ref)
+    ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, code(dtype)))
+    B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
+    dq = torch.empty_like(dq_ref)
+    B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, code(dtype), saved, ws)
+    assert torch.equal(G, G_ref)
+    assert torch.equal(dq, dq_ref)
+
+
 # ------------------------------------------------------------------ layer
 def _oracle_step(spec, inp):
     G_R = O.blocks_from_params(inp["q_R"], spec.b, spec.k)
