@@ -33,6 +33,11 @@ struct PipeArgs {
     float alpha = 1.f, beta1 = 0.f, beta2 = 0.f, gamma = 0.f;
     int mode = 0;
     int epi_vec = 0;           // set by pipe_gemm_general: epilogue may use vector accesses
+    // Second product of pipe_gemm_dual: A2^T B2 with A2 [K][M] and B2 [K][N] (m/n-major).
+    const void* A2 = nullptr;
+    int64_t lda2 = 0, strideA2 = 0;
+    const void* B2 = nullptr;
+    int64_t ldb2 = 0, strideB2 = 0;
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead
@@ -55,6 +60,11 @@ int pipe_tile_rows(PipeTile t);
 // large enough to fill the chip with them.  Operand layouts as in pipe_gemm
 // ((a_mn, b_mn) = (0, 0), (0, 1) or (1, 1)); no split-K.
 hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream);
+// Two products of the same b x b shape in one launch (64 x 64 tiles, general
+// epilogue): A B^T (k-major A and B) and A2^T B2 (m/n-major A2 and B2).
+// separate = false: the general epilogue sees their sum (modes 0 and 1);
+// separate = true:  mode 2, C = alpha P1 + beta1 Cin1 and C2 (bf16) = alpha (P1 + P2) + beta2 Cin1.
+hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p, hipStream_t stream);
 int pipe_tile_cols(PipeTile t);
 
 // Dense convenience wrappers (batch 1, no split).

@@ -331,12 +331,14 @@ __device__ __forceinline__ void store4(T* __restrict__ p, float4 v, bool vec, bo
     if (valid > 3) store_f32(p + 3, v.w);
 }
 
-template <class G, typename OutT>
-__device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[G::MI][G::NJ], float* tile,
-                                                 int m0, int n0, int wm, int wn, int z, int tid) {
+template <class G, typename OutT, bool TWO = false>
+__device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[G::MI][G::NJ],
+                                                 const f32x16_t (&acc2)[G::MI][G::NJ], float* tile, int m0, int n0,
+                                                 int wm, int wn, int z, int tid) {
     constexpr int BM = G::BM, BN = G::BN, MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     constexpr int kThreads = G::kThreads;
     using E = EpiTile<BM, BN>;
+    float* tile2 = tile + BM * E::kLd;   // second accumulator (mode 2)
     const int lane = tid & 63;
     block_barrier();   // every wave is done reading the operand stages
 #pragma unroll
@@ -348,6 +350,7 @@ __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16
                 const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int col = wn * WTN + j * 32 + (lane & 31);
                 tile[row * E::kLd + col] = acc[i][j][r];
+                if constexpr (TWO) tile2[row * E::kLd + col] = acc2[i][j][r];
             }
     __syncthreads();
     const float* __restrict__ cin1 = p.Cin1 ? p.Cin1 + (int64_t)z * p.strideCin1 : nullptr;
@@ -369,6 +372,18 @@ __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16
         float4 v = *reinterpret_cast<const float4*>(tile + row * E::kLd + c);
         v.x *= p.alpha; v.y *= p.alpha; v.z *= p.alpha; v.w *= p.alpha;
         const float4 a1 = cin1 ? load4(cin1 + (int64_t)gr * p.ldcin1 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (TWO) {   // mode 2: C = v + beta1 Cin1, C2 = v + w + beta2 Cin1
+            float4 w = *reinterpret_cast<const float4*>(tile2 + row * E::kLd + c);
+            w.x *= p.alpha; w.y *= p.alpha; w.z *= p.alpha; w.w *= p.alpha;
+            store4(c1 + (int64_t)gr * p.ldc + gc,
+                   make_float4(v.x + p.beta1 * a1.x, v.y + p.beta1 * a1.y, v.z + p.beta1 * a1.z, v.w + p.beta1 * a1.w),
+                   vec, full, valid);
+            store4(c2 + (int64_t)gr * p.ldc2 + gc,
+                   make_float4(v.x + w.x + p.beta2 * a1.x, v.y + w.y + p.beta2 * a1.y, v.z + w.z + p.beta2 * a1.z,
+                               v.w + w.w + p.beta2 * a1.w),
+                   vec, full, valid);
+            continue;
+        }
         if (p.mode == 1) {
             const float4 q2 = make_float4(2.f * a1.x, 2.f * a1.y, 2.f * a1.z, 2.f * a1.w);
             store4(c1 + (int64_t)gr * p.ldc + gc,
@@ -417,7 +432,8 @@ constexpr int kEpiPlain = 0, kEpiGeneral = 1;
 template <class G, bool A_MN, bool B_MN, int S>
 __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __restrict__ A, int64_t lda,
                                           const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M, int N,
-                                          int kb, int ke, int tid, f32x16_t (&acc)[G::MI][G::NJ]) {
+                                          int kb, int ke, int tid, f32x16_t (&acc)[G::MI][G::NJ],
+                                          bool zero = true) {
     constexpr int BM = G::BM, BN = G::BN;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     constexpr int kLoadsPerTile = G::kLoadsPerTile;
@@ -426,12 +442,14 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     const int wm = wave / G::NWN, wn = wave % G::NWN;
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const uint32_t base = lds_offset(lds);
+    if (zero) {
 #pragma unroll
-    for (int i = 0; i < G::MI; ++i)
+        for (int i = 0; i < G::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < G::NJ; ++j)
+            for (int j = 0; j < G::NJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
 
     DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
 #pragma unroll
@@ -465,7 +483,9 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     }
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2>
+// DUAL = 1: acc = op(A) op(B) + A2^T B2 (second product with m/n-major A2, B2);
+// DUAL = 2: the second product goes to its own accumulator (general epilogue mode 2).
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2, int DUAL = 0>
 __global__ void __launch_bounds__(64 * NWM * NWN)
 __attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
 pipe_gemm_kernel(const PipeArgs p) {
@@ -487,16 +507,26 @@ pipe_gemm_kernel(const PipeArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
-    f32x16_t acc[MI][NJ];
+    f32x16_t acc[MI][NJ], acc2[MI][NJ];
     main_loop<G, A_MN, B_MN, S>(lds, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, tid, acc);
+    if constexpr (DUAL != 0) {
+        const uint16_t* A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)z * p.strideA2;
+        const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)z * p.strideB2;
+        block_barrier();   // the second product reuses the LDS ring
+        if constexpr (DUAL == 1)
+            main_loop<G, true, true, S>(lds, A2, p.lda2, B2, p.ldb2, m0, n0, M, N, kb, ke, tid, acc, false);
+        else
+            main_loop<G, true, true, S>(lds, A2, p.lda2, B2, p.ldb2, m0, n0, M, N, kb, ke, tid, acc2, true);
+    }
 
     // epilogue: lane holds rows 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 per tile
     using OutT = typename std::conditional<OUT_F32, float, bf16_t>::type;
     const int col0 = n0 + wn * WTN + (lane & 31);
     const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
     if constexpr (EPI == kEpiGeneral) {
-        static_assert(EpiTile<BM, BN>::kBytes <= S * kStageBytes, "epilogue tile exceeds the LDS ring");
-        general_epilogue<G, OutT>(p, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid);
+        static_assert((DUAL == 2 ? 2 : 1) * EpiTile<BM, BN>::kBytes <= S * kStageBytes,
+                      "epilogue tile exceeds the LDS ring");
+        general_epilogue<G, OutT, DUAL == 2>(p, acc, acc2, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid);
         return;
     }
     OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
@@ -524,7 +554,8 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2>
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
+          int DUAL = 0>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -538,7 +569,9 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         if (p.C3) q.C3 = reinterpret_cast<bf16_t*>(p.C3) + (int64_t)y0 * p.strideC2;
         if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)y0 * p.strideCin1;
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN>),
+        if (p.A2) q.A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)y0 * p.strideA2;
+        if (p.B2) q.B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)y0 * p.strideB2;
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN, DUAL>),
                            dim3(tiles, q.batch, p.splits), dim3(64 * NWM * NWN), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -605,6 +638,23 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
                        : launch_general<128, false>(a_mn, b_mn, p, stream);
     }
     return out_f32 ? launch_general<64, true>(a_mn, b_mn, p, stream) : launch_general<64, false>(a_mn, b_mn, p, stream);
+}
+
+hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hipStream_t stream) {
+    if (p_in.M <= 0 || p_in.N <= 0 || p_in.batch <= 0) return hipSuccess;
+    if (p_in.splits != 1 || !p_in.A2 || !p_in.B2) return hipErrorInvalidValue;
+    PipeArgs p = p_in;
+    auto al = [](const void* ptr, int64_t ld, int64_t stride) {
+        return ptr == nullptr || (((uintptr_t)ptr % 16) == 0 && ld % 4 == 0 && stride % 4 == 0);
+    };
+    p.epi_vec = al(p.C, p.ldc, p.strideC) && al(p.C2, p.ldc2, p.strideC2) && al(p.Cin1, p.ldcin1, p.strideCin1) &&
+                al(p.Cin2, p.ldcin2, p.strideCin2);
+    if (separate) {
+        return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 4, 2, 2, 2>(p, stream)
+                       : launch<64, 64, false, false, false, kEpiGeneral, 4, 2, 2, 2>(p, stream);
+    }
+    return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 4, 2, 2, 1>(p, stream)
+                   : launch<64, 64, false, false, false, kEpiGeneral, 4, 2, 2, 1>(p, stream);
 }
 
 int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : t == PipeTile::Small ? 64 : 128; }
