@@ -25,6 +25,13 @@ timed on the host cores as a baseline.
                   script and record the dense GEMM's HBM traffic in
                   profiles/traffic_dense_gemm.json (scaled by a plain copy of
                   known size that every run performs).
+  --workload W    other workloads, same line format (the default is the one
+                  the metric is quoted on): up_proj / up_proj_mem (Llama-8B
+                  MLP up_proj shape, b=512, k=4, 4096 tokens), llama8b_layer
+                  and llama13b_layer (all 7 linears of a decoder layer, mem
+                  variant; the 8B line also times poetx_merge), cnp_13b (one
+                  Cayley-Neumann forward + backward over the 15280 b=256
+                  blocks of 40 Llama-13B layers).
 """
 import argparse
 import csv
@@ -45,7 +52,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 256 << 20      # plain copy every run performs (counter scale reference)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.json")
 GEMM_SRC = os.path.join(ROOT, "orthogonal_equivalence_poet_amd", "csrc", "dense_gemm.hip")
-DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false, false, 3>"   # dense NT (forward), demangled
+DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false,"   # dense NT (forward), demangled prefix
 COPY_KERNEL_TAG = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 
@@ -91,6 +98,12 @@ def build_state(spec):
     B.poetx_prepermute(S["W0"], S["Wt"], spec.m, spec.n, S["pi_R"], S["pi_P"])
     nR, nP, b = spec.nblk_R, spec.nblk_P, spec.b
     S["q"] = torch.cat([t(inp["q_R"]), t(inp["q_P"])]).contiguous()      # one flat batch of blocks
+    if spec.q_block_norm is not None:
+        # rescale every block's parameters so that its skew matrix has the given spectral norm
+        Q = torch.empty((nR + nP, b, b), dtype=torch.float32, device=dev)
+        B.poetx_skew_unpack(S["q"], Q, nR + nP, b)
+        S["q"] *= (spec.q_block_norm / torch.linalg.matrix_norm(Q, ord=2))[:, None]
+        del Q
     S["G"] = torch.empty((nR + nP, b, b), dtype=bf, device=dev)
     S["G_R"], S["G_P"] = S["G"][:nR], S["G"][nR:]
     S["dG"] = torch.empty((nR + nP, b, b), dtype=torch.float32, device=dev)
@@ -126,7 +139,8 @@ def make_step(spec, S):
 
 def stage_timings(spec, S, reps):
     """Every stage of the step alone, through the C ABI, same shapes and
-    launch configurations as inside poetx_linear_fwd / _bwd."""
+    launch configurations as inside poetx_linear_fwd / _bwd (the mem variant
+    repeats the P-side block product and the dense forward in its backward)."""
     import torch
     from orthogonal_equivalence_poet_amd import binding as B
     T, m, n, b, k = spec.T, spec.m, spec.n, spec.b, spec.k
@@ -148,7 +162,7 @@ def stage_timings(spec, S, reps):
     # (name, fn, algorithmic flops, algorithmic HBM bytes)
     stages = [
         ("cnp_fwd", lambda: B.poetx_cnp_fwd_save(S["q"], nblk, b, k, S["G"], S["cnp_saved"], S["ws"]),
-         2 * 2 * b ** 3 * nblk,
+         _products(k)[0] * 2 * b ** 3 * nblk,
          4 * nblk * b * (b - 1) // 2 + 2 * nblk * b * b),
         ("perm_gather_x", lambda: B.poetx_permute(S["x"], a, T, n, None, S["pi_P"], False), 0, 2 * 2 * T * n),
         ("blk_fwd_P", blk(NT, a, S["G_P"], h1, n), 2 * T * n * b, 2 * (2 * T * n + n * b)),
@@ -166,12 +180,20 @@ def stage_timings(spec, S, reps):
         ("perm_scatter_dx", lambda: B.poetx_permute(a, S["dx"], T, n, None, S["pi_P"], True), 0, 2 * 2 * T * n),
         ("cnp_bwd", lambda: B.poetx_cnp_bwd_saved(S["q"], S["dG"], nblk, b, k, S["dq"], B.POETX_BF16,
                                                   S["cnp_saved"], S["ws"]),
-         4 * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
+         _products(k)[1] * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
     ]
+    if spec.variant == "mem":   # recomputed in the backward, same kernels
+        stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages if nm in ("blk_fwd_P", "dense_fwd")]
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
-        st[name] = {"us": round(us, 2), "tflops": round(flops / us / 1e6, 1) if flops else None,
-                    "gbs": round(nbytes / us / 1e3, 1)}
+        tf = flops / us / 1e6 if flops else None
+        gbs = nbytes / us / 1e3
+        # dense products are bound by MFMA; block products, gradients, permutations and the
+        # b x b transform (at tens of blocks) by memory
+        mfma = name.startswith("dense")
+        st[name] = {"us": round(us, 2), "tflops": round(tf, 1) if tf else None, "gbs": round(gbs, 1),
+                    "bound": "mfma" if mfma else "hbm",
+                    "frac": round((tf / PEAK_BF16_TFLOPS) if mfma else (gbs / PEAK_HBM_GBS), 4)}
         st[name]["_flops"] = flops
     return st
 
@@ -242,6 +264,156 @@ def parse_pmc(pmc_dir):
     print(json.dumps(rec))
 
 
+def _products(k):
+    """b x b products of one forward / one saved-state backward of the transform."""
+    return {3: 2, 4: 3}.get(k, k), {3: 4, 4: 7}.get(k, 3 * k - 1)
+
+
+def _time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _base_line(args, value, unit, ms, workload, T):
+    return {"metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": workload, "global_batch": 1, "seq_len": T, "parallelism": "single GPU"}}
+
+
+def run_linear(args, spec, label):
+    """One linear: step throughput, every stage alone, dense roofline, oracle baseline."""
+    import torch
+    S, inp = build_state(spec)
+    step = make_step(spec, S)
+
+    # reference copy of known size (scale for the HBM counters)
+    cs = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    cd = torch.empty_like(cs)
+    cd.copy_(cs)
+
+    ms = _time_steps(step, args.steps, args.warmup)
+    tok_s = spec.T / (ms / 1e3)
+
+    st = stage_timings(spec, S, args.stage_reps)
+    gemm_names = [nm for nm in st if nm.startswith(("blk", "dense", "grad"))]
+    g_flops = sum(st[nm]["_flops"] for nm in gemm_names)
+    g_us = sum(st[nm]["us"] for nm in gemm_names)
+    gemm_tflops = g_flops / g_us / 1e6
+    dense = st["dense_fwd"]
+    dense_flops = dense["_flops"]
+    traffic = read_traffic() if label == "q_proj" else None
+    tr = None
+    if traffic and "FETCH_SIZE" in traffic and "WRITE_SIZE" in traffic:
+        tr = round(traffic["FETCH_SIZE"]["gemm_bytes_per_dispatch"] + traffic["WRITE_SIZE"]["gemm_bytes_per_dispatch"])
+    roof = {"kernel": f"dense Wt GEMM, forward (h2 = h1 Wt^T, {spec.T} x {spec.m} x {spec.n}, bf16, fp32 accumulate)",
+            "bound": "mfma", "achieved": round(dense_flops / dense["us"] / 1e6, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(dense_flops / dense["us"] / 1e6 / PEAK_BF16_TFLOPS, 4),
+            "traffic": tr, "avg_launch_us": dense["us"],
+            "algorithmic_flops_per_launch": dense_flops}
+    for v in st.values():
+        v.pop("_flops", None)
+    nR, nP = spec.nblk_R, spec.nblk_P
+    workload = (f"llama8b_{label}: W0 {spec.m}x{spec.n} bf16, b={spec.b} ({nR}+{nP} blocks), k={spec.k}, "
+                f"{spec.T // 2048} x 2048 tokens, {spec.variant} variant"
+                + (f", every Q block at spectral norm {spec.q_block_norm}" if spec.q_block_norm else "")
+                + "; step = cnp_fwd_save + linear_fwd + linear_bwd + cnp_bwd_saved")
+    out = _base_line(args, tok_s, "tokens/s", ms, workload, spec.T)
+    out.update({
+        "gemm_pct_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
+        "gemm_tflops": round(gemm_tflops, 1),
+        "gemm_gflop_per_step": round(g_flops / 1e9, 2),
+        "stages": st,
+        "roofline": roof,
+    })
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, inp)
+    return out
+
+
+def run_layer(args, specs, label, merge):
+    """All 7 linears of a decoder layer (mem variant): step throughput and the
+    whole-step rate of the algorithmic GEMM work; optionally the merge."""
+    import torch
+    from orthogonal_equivalence_poet_amd import binding as B
+    from orthogonal_equivalence_poet_amd import inputs as I
+    states = [build_state(sp)[0] for sp in specs]
+    steps = [make_step(sp, S) for sp, S in zip(specs, states)]
+
+    def step():
+        for f in steps:
+            f()
+    ms = _time_steps(step, args.steps, args.warmup)
+    T = specs[0].T
+    g_flops = 0
+    for sp in specs:
+        fwd = 2 * T * (sp.n * sp.b + sp.n * sp.m + sp.m * sp.b)
+        bwd = 2 * T * (2 * sp.m * sp.b + sp.n * sp.m + 2 * sp.n * sp.b) + 2 * T * (sp.n * sp.b + sp.n * sp.m)
+        g_flops += fwd + bwd
+    out = _base_line(args, T / (ms / 1e3), "tokens/s", ms,
+                     f"{label}: all 7 linears of one decoder layer, b=256, k=3, mem variant, "
+                     f"{T // 2048} x 2048 tokens; step = per linear cnp_fwd_save + linear_fwd + linear_bwd + "
+                     "cnp_bwd_saved", T)
+    out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
+    out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
+    out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
+    if merge:
+        merges = []
+        for sp, S in zip(specs, states):
+            pi_R2 = torch.from_numpy(I.permutation(sp.m, *sp.key, I.PIR2_ID)).cuda()
+            pi_P2 = torch.from_numpy(I.permutation(sp.n, *sp.key, I.PIP2_ID)).cuda()
+            ws = B.workspace(B.poetx_merge_workspace_bytes(S["desc"]))
+            qR, qP = S["q"][:sp.nblk_R], S["q"][sp.nblk_R:]
+            merges.append(lambda S=S, ws=ws, qR=qR, qP=qP, a=pi_R2, c=pi_P2:
+                          B.poetx_merge(S["desc"], S["Wt"], qR, qP, S["pi_R"], S["pi_P"], a, c, ws))
+        us = _time_events(lambda: [f() for f in merges], 5, warm=1)
+        out["merge_all_7_us"] = round(us, 1)
+    return out
+
+
+def run_cnp_13b(args):
+    """One Cayley-Neumann forward (saving) and backward over the b=256 blocks of
+    every POET-X linear in 40 Llama-13B layers."""
+    import torch
+    from orthogonal_equivalence_poet_amd import binding as B
+    from orthogonal_equivalence_poet_amd import inputs as I
+    b, k = 256, 3
+    nblk = I.llama13b_cnp_blocks()
+    q = torch.from_numpy(I.cnp_params(nblk, b, 1e-3, 5, 1, 0)).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dG = torch.randn((nblk, b, b), device="cuda", generator=gen)
+    G = torch.empty((nblk, b, b), dtype=torch.bfloat16, device="cuda")
+    dq = torch.empty_like(q)
+    saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, B.POETX_BF16))
+    ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, B.POETX_BF16))
+    fwd = lambda: B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
+    bwd = lambda: B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, B.POETX_BF16, saved, ws)
+    ms = _time_steps(lambda: (fwd(), bwd()), max(1, args.steps // 4), 2)
+    us_f = _time_events(fwd, 5, warm=1)
+    us_b = _time_events(bwd, 5, warm=1)
+    pf, pb = _products(k)
+    out = _base_line(args, nblk / (ms / 1e3), "blocks/s", ms,
+                     f"cnp_13b: one Cayley-Neumann forward (saving) + backward over {nblk} blocks of 256 "
+                     "(all POET-X linears of 40 Llama-13B layers), k=3, bf16 products", 0)
+    ntri = b * (b - 1) // 2
+    out["fwd_us"], out["bwd_us"] = round(us_f, 1), round(us_b, 1)
+    out["fwd_tflops"] = round(pf * 2 * b ** 3 * nblk / us_f / 1e6, 1)
+    out["bwd_tflops"] = round(pb * 2 * b ** 3 * nblk / us_b / 1e6, 1)
+    out["fwd_gbs"] = round((4 * ntri + 2 * b * b) * nblk / us_f / 1e3, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +422,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-dir", default=None)
+    ap.add_argument("--workload", default="q_proj",
+                    choices=["q_proj", "up_proj", "up_proj_mem", "llama8b_layer", "llama13b_layer", "cnp_13b"])
     args = ap.parse_args()
     if args.pmc_dir:
         parse_pmc(args.pmc_dir)
@@ -265,64 +439,18 @@ def main():
 
     B.load()
     torch.cuda.set_device(0)
-    spec = I.llama8b_q_proj()
-    S, inp = build_state(spec)
-    step = make_step(spec, S)
-
-    # reference copy of known size (scale for the HBM counters)
-    cs = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
-    cd = torch.empty_like(cs)
-    cd.copy_(cs)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    tok_s = spec.T / (ms / 1e3)
-
-    st = stage_timings(spec, S, args.stage_reps)
-    gemm_names = ["blk_fwd_P", "dense_fwd", "blk_fwd_R", "grad_R", "blk_bwd_R", "dense_bwd", "grad_P", "blk_bwd_P"]
-    g_flops = sum(st[nm]["_flops"] for nm in gemm_names)
-    g_us = sum(st[nm]["us"] for nm in gemm_names)
-    gemm_tflops = g_flops / g_us / 1e6
-    dense = st["dense_fwd"]
-    dense_flops = dense["_flops"]
-    traffic = read_traffic()
-    tr = None
-    if traffic and "FETCH_SIZE" in traffic and "WRITE_SIZE" in traffic:
-        tr = round(traffic["FETCH_SIZE"]["gemm_bytes_per_dispatch"] + traffic["WRITE_SIZE"]["gemm_bytes_per_dispatch"])
-    roof = {"kernel": "dense Wt GEMM, forward (h2 = h1 Wt^T, 2048 x 4096 x 4096, bf16, fp32 accumulate)",
-            "bound": "mfma", "achieved": round(dense_flops / dense["us"] / 1e6, 1),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(dense_flops / dense["us"] / 1e6 / PEAK_BF16_TFLOPS, 4),
-            "traffic": tr, "avg_launch_us": dense["us"],
-            "algorithmic_flops_per_launch": dense_flops}
-    for v in st.values():
-        v.pop("_flops", None)
-
-    out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama8b_q_proj: W0 4096x4096 bf16, b=256 (16+16 blocks), k=3, "
-                               "1 x 2048 tokens, fast variant; step = cnp_fwd_save + linear_fwd + linear_bwd + "
-                               "cnp_bwd_saved",
-                   "global_batch": 1, "seq_len": spec.T, "parallelism": "single GPU"},
-        "gemm_pct_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
-        "gemm_tflops": round(gemm_tflops, 1),
-        "gemm_gflop_per_step": round(g_flops / 1e9, 2),
-        "stages": st,
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, inp)
+    w = args.workload
+    if w == "q_proj":
+        out = run_linear(args, I.llama8b_q_proj(), "q_proj")
+    elif w in ("up_proj", "up_proj_mem"):
+        spec = I.llama8b_up_proj("mem" if w == "up_proj_mem" else "fast")
+        out = run_linear(args, spec, "up_proj")
+    elif w == "llama8b_layer":
+        out = run_layer(args, I.llama8b_layer(), "llama8b_layer", merge=True)
+    elif w == "llama13b_layer":
+        out = run_layer(args, I.llama13b_layer(), "llama13b_layer", merge=False)
+    else:
+        out = run_cnp_13b(args)
     print(json.dumps(out))
     return 0
 

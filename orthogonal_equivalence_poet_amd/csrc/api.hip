@@ -259,7 +259,16 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
 // D_1 = Q, D_{i+1} = Q + Q D_i, G = I + Q + D_k + Q D_k.  Every product is a
 // correction term; the leading terms are added in float32 by the epilogue.
 int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void* G, bool gbf16, CnpBufs& B,
-                hipStream_t s) {
+                bool save, hipStream_t s) {
+    if (cbf16 && gbf16 && cnp_fused_supported(b, k) && (!save || k == 3) && nblk * (b / 64) >= 1024) {
+        // many bf16 blocks of 128 or 256 (four or more panels per CU): Q once
+        // to bf16, then every power of Q per 64-row panel inside one kernel (the
+        // saving forward also keeps S and 2Q + S for the backward); few blocks
+        // keep the two batched products, which spread over more workgroups
+        HIP_TRY(skew_unpack(q, B.Qc, true, nblk, (int)b, s, nullptr));
+        HIP_TRY(cnp_fused_fwd(B.Qc, G, save ? B.Sc : nullptr, save ? B.Tc : nullptr, nblk, b, k, s));
+        return POETX_OK;
+    }
     POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
     const int ib = (int)b;
     const int64_t bb = b * b;
@@ -596,7 +605,7 @@ int poetx_cnp_fwd(const float* q, int64_t nblk, int64_t b, int k, void* G, int G
     Carver cv(ws);
     CnpBufs B;
     plan_cnp(cv, cv, nblk, b, k, cbf, false, B);
-    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, as_stream(stream));
+    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, false, as_stream(stream));
 }
 
 size_t poetx_cnp_saved_bytes(int64_t nblk, int64_t b, int k, int dtype) {
@@ -622,7 +631,7 @@ int poetx_cnp_fwd_save(const float* q, int64_t nblk, int64_t b, int k, void* G, 
     Carver cv(ws), sv(saved);
     CnpBufs B;
     plan_cnp(cv, sv, nblk, b, k, cbf, false, B);
-    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, as_stream(stream));
+    return cnp_forward(q, nblk, b, k, cbf, G, cbf, B, true, as_stream(stream));
 }
 
 size_t poetx_cnp_bwd_workspace_bytes(int64_t nblk, int64_t b, int k, int dtype) {
@@ -836,13 +845,13 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
         Carver c1(cnp_base);
         CnpBufs B;
         plan_cnp(c1, c1, m / b, b, d->k, bf, false, B);
-        POETX_TRY(cnp_forward(q_R, m / b, b, d->k, bf, G_R, bf, B, s));
+        POETX_TRY(cnp_forward(q_R, m / b, b, d->k, bf, G_R, bf, B, false, s));
     }
     {
         Carver c2(cnp_base);
         CnpBufs B;
         plan_cnp(c2, c2, n / b, b, d->k, bf, false, B);
-        POETX_TRY(cnp_forward(q_P, n / b, b, d->k, bf, G_P, bf, B, s));
+        POETX_TRY(cnp_forward(q_P, n / b, b, d->k, bf, G_P, bf, B, false, s));
     }
     // W1 = diag(G_R) . Wt  (row blocks);  W2 = W1 . diag(G_P)  (column blocks)
     HIP_TRY(gemm(GemmLayout::NN, bf, bf, b, n, b, m / b, Mat{G_R, b, b * b}, Mat{Wt, n, b * n}, W1, n, b * n, s));

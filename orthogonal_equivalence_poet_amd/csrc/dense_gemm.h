@@ -67,6 +67,13 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
 hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p, hipStream_t stream);
 int pipe_tile_cols(PipeTile t);
 
+// Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
+// kernel): Qc bf16 [nblk, b, b] -> G bf16; with S and T given (k >= 2) also
+// S = Q Q and T = 2Q + S in bf16.  One workgroup per 64-row panel of a block.
+bool cnp_fused_supported(int64_t b, int k);
+hipError_t cnp_fused_fwd(const void* Qc, void* G, void* S, void* T, int64_t nblk, int64_t b, int k,
+                         hipStream_t stream);
+
 // Dense convenience wrappers (batch 1, no split).
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
 // C[M][N] = A[M][K] . B^T (b_nn = false, B is [N][K]) or A . B (b_nn = true, B is [K][N]).

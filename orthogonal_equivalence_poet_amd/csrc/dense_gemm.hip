@@ -579,6 +579,149 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     return hipSuccess;
 }
 
+// A zero the compiler cannot see through: offsets built on it are recomputed
+// where they are used instead of being hoisted and kept live in registers.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    return z;
+}
+
+// ------------------------------------------------ fused Cayley-Neumann forward
+// One workgroup per (block, 64-row panel p) for bf16 blocks of b = 128 or 256:
+// the block's whole bf16 Q sits in LDS as the B operand ([b/64] k-tiles of
+// [b rows][64 k], swizzled as above) and the panel X (64 x b) as the A
+// operand.  Horner on the panel rows,
+//   X_1 = Q_p,  X_{i+1} = X_i Q = -(X_i Q^T)  (i = 1..k),
+//   G_p = I_p + 2 (X_1 + ... + X_k) + X_{k+1}  =  rows p of (I + Q) sum_{i<=k} Q^i,
+// keeps the sum in float32 registers and rounds each X_{i+1} to bf16 into LDS
+// for the next product; every power of Q is formed once per panel and nothing
+// but Q and G crosses HBM.  With S / T given (k >= 2) the kernel also writes
+// S_p = X_2 and T_p = 2 Q_p + S_p (what the saving forward keeps for k = 3).
+template <int B>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+cnp_fused_kernel(const uint16_t* __restrict__ Qc, uint16_t* __restrict__ G, uint16_t* __restrict__ Sv,
+                 uint16_t* __restrict__ Tv, int k, int total) {
+    constexpr int KT = B / 64;          // k-tiles of one product
+    constexpr int NP = B / 64;          // panels per block
+    constexpr int QB = B * 128;         // bytes of one Q k-tile
+    constexpr int XB = 64 * 128;        // bytes of one X k-tile
+    constexpr int MI = 2, NJ = B / 128; // each wave: 64 rows x B/4 columns
+    static_assert(KT * (QB + XB) <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[KT * (QB + XB)];
+    unsigned char* qs = lds;
+    unsigned char* xs = lds + KT * QB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
+    const int z = id / NP, p = id - z * NP;
+    const int64_t zoff = (int64_t)z * B * B;
+    const uint16_t* Qz = Qc + zoff;
+
+    const uint32_t qb = lds_offset(qs), xb = lds_offset(xs);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int j = 0; j < OperandLoads<B, false, 4>::n; ++j)
+            dma_one<B, false, 4>(j, qb + kt * QB, Qz, B, 0, B, kt * 64, B, wave, lane);
+#pragma unroll
+        for (int j = 0; j < OperandLoads<64, false, 4>::n; ++j)
+            dma_one<64, false, 4>(j, xb + kt * XB, Qz, B, 64 * p, B, kt * 64, B, wave, lane);
+    }
+    wait_vmcnt<0>();
+    block_barrier();
+
+    f32x16_t sum[MI][NJ], acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[i][j][r] = 0.f;
+    const int n_base = wave * (B / 4);
+    for (int it = 1; it <= k; ++it) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll 1
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                uint4 af[MI], bfr[NJ];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) af[i] = load_frag<false, 64>(xs + kt * XB, i * 32, ks, lane);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bfr[j] = load_frag<false, B>(qs + kt * QB, n_base + j * 32, ks, lane);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], acc[i][j]);
+            }
+        }
+        // X_{it+1} = -acc; weight 2 for it + 1 <= k, 1 for the last power
+        const float w = it < k ? -2.f : -1.f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sum[i][j][r] += w * acc[i][j][r];
+        if (it == 1 && Sv) {   // S_p = X_2, T_p = 2 Q_p + S_p
+            const int oz = opaque_zero();
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + oz;
+                        const int n = n_base + j * 32 + (lane & 31);
+                        const int row = 64 * p + m;
+                        const uint16_t qv = *reinterpret_cast<const uint16_t*>(
+                            qs + (n >> 6) * QB + row * 128 + ((((n & 63) >> 3) ^ swz_k(row)) << 4) + (n & 7) * 2);
+                        const float sv = -acc[i][j][r];
+                        Sv[zoff + (int64_t)row * B + n] = f32_to_bf16(sv);
+                        Tv[zoff + (int64_t)row * B + n] = f32_to_bf16(2.f * bf16_to_f32(qv) + sv);
+                    }
+        }
+        if (it < k) {
+            block_barrier();   // every wave is done reading X_it
+            const int oz = opaque_zero();
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + oz;
+                        const int n = n_base + j * 32 + (lane & 31);
+                        *reinterpret_cast<uint16_t*>(xs + (n >> 6) * XB + m * 128 +
+                                                     ((((n & 63) >> 3) ^ swz_k(m)) << 4) + (n & 7) * 2) =
+                            f32_to_bf16(-acc[i][j][r]);
+                    }
+            __syncthreads();
+        }
+    }
+    // G_p = I_p + 2 Q_p + sum
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n_base + j * 32 + (lane & 31);
+                const int row = 64 * p + m;
+                const uint16_t qv = *reinterpret_cast<const uint16_t*>(
+                    qs + (n >> 6) * QB + row * 128 + ((((n & 63) >> 3) ^ swz_k(row)) << 4) + (n & 7) * 2);
+                const float g = (row == n ? 1.f : 0.f) + 2.f * bf16_to_f32(qv) + sum[i][j][r];
+                G[zoff + (int64_t)row * B + n] = f32_to_bf16(g);
+            }
+}
+
 }  // namespace
 
 bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
@@ -673,6 +816,27 @@ hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B,
     p.M = M; p.N = N; p.K = K;
     p.k_per_split = K;
     return pipe_gemm(false, b_nn, false, p, stream, PipeTile::Tall);
+}
+
+bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }
+
+hipError_t cnp_fused_fwd(const void* Qc, void* G, void* S, void* T, int64_t nblk, int64_t b, int k,
+                         hipStream_t stream) {
+    if (nblk <= 0) return hipSuccess;
+    if (!cnp_fused_supported(b, k) || ((S == nullptr) != (T == nullptr)) || (S && k < 2)) return hipErrorInvalidValue;
+    const int64_t panels = nblk * (b / 64);
+    if (panels > 0x7fffffff) return hipErrorInvalidValue;
+    const auto q = static_cast<const uint16_t*>(Qc);
+    const auto g = static_cast<uint16_t*>(G);
+    const auto sv = static_cast<uint16_t*>(S);
+    const auto tv = static_cast<uint16_t*>(T);
+    if (b == 256)
+        hipLaunchKernelGGL(cnp_fused_kernel<256>, dim3((unsigned)panels), dim3(256), 0, stream, q, g, sv, tv, k,
+                           (int)panels);
+    else
+        hipLaunchKernelGGL(cnp_fused_kernel<128>, dim3((unsigned)panels), dim3(256), 0, stream, q, g, sv, tv, k,
+                           (int)panels);
+    return hipGetLastError();
 }
 
 }  // namespace poetx
