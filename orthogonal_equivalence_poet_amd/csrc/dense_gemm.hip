@@ -9,7 +9,8 @@
 //   small   the Cayley-Neumann b x b products (batched over blocks, general
 //           epilogue with float32 addends and several outputs)
 //
-// Workgroup tile BM x BN x 64 (256 x 128 for the dense products, 128 x 256 for
+// Workgroup tile BM x BN x 64 (256 x 128 for the dense products, 256 x 256 once
+// there are enough of those to fill the chip, 128 x 256 for
 // the block products, 128 x 128 for the block gradients, 64 x 64 or 128 x 128
 // for the small products), four waves in a 2 x 2 grid, each wave owning a
 // (BM/2) x (BN/2) sub-tile of v_mfma_f32_32x32x16_bf16 tiles (float32
@@ -741,6 +742,9 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     // instantiated combinations: dense / block products (k-major A, bf16 out) and
     // block gradients (m/n-major A and B, float32 out)
     if (!a_mn && !out_f32) {
+        if (tile == PipeTile::Big)
+            return b_mn ? launch<256, 256, false, true, false, kEpiPlain, 2, 2, 4>(p, stream)
+                        : launch<256, 256, false, false, false, kEpiPlain, 2, 2, 4>(p, stream);
         if (tile == PipeTile::Wide)
             return b_mn ? launch<128, 256, false, true, false, kEpiPlain, 3, 2, 4>(p, stream)
                         : launch<128, 256, false, false, false, kEpiPlain, 3, 2, 4>(p, stream);
@@ -800,8 +804,12 @@ hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hip
                    : launch<64, 64, false, false, false, kEpiGeneral, 4, 2, 2, 1>(p, stream);
 }
 
-int pipe_tile_rows(PipeTile t) { return t == PipeTile::Tall ? 256 : t == PipeTile::Small ? 64 : 128; }
-int pipe_tile_cols(PipeTile t) { return t == PipeTile::Wide ? 256 : t == PipeTile::Small ? 64 : 128; }
+int pipe_tile_rows(PipeTile t) {
+    return (t == PipeTile::Tall || t == PipeTile::Big) ? 256 : t == PipeTile::Small ? 64 : 128;
+}
+int pipe_tile_cols(PipeTile t) {
+    return (t == PipeTile::Wide || t == PipeTile::Big) ? 256 : t == PipeTile::Small ? 64 : 128;
+}
 
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     return M > 0 && N >= 8 && K >= BK && K % BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0;
@@ -815,7 +823,9 @@ hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B,
     p.C = C; p.ldc = ldc;
     p.M = M; p.N = N; p.K = K;
     p.k_per_split = K;
-    return pipe_gemm(false, b_nn, false, p, stream, PipeTile::Tall);
+    // 256 x 256 tiles (two-stage ring, two waves per SIMD) once they alone fill the chip
+    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    return pipe_gemm(false, b_nn, false, p, stream, big_tiles >= 256 ? PipeTile::Big : PipeTile::Tall);
 }
 
 bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }
