@@ -260,13 +260,12 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
 // correction term; the leading terms are added in float32 by the epilogue.
 int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void* G, bool gbf16, CnpBufs& B,
                 bool save, hipStream_t s) {
-    if (cbf16 && gbf16 && cnp_fused_supported(b, k) && (!save || k == 3) && nblk * (b / 64) >= 1024) {
-        // many bf16 blocks of 128 or 256 (four or more panels per CU): Q once
-        // to bf16, then every power of Q per 64-row panel inside one kernel (the
-        // saving forward also keeps S and 2Q + S for the backward); few blocks
-        // keep the two batched products, which spread over more workgroups
-        HIP_TRY(skew_unpack(q, B.Qc, true, nblk, (int)b, s, nullptr));
-        HIP_TRY(cnp_fused_fwd(B.Qc, G, save ? B.Sc : nullptr, save ? B.Tc : nullptr, nblk, b, k, s));
+    if (cbf16 && gbf16 && cnp_fused_supported(b, k) && (!save || k == 3) && (reinterpret_cast<uintptr_t>(G) & 15) == 0) {
+        // bf16 blocks of 128 or 256: one kernel from the packed parameters to G,
+        // every power of Q formed per panel on chip (the saving forward also
+        // keeps Q, S and 2Q + S in bf16 for the backward)
+        HIP_TRY(cnp_fused_fwd(q, G, save ? B.Qc : nullptr, save ? B.Sc : nullptr, save ? B.Tc : nullptr, nblk, b, k,
+                              s));
         return POETX_OK;
     }
     POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));

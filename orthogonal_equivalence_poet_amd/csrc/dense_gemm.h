@@ -69,10 +69,11 @@ hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p, hipStr
 int pipe_tile_cols(PipeTile t);
 
 // Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
-// kernel): Qc bf16 [nblk, b, b] -> G bf16; with S and T given (k >= 2) also
-// S = Q Q and T = 2Q + S in bf16.  One workgroup per 64-row panel of a block.
+// kernel): packed float32 parameters q [nblk, b(b-1)/2] -> G bf16 [nblk, b, b];
+// with Qc given also Q in bf16, with S and T given (k >= 2) also S = Q Q and
+// T = 2Q + S in bf16.  One workgroup per 64-row (few blocks: 32-row) panel.
 bool cnp_fused_supported(int64_t b, int k);
-hipError_t cnp_fused_fwd(const void* Qc, void* G, void* S, void* T, int64_t nblk, int64_t b, int k,
+hipError_t cnp_fused_fwd(const float* q, void* G, void* Qc, void* S, void* T, int64_t nblk, int64_t b, int k,
                          hipStream_t stream);
 
 // Dense convenience wrappers (batch 1, no split).

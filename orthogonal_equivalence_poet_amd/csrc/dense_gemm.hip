@@ -589,49 +589,160 @@ __device__ __forceinline__ int opaque_zero() {
 }
 
 // ------------------------------------------------ fused Cayley-Neumann forward
-// One workgroup per (block, 64-row panel p) for bf16 blocks of b = 128 or 256:
-// the block's whole bf16 Q sits in LDS as the B operand ([b/64] k-tiles of
-// [b rows][64 k], swizzled as above) and the panel X (64 x b) as the A
-// operand.  Horner on the panel rows,
-//   X_1 = Q_p,  X_{i+1} = X_i Q = -(X_i Q^T)  (i = 1..k),
-//   G_p = I_p + 2 (X_1 + ... + X_k) + X_{k+1}  =  rows p of (I + Q) sum_{i<=k} Q^i,
-// keeps the sum in float32 registers and rounds each X_{i+1} to bf16 into LDS
-// for the next product; every power of Q is formed once per panel and nothing
-// but Q and G crosses HBM.  With S / T given (k >= 2) the kernel also writes
+// One workgroup per (block z, panel p of PH rows) for bf16 blocks of b = 128 or
+// 256, straight from the packed parameters:
+//  1. Q = U - U^T is built in LDS in bf16 from the block's strict upper
+//     triangle U (row-major packed): each thread takes 8 x 8 sub-blocks of U
+//     (16-byte loads of their row segments) and writes their rows, and the
+//     negated rows of their transpose, as 16-byte chunks (a diagonal sub-block
+//     holds both halves and a zero diagonal).  The image is [b/64] k-tiles of
+//     [b rows][64 k], 128-byte rows of eight 16-byte chunks, chunk c of row r in
+//     slot c ^ (r & 7) ^ ((r >> 3) & 7): the MFMA fragment reads (16 consecutive
+//     rows, one chunk), the row writes (one row, consecutive chunks) and the
+//     transposed writes (rows 8 apart, one chunk) all meet at most two lanes
+//     per bank group.
+//  2. Horner on the panel rows, X_1 = Q_p, X_{i+1} = X_i Q, each product taken
+//     transposed, C = Q X_i^T = -X_{i+1}^T, so that a lane holds four
+//     consecutive columns of a row of X_{i+1} (one 8-byte LDS write).  X_1 is
+//     read from the Q image itself.
+//  3. G_p = I_p + 2 (X_1 + ... + X_k) + X_{k+1}, the rows p of
+//     (I + Q) sum_{i<=k} Q^i: the sum stays in float32 registers, each X_{i+1}
+//     is rounded to bf16 into LDS for the next product, and G_p is staged in the
+//     X buffer and stored as whole rows.
+// With Qc given the panel rows of Q are stored as well; with S / T (k >= 2)
 // S_p = X_2 and T_p = 2 Q_p + S_p (what the saving forward keeps for k = 3).
-template <int B>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-cnp_fused_kernel(const uint16_t* __restrict__ Qc, uint16_t* __restrict__ G, uint16_t* __restrict__ Sv,
-                 uint16_t* __restrict__ Tv, int k, int total) {
-    constexpr int KT = B / 64;          // k-tiles of one product
-    constexpr int NP = B / 64;          // panels per block
-    constexpr int QB = B * 128;         // bytes of one Q k-tile
-    constexpr int XB = 64 * 128;        // bytes of one X k-tile
-    constexpr int MI = 2, NJ = B / 128; // each wave: 64 rows x B/4 columns
-    static_assert(KT * (QB + XB) <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[KT * (QB + XB)];
+template <int B, int PH>
+struct FusedCnp {
+    static constexpr int KT = B / 64;         // k-tiles of one product
+    static constexpr int NP = B / PH;         // panels per block
+    static constexpr int QB = B * 128;        // bytes of one Q k-tile ([B rows][64 k])
+    static constexpr int XB = PH * 128;       // bytes of one X k-tile ([PH rows][64 k])
+    static constexpr int LDS = KT * (QB + XB);
+    static constexpr int MI = B / 128;        // wave w: rows n in [w B/4, (w+1) B/4) of C
+    static constexpr int NJ = PH / 32;        //         and all PH columns m
+    static constexpr int NPAR = B * (B - 1) / 2;
+    static constexpr int NB8 = B / 8;         // 8 x 8 sub-blocks per side
+    static constexpr int OFFDIAG = NB8 * (NB8 - 1) / 2;
+    static constexpr int TASKS = NB8 + OFFDIAG;
+};
+
+__device__ __forceinline__ int cnp_swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+
+// Byte offset of element (row, k) in a k-tiled image with k-tile size TILE.
+template <int TILE>
+__device__ __forceinline__ int img_off(int row, int kk) {
+    return (kk >> 6) * TILE + row * 128 + ((((kk & 63) >> 3) ^ cnp_swz(row)) << 4) + (kk & 7) * 2;
+}
+
+// k-major fragment of rows row0 .. row0 + 31 (lane l: row row0 + l % 32,
+// k = 16 ks + 8 (l / 32) + 0..7) from a k-tile of such an image.
+__device__ __forceinline__ uint4 img_frag(const unsigned char* __restrict__ tile, int row0, int ks, int lane) {
+    const int row = row0 + (lane & 31);
+    const int slot = (2 * ks + (lane >> 5)) ^ cnp_swz(row);
+    return *reinterpret_cast<const uint4*>(tile + row * 128 + slot * 16);
+}
+
+typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int B, int PH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, B == 256 ? 1 : 2)))
+cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t* __restrict__ Qc,
+                 uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv, int k, int total) {
+    using F = FusedCnp<B, PH>;
+    constexpr int KT = F::KT, QB = F::QB, XB = F::XB, MI = F::MI, NJ = F::NJ, NB8 = F::NB8;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS];
     unsigned char* qs = lds;
     unsigned char* xs = lds + KT * QB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int id = blockIdx.x;
     if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
-    const int z = id / NP, p = id - z * NP;
+    const int z = id / F::NP, p = id - z * F::NP;
     const int64_t zoff = (int64_t)z * B * B;
-    const uint16_t* Qz = Qc + zoff;
+    const float* __restrict__ qz = q + (int64_t)z * F::NPAR;
+    const int r0 = PH * p;   // first row of the panel
 
-    const uint32_t qb = lds_offset(qs), xb = lds_offset(xs);
+    // 1. the Q image.  Tasks: the strict upper sub-blocks (sub-rows R' and
+    // NB8 - 2 - R' sharing a run of NB8 tasks), then the diagonal ones; every
+    // thread issues the loads of all its tasks before it writes any.
+    constexpr int NTASK = (F::TASKS + 255) / 256;
+    float u[NTASK][8][8];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int s = 0; s < NTASK; ++s) {
+        const int t = tid + 256 * s;
+        if (t < F::OFFDIAG) {
+            const int Rp = t / NB8, cp = t - Rp * NB8;
+            const bool first = cp < NB8 - 1 - Rp;
+            const int R = first ? Rp : NB8 - 2 - Rp;
+            const int C = first ? Rp + 1 + cp : R + 1 + cp - (NB8 - 1 - Rp);
 #pragma unroll
-        for (int j = 0; j < OperandLoads<B, false, 4>::n; ++j)
-            dma_one<B, false, 4>(j, qb + kt * QB, Qz, B, 0, B, kt * 64, B, wave, lane);
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * R + i;
+                const float* src = qz + (r * B - r * (r + 1) / 2 - r - 1 + 8 * C);   // U[r][8C]
+                const f32x4u_t lo = *reinterpret_cast<const f32x4u_t*>(src);
+                const f32x4u_t hi = *reinterpret_cast<const f32x4u_t*>(src + 4);
+                u[s][i][0] = lo.x; u[s][i][1] = lo.y; u[s][i][2] = lo.z; u[s][i][3] = lo.w;
+                u[s][i][4] = hi.x; u[s][i][5] = hi.y; u[s][i][6] = hi.z; u[s][i][7] = hi.w;
+            }
+        } else if (t < F::TASKS) {   // diagonal sub-block: scalar loads, clamped below the diagonal
+            const int R = t - F::OFFDIAG;
 #pragma unroll
-        for (int j = 0; j < OperandLoads<64, false, 4>::n; ++j)
-            dma_one<64, false, 4>(j, xb + kt * XB, Qz, B, 64 * p, B, kt * 64, B, wave, lane);
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * R + i;
+                const int base = r * B - r * (r + 1) / 2 - r - 1;   // U[r][c] at base + c
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int c = 8 * R + j;
+                    const float v = qz[max(base + c, 0)];   // base + c >= -1 below the diagonal
+                    u[s][i][j] = c > r ? v : 0.f;
+                }
+            }
+        }
     }
-    wait_vmcnt<0>();
-    block_barrier();
+#pragma unroll
+    for (int s = 0; s < NTASK; ++s) {
+        const int t = tid + 256 * s;
+        if (t < F::OFFDIAG) {
+            const int Rp = t / NB8, cp = t - Rp * NB8;
+            const bool first = cp < NB8 - 1 - Rp;
+            const int R = first ? Rp : NB8 - 2 - Rp;
+            const int C = first ? Rp + 1 + cp : R + 1 + cp - (NB8 - 1 - Rp);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint4*>(qs + img_off<QB>(8 * R + i, 8 * C)) =
+                    make_uint4(pack_bf16x2(u[s][i][0], u[s][i][1]), pack_bf16x2(u[s][i][2], u[s][i][3]),
+                               pack_bf16x2(u[s][i][4], u[s][i][5]), pack_bf16x2(u[s][i][6], u[s][i][7]));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint4*>(qs + img_off<QB>(8 * C + j, 8 * R)) =
+                    make_uint4(pack_bf16x2(-u[s][0][j], -u[s][1][j]), pack_bf16x2(-u[s][2][j], -u[s][3][j]),
+                               pack_bf16x2(-u[s][4][j], -u[s][5][j]), pack_bf16x2(-u[s][6][j], -u[s][7][j]));
+        } else if (t < F::TASKS) {
+            // rows of the diagonal sub-block: U above the diagonal, -U^T below
+            const int R = t - F::OFFDIAG;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = j > i ? u[s][i][j] : (j < i ? -u[s][j][i] : 0.f);
+                *reinterpret_cast<uint4*>(qs + img_off<QB>(8 * R + i, 8 * R)) =
+                    make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7]));
+            }
+        }
+    }
+    __syncthreads();
 
+    // rows of an image as 16-byte chunks: PH rows x B/8 chunks over the workgroup
+    auto copy_rows = [&](uint16_t* __restrict__ dst, auto chunk_value) {
+        for (int u = tid; u < PH * (B / 8); u += 256) {
+            const int m = u / (B / 8), c8 = u - m * (B / 8);
+            *reinterpret_cast<uint4*>(dst + zoff + (int64_t)(r0 + m) * B + 8 * c8) = chunk_value(m, 8 * c8);
+        }
+    };
+    if (Qc)
+        copy_rows(Qc, [&](int m, int c) { return *reinterpret_cast<const uint4*>(qs + img_off<QB>(r0 + m, c)); });
+
+    // 2. Horner: acc = Q X_it^T, X_{it+1} = -acc^T
     f32x16_t sum[MI][NJ], acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -641,28 +752,37 @@ cnp_fused_kernel(const uint16_t* __restrict__ Qc, uint16_t* __restrict__ G, uint
             for (int r = 0; r < 16; ++r) sum[i][j][r] = 0.f;
     const int n_base = wave * (B / 4);
     for (int it = 1; it <= k; ++it) {
+        // B operand: X_1 = rows r0.. of the Q image, later X_it in the X buffer
+        const unsigned char* xb = it == 1 ? qs : xs;
+        const int xtile = it == 1 ? QB : XB;
+        const int xrow = it == 1 ? r0 : 0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-#pragma unroll 1
-        for (int kt = 0; kt < KT; ++kt) {
+        uint4 af[2][MI], bfr[2][NJ];
+        auto load = [&](int ks, uint4 (&a)[MI], uint4 (&b)[NJ]) {
+            const int kt = ks >> 2, kk = ks & 3;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                uint4 af[MI], bfr[NJ];
+            for (int i = 0; i < MI; ++i) a[i] = img_frag(qs + kt * QB, n_base + i * 32, kk, lane);
 #pragma unroll
-                for (int i = 0; i < MI; ++i) af[i] = load_frag<false, 64>(xs + kt * XB, i * 32, ks, lane);
+            for (int j = 0; j < NJ; ++j) b[j] = img_frag(xb + kt * xtile, xrow + j * 32, kk, lane);
+        };
+        load(0, af[0], bfr[0]);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bfr[j] = load_frag<false, B>(qs + kt * QB, n_base + j * 32, ks, lane);
+        for (int ks = 0; ks < 4 * KT; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < 4 * KT) load(ks + 1, af[cur ^ 1], bfr[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], acc[i][j]);
-            }
+                for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // X_{it+1} = -acc; weight 2 for it + 1 <= k, 1 for the last power
+        // X_{it+1} enters the sum with weight 2 up to X_k, 1 for X_{k+1}
         const float w = it < k ? -2.f : -1.f;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -670,57 +790,63 @@ cnp_fused_kernel(const uint16_t* __restrict__ Qc, uint16_t* __restrict__ G, uint
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sum[i][j][r] += w * acc[i][j][r];
-        if (it == 1 && Sv) {   // S_p = X_2, T_p = 2 Q_p + S_p
-            const int oz = opaque_zero();
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + oz;
-                        const int n = n_base + j * 32 + (lane & 31);
-                        const int row = 64 * p + m;
-                        const uint16_t qv = *reinterpret_cast<const uint16_t*>(
-                            qs + (n >> 6) * QB + row * 128 + ((((n & 63) >> 3) ^ swz_k(row)) << 4) + (n & 7) * 2);
-                        const float sv = -acc[i][j][r];
-                        Sv[zoff + (int64_t)row * B + n] = f32_to_bf16(sv);
-                        Tv[zoff + (int64_t)row * B + n] = f32_to_bf16(2.f * bf16_to_f32(qv) + sv);
-                    }
-        }
         if (it < k) {
             block_barrier();   // every wave is done reading X_it
-            const int oz = opaque_zero();
+            // lane: column m = 32 j + lane % 32 of C, rows n = n0 .. n0 + 3 per (i, r / 4)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + oz;
-                        const int n = n_base + j * 32 + (lane & 31);
-                        *reinterpret_cast<uint16_t*>(xs + (n >> 6) * XB + m * 128 +
-                                                     ((((n & 63) >> 3) ^ swz_k(m)) << 4) + (n & 7) * 2) =
-                            f32_to_bf16(-acc[i][j][r]);
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int m = j * 32 + (lane & 31);
+                        const int n0 = n_base + i * 32 + r4 * 8 + (lane >> 5) * 4;
+                        *reinterpret_cast<uint2*>(xs + img_off<XB>(m, n0)) =
+                            make_uint2(pack_bf16x2(-acc[i][j][4 * r4], -acc[i][j][4 * r4 + 1]),
+                                       pack_bf16x2(-acc[i][j][4 * r4 + 2], -acc[i][j][4 * r4 + 3]));
                     }
             __syncthreads();
+            if (it == 1 && Sv) {   // S_p = X_2, T_p = 2 Q_p + S_p
+                copy_rows(Sv, [&](int m, int c) { return *reinterpret_cast<const uint4*>(xs + img_off<XB>(m, c)); });
+                copy_rows(Tv, [&](int m, int c) {
+                    const uint4 sv = *reinterpret_cast<const uint4*>(xs + img_off<XB>(m, c));
+                    const uint4 qv = *reinterpret_cast<const uint4*>(qs + img_off<QB>(r0 + m, c));
+                    const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w}, q4[4] = {qv.x, qv.y, qv.z, qv.w};
+                    uint32_t t4[4];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h)
+                        t4[h] = pack_bf16x2(2.f * bf16_to_f32((uint16_t)q4[h]) + bf16_to_f32((uint16_t)s4[h]),
+                                            2.f * bf16_to_f32((uint16_t)(q4[h] >> 16)) +
+                                                bf16_to_f32((uint16_t)(s4[h] >> 16)));
+                    return make_uint4(t4[0], t4[1], t4[2], t4[3]);
+                });
+            }
         }
     }
-    // G_p = I_p + 2 Q_p + sum
+
+    // 3. G_p = I_p + 2 Q_p + sum, staged in the X buffer, then stored by rows
+    block_barrier();   // every wave is done reading the X buffer
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n_base + j * 32 + (lane & 31);
-                const int row = 64 * p + m;
-                const uint16_t qv = *reinterpret_cast<const uint16_t*>(
-                    qs + (n >> 6) * QB + row * 128 + ((((n & 63) >> 3) ^ swz_k(row)) << 4) + (n & 7) * 2);
-                const float g = (row == n ? 1.f : 0.f) + 2.f * bf16_to_f32(qv) + sum[i][j][r];
-                G[zoff + (int64_t)row * B + n] = f32_to_bf16(g);
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int m = j * 32 + (lane & 31);
+                const int n0 = n_base + i * 32 + r4 * 8 + (lane >> 5) * 4;
+                const uint2 qv = *reinterpret_cast<const uint2*>(qs + img_off<QB>(r0 + m, n0));
+                float g[4];
+                const uint32_t q2[2] = {qv.x, qv.y};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint16_t qh = (uint16_t)(q2[e >> 1] >> (16 * (e & 1)));
+                    g[e] = (r0 + m == n0 + e ? 1.f : 0.f) + 2.f * bf16_to_f32(qh) + sum[i][j][4 * r4 + e];
+                }
+                *reinterpret_cast<uint2*>(xs + img_off<XB>(m, n0)) =
+                    make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
             }
+    __syncthreads();
+    copy_rows(G, [&](int m, int c) { return *reinterpret_cast<const uint4*>(xs + img_off<XB>(m, c)); });
 }
 
 }  // namespace
@@ -830,22 +956,27 @@ hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B,
 
 bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }
 
-hipError_t cnp_fused_fwd(const void* Qc, void* G, void* S, void* T, int64_t nblk, int64_t b, int k,
+hipError_t cnp_fused_fwd(const float* q, void* G, void* Qc, void* S, void* T, int64_t nblk, int64_t b, int k,
                          hipStream_t stream) {
     if (nblk <= 0) return hipSuccess;
     if (!cnp_fused_supported(b, k) || ((S == nullptr) != (T == nullptr)) || (S && k < 2)) return hipErrorInvalidValue;
-    const int64_t panels = nblk * (b / 64);
+    // 64-row panels, or 32-row ones while 64-row panels would not give every CU one
+    const bool tall = nblk * (b / 64) >= 256;
+    const int64_t panels = nblk * (b / (tall ? 64 : 32));
     if (panels > 0x7fffffff) return hipErrorInvalidValue;
-    const auto q = static_cast<const uint16_t*>(Qc);
     const auto g = static_cast<uint16_t*>(G);
+    const auto qc = static_cast<uint16_t*>(Qc);
     const auto sv = static_cast<uint16_t*>(S);
     const auto tv = static_cast<uint16_t*>(T);
-    if (b == 256)
-        hipLaunchKernelGGL(cnp_fused_kernel<256>, dim3((unsigned)panels), dim3(256), 0, stream, q, g, sv, tv, k,
-                           (int)panels);
+    const dim3 grid((unsigned)panels);
+    if (b == 256 && tall)
+        hipLaunchKernelGGL((cnp_fused_kernel<256, 64>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
+    else if (b == 256)
+        hipLaunchKernelGGL((cnp_fused_kernel<256, 32>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
+    else if (tall)
+        hipLaunchKernelGGL((cnp_fused_kernel<128, 64>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     else
-        hipLaunchKernelGGL(cnp_fused_kernel<128>, dim3((unsigned)panels), dim3(256), 0, stream, q, g, sv, tv, k,
-                           (int)panels);
+        hipLaunchKernelGGL((cnp_fused_kernel<128, 32>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     return hipGetLastError();
 }
 

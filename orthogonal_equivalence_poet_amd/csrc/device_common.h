@@ -19,12 +19,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// float -> bf16, round to nearest even; NaN stays NaN (quiet).
+// float -> bf16, round to nearest even; NaN stays NaN (quiet).  gfx950
+// converts in hardware (v_cvt_pk_bf16_f32); its result equals the bit-level
+// rounding (add 0x7fff plus the kept lsb, NaN: upper half | 0x40) for every
+// float32 pattern, denormals and NaNs included.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two floats -> packed bf16 pair (lo in bits 0..15), one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> struct ElemTraits;
