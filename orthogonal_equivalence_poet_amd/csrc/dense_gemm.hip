@@ -197,11 +197,7 @@ __device__ __forceinline__ uint4 load_frag(const unsigned char* __restrict__ bas
     }
 }
 
-// One k-tile (four k-steps of 16).  Fragments are double-buffered in
-// registers: the LDS reads of step ks+1 are issued before the MFMAs of step
-// ks, and scheduling barriers keep the compiler from sinking them, so each
-// wave (one per SIMD) waits for LDS once per k-tile instead of once per
-// fragment.
+// Fragments of k-step ks for one wave (MI A fragments, NJ B fragments).
 template <class G, bool A_MN, bool B_MN>
 __device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st, int wm, int wn, int ks, int lane,
                                            uint4 (&af)[G::MI], uint4 (&bfr)[G::NJ]) {
@@ -211,6 +207,10 @@ __device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st,
     for (int j = 0; j < G::NJ; ++j) bfr[j] = load_frag<B_MN, G::BN>(st + G::kABytes, wn * G::WTN + j * 32, ks, lane);
 }
 
+// One k-tile (four k-steps of 16) with register double-buffered fragments:
+// the LDS reads of step ks+1 are issued before the MFMAs of step ks, and
+// scheduling barriers keep the compiler from sinking them; a quarter of the
+// next tile's loads goes out with each k-step.
 template <class G, bool A_MN, bool B_MN>
 __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, int wm, int wn, int lane,
                                              f32x16_t (&acc)[G::MI][G::NJ], const DmaJob& next, bool load_next) {
@@ -220,7 +220,6 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ s
     for (int ks = 0; ks < BK / 16; ++ks) {
         const int cur = ks & 1;
         if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(st, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
-        // a quarter of the next tile's loads per k-step
         if (load_next) {
             switch (ks) {
                 case 0: dma_part<G, A_MN, B_MN, 0, 4>(next); break;
@@ -452,6 +451,8 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
 
+    if (nk == 0) return;
+
     DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) {
@@ -461,25 +462,74 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
             dma_tile<G, A_MN, B_MN>(job);
         }
     }
-    int st = 0;        // stage of tile kt
-    int st_load = S - 1;   // stage that receives tile kt + S - 1
-    for (int kt = 0; kt < nk; ++kt) {
-        // this thread's loads of tile kt are done when at most those of the
-        // tiles after it (up to kt + S - 2) remain
+    // Tile kt becomes readable once this thread's loads of it are done (at most
+    // those of the tiles after it, up to kt + S - 2, remain) and every wave has
+    // passed the barrier; a ragged last m/n-major tile then gets its rows past K
+    // zeroed (they were loaded from clamped rows).
+    auto enter = [&](int kt, int stage) {
         wait_tiles<kLoadsPerTile, S>(min(nk, kt + S - 1) - kt - 1);
-        block_barrier();   // everyone's tile kt has landed; stage st_load (tile kt-1) is no longer read
+        block_barrier();
         if constexpr (A_MN || B_MN) {
             const int valid = ke - (kb + kt * BK);
-            if (valid < BK) {   // ragged last tile: rows past K were loaded from clamped rows
-                if constexpr (A_MN) zero_rows_mn<BM, G::kThreads>(lds + st * kStageBytes, valid, tid);
-                if constexpr (B_MN) zero_rows_mn<BN, G::kThreads>(lds + st * kStageBytes + kABytes, valid, tid);
+            if (valid < BK) {
+                if constexpr (A_MN) zero_rows_mn<BM, G::kThreads>(lds + stage * kStageBytes, valid, tid);
+                if constexpr (B_MN) zero_rows_mn<BN, G::kThreads>(lds + stage * kStageBytes + kABytes, valid, tid);
                 __syncthreads();
             }
         }
+    };
+    int st = 0;            // stage of tile kt
+    int st_load = S - 1;   // stage that receives tile kt + S - 1
+    // 256 x 128 tiles (three stages: tile kt + 1 was requested a whole tile
+    // ago) hand over to tile kt + 1 (wait, barrier, its first fragments) before
+    // the last k-step's MFMAs of tile kt, which then cover the barrier and the
+    // first LDS reads of the next tile; the same barrier frees tile kt's stage,
+    // as every wave holds tile kt's last fragments in registers by then.  Other
+    // tiles hand over at the top of each tile.
+    if constexpr (!(S >= 3 && BM == 256 && BN == 128)) {
+        for (int kt = 0; kt < nk; ++kt) {
+            enter(kt, st);
+            job.stage = base + st_load * kStageBytes;
+            job.k0 = kb + (kt + S - 1) * BK;
+            compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc, job, kt + S - 1 < nk);
+            st = st == S - 1 ? 0 : st + 1;
+            st_load = st_load == S - 1 ? 0 : st_load + 1;
+        }
+        return;
+    }
+    uint4 af[2][G::MI], bfr[2][G::NJ];
+    enter(0, 0);
+    load_frags<G, A_MN, B_MN>(lds, wm, wn, 0, lane, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
         job.stage = base + st_load * kStageBytes;
         job.k0 = kb + (kt + S - 1) * BK;
-        compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc, job, kt + S - 1 < nk);
-        st = st == S - 1 ? 0 : st + 1;
+        const bool load_next = kt + S - 1 < nk;
+        const unsigned char* cur_st = lds + st * kStageBytes;
+        const int st_next = st == S - 1 ? 0 : st + 1;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(cur_st, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            if (load_next) {
+                switch (ks) {
+                    case 0: dma_part<G, A_MN, B_MN, 0, 4>(job); break;
+                    case 1: dma_part<G, A_MN, B_MN, 1, 4>(job); break;
+                    case 2: dma_part<G, A_MN, B_MN, 2, 4>(job); break;
+                    default: dma_part<G, A_MN, B_MN, 3, 4>(job); break;
+                }
+            }
+            if (ks == BK / 16 - 1 && kt + 1 < nk) {
+                enter(kt + 1, st_next);
+                load_frags<G, A_MN, B_MN>(lds + st_next * kStageBytes, wm, wn, 0, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        st = st_next;
         st_load = st_load == S - 1 ? 0 : st_load + 1;
     }
 }
