@@ -630,6 +630,156 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     return hipSuccess;
 }
 
+// ------------------------------------------------ block gradients, split K
+// C (64 x 64 tile, float32) = A^T B with A [K][M] and B [K][N] m/n-major (the
+// token axis is K).  A stage holds KSW consecutive 64-k tiles; the waves form
+// KSW groups of WG waves, group g multiplies tile g of every stage into
+// accumulators of its own (WG = 4: a 2 x 2 grid of 32 x 32 wave tiles; WG = 1:
+// one wave owns the whole 64 x 64 tile), and the KSW partial tiles are summed
+// through LDS in group order at the end, so the result does not depend on
+// timing.  k-tiles past K (a ragged last stage) are still loaded, from clamped
+// rows, so every stage costs every thread the same number of loads, and skipped.
+template <int KSW, int WG, int S>
+__global__ void __launch_bounds__(64 * KSW * WG) __attribute__((amdgpu_waves_per_eu(1, 2)))
+grad_ks_kernel(const PipeArgs p) {
+    constexpr int NWT = KSW * WG;                 // waves
+    constexpr int kThreads = 64 * NWT;
+    using G = Geo<64, 64, WG == 4 ? 2 : 1, WG == 4 ? 2 : 1>;
+    constexpr int kTile = G::kStageBytes;        // A (64 k x 64 m) + B (64 k x 64 n)
+    constexpr int kStage = KSW * kTile;
+    constexpr int kRuns = OperandLoads<64, true, NWT>::n;   // per operand per k-tile per thread
+    constexpr int kLoads = KSW * 2 * kRuns;                 // per thread per stage
+    static_assert(S >= 2 && S * kStage <= 160 * 1024 && kLoads * (S - 1) < 64, "grad_ks geometry");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStage];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave / WG, wig = wave % WG;
+    const int wm = WG == 4 ? wig >> 1 : 0, wn = WG == 4 ? wig & 1 : 0;
+    const int M = p.M, N = p.N;
+    const int kb = blockIdx.z * p.k_per_split;
+    const int ke = min(p.K, kb + p.k_per_split);
+    int z, tm, tn;
+    batch_tile_coords((M + 63) / 64, (N + 63) / 64, z, tm, tn);
+    const int m0 = tm * 64, n0 = tn * 64;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
+    const uint32_t base = lds_offset(lds);
+    const int nk = ke > kb ? (ke - kb + 63) / 64 : 0;
+    const int ng = (nk + KSW - 1) / KSW;
+    f32x16_t acc[G::MI][G::NJ];
+#pragma unroll
+    for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto issue = [&](int g, int stage) {
+#pragma unroll
+        for (int t = 0; t < KSW; ++t) {
+            const uint32_t dst = base + stage * kStage + t * kTile;
+            const int k0 = kb + (KSW * g + t) * 64;
+#pragma unroll
+            for (int j = 0; j < kRuns; ++j) {
+                dma_one<64, true, NWT>(j, dst, A, p.lda, m0, M, k0, ke, wave, lane);
+                dma_one<64, true, NWT>(j, dst + G::kABytes, B, p.ldb, n0, N, k0, ke, wave, lane);
+            }
+        }
+    };
+#pragma unroll
+    for (int g = 0; g < S - 1; ++g)
+        if (g < ng) issue(g, g);
+    int st = 0, st_load = S - 1;
+    for (int g = 0; g < ng; ++g) {
+        wait_tiles<kLoads, S>(min(ng, g + S - 1) - g - 1);
+        block_barrier();   // stage g landed everywhere; stage g - 1 is no longer read
+        if (g + S - 1 < ng) issue(g + S - 1, st_load);
+        const int kt = KSW * g + grp;
+        if (kt < nk) {
+            unsigned char* tile = lds + st * kStage + grp * kTile;
+            const int valid = ke - (kb + kt * 64);
+            if (valid < 64) {
+                // rows past K came from clamped rows: every wave of the group
+                // zeroes all of them itself (identical writes) before its own
+                // reads, so the group needs no barrier of its own
+                zero_rows_mn<64, 64>(tile, valid, lane);
+                zero_rows_mn<64, 64>(tile + G::kABytes, valid, lane);
+            }
+            uint4 af[2][G::MI], bfr[2][G::NJ];
+            load_frags<G, true, true>(tile, wm, wn, 0, lane, af[0], bfr[0]);
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const int cur = ks & 1;
+                if (ks + 1 < BK / 16) load_frags<G, true, true>(tile, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        st = st == S - 1 ? 0 : st + 1;
+        st_load = st_load == S - 1 ? 0 : st_load + 1;
+    }
+    // sum of the KSW partial tiles, then rows of 64 floats to C
+    block_barrier();   // every wave is done reading the operand stages
+    float* part = reinterpret_cast<float*>(lds);   // [KSW][64 rows][64 + 4]
+    constexpr int kLd = 68;
+    static_assert(KSW * 64 * kLd * 4 <= S * kStage, "partial tiles exceed the LDS ring");
+#pragma unroll
+    for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * G::WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int col = wn * G::WTN + j * 32 + (lane & 31);
+                part[(grp * 64 + row) * kLd + col] = acc[i][j][r];
+            }
+    __syncthreads();
+    float* C = reinterpret_cast<float*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
+#pragma unroll
+    for (int u0 = 0; u0 < 64 * 16; u0 += kThreads) {
+        const int u = u0 + tid;
+        if (u >= 64 * 16) break;
+        const int row = u >> 4, c4 = (u & 15) * 4;
+        float4 v = *reinterpret_cast<const float4*>(part + row * kLd + c4);
+#pragma unroll
+        for (int w = 1; w < KSW; ++w) {
+            const float4 x = *reinterpret_cast<const float4*>(part + (w * 64 + row) * kLd + c4);
+            v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+        }
+        const int gr = m0 + row, gc = n0 + c4;
+        if (gr >= M) continue;
+        float* dst = C + (int64_t)gr * p.ldc + gc;
+        if (gc + 3 < N && (p.ldc & 3) == 0) {
+            *reinterpret_cast<float4*>(dst) = v;
+        } else {
+            if (gc < N) dst[0] = v.x;
+            if (gc + 1 < N) dst[1] = v.y;
+            if (gc + 2 < N) dst[2] = v.z;
+            if (gc + 3 < N) dst[3] = v.w;
+        }
+    }
+}
+
+template <int KSW, int WG, int S>
+hipError_t launch_grad_ks(const PipeArgs& p, hipStream_t stream) {
+    const int tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
+    constexpr int kMaxY = 65535;
+    for (int y0 = 0; y0 < p.batch; y0 += kMaxY) {
+        PipeArgs q = p;
+        q.batch = min(kMaxY, p.batch - y0);
+        q.A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)y0 * p.strideA;
+        q.B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)y0 * p.strideB;
+        q.C = reinterpret_cast<float*>(p.C) + (int64_t)y0 * p.strideC;
+        hipLaunchKernelGGL((grad_ks_kernel<KSW, WG, S>), dim3(tiles, q.batch, p.splits), dim3(64 * KSW * WG), 0,
+                           stream, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // A zero the compiler cannot see through: offsets built on it are recomputed
 // where they are used instead of being hoisted and kept live in registers.
 __device__ __forceinline__ int opaque_zero() {
@@ -929,7 +1079,12 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     }
     if (a_mn && b_mn && out_f32) {
         if (tile == PipeTile::Square) return launch<128, 128, true, true, true, kEpiPlain, 4>(p, stream);
-        if (tile == PipeTile::Small) return launch<64, 64, true, true, true, kEpiPlain, 4>(p, stream);
+        // 64 x 64 block-gradient tiles: two k-tiles per stage, one per group of
+        // four waves, for token runs up to 4096; longer runs stream better with
+        // one k-tile per stage and a four-stage ring
+        if (tile == PipeTile::Small)
+            return p.k_per_split <= 4096 ? launch_grad_ks<2, 4, 2>(p, stream)
+                                         : launch<64, 64, true, true, true, kEpiPlain, 4>(p, stream);
         return launch<256, 128, true, true, true, kEpiPlain, 3, 4, 2>(p, stream);
     }
     return hipErrorInvalidValue;
