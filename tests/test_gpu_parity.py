@@ -115,6 +115,8 @@ CNP_CASES = [
     (256, 3, "bf16", 1e-2, 0.7),
     (128, 3, "bf16", 0.05, None),
     (128, 2, "bf16", 1e-2, 0.5),
+    (64, 3, "bf16", 0.05, None),
+    (512, 3, "bf16", 1e-2, 0.5),
     (512, 4, "bf16", 1e-2, 0.5),
     (512, 4, "f32", 1e-2, 0.5),
 ]
