@@ -18,8 +18,10 @@ stream the library launches on (torch's current stream).
 Prints ONE JSON line.  Besides the step throughput it reports the time of every
 stage (each stage re-run alone through the C ABI with the same launch
 configuration), the aggregate MFMA efficiency of the block and dense GEMMs,
-the roofline of the dominant kernel (the dense Wt GEMM) and the float64 oracle
-timed on the host cores as a baseline.
+the roofline of the dominant kernel (the dense Wt GEMM), the float64 oracle
+timed on the host cores as a baseline, and, as context outside the timed step,
+the vendor library (torch.matmul, i.e. hipBLASLt) on the same dense shapes and a
+plain device copy (`vendor_reference`).
 
   --pmc-dir DIR   parse a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run of this
                   script and record the dense GEMM's HBM traffic in
@@ -284,6 +286,38 @@ def _time_steps(step, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def vendor_reference(spec, S, cs, cd, reps=20):
+    """Context, not the product path: the vendor library (torch.matmul -> hipBLASLt)
+    on the same dense shapes and weight, and a plain device copy of known size."""
+    import torch
+    import torch.nn.functional as F
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    a = torch.randn(spec.T, spec.n, device="cuda", generator=g).to(torch.bfloat16)
+    d = torch.randn(spec.T, spec.m, device="cuda", generator=g).to(torch.bfloat16)
+    Wt = S["Wt"]
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    nt = timed(lambda: F.linear(a, Wt))          # a Wt^T, as the dense forward
+    nn = timed(lambda: torch.matmul(d, Wt))      # d Wt, as the dense backward
+    cp = timed(lambda: cd.copy_(cs))
+    flops = 2.0 * spec.T * spec.m * spec.n
+    return {"hipblaslt_dense_nt_us": round(nt, 2), "hipblaslt_dense_nt_tflops": round(flops / nt / 1e6, 1),
+            "hipblaslt_dense_nn_us": round(nn, 2), "hipblaslt_dense_nn_tflops": round(flops / nn / 1e6, 1),
+            "copy_bytes": 2 * COPY_BYTES, "copy_gbs": round(2 * COPY_BYTES / cp / 1e3, 1)}
+
+
 def _base_line(args, value, unit, ms, workload, T):
     return {"metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -337,6 +371,7 @@ def run_linear(args, spec, label):
         "stages": st,
         "roofline": roof,
     })
+    out["vendor_reference"] = vendor_reference(spec, S, cs, cd)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp)
     return out
