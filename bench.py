@@ -186,6 +186,15 @@ def stage_timings(spec, S, reps):
     ]
     if spec.variant == "mem":   # recomputed in the backward, same kernels
         stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages if nm in ("blk_fwd_P", "dense_fwd")]
+    # the standalone skew unpack (to bf16) and pack of the same blocks; not part of the
+    # step (the fused forward unpacks on chip, the backward's pack is inside cnp_bwd)
+    ntri = b * (b - 1) // 2
+    Qb = torch.empty((nblk, b, b), dtype=bf, device="cuda")
+    dQ = torch.zeros((nblk, b, b), dtype=torch.float32, device="cuda")
+    stages += [
+        ("aux_skew_unpack", lambda: B.poetx_skew_unpack(S["q"], Qb, nblk, b), 0, 4 * nblk * ntri + 2 * nblk * b * b),
+        ("aux_skew_pack", lambda: B.poetx_skew_pack(dQ, S["dq"], nblk, b), 0, 4 * nblk * b * b + 4 * nblk * ntri),
+    ]
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
         tf = flops / us / 1e6 if flops else None
