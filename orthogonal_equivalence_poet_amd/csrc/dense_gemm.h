@@ -51,7 +51,7 @@ struct PipeArgs {
 // splitting the token axis).  Instantiated: k-major A with bf16 output (Tall,
 // Wide) and m/n-major A and B with float32 output (Tall, Square, Small); Big
 // 256 x 256 (dense products with at least 256 such tiles) for k-major A.
-enum class PipeTile { Tall, Wide, Square, Small, Big };
+enum class PipeTile { Tall, Wide, Square, Small, Big, Slim };
 bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                          int64_t strideA, int64_t strideB);
 hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile);

@@ -1068,6 +1068,12 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     // instantiated combinations: dense / block products (k-major A, bf16 out) and
     // block gradients (m/n-major A and B, float32 out)
     if (!a_mn && !out_f32) {
+        if (tile == PipeTile::Square)
+            return b_mn ? launch<128, 128, false, true, false, kEpiPlain, 4>(p, stream)
+                        : launch<128, 128, false, false, false, kEpiPlain, 4>(p, stream);
+        if (tile == PipeTile::Slim)
+            return b_mn ? launch<64, 128, false, true, false, kEpiPlain, 4>(p, stream)
+                        : launch<64, 128, false, false, false, kEpiPlain, 4>(p, stream);
         if (tile == PipeTile::Big)
             return b_mn ? launch<256, 256, false, true, false, kEpiPlain, 2, 2, 4>(p, stream)
                         : launch<256, 256, false, false, false, kEpiPlain, 2, 2, 4>(p, stream);
@@ -1136,7 +1142,7 @@ hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hip
 }
 
 int pipe_tile_rows(PipeTile t) {
-    return (t == PipeTile::Tall || t == PipeTile::Big) ? 256 : t == PipeTile::Small ? 64 : 128;
+    return (t == PipeTile::Tall || t == PipeTile::Big) ? 256 : (t == PipeTile::Small || t == PipeTile::Slim) ? 64 : 128;
 }
 int pipe_tile_cols(PipeTile t) {
     return (t == PipeTile::Wide || t == PipeTile::Big) ? 256 : t == PipeTile::Small ? 64 : 128;
@@ -1154,9 +1160,14 @@ hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B,
     p.C = C; p.ldc = ldc;
     p.M = M; p.N = N; p.K = K;
     p.k_per_split = K;
-    // 256 x 256 tiles (two-stage ring, two waves per SIMD) once they alone fill the chip
-    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    return pipe_gemm(false, b_nn, false, p, stream, big_tiles >= 256 ? PipeTile::Big : PipeTile::Tall);
+    // the largest tile whose grid still gives every CU a workgroup: 256 x 256
+    // (two-stage ring, two waves per SIMD), 256 x 128, 128 x 128, else 64 x 128
+    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const PipeTile t = tiles(256, 256) >= 256   ? PipeTile::Big
+                       : tiles(256, 128) >= 256 ? PipeTile::Tall
+                       : tiles(128, 128) >= 256 ? PipeTile::Square
+                                                : PipeTile::Slim;
+    return pipe_gemm(false, b_nn, false, p, stream, t);
 }
 
 bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }
