@@ -484,7 +484,11 @@ hipError_t block_apply(GemmLayout layout, bool bf16, int64_t T, int64_t d, int64
         p.M = (int)T; p.N = (int)b; p.K = (int)b;
         p.batch = (int)(d / b);
         p.k_per_split = (int)b;
-        return pipe_gemm(false, nn, false, p, s, b >= 256 ? PipeTile::Wide : PipeTile::Tall);
+        // 128 x 256 tiles for b >= 256 unless a few blocks leave CUs without a
+        // workgroup; then 64 x 128 (four times the workgroups)
+        PipeTile t = b >= 256 ? PipeTile::Wide : PipeTile::Tall;
+        if (t == PipeTile::Wide && ((T + 127) / 128) * ((b + 255) / 256) * (d / b) < 256) t = PipeTile::Slim;
+        return pipe_gemm(false, nn, false, p, s, t);
     }
     return gemm(layout, bf16, bf16, T, b, b, d / b, Mat{in, d, b}, Mat{G, b, b * b}, out, d, b, s);
 }

@@ -341,8 +341,11 @@ GEMM_CASES = [
     # layout, dense, M, N, K, dtype
     ("NT", True, 2048, 4096, 4096, "bf16"),
     ("NN", True, 2048, 4096, 4096, "bf16"),
-    ("NT", True, 300, 1024, 512, "bf16"),     # ragged M, several tiles
-    ("NN", True, 77, 136, 320, "bf16"),       # ragged M and N
+    ("NT", True, 300, 1024, 512, "bf16"),     # ragged M, several tiles (64 x 128 tiles)
+    ("NN", True, 77, 136, 320, "bf16"),       # ragged M and N (64 x 128 tiles)
+    ("NT", True, 2048, 1024, 4096, "bf16"),   # k/v-shaped: 64 x 128 tiles fill the chip
+    ("NT", True, 2048, 2048, 1024, "bf16"),   # 128 x 128 tiles
+    ("NN", True, 2000, 2048, 512, "bf16"),    # 128 x 128 tiles, ragged M
     ("NT", False, 333, 256, 256, "bf16"),
     ("NN", False, 333, 256, 256, "bf16"),
     ("TN", False, 256, 256, 999, "bf16"),     # ragged K (token axis)
@@ -385,8 +388,8 @@ def test_block_grad_parity(T, d, b, dtype):
         assert rel_fro(host(dG), ref) <= (1e-5 if dtype == "f32" else 1e-5)
 
 
-@pytest.mark.parametrize("T,d,b,dtype", [(2048, 4096, 256, "bf16"), (300, 1024, 512, "bf16"), (77, 192, 64, "bf16"),
-                                         (33, 96, 32, "f32"), (129, 128, 16, "bf16")])
+@pytest.mark.parametrize("T,d,b,dtype", [(2048, 4096, 256, "bf16"), (2048, 1024, 256, "bf16"), (300, 1024, 512, "bf16"),
+                                         (77, 192, 64, "bf16"), (33, 96, 32, "f32"), (129, 128, 16, "bf16")])
 @pytest.mark.parametrize("transpose", [True, False])
 def test_block_apply_parity(T, d, b, dtype, transpose):
     X = I.gaussian((T, d), 1.0, dtype, 404, T, d)
