@@ -31,7 +31,8 @@ plain device copy (`vendor_reference`).
                   the metric is quoted on): up_proj / up_proj_mem (Llama-8B
                   MLP up_proj shape, b=512, k=4, 4096 tokens), llama8b_layer
                   and llama13b_layer (all 7 linears of a decoder layer, mem
-                  variant; the 8B line also times poetx_merge), cnp_13b (one
+                  variant, one Cayley-Neumann forward and backward over all
+                  the layer's blocks; the 8B line also times poetx_merge), cnp_13b (one
                   Cayley-Neumann forward + backward over the 15280 b=256
                   blocks of 40 Llama-13B layers).
 """
@@ -393,11 +394,34 @@ def run_layer(args, specs, label, merge):
     from orthogonal_equivalence_poet_amd import binding as B
     from orthogonal_equivalence_poet_amd import inputs as I
     states = [build_state(sp)[0] for sp in specs]
-    steps = [make_step(sp, S) for sp, S in zip(specs, states)]
+    # one Cayley-Neumann batch for the whole layer (every linear has b = 256 and
+    # the same k): flat q, G, dG, dq; each linear's tensors are views into them
+    b, k = specs[0].b, specs[0].k
+    assert all(sp.b == b and sp.k == k for sp in specs)
+    nbs = [sp.nblk_R + sp.nblk_P for sp in specs]
+    nall = sum(nbs)
+    q_all = torch.cat([S["q"] for S in states]).contiguous()
+    G_all = torch.empty((nall, b, b), dtype=torch.bfloat16, device="cuda")
+    dG_all = torch.empty((nall, b, b), dtype=torch.float32, device="cuda")
+    dq_all = torch.empty_like(q_all)
+    o = 0
+    for sp, S, nb in zip(specs, states, nbs):
+        S["q"], S["G"], S["dG"], S["dq"] = q_all[o:o + nb], G_all[o:o + nb], dG_all[o:o + nb], dq_all[o:o + nb]
+        S["G_R"], S["G_P"] = S["G"][:sp.nblk_R], S["G"][sp.nblk_R:]
+        S["dG_R"], S["dG_P"] = S["dG"][:sp.nblk_R], S["dG"][sp.nblk_R:]
+        o += nb
+    cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nall, b, k, B.POETX_BF16))
+    cnp_ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(nall, b, k, B.POETX_BF16))
 
     def step():
-        for f in steps:
-            f()
+        B.poetx_cnp_fwd_save(q_all, nall, b, k, G_all, cnp_saved, cnp_ws)
+        for S in states:
+            B.poetx_linear_fwd(S["desc"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], S["y"],
+                               S["saved"], S["ws"])
+        for S in reversed(states):
+            B.poetx_linear_bwd(S["desc"], S["dy"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"],
+                               S["saved"], S["dx"], S["dG_R"], S["dG_P"], S["ws"])
+        B.poetx_cnp_bwd_saved(q_all, dG_all, nall, b, k, dq_all, B.POETX_BF16, cnp_saved, cnp_ws)
     ms = _time_steps(step, args.steps, args.warmup)
     T = specs[0].T
     g_flops = 0
@@ -407,8 +431,8 @@ def run_layer(args, specs, label, merge):
         g_flops += fwd + bwd
     out = _base_line(args, T / (ms / 1e3), "tokens/s", ms,
                      f"{label}: all 7 linears of one decoder layer, b=256, k=3, mem variant, "
-                     f"{T // 2048} x 2048 tokens; step = per linear cnp_fwd_save + linear_fwd + linear_bwd + "
-                     "cnp_bwd_saved", T)
+                     f"{T // 2048} x 2048 tokens; step = cnp_fwd_save over the layer's {nall} blocks + 7 x "
+                     "linear_fwd + 7 x linear_bwd + cnp_bwd_saved over the same blocks", T)
     out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
     out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
