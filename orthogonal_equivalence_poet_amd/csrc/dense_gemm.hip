@@ -1,29 +1,29 @@
-// Pipelined bf16 MFMA GEMM (float32 accumulation) for the large products of the
+// Pipelined bf16 MFMA GEMM (float32 accumulation) for the products of the
 // POET-X chain (the input-centric, matrix-free reformulation of the review's
 // Summary keeps W0 frozen and never materialises R W0 P):
 //   dense   h2  = h1 . Wt^T  (A k-major, B k-major)   dh1 = dh2 . Wt (B n-major)
 //   blocks  h1_j = a_j . G_j^T, dh2_j = dz_j . G_j     (batched over blocks j)
 //   grads   dG_j = dz_j^T h2_j                          (A and B m/n-major, K = tokens,
-//                                                        split along K, float32 out)
-//
+//                                                        float32 out)
 //   small   the Cayley-Neumann b x b products (batched over blocks, general
-//           epilogue with float32 addends and several outputs)
+//           epilogue with float32 addends and several outputs; paired products)
+// plus the fused Cayley-Neumann forward and the split-K block-gradient kernel.
 //
-// Workgroup tile BM x BN x 64 (256 x 128 for the dense products, 256 x 256 once
-// there are enough of those to fill the chip, 128 x 256 for
-// the block products, 128 x 128 for the block gradients, 64 x 64 or 128 x 128
-// for the small products), four waves in a 2 x 2 grid, each wave owning a
-// (BM/2) x (BN/2) sub-tile of v_mfma_f32_32x32x16_bf16 tiles (float32
-// accumulators in AGPRs).
+// Workgroup tiles BM x BN x 64 with v_mfma_f32_32x32x16_bf16 (float32
+// accumulators): dense products take the largest of 256 x 256, 256 x 128,
+// 128 x 128 and 64 x 128 whose grid still gives every CU a workgroup (the
+// large ones with eight waves of 64 x 64 or 128 x 64); block products 128 x 256
+// (64 x 128 for a few blocks); the small products 64 x 64 with four waves.
 //
 // Operand tiles travel global -> LDS by direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so no
 // VGPRs stage them and no ds_write is issued.  S LDS stages form a ring (S = 3
-// for the large tiles, 4 for the 128 x 128 and 64 x 64 ones): while the MFMAs
-// consume stage kt % S, the loads of tiles kt+1 .. kt+S-1 are in flight, so a
-// short product (K = 256) waits for memory once.  The loads are issued from inline asm so that the compiler does not
-// add a conservative vmcnt(0) before every LDS read; the kernel itself waits
-// (s_waitcnt vmcnt) for exactly the tile it is about to read, then barriers.
+// for 256 x 128 and 128 x 256, 2 for 256 x 256, 4 for the smaller tiles):
+// while the MFMAs consume stage kt % S, the loads of tiles kt+1 .. kt+S-1 are
+// in flight, so a short product (K = 256) waits for memory once.  The loads
+// are issued from inline asm so that the compiler does not add a conservative
+// vmcnt(0) before every LDS read; the kernel itself waits (s_waitcnt vmcnt)
+// for exactly the tile it is about to read, then barriers.
 //
 // LDS layouts (XOR-swizzled instead of padded, because a DMA writes whole
 // 1 KB runs):
@@ -31,7 +31,8 @@
 //     of row r sits in slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), which
 //     keeps the ds_read_b128 fragment reads free of bank conflicts;
 //   m/n-major tile [64 k][rows], 256- or 512-byte rows: chunk c of k-row k sits
-//     in slot c ^ 4 (k & 3) (128-byte rows: c ^ 4 ((k >> 1) & 1)); fragments are read with ds_read_b64_tr_b16, which
+//     in slot c ^ 4 (k & 3) (128-byte rows: c ^ 4 ((k >> 1) & 1)); fragments
+//     are read with ds_read_b64_tr_b16, which
 //     transposes 16-lane groups so that lane i receives four consecutive k of
 //     column i; the swizzle spreads the four k-rows x four chunks that 32 lanes
 //     touch over all 64 banks.
@@ -1115,12 +1116,9 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
                 al(p.Cin1, p.ldcin1, p.strideCin1) && al(p.Cin2, p.ldcin2, p.strideCin2);
     if (a_mn && !b_mn) return hipErrorInvalidValue;
     if (p.splits != 1) return hipErrorInvalidValue;
-    // 128 x 128 tiles only when they alone give about four workgroups per CU
-    const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-    if (big >= 1024) {
-        return out_f32 ? launch_general<128, true>(a_mn, b_mn, p, stream)
-                       : launch_general<128, false>(a_mn, b_mn, p, stream);
-    }
+    // 64 x 64 tiles: measured ahead of 128 x 128 ones for b = 256 and 512 from
+    // 32 to 320 blocks (the K = b products are short; more workgroups overlap
+    // their epilogues)
     return out_f32 ? launch_general<64, true>(a_mn, b_mn, p, stream) : launch_general<64, false>(a_mn, b_mn, p, stream);
 }
 
