@@ -43,6 +43,7 @@ __all__ = [
     "forward", "forward_from_blocks", "backward", "backward_from_blocks",
     "cnp_vjp", "merge", "effective_weight",
     "input_grad", "block_grad_entries", "block_grad_blocks", "merge_entries",
+    "adamw_step", "train_steps",
 ]
 
 
@@ -362,3 +363,59 @@ def merge_entries(Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_new, pi_P_new, entries)
         a, e = pi_R_new[i], pi_P_new[j]
         out[t] = R[a, :] @ W0 @ P[:, e]
     return out
+
+
+# ------------------------------------------------------------ training step
+# The step on either side of the layer: an optimizer update of the compact
+# parameters, and merge-then-reinitialize on a fixed schedule.  The pages fix
+# two numbers and no formula: the POET learning-rate scaling gamma = 0.5 and
+# the POET reset gap of 400 steps (SAI replication review, Weaknesses, the
+# single-run 8B/13B remark; the "Cayley approximation" remark ties gamma = 0.5
+# to R - I ~ 2Q: a step in q moves R about twice as far).  The baseline
+# optimizer throughout is AdamW.  Readings taken: q is updated by AdamW at the
+# rate lr * gamma; weight decay is decoupled and 0 by default (decay on q would
+# pull R towards I, not W towards 0); a merge (every reset gap updates) also
+# zeroes the moments and restarts the bias-correction count, since q itself
+# restarts from 0 in a new basis.
+def adamw_step(q, g, m, v, t: int, lr: float, gamma: float = 0.5, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8, weight_decay: float = 0.0):
+    """One AdamW update (Loshchilov and Hutter, "Decoupled Weight Decay
+    Regularization", 2019, with the bias-corrected moment estimates of Kingma
+    and Ba, "Adam", 2015) at the learning rate lr * gamma.  t >= 1 counts the
+    updates since the moments were last reset.  Returns (q', m', v')."""
+    q, g, m, v = (np.asarray(a, dtype=np.float64) for a in (q, g, m, v))
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** t)
+    v_hat = v / (1.0 - beta2 ** t)
+    eta = lr * gamma
+    q = q - eta * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * q)
+    return q, m, v
+
+
+def train_steps(xs, dys, W0, q_R, q_P, pi_R, pi_P, b: int, k: int, opt: dict, merge_every: int, new_perms):
+    """Training steps of one layer for L_s = <dY_s, Y_s>: backward to dq,
+    AdamW on (q_R, q_P), and after every `merge_every` updates a merge with the
+    next permutation pair from `new_perms` (an iterator of (pi_R', pi_P'))
+    followed by a reset of q, the moments and the count.  Returns
+    (Wt, q_R, q_P, pi_R, pi_P) after the last step, Wt in the stored
+    (pre-permuted) form."""
+    Wt = prepermute(W0, pi_R, pi_P)
+    q_R = np.asarray(q_R, dtype=np.float64)
+    q_P = np.asarray(q_P, dtype=np.float64)
+    mR, vR = np.zeros_like(q_R), np.zeros_like(q_R)
+    mP, vP = np.zeros_like(q_P), np.zeros_like(q_P)
+    t = 0
+    for x, dy in zip(xs, dys):
+        W0_cur = gather_matrix(pi_R).T @ Wt @ gather_matrix(pi_P)
+        _, dq_R, dq_P, _, _ = backward(dy, x, W0_cur, q_R, q_P, pi_R, pi_P, b, k)
+        t += 1
+        q_R, mR, vR = adamw_step(q_R, dq_R, mR, vR, t, **opt)
+        q_P, mP, vP = adamw_step(q_P, dq_P, mP, vP, t, **opt)
+        if t == merge_every:
+            pi_R_new, pi_P_new = next(new_perms)
+            Wt, q_R, q_P = merge(Wt, q_R, q_P, pi_R, pi_P, pi_R_new, pi_P_new, b, k)
+            pi_R, pi_P = pi_R_new, pi_P_new
+            mR, vR, mP, vP = (np.zeros_like(a) for a in (mR, vR, mP, vP))
+            t = 0
+    return Wt, q_R, q_P, pi_R, pi_P

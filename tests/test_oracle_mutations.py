@@ -57,6 +57,40 @@ def _merge_entries_old_perms(Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_new, pi_P_ne
     return O.__dict__["_orig_merge_e"](Wt, G_R, G_P, pi_R_old, pi_P_old, pi_R_old, pi_P_new, entries)
 
 
+def _adamw_no_bias_correction(q, g, m, v, t, **opt):
+    # bias correction forgotten: the count is frozen at a value where it vanishes
+    return O.__dict__["_orig_adamw"](q, g, m, v, 10 ** 6, **opt)
+
+
+def _adamw_unscaled_rate(q, g, m, v, t, **opt):
+    return O.__dict__["_orig_adamw"](q, g, m, v, t, **dict(opt, gamma=1.0))
+
+
+def _adamw_ascent(q, g, m, v, t, **opt):
+    q1, m1, v1 = O.__dict__["_orig_adamw"](q, g, m, v, t, **opt)
+    return 2 * np.asarray(q, float) - q1, m1, v1
+
+
+def _train_without_reset(xs, dys, W0, q_R, q_P, pi_R, pi_P, b, k, opt, merge_every, new_perms):
+    # the moments and the count run on through the merge
+    Wt = O.prepermute(W0, pi_R, pi_P)
+    mR = vR = np.zeros_like(q_R)
+    mP = vP = np.zeros_like(q_P)
+    t = seg = 0
+    for x, dy in zip(xs, dys):
+        W0_cur = O.gather_matrix(pi_R).T @ Wt @ O.gather_matrix(pi_P)
+        _, dq_R, dq_P, _, _ = O.backward(dy, x, W0_cur, q_R, q_P, pi_R, pi_P, b, k)
+        t += 1
+        seg += 1
+        q_R, mR, vR = O.adamw_step(q_R, dq_R, mR, vR, t, **opt)
+        q_P, mP, vP = O.adamw_step(q_P, dq_P, mP, vP, t, **opt)
+        if seg == merge_every:
+            pi_R2, pi_P2 = next(new_perms)
+            Wt, q_R, q_P = O.merge(Wt, q_R, q_P, pi_R, pi_P, pi_R2, pi_P2, b, k)
+            pi_R, pi_P, seg = pi_R2, pi_P2, 0
+    return Wt, q_R, q_P, pi_R, pi_P
+
+
 MUTATIONS = [
     ("params_grad_from_skew_grad", _pack_sign_flip, "_orig_pack",
      [P.test_skew_exact_and_pack_adjoint]),
@@ -80,10 +114,18 @@ MUTATIONS = [
      [P.test_sampled_input_grad_rows_brute_force]),
     ("merge_entries", _merge_entries_old_perms, "_orig_merge_e",
      [P.test_merge_entries_match_merged_function]),
+    ("adamw_step", _adamw_no_bias_correction, "_orig_adamw",
+     [P.test_adamw_constant_gradient_closed_form, P.test_adamw_matches_library_optimizer]),
+    ("adamw_step", _adamw_unscaled_rate, "_orig_adamw",
+     [P.test_adamw_constant_gradient_closed_form, P.test_train_step_decreases_the_loss_to_first_order]),
+    ("adamw_step", _adamw_ascent, "_orig_adamw",
+     [P.test_adamw_matches_library_optimizer, P.test_train_step_decreases_the_loss_to_first_order]),
+    ("train_steps", _train_without_reset, None,
+     [P.test_train_after_merge_starts_afresh]),
 ]
 
 
-@pytest.mark.parametrize("name,mutant,orig_key,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+@pytest.mark.parametrize("name,mutant,orig_key,pins", MUTATIONS, ids=[f"{m[0]}-{m[1].__name__}" for m in MUTATIONS])
 def test_pin_catches_mutation(monkeypatch, name, mutant, orig_key, pins):
     if orig_key:
         monkeypatch.setitem(O.__dict__, orig_key, getattr(O, name))

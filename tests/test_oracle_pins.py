@@ -391,3 +391,123 @@ def test_merge_entries_match_merged_function():
     W_new[np.ix_(pi_R2, pi_P2)] = Wt2
     y_before = O.forward(x, W0, q_R, q_P, pi_R, pi_P, b, k)
     assert np.allclose(x @ W_new.T, y_before, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------ training step
+# AdamW (Loshchilov and Hutter 2019; Adam's bias correction, Kingma and Ba 2015)
+# at the rate lr * gamma, gamma = 0.5 being the POET learning-rate scaling
+# (SAI replication review, Weaknesses, single-run 8B/13B remark).
+_OPT = dict(lr=3e-3, gamma=0.5, beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def test_adamw_constant_gradient_closed_form():
+    # With a constant gradient the bias-corrected moments are g and g^2 at every
+    # step, so each update is exactly lr gamma g / (|g| + eps).
+    rng = np.random.default_rng(31)
+    g = rng.standard_normal(50) * np.logspace(-4, 2, 50)
+    q0 = rng.standard_normal(50)
+    q, m, v = q0.copy(), np.zeros(50), np.zeros(50)
+    for t in range(1, 8):
+        q, m, v = O.adamw_step(q, g, m, v, t, **_OPT)
+        want = q0 - t * _OPT["lr"] * _OPT["gamma"] * g / (np.abs(g) + _OPT["eps"])
+        assert np.allclose(q, want, rtol=0, atol=1e-13)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    # No gradient: the moments stay 0 and decoupled decay shrinks q
+    # geometrically by (1 - lr gamma wd) per step.
+    q0 = np.linspace(-2, 3, 11)
+    q, m, v = q0.copy(), np.zeros(11), np.zeros(11)
+    for t in range(1, 6):
+        q, m, v = O.adamw_step(q, np.zeros(11), m, v, t, **_OPT, weight_decay=0.1)
+    assert np.allclose(q, q0 * (1 - _OPT["lr"] * _OPT["gamma"] * 0.1) ** 5, rtol=1e-15, atol=0)
+    assert not m.any() and not v.any()
+
+
+def test_adamw_matches_library_optimizer():
+    # torch.optim.AdamW in float64 on the CPU, at the scaled rate, over a random
+    # gradient sequence with weight decay.
+    import torch
+    rng = np.random.default_rng(32)
+    n, steps, wd = 40, 9, 0.05
+    grads = rng.standard_normal((steps, n)) * rng.uniform(1e-3, 10, n)
+    q0 = rng.standard_normal(n)
+    p = torch.tensor(q0.copy(), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=_OPT["lr"] * _OPT["gamma"], betas=(_OPT["beta1"], _OPT["beta2"]),
+                            eps=_OPT["eps"], weight_decay=wd)
+    q, m, v = q0.copy(), np.zeros(n), np.zeros(n)
+    for t in range(1, steps + 1):
+        p.grad = torch.tensor(grads[t - 1], dtype=torch.float64)
+        opt.step()
+        q, m, v = O.adamw_step(q, grads[t - 1], m, v, t, **_OPT, weight_decay=wd)
+    assert np.allclose(q, p.detach().numpy(), rtol=0, atol=1e-14)
+
+
+def test_adamw_is_invariant_to_gradient_scale():
+    rng = np.random.default_rng(33)
+    grads = rng.standard_normal((6, 30))
+    opt = dict(_OPT, eps=0.0)
+    a = b = (rng.standard_normal(30), np.zeros(30), np.zeros(30))
+    for t in range(1, 7):
+        a = O.adamw_step(*a[:1], grads[t - 1], *a[1:], t, **opt)
+        b = O.adamw_step(*b[:1], 1e3 * grads[t - 1], *b[1:], t, **opt)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-13)
+
+
+def _train_case(rng, steps, m=12, n=8, b=4, T=5):
+    W0, q_R, q_P, _, _, pi_R, pi_P = _layer(rng, m, n, b, T)
+    xs = rng.standard_normal((steps, T, n))
+    dys = rng.standard_normal((steps, T, m))
+    perms = [(rng.permutation(m), rng.permutation(n)) for _ in range(4)]
+    return W0, q_R, q_P, pi_R, pi_P, xs, dys, perms
+
+
+def test_train_step_decreases_the_loss_to_first_order():
+    # One step at a tiny rate changes L = <dY, Y> by <dq, delta q> to first
+    # order: the update goes against the gradient of L with respect to q, at the
+    # scaled rate.
+    rng = np.random.default_rng(34)
+    b, k = 4, 3
+    W0, q_R, q_P, pi_R, pi_P, xs, dys, _ = _train_case(rng, 1)
+    opt = dict(_OPT, lr=1e-7)
+    _, q_R1, q_P1, _, _ = O.train_steps(xs, dys, W0, q_R, q_P, pi_R, pi_P, b, k, opt, 400, iter(()))
+    L = lambda qr, qp: np.sum(dys[0] * O.forward(xs[0], W0, qr, qp, pi_R, pi_P, b, k))
+    _, dq_R, dq_P, _, _ = O.backward(dys[0], xs[0], W0, q_R, q_P, pi_R, pi_P, b, k)
+    eta = opt["lr"] * opt["gamma"]
+    want = -eta * (np.sum(dq_R ** 2 / (np.abs(dq_R) + opt["eps"])) + np.sum(dq_P ** 2 / (np.abs(dq_P) + opt["eps"])))
+    got = L(q_R1, q_P1) - L(q_R, q_P)
+    assert want < 0 and abs(got - want) < 1e-4 * abs(want)
+
+
+def test_train_merge_keeps_the_function():
+    # At the merge step the layer's function is the one the last update left:
+    # the merged weight with q = 0 and the new permutations computes what the
+    # unmerged weight with the updated q computes.
+    rng = np.random.default_rng(35)
+    b, k, M = 4, 3, 3
+    W0, q_R, q_P, pi_R, pi_P, xs, dys, perms = _train_case(rng, M)
+    Wt_a, qR_a, qP_a, piR_a, piP_a = O.train_steps(xs, dys, W0, q_R, q_P, pi_R, pi_P, b, k, _OPT, M + 1, iter(()))
+    Wt_b, qR_b, qP_b, piR_b, piP_b = O.train_steps(xs, dys, W0, q_R, q_P, pi_R, pi_P, b, k, _OPT, M, iter(perms))
+    assert not qR_b.any() and not qP_b.any()
+    assert np.array_equal(piR_b, perms[0][0]) and np.array_equal(piP_b, perms[0][1])
+    assert np.array_equal(piR_a, pi_R) and not np.allclose(qR_a, q_R)
+    x = rng.standard_normal((7, W0.shape[1]))
+    W0_a = Wt_a[np.argsort(piR_a)][:, np.argsort(piP_a)]
+    W0_b = Wt_b[np.argsort(piR_b)][:, np.argsort(piP_b)]
+    assert np.allclose(O.forward(x, W0_a, qR_a, qP_a, piR_a, piP_a, b, k), x @ W0_b.T, rtol=0, atol=1e-12)
+
+
+def test_train_after_merge_starts_afresh():
+    # After a merge nothing of the previous segment survives but the weight: two
+    # segments of M steps equal one segment of M steps followed by a new run of
+    # M steps from the merged state (moments and count reset with q).
+    rng = np.random.default_rng(36)
+    b, k, M = 4, 3, 3
+    W0, q_R, q_P, pi_R, pi_P, xs, dys, perms = _train_case(rng, 2 * M)
+    full = O.train_steps(xs, dys, W0, q_R, q_P, pi_R, pi_P, b, k, _OPT, M, iter(perms))
+    Wt1, qR1, qP1, piR1, piP1 = O.train_steps(xs[:M], dys[:M], W0, q_R, q_P, pi_R, pi_P, b, k, _OPT, M,
+                                              iter(perms[:1]))
+    W0_1 = Wt1[np.argsort(piR1)][:, np.argsort(piP1)]
+    second = O.train_steps(xs[M:], dys[M:], W0_1, qR1, qP1, piR1, piP1, b, k, _OPT, M, iter(perms[1:]))
+    for a, c in zip(full, second):
+        assert np.allclose(a, c, rtol=0, atol=1e-12)
