@@ -32,7 +32,9 @@ plain device copy (`vendor_reference`).
                   MLP up_proj shape, b=512, k=4, 4096 tokens), llama8b_layer
                   and llama13b_layer (all 7 linears of a decoder layer, mem
                   variant, one Cayley-Neumann forward and backward over all
-                  the layer's blocks; the 8B line also times poetx_merge), cnp_13b (one
+                  the layer's blocks; both also time the AdamW update of all
+                  the layer's q and the step with it, and the 8B line times
+                  poetx_merge and the step with a merge every 400), cnp_13b (one
                   Cayley-Neumann forward + backward over the 15280 b=256
                   blocks of 40 Llama-13B layers).
 """
@@ -192,9 +194,15 @@ def stage_timings(spec, S, reps):
     ntri = b * (b - 1) // 2
     Qb = torch.empty((nblk, b, b), dtype=bf, device="cuda")
     dQ = torch.zeros((nblk, b, b), dtype=torch.float32, device="cuda")
+    # the optimizer update of the same parameters (outside the step): AdamW at the
+    # POET-scaled rate on a copy of q, reading q, dq, m, v and writing q, m, v
+    q_opt, m_opt, v_opt = S["q"].clone(), torch.zeros_like(S["q"]), torch.zeros_like(S["q"])
+    opt_p = B.adamw_params(1e-6)
     stages += [
         ("aux_skew_unpack", lambda: B.poetx_skew_unpack(S["q"], Qb, nblk, b), 0, 4 * nblk * ntri + 2 * nblk * b * b),
         ("aux_skew_pack", lambda: B.poetx_skew_pack(dQ, S["dq"], nblk, b), 0, 4 * nblk * b * b + 4 * nblk * ntri),
+        ("aux_adamw", lambda: B.poetx_adamw_step(q_opt, S["dq"], m_opt, v_opt, nblk * ntri, 1, opt_p), 0,
+         28 * nblk * ntri),
     ]
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
@@ -436,6 +444,19 @@ def run_layer(args, specs, label, merge):
     out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
     out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
+    # training-step closure: the AdamW update of every q of the layer in one call,
+    # and the merge + optimizer reset that a reset gap of 400 updates amortizes
+    count = q_all.numel()
+    m_all, v_all = torch.zeros_like(q_all), torch.zeros_like(q_all)
+    opt_p = B.adamw_params(1e-6)
+    opt = lambda: B.poetx_adamw_step(q_all, dq_all, m_all, v_all, count, 1, opt_p)
+    us_opt = _time_events(opt, 20, warm=3)
+    out["adamw"] = {"params": count, "us": round(us_opt, 1), "gbs": round(28 * count / us_opt / 1e3, 1),
+                    "frac_hbm": round(28 * count / us_opt / 1e3 / PEAK_HBM_GBS, 4)}
+    ms_train = _time_steps(lambda: (step(), opt()), args.steps, max(3, args.warmup // 4))
+    out["train_step_ms"] = round(ms_train, 4)
+    us_reset = _time_events(lambda: B.poetx_adamw_reset(m_all, v_all, count), 10, warm=2)
+    out["adamw_reset_us"] = round(us_reset, 1)
     if merge:
         merges = []
         for sp, S in zip(specs, states):
@@ -447,6 +468,7 @@ def run_layer(args, specs, label, merge):
                           B.poetx_merge(S["desc"], S["Wt"], qR, qP, S["pi_R"], S["pi_P"], a, c, ws))
         us = _time_events(lambda: [f() for f in merges], 5, warm=1)
         out["merge_all_7_us"] = round(us, 1)
+        out["train_step_ms_reset_gap_400"] = round(ms_train + (us + us_reset) / 1e3 / 400, 4)
     return out
 
 

@@ -238,6 +238,45 @@ size_t poetx_block_grad_workspace_bytes(int64_t T, int64_t d, int64_t b, int dty
 int poetx_block_grad(int dtype, int64_t T, int64_t d, int64_t b, const void* A, const void* B, float* dG,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ training step */
+/* The optimizer on the compact parameters (the review's Summary: optimizer
+ * state lives on the b(b-1)/2 values per block only; Weaknesses, single-run
+ * 8B/13B remark: the POET learning-rate scaling gamma = 0.5 and a reset gap of
+ * 400 steps).  The update is decoupled-decay AdamW with bias-corrected moments at
+ * the rate eta = lr * gamma (gamma = 0.5 on the pages: R - I is about 2Q, the
+ * review's "Cayley approximation" weakness, so q takes half the step):
+ *   m = beta1 m + (1 - beta1) dq
+ *   v = beta2 v + (1 - beta2) dq^2
+ *   q = q - eta ( m / (1 - beta1^step) / (sqrt(v / (1 - beta2^step)) + eps)
+ *                 + weight_decay q )
+ * The schedule is the caller's: every reset gap updates it calls poetx_merge
+ * (which zeroes q) and poetx_adamw_reset on the same parameters, and counts
+ * `step` from 1 again. */
+typedef struct poetx_adamw_params {
+    double lr;           /* base learning rate (finite) */
+    double gamma;        /* POET learning-rate scaling (finite; 0.5 on the pages) */
+    double beta1, beta2; /* moment decay rates, in [0, 1) */
+    double eps;          /* added to the root of the second moment, >= 0 */
+    double weight_decay; /* decoupled decay on q, >= 0 (0 keeps q's origin, R = I) */
+} poetx_adamw_params;
+
+/* One update of count float32 parameters in place.  q, m, v: float32 [count]
+ * (updated); dq: float32 [count] (read).  step >= 1 counts the updates since
+ * the last reset.  The four arrays must not overlap (16-byte aligned arrays
+ * take the vector path, others a scalar one with identical results).  The
+ * arithmetic is float32 with IEEE sqrt and division; the coefficients
+ * (1 - beta, the bias corrections, eta) are formed on the host in double from
+ * the double parameters and then rounded once, so 1 - beta2 keeps its digits.
+ * Non-finite gradients propagate.
+ * Errors: p NULL, step < 1, a rate outside its range -> INVALID_ARG;
+ * count < 0 or >= 2^31 -> SHAPE; count == 0 does nothing. */
+int poetx_adamw_step(float* q, const float* dq, float* m, float* v, int64_t count, int64_t step,
+                     const poetx_adamw_params* p, void* stream);
+
+/* m[i] = v[i] = 0 for i < count: the optimizer reset that follows a merge.
+ * A fill kernel (no memset node), so a captured graph replays it. */
+int poetx_adamw_reset(float* m, float* v, int64_t count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

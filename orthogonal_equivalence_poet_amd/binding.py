@@ -32,6 +32,7 @@ EXPORTS = [
     "poetx_linear_bwd_workspace_bytes", "poetx_linear_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
     "poetx_gemm", "poetx_block_apply", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
+    "poetx_adamw_step", "poetx_adamw_reset",
 ]
 
 
@@ -44,6 +45,11 @@ class PoetxError(RuntimeError):
 class LinearDesc(C.Structure):
     _fields_ = [("T", C.c_int64), ("m", C.c_int64), ("n", C.c_int64), ("b", C.c_int64),
                 ("k", C.c_int32), ("dtype", C.c_int32), ("variant", C.c_int32), ("reserved", C.c_int32)]
+
+
+class AdamwParams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("gamma", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double)]
 
 
 _lib: Optional[C.CDLL] = None
@@ -79,6 +85,8 @@ _SIGS = {
     "poetx_block_apply": ([_I32, _I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP], _I32),
     "poetx_block_grad_workspace_bytes": ([_I64, _I64, _I64, _I32], _SZ),
     "poetx_block_grad": ([_I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
+    "poetx_adamw_step": ([_VP, _VP, _VP, _VP, _I64, _I64, C.POINTER(AdamwParams), _VP], _I32),
+    "poetx_adamw_reset": ([_VP, _VP, _I64, _VP], _I32),
 }
 
 
@@ -273,3 +281,16 @@ def poetx_block_grad(A, B, dG, T, d, b, ws=None, stream=None):
     p, nbytes = _ws(ws)
     _check("poetx_block_grad", load().poetx_block_grad(_dtype_code(A), T, d, b, _ptr(A), _ptr(B), _ptr(dG), p,
                                                        nbytes, _stream(stream)))
+
+
+def adamw_params(lr, gamma=0.5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0) -> AdamwParams:
+    return AdamwParams(lr, gamma, beta1, beta2, eps, weight_decay)
+
+
+def poetx_adamw_step(q, dq, m, v, count, step, params: AdamwParams, stream=None):
+    _check("poetx_adamw_step", load().poetx_adamw_step(_ptr(q), _ptr(dq), _ptr(m), _ptr(v), count, step,
+                                                       C.byref(params), _stream(stream)))
+
+
+def poetx_adamw_reset(m, v, count, stream=None):
+    _check("poetx_adamw_reset", load().poetx_adamw_reset(_ptr(m), _ptr(v), count, _stream(stream)))

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "dense_gemm.h"
@@ -939,6 +940,39 @@ int poetx_block_grad(int dtype, int64_t T, int64_t d, int64_t b, const void* A, 
     int64_t kps;
     plan_splits(T, b, d / b, dtype == POETX_BF16, splits, kps);
     return block_grad(dtype == POETX_BF16, T, d, b, A, B, dG, splits, kps, static_cast<float*>(ws), s);
+}
+
+int poetx_adamw_step(float* q, const float* dq, float* m, float* v, int64_t count, int64_t step,
+                     const poetx_adamw_params* p, void* stream) {
+    if (!p) return POETX_ERR_INVALID_ARG;
+    if (count < 0 || count > kMaxExtent) return POETX_ERR_SHAPE;
+    const double lr = p->lr, gamma = p->gamma, b1 = p->beta1, b2 = p->beta2, eps = p->eps, wd = p->weight_decay;
+    if (step < 1 || !std::isfinite(lr) || !std::isfinite(gamma) || !(b1 >= 0.0 && b1 < 1.0) ||
+        !(b2 >= 0.0 && b2 < 1.0) || !(eps >= 0.0 && std::isfinite(eps)) || !(wd >= 0.0 && std::isfinite(wd)))
+        return POETX_ERR_INVALID_ARG;
+    if (count == 0) return POETX_OK;
+    if (!q || !dq || !m || !v) return POETX_ERR_INVALID_ARG;
+    const double eta = lr * gamma;
+    const double t = (double)step;
+    AdamwCoef c;
+    c.beta1 = (float)b1;
+    c.one_minus_beta1 = (float)(1.0 - b1);
+    c.beta2 = (float)b2;
+    c.one_minus_beta2 = (float)(1.0 - b2);
+    c.eps = (float)eps;
+    c.decay = (float)(1.0 - eta * wd);
+    c.step = (float)(eta / (1.0 - std::pow(b1, t)));
+    c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t)));
+    HIP_TRY(adamw_step(q, dq, m, v, count, c, as_stream(stream)));
+    return POETX_OK;
+}
+
+int poetx_adamw_reset(float* m, float* v, int64_t count, void* stream) {
+    if (count < 0 || count > kMaxExtent) return POETX_ERR_SHAPE;
+    if (count == 0) return POETX_OK;
+    if (!m || !v) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(zero_pair(m, v, count, as_stream(stream)));
+    return POETX_OK;
 }
 
 }  // extern "C"

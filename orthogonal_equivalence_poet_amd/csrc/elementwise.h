@@ -21,4 +21,16 @@ hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int*
                         hipStream_t s);
 hipError_t check_perm(const int* pi, int64_t len, int* ok, int* counts, int* bad, hipStream_t s);
 
+// AdamW coefficients for one step, worked out on the host in double:
+// decay = 1 - eta wd, step = eta / (1 - beta1^t), inv_sqrt_bc2 = 1 / sqrt(1 - beta2^t)
+// with eta = lr * gamma.  Per element:  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+// q = decay q - step m / (sqrt(v) inv_sqrt_bc2 + eps).
+struct AdamwCoef {
+    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, decay, step, inv_sqrt_bc2;
+};
+hipError_t adamw_step(float* q, const float* g, float* m, float* v, int64_t count, const AdamwCoef& c,
+                      hipStream_t s);
+// a[i] = b[i] = 0 for i < count (a fill kernel, so a captured graph replays it).
+hipError_t zero_pair(float* a, float* b, int64_t count, hipStream_t s);
+
 }  // namespace poetx

@@ -135,3 +135,22 @@ def test_cnp_saved_validation(B):
     assert lib.poetx_cnp_bwd_saved(FAKE, FAKE, 4, 256, 3, FAKE, 1, FAKE, sb, FAKE, 0, None) == 4
     assert lib.poetx_cnp_fwd_save(FAKE, 4, 24, 3, FAKE, 1, FAKE, sb, FAKE, ws, None) == 3
     assert lib.poetx_cnp_saved_bytes(4, 24, 3, 1) == 0
+
+
+def test_adamw_validation(B):
+    lib = B.load()
+    ok = B.adamw_params(1e-3)
+    fake = 256  # never dereferenced: every case below fails validation or has count == 0
+    step = lambda count, t, p: lib.poetx_adamw_step(fake, fake, fake, fake, count, t, C.byref(p) if p else None, None)
+    assert lib.poetx_adamw_step(None, None, None, None, 0, 1, C.byref(ok), None) == B.POETX_OK
+    assert step(10, 1, None) == B.POETX_ERR_INVALID_ARG
+    assert step(10, 0, ok) == B.POETX_ERR_INVALID_ARG
+    assert step(-1, 1, ok) == B.POETX_ERR_SHAPE
+    assert step(1 << 31, 1, ok) == B.POETX_ERR_SHAPE
+    for bad in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1.0), dict(weight_decay=-0.5), dict(lr=float("inf")),
+                dict(gamma=float("nan")), dict(beta2=float("nan"))):
+        assert step(10, 1, B.adamw_params(**{"lr": 1e-3, **bad})) == B.POETX_ERR_INVALID_ARG, bad
+    assert lib.poetx_adamw_step(fake, None, fake, fake, 10, 1, C.byref(ok), None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_adamw_reset(None, None, 0, None) == B.POETX_OK
+    assert lib.poetx_adamw_reset(fake, None, 4, None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_adamw_reset(fake, fake, -2, None) == B.POETX_ERR_SHAPE
