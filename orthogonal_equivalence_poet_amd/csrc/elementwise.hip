@@ -56,15 +56,20 @@ __global__ void __launch_bounds__(256) skew_unpack_kernel(const float* __restric
 }
 
 // dq[j][idx(r,c)] = dQ[j][r][c] - dQ[j][c][r] for r < c.  One workgroup per
-// (block, upper 32 x 32 tile); the mirrored tile is staged in LDS.
+// (block, 32 x 32 tile on or above the diagonal; the grid holds only those);
+// the mirrored tile is staged in LDS.
 __global__ void __launch_bounds__(256) skew_pack_kernel(const float* __restrict__ dQ, float* __restrict__ dq,
                                                         int b) {
     __shared__ float up[kSkewTile][kSkewTile + 1];
     __shared__ float lo[kSkewTile][kSkewTile + 1];
     const int tiles = b / kSkewTile;
-    const int ti = blockIdx.x / tiles;
-    const int tj = blockIdx.x % tiles;
-    if (ti > tj) return;
+    // tile row ti holds the tiles - ti pairs (ti, ti .. tiles - 1)
+    int ti = 0, t = blockIdx.x;
+    while (t >= tiles - ti) {
+        t -= tiles - ti;
+        ++ti;
+    }
+    const int tj = ti + t;
     const int64_t blk = blockIdx.y;
     const int64_t ntri = (int64_t)b * (b - 1) / 2;
     const float* G = dQ + blk * (int64_t)b * b;
@@ -265,6 +270,43 @@ __global__ void combine_kernel(int64_t total, int b, const float* __restrict__ i
     if (outc) store_f32(outc + i, v);
 }
 
+// The same on four consecutive elements of one row (b % 4 == 0, 16-byte
+// aligned arrays): float4 loads and stores.
+template <typename CT>
+__global__ void combine4_kernel(int64_t total4, int b, const float* __restrict__ in0, float c0,
+                                const float* __restrict__ in1, float c1, const float* __restrict__ in2, float c2,
+                                float gamma, float* __restrict__ out32, CT* __restrict__ outc) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total4) return;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](const float* in, float c) {
+        const float4 a = reinterpret_cast<const float4*>(in)[i];
+        v.x += c * a.x;
+        v.y += c * a.y;
+        v.z += c * a.z;
+        v.w += c * a.w;
+    };
+    if (in0) add(in0, c0);
+    if (in1) add(in1, c1);
+    if (in2) add(in2, c2);
+    if (gamma != 0.f) {
+        const int64_t e = (4 * i) % ((int64_t)b * b);
+        const int d = (int)(e / b) - (int)(e % b);   // the diagonal sits at offset d in this group of four
+        if (d == 0) v.x += gamma;
+        if (d == 1) v.y += gamma;
+        if (d == 2) v.z += gamma;
+        if (d == 3) v.w += gamma;
+    }
+    if (out32) reinterpret_cast<float4*>(out32)[i] = v;
+    if (outc) {
+        if constexpr (sizeof(CT) == 4) {
+            reinterpret_cast<float4*>(outc)[i] = v;
+        } else {
+            reinterpret_cast<uint2*>(outc)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
+    }
+}
+
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < words) p[i] = 0u;
@@ -338,7 +380,8 @@ hipError_t skew_pack(const float* dQ, float* dq, int64_t nblk, int b, hipStream_
         const int64_t ntri = (int64_t)b * (b - 1) / 2, bb = (int64_t)b * b;
         for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGridY) {
             const unsigned nz = (unsigned)std::min<int64_t>(kMaxGridY, nblk - z0);
-            dim3 grid((b / kSkewTile) * (b / kSkewTile), nz);
+            const int tiles = b / kSkewTile;
+            dim3 grid(tiles * (tiles + 1) / 2, nz);
             hipLaunchKernelGGL(skew_pack_kernel, grid, dim3(256), 0, s, dQ + z0 * bb, dq + z0 * ntri, b);
         }
     } else {
@@ -356,8 +399,10 @@ hipError_t permute_2d(const void* src, void* dst, bool bf16, int64_t rows, int64
     const int esz = bf16 ? 2 : 4;
     const int64_t row_bytes = cols * esz;
     if (row_bytes <= (int64_t)permute_lds_row_limit_bytes() && (cols % (16 / esz)) == 0) {
-        // ~32 KB of rows per workgroup (at least one row).
-        int rpw = (int)std::max<int64_t>(1, (32 * 1024) / row_bytes);
+        // The fewest rows that make at least 4 KB per workgroup: many small
+        // workgroups keep more loads in flight per CU than a few large ones
+        // (measured on 1024- to 14336-column bf16 rows at 2048 to 8192 rows).
+        int rpw = (int)std::max<int64_t>(1, (4 * 1024 + row_bytes - 1) / row_bytes);
         rpw = (int)std::min<int64_t>(rpw, rows);
         const size_t smem = (size_t)rpw * row_bytes;
         const unsigned grid = (unsigned)((rows + rpw - 1) / rpw);
@@ -390,6 +435,17 @@ hipError_t combine(int64_t nblk, int b, const float* in0, float c0, const float*
                    float c2, float gamma, float* out32, void* outc, bool outc_bf16, hipStream_t s) {
     const int64_t total = nblk * (int64_t)b * b;
     if (total <= 0) return hipSuccess;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    if (b % 4 == 0 && al16(in0) && al16(in1) && al16(in2) && al16(out32) && al16(outc)) {
+        const int64_t total4 = total / 4;
+        if (outc_bf16)
+            hipLaunchKernelGGL(combine4_kernel<bf16_t>, dim3(blocks_for(total4, 256)), dim3(256), 0, s, total4, b,
+                               in0, c0, in1, c1, in2, c2, gamma, out32, (bf16_t*)outc);
+        else
+            hipLaunchKernelGGL(combine4_kernel<float>, dim3(blocks_for(total4, 256)), dim3(256), 0, s, total4, b,
+                               in0, c0, in1, c1, in2, c2, gamma, out32, (float*)outc);
+        return hipGetLastError();
+    }
     if (outc_bf16)
         hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s, total, b, in0, c0,
                            in1, c1, in2, c2, gamma, out32, (bf16_t*)outc);
