@@ -45,12 +45,12 @@ struct PipeArgs {
 // with splits > 1 split s writes its partial sum at C + s * strideSplit.
 // Requirements (pipe_gemm_supported): K-contiguous operands need K % 64 == 0;
 // every leading dimension, stride and contiguous extent a multiple of 8.
-// Workgroup tile: Tall 256 x 128 (dense products), Wide 128 x 256 (block
-// products: one workgroup spans a whole block of 256 outputs), Square 128 x 128
-// and Small 64 x 64 (block gradients: enough tiles to fill the chip without
-// splitting the token axis).  Instantiated: k-major A with bf16 output (Tall,
-// Wide) and m/n-major A and B with float32 output (Tall, Square, Small); Big
-// 256 x 256 (dense products with at least 256 such tiles) for k-major A.
+// Workgroup tiles, k-major A with bf16 output (dense and block products): Big
+// 256 x 256, Tall 256 x 128, Wide 128 x 256 (a block product's workgroup spans
+// a whole block of 256 outputs), Square 128 x 128 and Slim 64 x 128; callers
+// take the largest whose grid still gives every CU a workgroup.  m/n-major A
+// and B with float32 output (block gradients): Square 128 x 128 and Small
+// 64 x 64 (enough tiles to fill the chip without splitting the token axis).
 enum class PipeTile { Tall, Wide, Square, Small, Big, Slim };
 bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                          int64_t strideA, int64_t strideB);

@@ -389,6 +389,7 @@ def test_block_grad_parity(T, d, b, dtype):
 
 
 @pytest.mark.parametrize("T,d,b,dtype", [(2048, 4096, 256, "bf16"), (2048, 1024, 256, "bf16"), (300, 1024, 512, "bf16"),
+                                         (2100, 14336, 256, "bf16"), (4096, 4096, 512, "bf16"),
                                          (77, 192, 64, "bf16"), (33, 96, 32, "f32"), (129, 128, 16, "bf16")])
 @pytest.mark.parametrize("transpose", [True, False])
 def test_block_apply_parity(T, d, b, dtype, transpose):
