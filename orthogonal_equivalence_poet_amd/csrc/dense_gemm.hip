@@ -18,7 +18,8 @@
 // Operand tiles travel global -> LDS by direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so no
 // VGPRs stage them and no ds_write is issued.  S LDS stages form a ring (S = 3
-// for 256 x 128 and 128 x 256, 2 for 256 x 256, 4 for the smaller tiles):
+// for 256 x 128 and 128 x 256, 2 for 256 x 256, 4 for the smaller tiles, 2 or 3
+// for the b x b products, whose epilogues need more workgroups per CU):
 // while the MFMAs consume stage kt % S, the loads of tiles kt+1 .. kt+S-1 are
 // in flight, so a short product (K = 256) waits for memory once.  The loads
 // are issued from inline asm so that the compiler does not add a conservative
@@ -1097,11 +1098,11 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     return hipErrorInvalidValue;
 }
 
-template <int T, bool OUT_F32>
+template <int T, bool OUT_F32, int S>
 hipError_t launch_general(bool a_mn, bool b_mn, const PipeArgs& p, hipStream_t stream) {
-    if (!a_mn && !b_mn) return launch<T, T, false, false, OUT_F32, kEpiGeneral, 4>(p, stream);
-    if (!a_mn && b_mn) return launch<T, T, false, true, OUT_F32, kEpiGeneral, 4>(p, stream);
-    return launch<T, T, true, true, OUT_F32, kEpiGeneral, 4>(p, stream);
+    if (!a_mn && !b_mn) return launch<T, T, false, false, OUT_F32, kEpiGeneral, S>(p, stream);
+    if (!a_mn && b_mn) return launch<T, T, false, true, OUT_F32, kEpiGeneral, S>(p, stream);
+    return launch<T, T, true, true, OUT_F32, kEpiGeneral, S>(p, stream);
 }
 
 hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p_in, hipStream_t stream) {
@@ -1117,9 +1118,16 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
     if (a_mn && !b_mn) return hipErrorInvalidValue;
     if (p.splits != 1) return hipErrorInvalidValue;
     // 64 x 64 tiles: measured ahead of 128 x 128 ones for b = 256 and 512 from
-    // 32 to 320 blocks (the K = b products are short; more workgroups overlap
-    // their epilogues)
-    return out_f32 ? launch_general<64, true>(a_mn, b_mn, p, stream) : launch_general<64, false>(a_mn, b_mn, p, stream);
+    // 32 to 4000 blocks (the K = b products are short and bound by their
+    // epilogue traffic; more workgroups per CU overlap it).  For the same reason
+    // the ring is shallow: two stages (five workgroups per CU) for K <= 256,
+    // three for longer K (same-process sweep: 320 blocks of 256 101 -> 76 us,
+    // 36 blocks of 512 40 -> 32 us, against four stages).
+    if (p.k_per_split <= 256)
+        return out_f32 ? launch_general<64, true, 2>(a_mn, b_mn, p, stream)
+                       : launch_general<64, false, 2>(a_mn, b_mn, p, stream);
+    return out_f32 ? launch_general<64, true, 3>(a_mn, b_mn, p, stream)
+                   : launch_general<64, false, 3>(a_mn, b_mn, p, stream);
 }
 
 hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hipStream_t stream) {
@@ -1131,12 +1139,17 @@ hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hip
     };
     p.epi_vec = al(p.C, p.ldc, p.strideC) && al(p.C2, p.ldc2, p.strideC2) && al(p.Cin1, p.ldcin1, p.strideCin1) &&
                 al(p.Cin2, p.ldcin2, p.strideCin2);
+    // shallow rings as for pipe_gemm_general (mode 2 keeps two epilogue tiles,
+    // so at least three stages): 320 blocks of 256 119 -> 98 us and 109 -> 96 us
     if (separate) {
-        return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 4, 2, 2, 2>(p, stream)
-                       : launch<64, 64, false, false, false, kEpiGeneral, 4, 2, 2, 2>(p, stream);
+        return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 3, 2, 2, 2>(p, stream)
+                       : launch<64, 64, false, false, false, kEpiGeneral, 3, 2, 2, 2>(p, stream);
     }
-    return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 4, 2, 2, 1>(p, stream)
-                   : launch<64, 64, false, false, false, kEpiGeneral, 4, 2, 2, 1>(p, stream);
+    if (p.k_per_split <= 256)
+        return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 2, 2, 2, 1>(p, stream)
+                       : launch<64, 64, false, false, false, kEpiGeneral, 2, 2, 2, 1>(p, stream);
+    return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 3, 2, 2, 1>(p, stream)
+                   : launch<64, 64, false, false, false, kEpiGeneral, 3, 2, 2, 1>(p, stream);
 }
 
 int pipe_tile_rows(PipeTile t) {
