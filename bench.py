@@ -145,7 +145,8 @@ def make_step(spec, S):
 def stage_timings(spec, S, reps):
     """Every stage of the step alone, through the C ABI, same shapes and
     launch configurations as inside poetx_linear_fwd / _bwd (the mem variant
-    repeats the P-side block product and the dense forward in its backward)."""
+    repeats the input gather, the P-side block product and the dense forward in
+    its backward; the fast variant keeps their outputs)."""
     import torch
     from orthogonal_equivalence_poet_amd import binding as B
     T, m, n, b, k = spec.T, spec.m, spec.n, spec.b, spec.k
@@ -187,8 +188,9 @@ def stage_timings(spec, S, reps):
                                                   S["cnp_saved"], S["ws"]),
          _products(k)[1] * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
     ]
-    if spec.variant == "mem":   # recomputed in the backward, same kernels
-        stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages if nm in ("blk_fwd_P", "dense_fwd")]
+    if spec.variant == "mem":   # recomputed in the backward, same kernels (fast keeps a and h2)
+        stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages
+                   if nm in ("perm_gather_x", "blk_fwd_P", "dense_fwd")]
     # the standalone skew unpack (to bf16) and pack of the same blocks; not part of the
     # step (the fused forward unpacks on chip, the backward's pack is inside cnp_bwd)
     ntri = b * (b - 1) // 2

@@ -69,8 +69,9 @@ enum {
 
 enum { POETX_F32 = 0, POETX_BF16 = 1 };
 
-/* fast saves h2 = Wt P-side output for the backward; mem keeps only x and
- * recomputes (review Summary: POET-X_fast / checkpointed POET-X_mem). */
+/* fast saves h2 (the dense product's output) and a (x gathered by pi_P) for
+ * the backward; mem keeps only x and recomputes both (review Summary:
+ * POET-X_fast / checkpointed POET-X_mem). */
 enum { POETX_FAST = 0, POETX_MEM = 1 };
 
 typedef struct poetx_linear_desc {
@@ -166,9 +167,10 @@ int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size
  *   z  = h2 . blockdiag(G_R)^T       [T, m]
  *   y  = z scattered by pi_R         [T, m]   (y = x P^T W0^T R^T)
  * x: dtype [T, n]; Wt: dtype [m, n]; G_R: dtype [m/b, b, b]; G_P: dtype
- * [n/b, b, b]; y: dtype [T, m].  FAST writes h2 (dtype [T, m]) to `saved`,
- * which must hold poetx_linear_saved_bytes(d) bytes; MEM writes nothing there
- * (saved may be NULL). */
+ * [n/b, b, b]; y: dtype [T, m].  FAST writes h2 (dtype [T, m]) and a (dtype
+ * [T, n], at the next 256-byte boundary after h2) to `saved`, which must hold
+ * poetx_linear_saved_bytes(d) bytes; MEM writes nothing there (saved may be
+ * NULL). */
 size_t poetx_linear_saved_bytes(const poetx_linear_desc* d);
 size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d);
 int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
@@ -180,8 +182,8 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
  *   dx  = dy R W0 P                              dtype [T, n]
  *   dG_R[j] = (Pi_R dR Pi_R^T) block j, dR = dy^T x P^T W0^T     float32 [m/b, b, b]
  *   dG_P[j] = (Pi_P dP Pi_P^T) block j, dP = W0^T R^T dy^T x     float32 [n/b, b, b]
- * FAST reads h2 from `saved` (written by poetx_linear_fwd with the same
- * inputs); MEM recomputes it from x.  Feed dG_R / dG_P to poetx_cnp_bwd to
+ * FAST reads h2 and a from `saved` (written by poetx_linear_fwd with the
+ * same inputs); MEM recomputes both from x.  Feed dG_R / dG_P to poetx_cnp_bwd to
  * obtain dq_R / dq_P.  T == 0 writes zero block gradients. */
 size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d);
 int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,

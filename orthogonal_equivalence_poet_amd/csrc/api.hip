@@ -534,6 +534,12 @@ int block_grad(bool bf16, int64_t T, int64_t d, int64_t b, const void* A, const 
     return POETX_OK;
 }
 
+// FAST keeps h2 [T, m] and a = x gathered by pi_P [T, n] in `saved`, a at this
+// 256-byte aligned offset.
+size_t fast_saved_a_offset(const poetx_linear_desc* d) {
+    return (esize(d->dtype) * (size_t)(d->T * d->m) + 255) & ~size_t(255);
+}
+
 int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
                    hipStream_t s) {
@@ -724,7 +730,7 @@ int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size
 
 size_t poetx_linear_saved_bytes(const poetx_linear_desc* d) {
     if (check_desc(d) != POETX_OK || d->variant != POETX_FAST) return 0;
-    return esize(d->dtype) * (size_t)(d->T * d->m);
+    return fast_saved_a_offset(d) + esize(d->dtype) * (size_t)(d->T * d->n);
 }
 
 size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
@@ -750,8 +756,10 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
     LinearBufs L;
     plan_linear(cv, d, false, L);
     void* h2 = saved;
+    void* a = L.buf[0];
     if (d->variant == POETX_MEM) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
-    return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, L.buf[0], L.buf[1], as_stream(stream));
+    else a = static_cast<char*>(saved) + fast_saved_a_offset(d);
+    return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, a, L.buf[1], as_stream(stream));
 }
 
 size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {
@@ -783,12 +791,17 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     LinearBufs L;
     plan_linear(cv, d, true, L);
     const bool bf = d->dtype == POETX_BF16;
-    void* bufA = L.buf[0];
+    const void* bufA = L.buf[0];
     void* bufB = L.buf[1];
     void* bufC = L.buf[2];
-    // a = x gathered by pi_P (kept for dG_P)
-    HIP_TRY(permute_2d(x, bufA, bf, T, n, nullptr, pi_P, false, s));
     const void* h2 = saved;
+    if (d->variant == POETX_FAST) {
+        // a = x gathered by pi_P, kept by the forward
+        bufA = static_cast<const char*>(saved) + fast_saved_a_offset(d);
+    } else {
+        // a = x gathered by pi_P again (kept for dG_P)
+        HIP_TRY(permute_2d(x, L.buf[0], bf, T, n, nullptr, pi_P, false, s));
+    }
     if (d->variant == POETX_MEM) {
         // recompute h1 and h2 from x
         HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, bufA, G_P, bufB, s));

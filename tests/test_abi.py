@@ -115,7 +115,10 @@ def test_cnp_and_skew_validation(B):
 def test_workspace_sizes_scale(B):
     lib = B.load()
     d = B.desc(2048, 4096, 4096, 256, 3, B.POETX_BF16, B.POETX_FAST)
-    assert lib.poetx_linear_saved_bytes(C.byref(d)) == 2048 * 4096 * 2
+    # FAST keeps h2 [T, m] and the gathered input a [T, n] (at a 256-byte boundary)
+    assert lib.poetx_linear_saved_bytes(C.byref(d)) == 2048 * 4096 * 2 + 2048 * 4096 * 2
+    d3 = B.desc(7, 48, 32, 16, 3, B.POETX_F32, B.POETX_FAST)
+    assert lib.poetx_linear_saved_bytes(C.byref(d3)) == (7 * 48 * 4 + 255) // 256 * 256 + 7 * 32 * 4
     dm = B.desc(2048, 4096, 4096, 256, 3, B.POETX_BF16, B.POETX_MEM)
     assert lib.poetx_linear_saved_bytes(C.byref(dm)) == 0
     assert lib.poetx_linear_bwd_workspace_bytes(C.byref(dm)) >= 3 * 2048 * 4096 * 2
