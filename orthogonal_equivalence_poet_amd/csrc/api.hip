@@ -170,7 +170,7 @@ struct CnpBufs {
     float* Q32 = nullptr; void* Qc = nullptr;
     // k = 3: U32 = 2Q + 2S, Sc = S, Tc = 2Q + S (one fused epilogue)
     float* U32 = nullptr; void* Sc = nullptr; void* Tc = nullptr;
-    // k = 4: S, P1 = Q + S, E = P1 + P1 S, W = Q + E
+    // k = 4: S, P1 = Q + S (bf16 path: only its compute copy), E = P1 + P1 S, W (backward scratch)
     float* S32 = nullptr; float* P32 = nullptr; void* Pc = nullptr; float* E32 = nullptr; void* Ec = nullptr;
     float* W32 = nullptr;
     // Horner (other k): D_1..D_k
@@ -203,8 +203,14 @@ void plan_cnp(Carver& cv, Carver& sv, int64_t nblk, int64_t b, int k, bool cbf16
     } else if (k == 4) {
         B.S32 = sv.take_n<float>(e);
         B.Sc = ctake(sv, cbf16, e, B.S32);
-        B.P32 = cv.take_n<float>(e);
-        B.Pc = ctake(cv, cbf16, e, B.P32);
+        // bf16: P1 comes out of the square's epilogue and is kept with it;
+        // float32: P1 is formed in its own pass
+        if (cbf16) {
+            B.Pc = sv.take(2 * (size_t)e);
+        } else {
+            B.P32 = cv.take_n<float>(e);
+            B.Pc = B.P32;
+        }
         B.E32 = cv.take_n<float>(e);
         B.Ec = ctake(cv, cbf16, e, B.E32);
         B.W32 = cv.take_n<float>(e);
@@ -231,7 +237,8 @@ void plan_cnp(Carver& cv, Carver& sv, int64_t nblk, int64_t b, int k, bool cbf16
 
 // Shared front part: Q in float32 and in the compute dtype (one pass), and the
 // square S = Q Q = -Q Q^T.  For k = 3 the square's epilogue also emits
-// Tc = 2Q + S and U = 2Q + 2S; for k = 4 it emits S (float32 and compute).
+// Tc = 2Q + S and U = 2Q + 2S; for k = 4 it emits S (float32 and compute) and,
+// on the bf16 path, P1 = Q + S in bf16 (float32: a separate pass).
 int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, CnpBufs& B, hipStream_t s) {
     HIP_TRY(skew_unpack(q, B.Q32, false, nblk, (int)b, s, cbf16 ? B.Qc : nullptr));
     if (k == 3) {
@@ -249,8 +256,25 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
         g.k_per_split = (int)b;
         HIP_TRY(small_gemm(g, GemmLayout::NT, cbf16, false, s));
     } else if (k == 4) {
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Qc, b), B.S32, b, b * b, s,
-                     -1.f, nullptr, 0, nullptr, 0, 0, cbf16 ? B.Sc : nullptr));
+        if (cbf16) {
+            GemmArgs g;
+            g.A = B.Qc; g.lda = b; g.strideA = b * b;
+            g.B = B.Qc; g.ldb = b; g.strideB = b * b;
+            g.C = B.S32; g.ldc = b; g.strideC = b * b;
+            g.C2 = B.Sc; g.ldc2 = b; g.strideC2 = b * b;
+            g.C3 = B.Pc;
+            g.Cin1 = B.Q32; g.ldcin1 = b; g.strideCin1 = b * b;
+            g.alpha = -1.f;
+            g.mode = 3;
+            g.M = g.N = g.K = (int)b;
+            g.batch = (int)nblk;
+            g.k_per_split = (int)b;
+            HIP_TRY(small_gemm(g, GemmLayout::NT, cbf16, false, s));
+        } else {
+            HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.Qc, b), B.S32, b, b * b, s,
+                         -1.f));
+            HIP_TRY(combine(nblk, (int)b, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, nullptr, false, s));
+        }
     }
     return POETX_OK;
 }
@@ -276,12 +300,11 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
         HIP_TRY(gemm(GemmLayout::NT, cbf16, gbf16, b, b, b, nblk, sq(B.Tc, b), sq(B.Sc, b), G, b, bb, s, 1.f,
                      B.U32, 1.f, nullptr, 0, 1.f));
     } else if (k == 4) {
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, cbf16 ? B.Pc : nullptr, cbf16, s));
+        // E = P1 + P1 S with P1 = Q + S taken as two addends; G = I + Q + E + Q E
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(B.Sc, b), B.E32, b, bb, s, 1.f,
-                     B.P32, 1.f, nullptr, 0, 0, cbf16 ? B.Ec : nullptr));
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.E32, 1.f, nullptr, 0, 0, B.W32, nullptr, false, s));
+                     B.Q32, 1.f, B.S32, 1.f, 0, cbf16 ? B.Ec : nullptr));
         HIP_TRY(gemm(GemmLayout::NN, cbf16, gbf16, b, b, b, nblk, sq(B.Qc, b), sq(B.Ec, b), G, b, bb, s, 1.f,
-                     B.W32, 1.f, nullptr, 0, 1.f));
+                     B.Q32, 1.f, B.E32, 1.f, 1.f));
     } else {
         // rolling D buffers: slots 1 (= Q), 2, 3
         int cur = 1;
@@ -351,10 +374,12 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.c_c, b), dQ, b, bb, s, 1.f,
                      B.e32, 1.f));
     } else if (k == 4) {
-        // recompute P1 = Q + S and E = P1 + P1 S
-        HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, cbf16 ? B.Pc : nullptr, cbf16, s));
+        // recompute E = P1 + P1 S (P1 = Q + S came with the square; a float32
+        // P1 lives in the workspace, so a saved backward forms it again)
+        if (!cbf16 && saved)
+            HIP_TRY(combine(nblk, ib, B.Q32, 1.f, B.S32, 1.f, nullptr, 0, 0, B.P32, nullptr, false, s));
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(B.Sc, b), B.E32, b, bb, s, 1.f,
-                     B.P32, 1.f, nullptr, 0, 0, cbf16 ? B.Ec : nullptr));
+                     B.Q32, 1.f, B.S32, 1.f, 0, cbf16 ? B.Ec : nullptr));
         // X1 = dG + dG E^T ; dE = dG + Q^T dG
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Ec, b), B.a32, b, bb, s, 1.f, dG,
                      1.f));

@@ -22,7 +22,9 @@ struct PipeArgs {
     // General epilogue (pipe_gemm_general only).  With v = alpha * acc:
     //   mode 0: o = v + beta1 Cin1 + beta2 Cin2 + gamma [row == col];
     //           C = o (output dtype, if C), C2 = o (bf16, if C2);
-    //   mode 1 (Cayley-Neumann square): C = 2 Cin1 + 2 v, C2 = v, C3 = 2 Cin1 + v.
+    //   mode 1 (Cayley-Neumann square, k = 3): C = 2 Cin1 + 2 v, C2 = v, C3 = 2 Cin1 + v;
+    //   mode 3 (Cayley-Neumann square, k = 4): C = v, C2 = v, C3 = Cin1 + v
+    //           (pipe_gemm_general only).
     void* C2 = nullptr;        // bf16
     void* C3 = nullptr;        // bf16, same layout as C2
     int64_t ldc2 = 0, strideC2 = 0;

@@ -386,6 +386,13 @@ __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16
                    vec, full, valid);
             continue;
         }
+        if (p.mode == 3) {   // k = 4 square: C = v, C2 = v, C3 = Cin1 + v
+            store4(c1 + (int64_t)gr * p.ldc + gc, v, vec, full, valid);
+            store4(c2 + (int64_t)gr * p.ldc2 + gc, v, vec, full, valid);
+            store4(c3 + (int64_t)gr * p.ldc2 + gc, make_float4(a1.x + v.x, a1.y + v.y, a1.z + v.z, a1.w + v.w), vec,
+                   full, valid);
+            continue;
+        }
         if (p.mode == 1) {
             const float4 q2 = make_float4(2.f * a1.x, 2.f * a1.y, 2.f * a1.z, 2.f * a1.w);
             store4(c1 + (int64_t)gr * p.ldc + gc,

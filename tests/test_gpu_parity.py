@@ -171,7 +171,8 @@ def test_cnp_fused_forward_many_blocks(b, k, std, norm):
 
 @pytest.mark.parametrize("b,k,dtype,nblk", [(256, 3, "bf16", 6), (256, 3, "bf16", 256), (128, 3, "bf16", 512),
                                             (64, 3, "f32", 6), (128, 4, "bf16", 6), (128, 4, "bf16", 512),
-                                            (64, 5, "bf16", 6), (16, 2, "f32", 6)])
+                                            (64, 5, "bf16", 6), (16, 2, "f32", 6), (64, 4, "f32", 6),
+                                            (512, 4, "bf16", 36)])
 def test_cnp_saved_variant_is_bitwise_identical(b, k, dtype, nblk):
     """Forward keeping the square and its companions, backward reusing them:
     the same products on the same values as the recomputing pair."""
