@@ -386,16 +386,47 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(dGc, b), B.b32, b, bb, s, 1.f, dG,
                      1.f, nullptr, 0, 0, cbf16 ? B.c_c : nullptr));
         const void* dEc = cbf16 ? B.c_c : static_cast<void*>(B.b32);
-        // dP1 = dE + dE S ; dS = P1^T dE + dP1
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dEc, b), sq(B.Sc, b), B.e32, b, bb, s, 1.f,
-                     B.b32, 1.f));
-        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(dEc, b), nullptr, b, bb, s, 1.f,
-                     B.e32, 1.f, nullptr, 0, 0, B.d_c));
-        // dQ = X1 + dP1 + dS Q^T + Q^T dS
-        HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.d_c, b), sq(B.Qc, b), B.W32, b, bb, s, 1.f,
-                     B.a32, 1.f, B.e32, 1.f));
-        HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.d_c, b), dQ, b, bb, s, 1.f, B.W32,
-                     1.f));
+        if (dual) {
+            // the last four products paired per launch, as for k = 3:
+            // dP1 = dE + dE S (float32) and dS = dP1 + P1^T dE (bf16) from one,
+            // dQ = X1 + dP1 + dS Q^T + Q^T dS from the other
+            PipeArgs d;
+            d.A = dEc; d.lda = b; d.strideA = bb;
+            d.B = B.Sc; d.ldb = b; d.strideB = bb;
+            d.A2 = B.Pc; d.lda2 = b; d.strideA2 = bb;
+            d.B2 = dEc; d.ldb2 = b; d.strideB2 = bb;
+            d.C = B.e32; d.ldc = b; d.strideC = bb;
+            d.C2 = B.d_c; d.ldc2 = b; d.strideC2 = bb;
+            d.Cin1 = B.b32; d.ldcin1 = b; d.strideCin1 = bb;
+            d.beta1 = 1.f; d.beta2 = 1.f;
+            d.M = d.N = d.K = ib;
+            d.batch = (int)nblk;
+            d.k_per_split = ib;
+            HIP_TRY(pipe_gemm_dual(true, true, d, s));
+            PipeArgs e;
+            e.A = B.d_c; e.lda = b; e.strideA = bb;
+            e.B = B.Qc; e.ldb = b; e.strideB = bb;
+            e.A2 = B.Qc; e.lda2 = b; e.strideA2 = bb;
+            e.B2 = B.d_c; e.ldb2 = b; e.strideB2 = bb;
+            e.C = dQ; e.ldc = b; e.strideC = bb;
+            e.Cin1 = B.a32; e.ldcin1 = b; e.strideCin1 = bb; e.beta1 = 1.f;
+            e.Cin2 = B.e32; e.ldcin2 = b; e.strideCin2 = bb; e.beta2 = 1.f;
+            e.M = e.N = e.K = ib;
+            e.batch = (int)nblk;
+            e.k_per_split = ib;
+            HIP_TRY(pipe_gemm_dual(false, true, e, s));
+        } else {
+            // dP1 = dE + dE S ; dS = P1^T dE + dP1
+            HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dEc, b), sq(B.Sc, b), B.e32, b, bb, s, 1.f,
+                         B.b32, 1.f));
+            HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Pc, b), sq(dEc, b), nullptr, b, bb, s,
+                         1.f, B.e32, 1.f, nullptr, 0, 0, B.d_c));
+            // dQ = X1 + dP1 + dS Q^T + Q^T dS
+            HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(B.d_c, b), sq(B.Qc, b), B.W32, b, bb, s,
+                         1.f, B.a32, 1.f, B.e32, 1.f));
+            HIP_TRY(gemm(GemmLayout::TN, cbf16, false, b, b, b, nblk, sq(B.Qc, b), sq(B.d_c, b), dQ, b, bb, s, 1.f,
+                         B.W32, 1.f));
+        }
     } else {
         // recompute D_2..D_k (D_1 = Q)
         for (int i = 1; i < k; ++i)
