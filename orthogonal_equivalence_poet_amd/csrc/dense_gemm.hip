@@ -333,10 +333,45 @@ __device__ __forceinline__ void store4(T* __restrict__ p, float4 v, bool vec, bo
     if (valid > 3) store_f32(p + 3, v.w);
 }
 
+// The float32 addends Cin1 / Cin2 of the chunks a thread writes in the general
+// epilogue, loaded before the main loop so that their latency hides behind it
+// (tiles with at most four chunks per thread; the b x b products are bound by
+// this traffic).  Rows or columns outside the product read as zero.
+template <int BM, int BN, int kThreads>
+struct EpiAddends {
+    static constexpr int kChunks = BM * BN / 4;
+    static constexpr int kPer = kChunks / kThreads;
+    static constexpr bool kOn = kChunks % kThreads == 0 && kPer <= 4;
+    float4 a1[kOn ? kPer : 1], a2[kOn ? kPer : 1];
+};
+
+template <int BM, int BN, int kThreads>
+__device__ __forceinline__ void load_addends(const PipeArgs& p, int m0, int n0, int z, int tid,
+                                             EpiAddends<BM, BN, kThreads>& e) {
+    using E = EpiAddends<BM, BN, kThreads>;
+    const float* __restrict__ cin1 = p.Cin1 ? p.Cin1 + (int64_t)z * p.strideCin1 : nullptr;
+    const float* __restrict__ cin2 = p.Cin2 ? p.Cin2 + (int64_t)z * p.strideCin2 : nullptr;
+    const bool vec = p.epi_vec != 0;
+#pragma unroll
+    for (int k = 0; k < E::kPer; ++k) {
+        const int u = k * kThreads + tid;
+        const int row = u / (BN / 4);
+        const int c = (u % (BN / 4)) * 4;
+        const int gr = m0 + row, gc = n0 + c;
+        const bool in = gr < p.M && gc < p.N;
+        const int valid = in ? min(4, p.N - gc) : 0;
+        const bool full = valid == 4;
+        e.a1[k] = cin1 && in ? load4(cin1 + (int64_t)gr * p.ldcin1 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        e.a2[k] = cin2 && in ? load4(cin2 + (int64_t)gr * p.ldcin2 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
 template <class G, typename OutT, bool TWO = false>
 __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16_t (&acc)[G::MI][G::NJ],
                                                  const f32x16_t (&acc2)[G::MI][G::NJ], float* tile, int m0, int n0,
-                                                 int wm, int wn, int z, int tid) {
+                                                 int wm, int wn, int z, int tid,
+                                                 const EpiAddends<G::BM, G::BN, G::kThreads>& pre) {
+    using Pre = EpiAddends<G::BM, G::BN, G::kThreads>;
     constexpr int BM = G::BM, BN = G::BN, MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     constexpr int kThreads = G::kThreads;
     using E = EpiTile<BM, BN>;
@@ -373,7 +408,14 @@ __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16
         const bool full = valid == 4;
         float4 v = *reinterpret_cast<const float4*>(tile + row * E::kLd + c);
         v.x *= p.alpha; v.y *= p.alpha; v.z *= p.alpha; v.w *= p.alpha;
-        const float4 a1 = cin1 ? load4(cin1 + (int64_t)gr * p.ldcin1 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 a1, a2;
+        if constexpr (Pre::kOn) {
+            a1 = pre.a1[u0 / kThreads];
+            a2 = pre.a2[u0 / kThreads];
+        } else {
+            a1 = cin1 ? load4(cin1 + (int64_t)gr * p.ldcin1 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+            a2 = cin2 ? load4(cin2 + (int64_t)gr * p.ldcin2 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         if constexpr (TWO) {   // mode 2: C = v + beta1 Cin1, C2 = v + w + beta2 Cin1
             float4 w = *reinterpret_cast<const float4*>(tile2 + row * E::kLd + c);
             w.x *= p.alpha; w.y *= p.alpha; w.z *= p.alpha; w.w *= p.alpha;
@@ -402,7 +444,6 @@ __device__ __forceinline__ void general_epilogue(const PipeArgs& p, const f32x16
                    full, valid);
             continue;
         }
-        const float4 a2 = cin2 ? load4(cin2 + (int64_t)gr * p.ldcin2 + gc, vec, full, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 o = make_float4(v.x + p.beta1 * a1.x + p.beta2 * a2.x, v.y + p.beta1 * a1.y + p.beta2 * a2.y,
                                v.z + p.beta1 * a1.z + p.beta2 * a2.z, v.w + p.beta1 * a1.w + p.beta2 * a2.w);
         if (p.gamma != 0.f) {
@@ -568,6 +609,8 @@ pipe_gemm_kernel(const PipeArgs p) {
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
     f32x16_t acc[MI][NJ], acc2[MI][NJ];
+    EpiAddends<BM, BN, G::kThreads> pre;
+    if constexpr (EPI == kEpiGeneral && EpiAddends<BM, BN, G::kThreads>::kOn) load_addends(p, m0, n0, z, tid, pre);
     main_loop<G, A_MN, B_MN, S>(lds, A, p.lda, B, p.ldb, m0, n0, M, N, kb, ke, tid, acc);
     if constexpr (DUAL != 0) {
         const uint16_t* A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)z * p.strideA2;
@@ -586,7 +629,8 @@ pipe_gemm_kernel(const PipeArgs p) {
     if constexpr (EPI == kEpiGeneral) {
         static_assert((DUAL == 2 ? 2 : 1) * EpiTile<BM, BN>::kBytes <= S * kStageBytes,
                       "epilogue tile exceeds the LDS ring");
-        general_epilogue<G, OutT, DUAL == 2>(p, acc, acc2, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid);
+        general_epilogue<G, OutT, DUAL == 2>(p, acc, acc2, reinterpret_cast<float*>(lds), m0, n0, wm, wn, z, tid,
+                                             pre);
         return;
     }
     OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
