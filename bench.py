@@ -66,6 +66,27 @@ def gemm_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+FLUSH_BYTES = 512 << 20   # written before every "cold" launch, twice the last-level cache
+
+
+def _time_cold(fn, reps, flush):
+    """Mean microseconds of fn alone with the caches flushed before every launch
+    (a 512 MB write between launches; only the launch itself is timed)."""
+    import torch
+    fn()
+    tot = 0.0
+    for _ in range(reps):
+        flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b)
+    return tot / reps * 1e3
+
+
 def _time_events(fn, reps, warm=3):
     import torch
     for _ in range(warm):
@@ -206,6 +227,7 @@ def stage_timings(spec, S, reps):
         ("aux_adamw", lambda: B.poetx_adamw_step(q_opt, S["dq"], m_opt, v_opt, nblk * ntri, 1, opt_p), 0,
          28 * nblk * ntri),
     ]
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
         tf = flops / us / 1e6 if flops else None
@@ -216,6 +238,10 @@ def stage_timings(spec, S, reps):
         st[name] = {"us": round(us, 2), "tflops": round(tf, 1) if tf else None, "gbs": round(gbs, 1),
                     "bound": "mfma" if mfma else "hbm",
                     "frac": round((tf / PEAK_BF16_TFLOPS) if mfma else (gbs / PEAK_HBM_GBS), 4)}
+        if not mfma:   # the memory-bound stages also cold: nothing of theirs left in L2 / MALL
+            cold = _time_cold(fn, 5, flush)
+            st[name]["cold_us"] = round(cold, 2)
+            st[name]["cold_gbs"] = round(nbytes / cold / 1e3, 1)
         st[name]["_flops"] = flops
     return st
 
@@ -234,11 +260,20 @@ def cpu_baseline(spec, inp, budget_s=12.0, max_reps=3):
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    lib = f"{blas[0].get('internal_api', '?')} {blas[0].get('version', '')}".strip() if blas else "?"
+    cpu = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "?")
+    except OSError:
+        pass
     return {"value": round(spec.T * reps / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the full {spec.T}-token batch of the same layer, {reps} oracle step(s) "
                       f"(float64 numpy: Cayley-Neumann blocks, dense R W0 P forward, backward with block "
-                      f"gradients and parameter gradients) in {el:.1f} s"}
+                      f"gradients and parameter gradients) in {el:.1f} s",
+            "cpu": cpu, "blas": lib}
 
 
 def read_traffic():
@@ -291,19 +326,25 @@ def _products(k):
     return {3: 2, 4: 3}.get(k, k), {3: 4, 4: 7}.get(k, 3 * k - 1)
 
 
-def _time_steps(step, steps, warmup):
+def _time_steps(step, steps, warmup, per_step=None):
+    """Mean ms per step over exactly `steps` steps after `warmup` untimed ones,
+    bracketed by device synchronisation.  With a dict `per_step`, events between
+    the steps (same stream, no synchronisation) also give the median and minimum."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    if per_step is not None:
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        per_step["median"] = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+        per_step["min"] = t[0]
+    return ev[0].elapsed_time(ev[steps]) / steps
 
 
 def vendor_reference(spec, S, cs, cd, reps=20):
@@ -356,7 +397,8 @@ def run_linear(args, spec, label):
     cd = torch.empty_like(cs)
     cd.copy_(cs)
 
-    ms = _time_steps(step, args.steps, args.warmup)
+    per = {}
+    ms = _time_steps(step, args.steps, args.warmup, per)
     tok_s = spec.T / (ms / 1e3)
 
     st = stage_timings(spec, S, args.stage_reps)
@@ -384,6 +426,8 @@ def run_linear(args, spec, label):
                 + (f", every Q block at spectral norm {spec.q_block_norm}" if spec.q_block_norm else "")
                 + "; step = cnp_fwd_save + linear_fwd + linear_bwd + cnp_bwd_saved")
     out = _base_line(args, tok_s, "tokens/s", ms, workload, spec.T)
+    out["ms_per_step_median"] = round(per["median"], 4)
+    out["ms_per_step_min"] = round(per["min"], 4)
     out.update({
         "gemm_pct_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(gemm_tflops, 1),
@@ -432,7 +476,8 @@ def run_layer(args, specs, label, merge):
             B.poetx_linear_bwd(S["desc"], S["dy"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"],
                                S["saved"], S["dx"], S["dG_R"], S["dG_P"], S["ws"])
         B.poetx_cnp_bwd_saved(q_all, dG_all, nall, b, k, dq_all, B.POETX_BF16, cnp_saved, cnp_ws)
-    ms = _time_steps(step, args.steps, args.warmup)
+    per = {}
+    ms = _time_steps(step, args.steps, args.warmup, per)
     T = specs[0].T
     g_flops = 0
     for sp in specs:
@@ -443,6 +488,8 @@ def run_layer(args, specs, label, merge):
                      f"{label}: all 7 linears of one decoder layer, b=256, k=3, mem variant, "
                      f"{T // 2048} x 2048 tokens; step = cnp_fwd_save over the layer's {nall} blocks + 7 x "
                      "linear_fwd + 7 x linear_bwd + cnp_bwd_saved over the same blocks", T)
+    out["ms_per_step_median"] = round(per["median"], 4)
+    out["ms_per_step_min"] = round(per["min"], 4)
     out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
     out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
