@@ -400,6 +400,17 @@ def run_linear(args, spec, label):
     per = {}
     ms = _time_steps(step, args.steps, args.warmup, per)
     tok_s = spec.T / (ms / 1e3)
+    # the same step captured in a HIP graph (the library allocates nothing and
+    # records no memset nodes): its replays, timed the same way, as context
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    ms_graph = _time_steps(graph.replay, args.steps, args.warmup)
 
     st = stage_timings(spec, S, args.stage_reps)
     gemm_names = [nm for nm in st if nm.startswith(("blk", "dense", "grad"))]
@@ -428,6 +439,7 @@ def run_linear(args, spec, label):
     out = _base_line(args, tok_s, "tokens/s", ms, workload, spec.T)
     out["ms_per_step_median"] = round(per["median"], 4)
     out["ms_per_step_min"] = round(per["min"], 4)
+    out["ms_per_step_graph"] = round(ms_graph, 4)
     out.update({
         "gemm_pct_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(gemm_tflops, 1),
