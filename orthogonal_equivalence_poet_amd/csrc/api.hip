@@ -332,6 +332,7 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         dGc = B.dGc;
     }
     float* dQ = B.g32;
+    bool packed = false;   // dq already written by the last product pair
     const bool dual = cbf16 && b % 64 == 0 && pipe_gemm_supported(false, false, b, b, b, b, b, bb, bb) &&
                       pipe_gemm_supported(true, true, b, b, b, b, b, bb, bb);
     if (k == 3 && dual) {
@@ -361,7 +362,9 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         e.M = e.N = e.K = ib;
         e.batch = (int)nblk;
         e.k_per_split = ib;
-        HIP_TRY(pipe_gemm_dual(false, true, e, s));
+        // the skew pack rides on the second launch (mirrored tile pairs)
+        HIP_TRY(cnp_pack_pair(e, dq, ib, s));
+        packed = true;
     } else if (k == 3) {
         // G = A B with A = I + T, B = I + S (T = 2Q + S, S symmetric):
         // dA = dG + dG S ;  dS = dA + dB with dB = dG + T^T dG ;  dQ = 2 dA + dS Q^T + Q^T dS
@@ -414,7 +417,8 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
             e.M = e.N = e.K = ib;
             e.batch = (int)nblk;
             e.k_per_split = ib;
-            HIP_TRY(pipe_gemm_dual(false, true, e, s));
+            HIP_TRY(cnp_pack_pair(e, dq, ib, s));
+            packed = true;
         } else {
             // dP1 = dE + dE S ; dS = P1^T dE + dP1
             HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dEc, b), sq(B.Sc, b), B.e32, b, bb, s, 1.f,
@@ -455,7 +459,7 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         // D_1 = Q: acc += dD_1
         HIP_TRY(combine(nblk, ib, acc, 1.f, dD32[cur], 1.f, nullptr, 0, 0, dQ, nullptr, false, s));
     }
-    HIP_TRY(skew_pack(dQ, dq, nblk, ib, s));
+    if (!packed) HIP_TRY(skew_pack(dQ, dq, nblk, ib, s));
     return POETX_OK;
 }
 

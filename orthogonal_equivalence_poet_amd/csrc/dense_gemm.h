@@ -70,6 +70,13 @@ hipError_t pipe_gemm_general(bool a_mn, bool b_mn, bool out_f32, const PipeArgs&
 hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p, hipStream_t stream);
 int pipe_tile_cols(PipeTile t);
 
+// The last product pair of the Cayley-Neumann backward with the skew pack
+// folded in, for b x b blocks with b % 64 == 0 (M = N = K = b, A and B k-major,
+// A2 and B2 m/n-major, no C outputs): with dQ = alpha (A B^T + A2^T B2) +
+// beta1 Cin1 + beta2 Cin2, writes dq [batch, b(b-1)/2] with
+// dq[idx(r, c)] = dQ[r][c] - dQ[c][r] for r < c (row-major upper triangle).
+hipError_t cnp_pack_pair(const PipeArgs& p, float* dq, int b, hipStream_t stream);
+
 // Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
 // kernel): packed float32 parameters q [nblk, b(b-1)/2] -> G bf16 [nblk, b, b];
 // with Qc given also Q in bf16, with S and T given (k >= 2) also S = Q Q and

@@ -658,6 +658,85 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
+// The last product pair of the Cayley-Neumann backward with the skew pack
+// folded in: dQ = A B^T + A2^T B2 + beta1 Cin1 + beta2 Cin2 over b x b blocks,
+// and dq[idx(r, c)] = dQ[r][c] - dQ[c][r] (r < c) written straight from the
+// workgroup.  A workgroup owns a mirrored pair of 64 x 64 tiles (I, J) and
+// (J, I), I <= J, one per group of four waves (a diagonal pair computes its
+// tile twice, so that both groups pass the same barriers); the two dQ tiles
+// meet in LDS and only the packed upper triangle leaves the chip.  dQ values
+// are formed exactly as the general epilogue forms them, so dq matches the
+// unfused product + pack bit for bit.
+__device__ __forceinline__ int64_t upper_index(int r, int c, int b) {
+    return (int64_t)r * b - (int64_t)r * (r + 1) / 2 + (c - r - 1);
+}
+
+template <int S>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 4)))
+cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
+    using G = Geo<64, 64, 2, 2>;
+    constexpr int kRing = S * G::kStageBytes;
+    constexpr int kLd = 68;                      // floats per staged row
+    static_assert(64 * kLd * 4 <= kRing, "staged tile exceeds a group's ring");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kRing];
+    const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
+    const int lane = tid & 63, w4 = (tid >> 6) & 3;
+    const int wm = w4 >> 1, wn = w4 & 1;
+    const int nt = b / 64;
+    int ti = 0, t = blockIdx.x;
+    while (t >= nt - ti) {
+        t -= nt - ti;
+        ++ti;
+    }
+    const int tj = ti + t;
+    const int z = blockIdx.y;
+    // group 0: tile (ti, tj); group 1: tile (tj, ti)
+    const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
+    const uint16_t* A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)z * p.strideA2;
+    const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)z * p.strideB2;
+    unsigned char* ring = lds + grp * kRing;
+    EpiAddends<64, 64, 256> pre;
+    load_addends(p, m0, n0, z, gtid, pre);
+    f32x16_t acc[1][1];
+    main_loop<G, false, false, S>(ring, A, p.lda, B, p.ldb, m0, n0, b, b, 0, b, gtid, acc);
+    block_barrier();   // the second product reuses the LDS ring
+    main_loop<G, true, true, S>(ring, A2, p.lda2, B2, p.ldb2, m0, n0, b, b, 0, b, gtid, acc, false);
+    block_barrier();   // every wave is done reading the operand stages
+    float* tile = reinterpret_cast<float*>(ring);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = wn * 32 + (lane & 31);
+        tile[row * kLd + col] = acc[0][0][r];
+    }
+    __syncthreads();
+    // dQ = alpha acc + beta1 Cin1 + beta2 Cin2, in place, as the general epilogue forms it
+#pragma unroll
+    for (int k = 0; k < EpiAddends<64, 64, 256>::kPer; ++k) {
+        const int u = k * 256 + gtid;
+        const int row = u / 16, c = (u % 16) * 4;
+        float4 v = *reinterpret_cast<const float4*>(tile + row * kLd + c);
+        v.x *= p.alpha; v.y *= p.alpha; v.z *= p.alpha; v.w *= p.alpha;
+        const float4 a1 = pre.a1[k], a2 = pre.a2[k];
+        const float4 o = make_float4(v.x + p.beta1 * a1.x + p.beta2 * a2.x, v.y + p.beta1 * a1.y + p.beta2 * a2.y,
+                                     v.z + p.beta1 * a1.z + p.beta2 * a2.z, v.w + p.beta1 * a1.w + p.beta2 * a2.w);
+        *reinterpret_cast<float4*>(tile + row * kLd + c) = o;
+    }
+    __syncthreads();
+    const float* t0 = reinterpret_cast<const float*>(lds);
+    const float* t1 = ti == tj ? t0 : reinterpret_cast<const float*>(lds + kRing);
+    float* out = dq + (int64_t)z * ((int64_t)b * (b - 1) / 2);
+#pragma unroll
+    for (int k = 0; k < 64 * 64 / 512; ++k) {
+        const int u = k * 512 + tid;
+        const int rl = u >> 6, cl = u & 63;
+        const int r = 64 * ti + rl, c = 64 * tj + cl;
+        if (r < c) out[upper_index(r, c, b)] = t0[rl * kLd + cl] - t1[cl * kLd + rl];
+    }
+}
+
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
           int DUAL = 0>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
@@ -1201,6 +1280,38 @@ hipError_t pipe_gemm_dual(bool separate, bool out_f32, const PipeArgs& p_in, hip
                        : launch<64, 64, false, false, false, kEpiGeneral, 2, 2, 2, 1>(p, stream);
     return out_f32 ? launch<64, 64, false, false, true, kEpiGeneral, 3, 2, 2, 1>(p, stream)
                    : launch<64, 64, false, false, false, kEpiGeneral, 3, 2, 2, 1>(p, stream);
+}
+
+hipError_t cnp_pack_pair(const PipeArgs& p_in, float* dq, int b, hipStream_t stream) {
+    if (p_in.batch <= 0) return hipSuccess;
+    if (b % 64 != 0 || !p_in.A2 || !p_in.B2 || p_in.M != b || p_in.N != b || p_in.K != b)
+        return hipErrorInvalidValue;
+    PipeArgs p = p_in;
+    auto al = [](const void* ptr, int64_t ld, int64_t stride) {
+        return ptr == nullptr || (((uintptr_t)ptr % 16) == 0 && ld % 4 == 0 && stride % 4 == 0);
+    };
+    p.epi_vec = al(p.Cin1, p.ldcin1, p.strideCin1) && al(p.Cin2, p.ldcin2, p.strideCin2);
+    const int nt = b / 64;
+    const int64_t ntri = (int64_t)b * (b - 1) / 2;
+    constexpr int kMaxY = 65535;
+    for (int y0 = 0; y0 < p_in.batch; y0 += kMaxY) {
+        PipeArgs q = p;
+        q.batch = min(kMaxY, p_in.batch - y0);
+        q.A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)y0 * p.strideA;
+        q.B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)y0 * p.strideB;
+        q.A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)y0 * p.strideA2;
+        q.B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)y0 * p.strideB2;
+        if (p.Cin1) q.Cin1 = p.Cin1 + (int64_t)y0 * p.strideCin1;
+        if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
+        const dim3 grid(nt * (nt + 1) / 2, q.batch);
+        if (b <= 256)
+            hipLaunchKernelGGL(cnp_pack_pair_kernel<2>, grid, dim3(512), 0, stream, q, dq + (int64_t)y0 * ntri, b);
+        else
+            hipLaunchKernelGGL(cnp_pack_pair_kernel<3>, grid, dim3(512), 0, stream, q, dq + (int64_t)y0 * ntri, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 int pipe_tile_rows(PipeTile t) {
