@@ -156,10 +156,12 @@ def test_cnp_bwd_parity(b, k, dtype, std, norm):
 # bf16 blocks of 128 or 256 take the fused per-panel forward (32-row panels for
 # a few blocks, as in the cases above; 64-row panels once there are 256 or more
 # of those); here many blocks, a sample of which is checked against the oracle.
-@pytest.mark.parametrize("b,k,std,norm", [(256, 3, 1e-3, None), (256, 1, 0.05, None), (256, 4, 1e-2, 0.5),
-                                          (256, 7, 1e-2, 0.6), (128, 3, 0.05, None), (128, 2, 1e-2, 0.5)])
-def test_cnp_fused_forward_many_blocks(b, k, std, norm):
-    nblk = 1024 * 64 // b
+@pytest.mark.parametrize("b,k,std,norm,nblk", [(256, 3, 1e-3, None, 256), (256, 1, 0.05, None, 256),
+                                               (256, 4, 1e-2, 0.5, 256), (256, 7, 1e-2, 0.6, 256),
+                                               (128, 3, 0.05, None, 512), (128, 2, 1e-2, 0.5, 512),
+                                               (256, 3, 1e-3, None, 1024), (256, 4, 1e-2, 0.5, 1100)])
+def test_cnp_fused_forward_many_blocks(b, k, std, norm, nblk):
+    # from 1024 blocks of 256 one workgroup runs all panels of a block
     q = _q(nblk, b, std, 500 + b + k)
     js = [0, 1, nblk // 2, nblk - 1]
     if norm is not None:
@@ -169,7 +171,8 @@ def test_cnp_fused_forward_many_blocks(b, k, std, norm):
     assert rel_fro(G, ref) <= tol("bf16")
 
 
-@pytest.mark.parametrize("b,k,dtype,nblk", [(256, 3, "bf16", 6), (256, 3, "bf16", 256), (128, 3, "bf16", 512),
+@pytest.mark.parametrize("b,k,dtype,nblk", [(256, 3, "bf16", 6), (256, 3, "bf16", 256), (256, 3, "bf16", 1030),
+                                            (128, 3, "bf16", 512),
                                             (64, 3, "f32", 6), (128, 4, "bf16", 6), (128, 4, "bf16", 512),
                                             (64, 5, "bf16", 6), (16, 2, "f32", 6), (64, 4, "f32", 6),
                                             (512, 4, "bf16", 36)])
