@@ -976,10 +976,7 @@ __device__ __forceinline__ uint4 img_frag(const unsigned char* __restrict__ tile
 
 typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
 
-// ALLP: one workgroup per block runs every panel of it in turn (the Q image is
-// built once per block instead of once per panel; the stores of a panel drain
-// while the next one computes), for batches with several blocks per CU.
-template <int B, int PH, bool ALLP = false>
+template <int B, int PH>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, B == 256 ? 1 : 2)))
 cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t* __restrict__ Qc,
                  uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv, int k, int total) {
@@ -991,10 +988,10 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int id = blockIdx.x;
     if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
-    const int z = ALLP ? id : id / F::NP;
-    const int p_first = ALLP ? 0 : id - z * F::NP;
+    const int z = id / F::NP, p = id - z * F::NP;
     const int64_t zoff = (int64_t)z * B * B;
     const float* __restrict__ qz = q + (int64_t)z * F::NPAR;
+    const int r0 = PH * p;   // first row of the panel
 
     // 1. the Q image.  Tasks: the strict upper sub-blocks (sub-rows R' and
     // NB8 - 2 - R' sharing a run of NB8 tasks), then the diagonal ones; every
@@ -1066,9 +1063,6 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
         }
     }
     __syncthreads();
-
-  for (int p = p_first; p < (ALLP ? F::NP : p_first + 1); ++p) {
-    const int r0 = PH * p;   // first row of the panel
 
     // rows of an image as 16-byte chunks: PH rows x B/8 chunks over the workgroup
     auto copy_rows = [&](uint16_t* __restrict__ dst, auto chunk_value) {
@@ -1185,7 +1179,6 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
             }
     __syncthreads();
     copy_rows(G, [&](int m, int c) { return *reinterpret_cast<const uint4*>(xs + img_off<XB>(m, c)); });
-  }
 }
 
 }  // namespace
@@ -1356,21 +1349,16 @@ hipError_t cnp_fused_fwd(const float* q, void* G, void* Qc, void* S, void* T, in
                          hipStream_t stream) {
     if (nblk <= 0) return hipSuccess;
     if (!cnp_fused_supported(b, k) || ((S == nullptr) != (T == nullptr)) || (S && k < 2)) return hipErrorInvalidValue;
-    // 64-row panels, or 32-row ones while 64-row panels would not give every CU one;
-    // with four or more blocks per CU one workgroup runs all panels of a block
+    // 64-row panels, or 32-row ones while 64-row panels would not give every CU one
     const bool tall = nblk * (b / 64) >= 256;
-    const bool allp = b == 256 && nblk >= 1024;
-    const int64_t panels = allp ? nblk : nblk * (b / (tall ? 64 : 32));
+    const int64_t panels = nblk * (b / (tall ? 64 : 32));
     if (panels > 0x7fffffff) return hipErrorInvalidValue;
     const auto g = static_cast<uint16_t*>(G);
     const auto qc = static_cast<uint16_t*>(Qc);
     const auto sv = static_cast<uint16_t*>(S);
     const auto tv = static_cast<uint16_t*>(T);
     const dim3 grid((unsigned)panels);
-    if (allp)
-        hipLaunchKernelGGL((cnp_fused_kernel<256, 64, true>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k,
-                           (int)panels);
-    else if (b == 256 && tall)
+    if (b == 256 && tall)
         hipLaunchKernelGGL((cnp_fused_kernel<256, 64>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     else if (b == 256)
         hipLaunchKernelGGL((cnp_fused_kernel<256, 32>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);

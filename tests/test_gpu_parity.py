@@ -161,7 +161,7 @@ def test_cnp_bwd_parity(b, k, dtype, std, norm):
                                                (128, 3, 0.05, None, 512), (128, 2, 1e-2, 0.5, 512),
                                                (256, 3, 1e-3, None, 1024), (256, 4, 1e-2, 0.5, 1100)])
 def test_cnp_fused_forward_many_blocks(b, k, std, norm, nblk):
-    # from 1024 blocks of 256 one workgroup runs all panels of a block
+    # 64-row panels at many blocks, including ragged block counts
     q = _q(nblk, b, std, 500 + b + k)
     js = [0, 1, nblk // 2, nblk - 1]
     if norm is not None:
