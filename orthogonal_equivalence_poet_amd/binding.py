@@ -96,7 +96,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"libpoetx is not built ({path} missing); run __graft_entry__.build()")
+        raise RuntimeError(f"libpoetx is not built ({path} missing); run orthogonal_equivalence_poet_amd.build.build()")
     lib = C.CDLL(path)
     for name, (args, res) in _SIGS.items():
         fn = getattr(lib, name)
