@@ -154,3 +154,62 @@ def test_training_loop_parity(m, n, b, T, steps, merge_every):
     # q has moved since the last merge (steps % merge_every updates)
     assert np.abs(want[1]).max() > 0
     assert rel_fro(got[1], want[1]) < TOL and rel_fro(got[2], want[2]) < TOL
+
+
+# ------------------------------------------------ a layer's linears in one batch
+@pytest.mark.parametrize("dtype,variant", [("f32", B.POETX_FAST), ("bf16", B.POETX_MEM)])
+def test_layer_linears_share_one_cayley_neumann_batch(dtype, variant):
+    """Several linears of one layer (different shapes, same b and k) run their
+    Cayley-Neumann forward and backward as one flat batch of blocks, each
+    linear taking views into the flat q, G, dG and dq; every linear's outputs
+    match the oracle run on it alone."""
+    b, k, T = 64, 3, 80
+    shapes = [(256, 128), (64, 256), (192, 192)]
+    specs = [I.LinearSpec("layer", m=m, n=n, b=b, k=k, T=T, dtype=dtype, q_std=0.02, key=(14, i, m))
+             for i, (m, n) in enumerate(shapes)]
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    code = B.POETX_F32 if dtype == "f32" else B.POETX_BF16
+    nbs = [sp.nblk_R + sp.nblk_P for sp in specs]
+    nall = sum(nbs)
+    q_all = torch.cat([torch.cat([dev(inp["q_R"]), dev(inp["q_P"])]) for inp in inps]).contiguous()
+    G_all = torch.empty((nall, b, b), dtype=td, device=DEV)
+    dG_all = torch.empty((nall, b, b), dtype=torch.float32, device=DEV)
+    dq_all = torch.empty_like(q_all)
+    cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nall, b, k, code))
+    cnp_ws = B.workspace(max(B.poetx_cnp_fwd_workspace_bytes(nall, b, k, code),
+                             B.poetx_cnp_bwd_workspace_bytes(nall, b, k, code)))
+    st = []
+    o = 0
+    for sp, inp, nb in zip(specs, inps, nbs):
+        d = B.desc(T, sp.m, sp.n, b, k, code, variant)
+        S = {"d": d, "sp": sp, "x": dev(inp["x"], dtype), "dy": dev(inp["dy"], dtype),
+             "pi_R": dev_i32(inp["pi_R"]), "pi_P": dev_i32(inp["pi_P"]),
+             "G_R": G_all[o:o + sp.nblk_R], "G_P": G_all[o + sp.nblk_R:o + nb],
+             "dG_R": dG_all[o:o + sp.nblk_R], "dG_P": dG_all[o + sp.nblk_R:o + nb],
+             "dq": dq_all[o:o + nb],
+             "y": torch.empty((T, sp.m), dtype=td, device=DEV), "dx": torch.empty((T, sp.n), dtype=td, device=DEV),
+             "saved": B.workspace(B.poetx_linear_saved_bytes(d)),
+             "ws": B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d), B.poetx_linear_bwd_workspace_bytes(d)))}
+        S["Wt"] = torch.empty((sp.m, sp.n), dtype=td, device=DEV)
+        B.poetx_prepermute(dev(inp["W0"], dtype), S["Wt"], sp.m, sp.n, S["pi_R"], S["pi_P"])
+        st.append(S)
+        o += nb
+    B.poetx_cnp_fwd_save(q_all, nall, b, k, G_all, cnp_saved, cnp_ws)
+    for S in st:
+        B.poetx_linear_fwd(S["d"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], S["y"], S["saved"],
+                           S["ws"])
+    for S in reversed(st):
+        B.poetx_linear_bwd(S["d"], S["dy"], S["x"], S["Wt"], S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], S["saved"],
+                           S["dx"], S["dG_R"], S["dG_P"], S["ws"])
+    B.poetx_cnp_bwd_saved(q_all, dG_all, nall, b, k, dq_all, code, cnp_saved, cnp_ws)
+    torch.cuda.synchronize()
+    tolr = TOL if dtype == "f32" else 1.5e-2
+    for S, inp in zip(st, inps):
+        sp = S["sp"]
+        args = (inp["W0"], inp["q_R"], inp["q_P"], inp["pi_R"], inp["pi_P"], b, k)
+        y = O.forward(inp["x"], *args)
+        dx, dq_R, dq_P, _, _ = O.backward(inp["dy"], inp["x"], *args)
+        dq = host(S["dq"])
+        assert rel_fro(host(S["y"]), y) < tolr and rel_fro(host(S["dx"]), dx) < tolr
+        assert rel_fro(dq[:sp.nblk_R], dq_R) < tolr and rel_fro(dq[sp.nblk_R:], dq_P) < tolr
