@@ -1,4 +1,6 @@
 """libpoetx: the POET-X linear layer as hand-written gfx950 HIP kernels behind a
-C ABI (include/poetx.h).  ``binding`` is the ctypes layer; ``inputs`` draws the
-seeded synthetic workloads; ``layer`` drives one training step of a layer."""
-__all__ = ["binding", "inputs"]
+C ABI (include/poetx.h).  ``binding`` is the ctypes layer; ``layer`` wraps one
+linear as a torch module (POETLinear: autograd forward and backward, the
+library's AdamW step and merge-then-reinitialize); ``inputs`` draws the seeded
+synthetic workloads."""
+__all__ = ["binding", "inputs", "layer"]
