@@ -36,6 +36,39 @@ def _perm(d: int, generator: Optional[torch.Generator], device) -> torch.Tensor:
     return torch.randperm(d, generator=generator).to(device=device, dtype=torch.int32)
 
 
+class _CayleyNeumannFn(torch.autograd.Function):
+    """G = (I + Q) sum_{i<=k} Q^i for every block of q [nblk, b(b-1)/2]."""
+
+    @staticmethod
+    def forward(ctx, q, b, k, dtype):
+        nblk = q.shape[0]
+        code = _code(dtype)
+        q = q.detach().contiguous()
+        G = torch.empty((nblk, b, b), dtype=dtype, device=q.device)
+        ws = B.workspace(max(B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code),
+                             B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, code)), q.device)
+        saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), q.device)
+        B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
+        ctx.stash = (q, b, k, code, saved, ws)
+        return G
+
+    @staticmethod
+    def backward(ctx, dG):
+        q, b, k, code, saved, ws = ctx.stash
+        dq = torch.empty_like(q)
+        B.poetx_cnp_bwd_saved(q, dG.float().contiguous(), q.shape[0], b, k, dq, code, saved, ws)
+        ctx.stash = None
+        return dq, None, None, None
+
+
+def cayley_neumann(q: torch.Tensor, b: int, k: int = 3, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """The orthogonal blocks of the compact parameters q [nblk, b(b-1)/2] (float32,
+    on a GPU): G [nblk, b, b] in `dtype`, differentiable with respect to q.  The
+    review's Summary names the fused Cayley-Neumann transform as a separate
+    operator; this is that operator over any number of blocks."""
+    return _CayleyNeumannFn.apply(q, int(b), int(k), dtype)
+
+
 class _PoetLinearFn(torch.autograd.Function):
     """y = R W0 P x for x [T, n]; gradients for x, q_R and q_P (none for W0)."""
 

@@ -88,3 +88,19 @@ def test_module_training_loop_matches_oracle():
     assert rel_fro(host(lay.Wt), Wt) < 1e-5
     assert np.abs(q_R).max() > 0
     assert rel_fro(host(lay.q_R), q_R) < 1e-5 and rel_fro(host(lay.q_P), q_P) < 1e-5
+
+
+@pytest.mark.parametrize("b,k,dtype", [(64, 3, torch.float32), (256, 3, torch.bfloat16), (128, 4, torch.bfloat16)])
+def test_cayley_neumann_operator(b, k, dtype):
+    from orthogonal_equivalence_poet_amd.layer import cayley_neumann
+    nblk = 6
+    q_np = I.gaussian((nblk, b * (b - 1) // 2), 0.02, "f32", 23, b, k)
+    dG_np = I.gaussian((nblk, b, b), 1.0, "f32", 24, b, k)
+    q = torch.from_numpy(q_np).to(DEV).requires_grad_(True)
+    G = cayley_neumann(q, b, k, dtype)
+    (G.float() * torch.from_numpy(dG_np).to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == torch.float32 else 1.5e-2
+    assert rel_fro(host(G), O.blocks_from_params(q_np, b, k)) < tol
+    ref = O.params_grad_from_skew_grad(O.cnp_vjp(O.skew_from_params(q_np, b), dG_np, k))
+    assert rel_fro(host(q.grad), ref) < tol
