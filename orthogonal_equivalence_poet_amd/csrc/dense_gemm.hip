@@ -572,11 +572,15 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
                 enter(kt + 1, st_next);
                 load_frags<G, A_MN, B_MN>(lds + st_next * kStageBytes, wm, wn, 0, lane, af[cur ^ 1], bfr[cur ^ 1]);
             }
+            // The MFMAs run at raised wave priority, so the arbiter favours the
+            // waves that keep the matrix cores busy over those issuing loads.
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < G::MI; ++i)
 #pragma unroll
                 for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
         st = st_next;
