@@ -21,7 +21,9 @@ configuration), the aggregate MFMA efficiency of the block and dense GEMMs,
 the roofline of the dominant kernel (the dense Wt GEMM), the float64 oracle
 timed on the host cores as a baseline, and, as context outside the timed step,
 the vendor library (torch.matmul, i.e. hipBLASLt) on the same dense shapes and a
-plain device copy (`vendor_reference`).
+plain device copy (`vendor_reference`), and the same step with every variant
+of the linear (`variants`: fast, mem, all four permutations on the
+activations, and the original weight-centric POET with dense R and P).
 
   --pmc-dir DIR   parse a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run of this
                   script and record the dense GEMM's HBM traffic in
@@ -379,6 +381,37 @@ def vendor_reference(spec, S, cs, cd, reps=20):
             "copy_bytes": 2 * COPY_BYTES, "copy_gbs": round(2 * COPY_BYTES / cp / 1e3, 1)}
 
 
+def variant_steps(spec, S, steps=10, warmup=5):
+    """Context, not the product path: the same step (transform forward, linear
+    forward and backward, transform backward) with every variant of the linear:
+    the fast and mem chains, the chain with all four permutations on the
+    activations, and the original weight-centric POET (dense R and P, W_RP
+    formed every step).  Mean ms per step over `steps` after `warmup`."""
+    from orthogonal_equivalence_poet_amd import binding as B
+    nblk = spec.nblk_R + spec.nblk_P
+    out = {}
+    for name, var in (("fast", B.POETX_FAST), ("mem", B.POETX_MEM), ("four_perm", B.POETX_FOUR_PERM),
+                      ("weight_centric", B.POETX_WEIGHT_CENTRIC)):
+        d = B.desc(spec.T, spec.m, spec.n, spec.b, spec.k, B.POETX_BF16, var)
+        weight = S["Wt"] if var in (B.POETX_FAST, B.POETX_MEM) else S["W0"]
+        saved = B.workspace(B.poetx_linear_saved_bytes(d)) if var != B.POETX_MEM else None
+        ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d), B.poetx_linear_bwd_workspace_bytes(d),
+                             B.poetx_cnp_fwd_workspace_bytes(nblk, spec.b, spec.k, B.POETX_BF16),
+                             B.poetx_cnp_bwd_workspace_bytes(nblk, spec.b, spec.k, B.POETX_BF16)))
+
+        def step():
+            B.poetx_cnp_fwd_save(S["q"], nblk, spec.b, spec.k, S["G"], S["cnp_saved"], ws)
+            B.poetx_linear_fwd(d, S["x"], weight, S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], S["y"], saved, ws)
+            B.poetx_linear_bwd(d, S["dy"], S["x"], weight, S["G_R"], S["G_P"], S["pi_R"], S["pi_P"], saved,
+                               S["dx"], S["dG_R"], S["dG_P"], ws)
+            B.poetx_cnp_bwd_saved(S["q"], S["dG"], nblk, spec.b, spec.k, S["dq"], B.POETX_BF16, S["cnp_saved"],
+                                  ws)
+        out[f"{name}_ms"] = round(_time_steps(step, steps, warmup), 4)
+    out["weight_centric_over_fast"] = round(out["weight_centric_ms"] / out["fast_ms"], 2)
+    out["four_perm_over_fast"] = round(out["four_perm_ms"] / out["fast_ms"], 3)
+    return out
+
+
 def _base_line(args, value, unit, ms, workload, T):
     return {"metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -448,6 +481,7 @@ def run_linear(args, spec, label):
         "roofline": roof,
     })
     out["vendor_reference"] = vendor_reference(spec, S, cs, cd)
+    out["variants"] = variant_steps(spec, S)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp)
     return out

@@ -71,8 +71,24 @@ enum { POETX_F32 = 0, POETX_BF16 = 1 };
 
 /* fast saves h2 (the dense product's output) and a (x gathered by pi_P) for
  * the backward; mem keeps only x and recomputes both (review Summary:
- * POET-X_fast / checkpointed POET-X_mem). */
-enum { POETX_FAST = 0, POETX_MEM = 1 };
+ * POET-X_fast / checkpointed POET-X_mem).
+ *
+ * Two comparison variants compute the same y, dx, dG_R and dG_P (to rounding)
+ * without one of the reformulations, for measuring what that reformulation
+ * buys (review Summary, "permutation reduction" and the original weight-centric
+ * POET; Reproducibility & code, the original-POET single-layer timing and the
+ * 4-permute against 2-permute comparison):
+ *   four_perm:       the fast chain over W0 itself, applying all four
+ *                    permutations to the activations (two gathers and two
+ *                    scatters each way) instead of absorbing two into Wt;
+ *   weight_centric:  the original POET: R and P are built as dense m x m and
+ *                    n x n matrices, W_RP = R (W0 P) is formed and y = x W_RP^T;
+ *                    the backward forms dW_RP = dy^T x and takes
+ *                    dR = dW_RP (W0 P)^T and dP = W0^T (R^T dW_RP) from it.
+ * With either of them the weight argument of poetx_linear_fwd / _bwd is W0
+ * [m, n] itself, not the pre-permuted Wt, and poetx_merge does not apply
+ * (POETX_ERR_UNSUPPORTED). */
+enum { POETX_FAST = 0, POETX_MEM = 1, POETX_FOUR_PERM = 2, POETX_WEIGHT_CENTRIC = 3 };
 
 typedef struct poetx_linear_desc {
     int64_t T;       /* tokens (rows of x and y), >= 0 */
@@ -81,7 +97,7 @@ typedef struct poetx_linear_desc {
     int64_t b;       /* block size of R and P */
     int32_t k;       /* Neumann order (highest power of Q kept) */
     int32_t dtype;   /* POETX_F32 or POETX_BF16 */
-    int32_t variant; /* POETX_FAST or POETX_MEM */
+    int32_t variant; /* POETX_FAST, POETX_MEM, POETX_FOUR_PERM or POETX_WEIGHT_CENTRIC */
     int32_t reserved;/* must be 0 */
 } poetx_linear_desc;
 
@@ -170,7 +186,9 @@ int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size
  * [n/b, b, b]; y: dtype [T, m].  FAST writes h2 (dtype [T, m]) and a (dtype
  * [T, n], at the next 256-byte boundary after h2) to `saved`, which must hold
  * poetx_linear_saved_bytes(d) bytes; MEM writes nothing there (saved may be
- * NULL). */
+ * NULL).  FOUR_PERM saves the same two tensors (h2 here is the dense product's
+ * output gathered by pi_R).  WEIGHT_CENTRIC saves the dense R (dtype [m, m]),
+ * W0 P and W_RP (dtype [m, n] each), each at a 256-byte boundary. */
 size_t poetx_linear_saved_bytes(const poetx_linear_desc* d);
 size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d);
 int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
@@ -182,9 +200,9 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
  *   dx  = dy R W0 P                              dtype [T, n]
  *   dG_R[j] = (Pi_R dR Pi_R^T) block j, dR = dy^T x P^T W0^T     float32 [m/b, b, b]
  *   dG_P[j] = (Pi_P dP Pi_P^T) block j, dP = W0^T R^T dy^T x     float32 [n/b, b, b]
- * FAST reads h2 and a from `saved` (written by poetx_linear_fwd with the
- * same inputs); MEM recomputes both from x.  Feed dG_R / dG_P to poetx_cnp_bwd to
- * obtain dq_R / dq_P.  T == 0 writes zero block gradients. */
+ * FAST, FOUR_PERM and WEIGHT_CENTRIC read what poetx_linear_fwd saved for the
+ * same inputs; MEM recomputes h2 and a from x.  Feed dG_R / dG_P to poetx_cnp_bwd
+ * to obtain dq_R / dq_P.  T == 0 writes zero block gradients. */
 size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d);
 int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,
                      const void* Wt, const void* G_R, const void* G_P, const int32_t* pi_R,
@@ -200,7 +218,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,
  * Wt is updated in place (dtype [m, n]); the caller draws pi_new (no RNG in
  * the library) and uses it from then on.  Passing pi_new == pi_old gives a
  * pure fold; with q == 0 as well the call leaves Wt bit-identical.
- * d->T and d->variant are ignored. */
+ * d->T is ignored; d->variant must be POETX_FAST or POETX_MEM (the stored
+ * weight of the other two is W0 itself; POETX_ERR_UNSUPPORTED). */
 size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d);
 int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P,
                 const int32_t* pi_R_old, const int32_t* pi_P_old, const int32_t* pi_R_new,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpoetx.so")
 
 POETX_OK, POETX_ERR_INVALID_ARG, POETX_ERR_SHAPE, POETX_ERR_UNSUPPORTED, POETX_ERR_WORKSPACE, POETX_ERR_HIP = range(6)
 POETX_F32, POETX_BF16 = 0, 1
-POETX_FAST, POETX_MEM = 0, 1
+POETX_FAST, POETX_MEM, POETX_FOUR_PERM, POETX_WEIGHT_CENTRIC = 0, 1, 2, 3
 POETX_GEMM_NT, POETX_GEMM_NN, POETX_GEMM_TN = 0, 1, 2
 
 EXPORTS = [

@@ -71,7 +71,7 @@ int check_nblk(int64_t nblk, int64_t b) {
 
 int check_desc(const poetx_linear_desc* d) {
     if (!d) return POETX_ERR_INVALID_ARG;
-    if (!dtype_ok(d->dtype) || (d->variant != POETX_FAST && d->variant != POETX_MEM) || d->reserved != 0)
+    if (!dtype_ok(d->dtype) || d->variant < POETX_FAST || d->variant > POETX_WEIGHT_CENTRIC || d->reserved != 0)
         return POETX_ERR_INVALID_ARG;
     POETX_TRY(check_block(d->b));
     POETX_TRY(check_k(d->k));
@@ -600,6 +600,139 @@ size_t fast_saved_a_offset(const poetx_linear_desc* d) {
     return (esize(d->dtype) * (size_t)(d->T * d->m) + 255) & ~size_t(255);
 }
 
+// ------------------------------------------------- four-permutation chain
+// The chain over W0 itself, all four permutations applied to the activations:
+// y_t = Pi_R^T D_R Pi_R W0 Pi_P^T D_P Pi_P x_t.
+int four_perm_forward(const poetx_linear_desc* d, const void* x, const void* W0, const void* G_R, const void* G_P,
+                      const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2g, void* a, void* buf0, void* buf1,
+                      hipStream_t s) {
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, m = d->m, n = d->n, b = d->b;
+    // a = Pi_P x;  h1 = D_P a;  Pi_P^T h1
+    HIP_TRY(permute_2d(x, a, bf, T, n, nullptr, pi_P, false, s));
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, a, G_P, buf1, s));
+    HIP_TRY(permute_2d(buf1, buf0, bf, T, n, nullptr, pi_P, true, s));
+    // h2 = W0 (Pi_P^T h1);  Pi_R h2 (saved)
+    HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, buf0, n, W0, n, buf1, m, s));
+    HIP_TRY(permute_2d(buf1, h2g, bf, T, m, nullptr, pi_R, false, s));
+    // z = D_R Pi_R h2;  y = Pi_R^T z
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, m, b, h2g, G_R, buf0, s));
+    HIP_TRY(permute_2d(buf0, y, bf, T, m, nullptr, pi_R, true, s));
+    return POETX_OK;
+}
+
+int four_perm_backward(const poetx_linear_desc* d, const void* dy, const void* W0, const void* G_R, const void* G_P,
+                       const int32_t* pi_R, const int32_t* pi_P, const void* h2g, const void* a, void* dx,
+                       float* dG_R, float* dG_P, const LinearBufs& L, hipStream_t s) {
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, m = d->m, n = d->n, b = d->b;
+    void* b1 = L.buf[1];
+    void* b2 = L.buf[2];
+    // dz = Pi_R dy;  dG_R[j] = dz_j^T (Pi_R h2)_j;  Pi_R^T (dz D_R)
+    HIP_TRY(permute_2d(dy, b1, bf, T, m, nullptr, pi_R, false, s));
+    POETX_TRY(block_grad(bf, T, m, b, b1, h2g, dG_R, L.splits_R, L.kps_R, L.part, s));
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, m, b, b1, G_R, b2, s));
+    HIP_TRY(permute_2d(b2, b1, bf, T, m, nullptr, pi_R, true, s));
+    // dh1 = Pi_P (dh2 W0);  dG_P[j] = dh1_j^T a_j;  dx = Pi_P^T (dh1 D_P)
+    HIP_TRY(dense_gemm(GemmLayout::NN, bf, T, n, m, b1, m, W0, n, b2, n, s));
+    HIP_TRY(permute_2d(b2, b1, bf, T, n, nullptr, pi_P, false, s));
+    POETX_TRY(block_grad(bf, T, n, b, b1, a, dG_P, L.splits_P, L.kps_P, L.part, s));
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, n, b, b1, G_P, b2, s));
+    HIP_TRY(permute_2d(b2, dx, bf, T, n, nullptr, pi_P, true, s));
+    return POETX_OK;
+}
+
+// --------------------------------------------------- weight-centric POET
+// The saved buffer: dense R [m, m], W0 P [m, n] and W_RP [m, n], each at a
+// 256-byte boundary.
+struct WcSaved {
+    void* R = nullptr;
+    void* WP = nullptr;
+    void* W = nullptr;
+};
+
+void plan_wc_saved(Carver& cv, const poetx_linear_desc* d, WcSaved& S) {
+    const size_t es = esize(d->dtype);
+    S.R = cv.take(es * (size_t)(d->m * d->m));
+    S.WP = cv.take(es * (size_t)(d->m * d->n));
+    S.W = cv.take(es * (size_t)(d->m * d->n));
+}
+
+// One dense product of the weight-centric path, of any layout and output type:
+// bf16 on the pipelined kernel where its operand rules allow (the largest tile
+// whose grid still gives every CU a workgroup), else the register-staged one.
+hipError_t wc_gemm(GemmLayout layout, bool bf, bool out_f32, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, hipStream_t s) {
+    const bool a_mn = layout == GemmLayout::TN, b_mn = layout != GemmLayout::NT;
+    if (bf && pipe_gemm_supported(a_mn, b_mn, M, N, K, lda, ldb, 0, 0)) {
+        if (!a_mn && !out_f32 && dense_gemm_supported(M, N, K, lda, ldb))
+            return dense_gemm_bf16(b_mn, A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, s);
+        PipeArgs p;
+        p.A = A; p.lda = lda;
+        p.B = B; p.ldb = ldb;
+        p.C = C; p.ldc = ldc;
+        p.M = (int)M; p.N = (int)N; p.K = (int)K;
+        p.k_per_split = (int)K;
+        const int64_t tall = ((M + 255) / 256) * ((N + 127) / 128);
+        return pipe_gemm(a_mn, b_mn, out_f32, p, s, tall >= 256 ? PipeTile::Tall : PipeTile::Square);
+    }
+    return gemm(layout, bf, bf && !out_f32, M, N, K, 1, Mat{A, lda, 0}, Mat{B, ldb, 0}, C, ldc, 0, s, 1.f, nullptr,
+                0, nullptr, 0, 0, nullptr, true);
+}
+
+// R = Pi_R^T diag(G_R) Pi_R and P likewise as dense matrices;  W_RP = R (W0 P);
+// y = x W_RP^T.
+int wc_forward(const poetx_linear_desc* d, const void* x, const void* W0, const void* G_R, const void* G_P,
+               const int32_t* pi_R, const int32_t* pi_P, void* y, const WcSaved& S, void* Pd, int32_t* inv_R,
+               int32_t* inv_P, hipStream_t s) {
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, m = d->m, n = d->n;
+    const int b = (int)d->b;
+    HIP_TRY(invert_perm(pi_R, inv_R, m, s));
+    HIP_TRY(invert_perm(pi_P, inv_P, n, s));
+    HIP_TRY(blockdiag_dense(G_R, inv_R, S.R, bf, m, b, s));
+    HIP_TRY(blockdiag_dense(G_P, inv_P, Pd, bf, n, b, s));
+    HIP_TRY(wc_gemm(GemmLayout::NN, bf, false, m, n, n, W0, n, Pd, n, S.WP, n, s));
+    HIP_TRY(wc_gemm(GemmLayout::NN, bf, false, m, n, m, S.R, m, S.WP, n, S.W, n, s));
+    HIP_TRY(wc_gemm(GemmLayout::NT, bf, false, T, m, n, x, n, S.W, n, y, m, s));
+    return POETX_OK;
+}
+
+// Backward buffers: dW_RP and R^T dW_RP (dtype [m, n]), dR (float32 [m, m]),
+// dP (float32 [n, n]).
+struct WcBufs {
+    void* dW = nullptr;
+    void* E = nullptr;
+    float* dR = nullptr;
+    float* dP = nullptr;
+};
+
+void plan_wc_bwd(Carver& cv, const poetx_linear_desc* d, WcBufs& B) {
+    const size_t es = esize(d->dtype);
+    B.dW = cv.take(es * (size_t)(d->m * d->n));
+    B.E = cv.take(es * (size_t)(d->m * d->n));
+    B.dR = cv.take_n<float>(d->m * d->m);
+    B.dP = cv.take_n<float>(d->n * d->n);
+}
+
+// dx = dy W_RP;  dW_RP = dy^T x;  dR = dW_RP (W0 P)^T;  dP = W0^T (R^T dW_RP);
+// dG = the diagonal blocks of Pi dR Pi^T and Pi_P dP Pi_P^T.
+int wc_backward(const poetx_linear_desc* d, const void* dy, const void* x, const void* W0, const int32_t* pi_R,
+                const int32_t* pi_P, const WcSaved& S, void* dx, float* dG_R, float* dG_P, const WcBufs& B,
+                hipStream_t s) {
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, m = d->m, n = d->n;
+    const int b = (int)d->b;
+    HIP_TRY(wc_gemm(GemmLayout::NN, bf, false, T, n, m, dy, m, S.W, n, dx, n, s));
+    HIP_TRY(wc_gemm(GemmLayout::TN, bf, false, m, n, T, dy, m, x, n, B.dW, n, s));
+    HIP_TRY(wc_gemm(GemmLayout::NT, bf, true, m, m, n, B.dW, n, S.WP, n, B.dR, m, s));
+    HIP_TRY(wc_gemm(GemmLayout::TN, bf, false, m, n, m, S.R, m, B.dW, n, B.E, n, s));
+    HIP_TRY(wc_gemm(GemmLayout::TN, bf, true, n, n, m, W0, n, B.E, n, B.dP, n, s));
+    HIP_TRY(blockdiag_gather(B.dR, pi_R, dG_R, m, b, s));
+    HIP_TRY(blockdiag_gather(B.dP, pi_P, dG_P, n, b, s));
+    return POETX_OK;
+}
+
 int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
                    hipStream_t s) {
@@ -789,13 +922,25 @@ int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size
 }
 
 size_t poetx_linear_saved_bytes(const poetx_linear_desc* d) {
-    if (check_desc(d) != POETX_OK || d->variant != POETX_FAST) return 0;
+    if (check_desc(d) != POETX_OK || d->variant == POETX_MEM) return 0;
+    if (d->variant == POETX_WEIGHT_CENTRIC) {
+        Carver cv(nullptr);
+        WcSaved S;
+        plan_wc_saved(cv, d, S);
+        return cv.off;
+    }
     return fast_saved_a_offset(d) + esize(d->dtype) * (size_t)(d->T * d->n);
 }
 
 size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
     if (check_desc(d) != POETX_OK) return 0;
     Carver cv(nullptr);
+    if (d->variant == POETX_WEIGHT_CENTRIC) {
+        cv.take(esize(d->dtype) * (size_t)(d->n * d->n));  // dense P
+        cv.take_n<int32_t>(d->m);                          // pi_R^-1
+        cv.take_n<int32_t>(d->n);                          // pi_P^-1
+        return cv.off;
+    }
     LinearBufs L;
     plan_linear(cv, d, false, L);
     if (d->variant == POETX_MEM) cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
@@ -808,13 +953,26 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
     POETX_TRY(check_desc(d));
     if (d->T == 0) return POETX_OK;
     if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
-    if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (d->variant != POETX_MEM && !saved) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_fwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
     Carver cv(ws);
+    if (d->variant == POETX_WEIGHT_CENTRIC) {
+        Carver sv(saved);
+        WcSaved S;
+        plan_wc_saved(sv, d, S);
+        void* Pd = cv.take(esize(d->dtype) * (size_t)(d->n * d->n));
+        int32_t* inv_R = cv.take_n<int32_t>(d->m);
+        int32_t* inv_P = cv.take_n<int32_t>(d->n);
+        return wc_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, S, Pd, inv_R, inv_P, as_stream(stream));
+    }
     LinearBufs L;
     plan_linear(cv, d, false, L);
+    if (d->variant == POETX_FOUR_PERM)
+        return four_perm_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, saved,
+                                 static_cast<char*>(saved) + fast_saved_a_offset(d), L.buf[0], L.buf[1],
+                                 as_stream(stream));
     void* h2 = saved;
     void* a = L.buf[0];
     if (d->variant == POETX_MEM) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
@@ -825,6 +983,11 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
 size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {
     if (check_desc(d) != POETX_OK) return 0;
     Carver cv(nullptr);
+    if (d->variant == POETX_WEIGHT_CENTRIC) {
+        WcBufs B;
+        plan_wc_bwd(cv, d, B);
+        return cv.off;
+    }
     LinearBufs L;
     plan_linear(cv, d, true, L);
     return cv.off;
@@ -843,13 +1006,24 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
         return POETX_OK;
     }
     if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
-    if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (d->variant != POETX_MEM && !saved) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_bwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
     Carver cv(ws);
+    if (d->variant == POETX_WEIGHT_CENTRIC) {
+        Carver sv(const_cast<void*>(saved));
+        WcSaved S;
+        plan_wc_saved(sv, d, S);
+        WcBufs B;
+        plan_wc_bwd(cv, d, B);
+        return wc_backward(d, dy, x, Wt, pi_R, pi_P, S, dx, dG_R, dG_P, B, s);
+    }
     LinearBufs L;
     plan_linear(cv, d, true, L);
+    if (d->variant == POETX_FOUR_PERM)
+        return four_perm_backward(d, dy, Wt, G_R, G_P, pi_R, pi_P, saved,
+                                  static_cast<const char*>(saved) + fast_saved_a_offset(d), dx, dG_R, dG_P, L, s);
     const bool bf = d->dtype == POETX_BF16;
     const void* bufA = L.buf[0];
     void* bufB = L.buf[1];
@@ -885,7 +1059,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
 }
 
 size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d) {
-    if (check_desc(d) != POETX_OK) return 0;
+    if (check_desc(d) != POETX_OK || (d->variant != POETX_FAST && d->variant != POETX_MEM)) return 0;
     const bool bf = d->dtype == POETX_BF16;
     Carver cv(nullptr);
     const size_t es = esize(d->dtype);
@@ -904,6 +1078,7 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
                 const int32_t* pi_P_old, const int32_t* pi_R_new, const int32_t* pi_P_new, void* ws,
                 size_t ws_bytes, void* stream) {
     POETX_TRY(check_desc(d));
+    if (d->variant != POETX_FAST && d->variant != POETX_MEM) return POETX_ERR_UNSUPPORTED;
     if (!Wt || !q_R || !q_P || !pi_R_old || !pi_P_old || !pi_R_new || !pi_P_new) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_merge_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;

@@ -53,6 +53,8 @@ struct PipeArgs {
 // take the largest whose grid still gives every CU a workgroup.  m/n-major A
 // and B with float32 output (block gradients): Square 128 x 128 and Small
 // 64 x 64 (enough tiles to fill the chip without splitting the token axis).
+// Dense products of the weight-centric variant: k-major A with float32 output
+// and m/n-major A and B with bf16 output, each in Tall and Square.
 enum class PipeTile { Tall, Wide, Square, Small, Big, Slim };
 bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                          int64_t strideA, int64_t strideB);

@@ -1201,8 +1201,8 @@ bool pipe_gemm_supported(bool a_mn, bool b_mn, int64_t M, int64_t N, int64_t K, 
 
 hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipStream_t stream, PipeTile tile) {
     if (p.M <= 0 || p.N <= 0 || p.batch <= 0 || p.splits <= 0) return hipSuccess;
-    // instantiated combinations: dense / block products (k-major A, bf16 out) and
-    // block gradients (m/n-major A and B, float32 out)
+    // instantiated combinations: dense / block products (k-major A, bf16 out),
+    // block gradients (m/n-major A and B, float32 out) and the two below
     if (!a_mn && !out_f32) {
         if (tile == PipeTile::Square)
             return b_mn ? launch<128, 128, false, true, false, kEpiPlain, 4>(p, stream)
@@ -1218,6 +1218,19 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
                         : launch<128, 256, false, false, false, kEpiPlain, 3, 2, 4>(p, stream);
         return b_mn ? launch<256, 128, false, true, false, kEpiPlain, 3, 4, 2>(p, stream)
                     : launch<256, 128, false, false, false, kEpiPlain, 3, 4, 2>(p, stream);
+    }
+    // dense products of the weight-centric variant: float32 output with k-major
+    // A (NT, NN), bf16 output with m/n-major A and B (TN)
+    if (!a_mn && out_f32) {
+        if (tile == PipeTile::Square)
+            return b_mn ? launch<128, 128, false, true, true, kEpiPlain, 4>(p, stream)
+                        : launch<128, 128, false, false, true, kEpiPlain, 4>(p, stream);
+        return b_mn ? launch<256, 128, false, true, true, kEpiPlain, 3, 4, 2>(p, stream)
+                    : launch<256, 128, false, false, true, kEpiPlain, 3, 4, 2>(p, stream);
+    }
+    if (a_mn && b_mn && !out_f32) {
+        if (tile == PipeTile::Square) return launch<128, 128, true, true, false, kEpiPlain, 4>(p, stream);
+        return launch<256, 128, true, true, false, kEpiPlain, 3, 4, 2>(p, stream);
     }
     if (a_mn && b_mn && out_f32) {
         if (tile == PipeTile::Square) return launch<128, 128, true, true, true, kEpiPlain, 4>(p, stream);

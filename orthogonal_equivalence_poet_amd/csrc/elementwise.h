@@ -20,6 +20,13 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int* sigma, int64_t len,
                         hipStream_t s);
 hipError_t check_perm(const int* pi, int64_t len, int* ok, int* counts, int* bad, hipStream_t s);
+// inv[pi[i]] = i.
+hipError_t invert_perm(const int* pi, int* inv, int64_t len, hipStream_t s);
+// out (d x d, 16-byte aligned, d % b == 0) = Pi^T diag(G) Pi as a dense matrix, given
+// inv = pi^-1 and the blocks G [d / b, b, b] in the same dtype.
+hipError_t blockdiag_dense(const void* G, const int* inv, void* out, bool bf16, int64_t d, int b, hipStream_t s);
+// dG [d / b, b, b] = the diagonal blocks of Pi D Pi^T, D dense float32 d x d.
+hipError_t blockdiag_gather(const float* D, const int* pi, float* dG, int64_t d, int b, hipStream_t s);
 
 // AdamW coefficients for one step, worked out on the host in double:
 // decay = 1 - eta wd, step = eta / (1 - beta1^t), inv_sqrt_bc2 = 1 / sqrt(1 - beta2^t)

@@ -1,7 +1,8 @@
 // Memory-bound kernels of libpoetx: compact skew unpack / pack, the 2-D
 // permutation (gather or scatter of columns, optional row gather), the
 // split-K reduction, the float32 combine used between Cayley-Neumann
-// products, fills and permutation helpers.
+// products, fills, permutation helpers and the dense block-diagonal transforms
+// of the weight-centric variant.
 #include <algorithm>
 
 #include "device_common.h"
@@ -342,6 +343,45 @@ __global__ void finish_check_kernel(const int* __restrict__ bad, int* __restrict
     if (threadIdx.x == 0 && blockIdx.x == 0) ok[0] = bad[0] ? 0 : 1;
 }
 
+// ------------------------------------------- dense block-diagonal transforms
+// out (d x d) = Pi^T diag(G_0, G_1, ...) Pi as a dense matrix, inv the inverse
+// of pi: out[a][c] = G[i / b][i % b][j % b] with i = inv[a], j = inv[c] when i
+// and j fall in the same block, else 0.  One thread writes V consecutive
+// outputs of a row (one 16-byte store).
+template <typename T>
+__global__ void __launch_bounds__(256) blockdiag_dense_kernel(const T* __restrict__ G, const int* __restrict__ inv,
+                                                              T* __restrict__ out, int64_t d, int b) {
+    constexpr int V = ElemTraits<T>::kVec;
+    const int64_t chunks = d / V;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= d * chunks) return;
+    const int64_t a = idx / chunks;
+    const int64_t c0 = (idx % chunks) * V;
+    const int64_t i = inv[a];
+    const int64_t blk = i / b;
+    const T* __restrict__ grow = G + i * b;  // row i % b of block blk
+    T v[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int64_t j = inv[c0 + e];
+        store_f32(&v[e], j / b == blk ? load_f32(grow + (j - blk * b)) : 0.f);
+    }
+    uint4 w;
+    __builtin_memcpy(&w, v, sizeof(w));
+    *reinterpret_cast<uint4*>(out + a * d + c0) = w;
+}
+
+// dG[j][r][c] = D[pi[j b + r]][pi[j b + c]]: the diagonal b x b blocks of
+// Pi D Pi^T for a dense float32 d x d matrix D.
+__global__ void __launch_bounds__(256) blockdiag_gather_kernel(const float* __restrict__ D, const int* __restrict__ pi,
+                                                               float* __restrict__ dG, int64_t d, int b) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= d * b) return;
+    const int64_t row = idx / b;
+    const int64_t col = (row / b) * b + idx % b;
+    dG[idx] = D[(int64_t)pi[row] * d + pi[col]];
+}
+
 constexpr int64_t kMaxGridY = 65535;
 
 inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
@@ -468,6 +508,33 @@ hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int*
     hipLaunchKernelGGL(invert_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi_old, inv_tmp, len);
     hipLaunchKernelGGL(compose_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, inv_tmp, pi_new, sigma,
                        len);
+    return hipGetLastError();
+}
+
+hipError_t invert_perm(const int* pi, int* inv, int64_t len, hipStream_t s) {
+    if (len <= 0) return hipSuccess;
+    hipLaunchKernelGGL(invert_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi, inv, len);
+    return hipGetLastError();
+}
+
+hipError_t blockdiag_dense(const void* G, const int* inv, void* out, bool bf16, int64_t d, int b, hipStream_t s) {
+    if (d <= 0) return hipSuccess;
+    const int V = bf16 ? 8 : 4;
+    if (d % b || d % V || ((uintptr_t)out & 15)) return hipErrorInvalidValue;
+    const int64_t threads = d * (d / V);
+    if (bf16)
+        hipLaunchKernelGGL(blockdiag_dense_kernel<bf16_t>, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
+                           (const bf16_t*)G, inv, (bf16_t*)out, d, b);
+    else
+        hipLaunchKernelGGL(blockdiag_dense_kernel<float>, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
+                           (const float*)G, inv, (float*)out, d, b);
+    return hipGetLastError();
+}
+
+hipError_t blockdiag_gather(const float* D, const int* pi, float* dG, int64_t d, int b, hipStream_t s) {
+    if (d <= 0) return hipSuccess;
+    if (d % b) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(blockdiag_gather_kernel, dim3(blocks_for(d * b, 256)), dim3(256), 0, s, D, pi, dG, d, b);
     return hipGetLastError();
 }
 

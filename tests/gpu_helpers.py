@@ -51,6 +51,10 @@ def cnp_bwd(q: torch.Tensor, dG: torch.Tensor, nblk: int, b: int, k: int, dtype:
     return dq
 
 
+VARIANTS = {"fast": B.POETX_FAST, "mem": B.POETX_MEM, "four_perm": B.POETX_FOUR_PERM,
+            "weight_centric": B.POETX_WEIGHT_CENTRIC}
+
+
 class GpuLayer:
     """Device state of one POET-X linear plus one forward/backward step."""
 
@@ -67,8 +71,10 @@ class GpuLayer:
         self.q_P = dev(inp["q_P"])
         self.x = dev(inp["x"], s.dtype)
         self.dy = dev(inp["dy"], s.dtype) if "dy" in inp else None
-        var = B.POETX_MEM if self.variant == "mem" else B.POETX_FAST
+        var = VARIANTS[self.variant]
         self.desc = B.desc(s.T, s.m, s.n, s.b, s.k, code(s.dtype), var)
+        # the chain variants take the pre-permuted weight, the comparison ones W0 itself
+        self.weight = self.Wt if var in (B.POETX_FAST, B.POETX_MEM) else self.W0
 
     def forward(self):
         s = self.spec
@@ -78,7 +84,7 @@ class GpuLayer:
         nsaved = B.poetx_linear_saved_bytes(self.desc)
         self.saved = B.workspace(nsaved)
         ws = B.workspace(B.poetx_linear_fwd_workspace_bytes(self.desc))
-        B.poetx_linear_fwd(self.desc, self.x, self.Wt, self.G_R, self.G_P, self.pi_R, self.pi_P, self.y,
+        B.poetx_linear_fwd(self.desc, self.x, self.weight, self.G_R, self.G_P, self.pi_R, self.pi_P, self.y,
                            self.saved, ws)
         return self.y
 
@@ -88,7 +94,7 @@ class GpuLayer:
         self.dG_R = torch.empty((s.nblk_R, s.b, s.b), dtype=torch.float32, device=DEV)
         self.dG_P = torch.empty((s.nblk_P, s.b, s.b), dtype=torch.float32, device=DEV)
         ws = B.workspace(B.poetx_linear_bwd_workspace_bytes(self.desc))
-        B.poetx_linear_bwd(self.desc, self.dy, self.x, self.Wt, self.G_R, self.G_P, self.pi_R, self.pi_P,
+        B.poetx_linear_bwd(self.desc, self.dy, self.x, self.weight, self.G_R, self.G_P, self.pi_R, self.pi_P,
                            self.saved, self.dx, self.dG_R, self.dG_P, ws)
         self.dq_R = cnp_bwd(self.q_R, self.dG_R, s.nblk_R, s.b, s.k, s.dtype)
         self.dq_P = cnp_bwd(self.q_P, self.dG_P, s.nblk_P, s.b, s.k, s.dtype)

@@ -94,6 +94,34 @@ def test_empty_batch_forward_is_a_no_op(B):
     assert lib.poetx_linear_fwd(C.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 0
 
 
+def test_comparison_variant_sizes_and_merge_rejection(B):
+    lib = B.load()
+    T, m, n, b = 2048, 4096, 1024, 256
+    fast = B.desc(T, m, n, b, 3, B.POETX_BF16, B.POETX_FAST)
+    four = B.desc(T, m, n, b, 3, B.POETX_BF16, B.POETX_FOUR_PERM)
+    wc = B.desc(T, m, n, b, 3, B.POETX_BF16, B.POETX_WEIGHT_CENTRIC)
+    # four_perm keeps the same two activations as fast
+    assert lib.poetx_linear_saved_bytes(C.byref(four)) == lib.poetx_linear_saved_bytes(C.byref(fast))
+    assert lib.poetx_linear_fwd_workspace_bytes(C.byref(four)) == lib.poetx_linear_fwd_workspace_bytes(C.byref(fast))
+    # weight-centric keeps dense R, W0 P and W_RP; its backward needs dW_RP, R^T dW_RP, dR and dP
+    assert lib.poetx_linear_saved_bytes(C.byref(wc)) == 2 * (m * m + 2 * m * n)
+    assert lib.poetx_linear_bwd_workspace_bytes(C.byref(wc)) == 2 * 2 * m * n + 4 * m * m + 4 * n * n
+    assert lib.poetx_linear_fwd_workspace_bytes(C.byref(wc)) >= 2 * n * n + 4 * (m + n)
+    # the four variant values are accepted, a fifth is not
+    assert lib.poetx_linear_saved_bytes(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 4))) == 0
+    assert lib.poetx_linear_fwd(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 4)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.POETX_ERR_INVALID_ARG
+    # saved is required by every variant but mem
+    for d in (four, wc):
+        need = lib.poetx_linear_fwd_workspace_bytes(C.byref(d))
+        assert lib.poetx_linear_fwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need,
+                                    None) == B.POETX_ERR_INVALID_ARG
+        # merge folds into the pre-permuted weight, which these variants do not keep
+        assert lib.poetx_merge_workspace_bytes(C.byref(d)) == 0
+        assert lib.poetx_merge(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == B.POETX_ERR_UNSUPPORTED
+
+
 def test_cnp_and_skew_validation(B):
     lib = B.load()
     assert lib.poetx_cnp_fwd(FAKE, 4, 24, 3, FAKE, 0, FAKE, 1 << 30, None) == 3

@@ -262,6 +262,48 @@ def test_layer_ragged(m, n, b, k, T, dtype, variant):
     _check_step(g, _oracle_step(spec, inp), dtype)
 
 
+# The comparison variants (all four permutations on the activations; the
+# original weight-centric POET with dense R and P) against the same oracle.
+@pytest.mark.parametrize("m,n,b,k,T,dtype", RAGGED + [(64, 48, 16, 3, 40, "bf16"), (1024, 512, 256, 3, 2048, "bf16")])
+@pytest.mark.parametrize("variant", ["four_perm", "weight_centric"])
+def test_comparison_variants_ragged(m, n, b, k, T, dtype, variant):
+    spec = I.LinearSpec(f"cmp_{m}x{n}", m=m, n=n, b=b, k=k, T=T, dtype=dtype, q_std=0.02, key=(17, m, T))
+    inp = I.make_linear_inputs(spec)
+    g = GpuLayer(spec, inp, variant)
+    g.forward()
+    g.backward()
+    _check_step(g, _oracle_step(spec, inp), dtype)
+
+
+@pytest.mark.parametrize("variant", ["four_perm", "weight_centric"])
+def test_comparison_variants_tiny_and_deterministic(variant):
+    spec = I.tiny()
+    inp = I.make_linear_inputs(spec)
+    outs = []
+    for _ in range(2):
+        g = GpuLayer(spec, inp, variant)
+        g.forward()
+        g.backward()
+        outs.append([t.clone() for t in (g.y, g.dx, g.dG_R, g.dG_P)])
+    _check_step(g, _oracle_step(spec, inp), "f32")
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
+
+
+def test_comparison_variants_empty_batch():
+    spec = I.LinearSpec("empty_cmp", m=256, n=128, b=64, k=3, T=0, dtype="bf16", key=(18, 0, 0))
+    inp = I.make_linear_inputs(spec)
+    for variant in ("four_perm", "weight_centric"):
+        g = GpuLayer(spec, inp, variant)
+        g.forward()
+        g.dG_R = torch.full((4, 64, 64), 7.0, device=DEV)
+        g.dG_P = torch.full((2, 64, 64), 7.0, device=DEV)
+        ws = B.workspace(B.poetx_linear_bwd_workspace_bytes(g.desc))
+        B.poetx_linear_bwd(g.desc, g.dy, g.x, g.weight, g.G_R, g.G_P, g.pi_R, g.pi_P, g.saved, g.x, g.dG_R,
+                           g.dG_P, ws)
+        assert not g.dG_R.any() and not g.dG_P.any()
+
+
 def test_fast_and_mem_agree_bitwise_and_runs_are_deterministic():
     spec = I.LinearSpec("det", m=1024, n=512, b=256, k=3, T=700, dtype="bf16", key=(8, 0, 0))
     inp = I.make_linear_inputs(spec)
