@@ -139,8 +139,9 @@ def build_state(spec):
     S["dq"] = torch.empty_like(S["q"])
     S["y"] = torch.empty((spec.T, spec.m), dtype=bf, device=dev)
     S["dx"] = torch.empty((spec.T, spec.n), dtype=bf, device=dev)
-    S["desc"] = B.desc(spec.T, spec.m, spec.n, b, spec.k, B.POETX_BF16, B.POETX_FAST)
-    S["saved"] = B.workspace(B.poetx_linear_saved_bytes(S["desc"]))
+    var = B.POETX_MEM if spec.variant == "mem" else B.POETX_FAST
+    S["desc"] = B.desc(spec.T, spec.m, spec.n, b, spec.k, B.POETX_BF16, var)
+    S["saved"] = B.workspace(B.poetx_linear_saved_bytes(S["desc"])) if var == B.POETX_FAST else None
     ws = max(B.poetx_linear_fwd_workspace_bytes(S["desc"]), B.poetx_linear_bwd_workspace_bytes(S["desc"]),
              B.poetx_cnp_fwd_workspace_bytes(nR + nP, b, spec.k, B.POETX_BF16),
              B.poetx_cnp_bwd_workspace_bytes(nR + nP, b, spec.k, B.POETX_BF16))
@@ -539,6 +540,10 @@ def run_layer(args, specs, label, merge):
     out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
     out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
+    # the same step with q/k/v and gate/up as groups of linears sharing an input
+    ms_grouped = grouped_layer_step(args, specs, states)
+    out["grouped"] = {"ms_per_step": round(ms_grouped, 4), "tokens_per_s": round(T / (ms_grouped / 1e3), 1),
+                      "groups": "q/k/v, o, gate/up, down", "over_ungrouped": round(ms_grouped / ms, 3)}
     # training-step closure: the AdamW update of every q of the layer in one call,
     # and the merge + optimizer reset that a reset gap of 400 updates amortizes
     count = q_all.numel()
@@ -565,6 +570,75 @@ def run_layer(args, specs, label, merge):
         out["merge_all_7_us"] = round(us, 1)
         out["train_step_ms_reset_gap_400"] = round(ms_train + (us + us_reset) / 1e3 / 400, 4)
     return out
+
+
+def grouped_layer_step(args, specs, states):
+    """The same layer step with the linears that read the same input (q, k, v;
+    gate, up) run as groups (poetx_group_fwd / _bwd: every stage one launch for
+    the group), the others alone; one Cayley-Neumann batch ordered so that each
+    group's R blocks and P blocks are contiguous.  Mean ms per step."""
+    import torch
+    from orthogonal_equivalence_poet_amd import binding as B
+    b, k, T = specs[0].b, specs[0].k, specs[0].T
+    names = [sp.name.split("_", 1)[1] for sp in specs]
+    parts = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+    qs, units, o = [], [], 0
+    for part in parts:
+        idx = [names.index(nm) for nm in part]
+        sps, sts = [specs[i] for i in idx], [states[i] for i in idx]
+        qR = [S["q"][:sp.nblk_R] for sp, S in zip(sps, sts)]
+        qP = [S["q"][sp.nblk_R:] for sp, S in zip(sps, sts)]
+        nR, nP = sum(sp.nblk_R for sp in sps), sum(sp.nblk_P for sp in sps)
+        qs += qR + qP
+        units.append(dict(sps=sps, sts=sts, r=(o, o + nR), p=(o + nR, o + nR + nP)))
+        o += nR + nP
+    nall = o
+    q_all = torch.cat(qs).contiguous()
+    G_all = torch.empty((nall, b, b), dtype=torch.bfloat16, device="cuda")
+    dG_all = torch.empty((nall, b, b), dtype=torch.float32, device="cuda")
+    dq_all = torch.empty_like(q_all)
+    cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nall, b, k, B.POETX_BF16))
+    cnp_ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(nall, b, k, B.POETX_BF16))
+    calls = []
+    for u in units:
+        sps, sts = u["sps"], u["sts"]
+        G_R, G_P = G_all[u["r"][0]:u["r"][1]], G_all[u["p"][0]:u["p"][1]]
+        dG_R, dG_P = dG_all[u["r"][0]:u["r"][1]], dG_all[u["p"][0]:u["p"][1]]
+        x = sts[0]["x"]
+        M = sum(sp.m for sp in sps)
+        if len(sps) == 1:
+            S = sts[0]
+            fwd = (lambda S=S, G_R=G_R, G_P=G_P: B.poetx_linear_fwd(S["desc"], S["x"], S["Wt"], G_R, G_P, S["pi_R"],
+                                                                     S["pi_P"], S["y"], S["saved"], S["ws"]))
+            bwd = (lambda S=S, G_R=G_R, G_P=G_P, dG_R=dG_R, dG_P=dG_P:
+                   B.poetx_linear_bwd(S["desc"], S["dy"], S["x"], S["Wt"], G_R, G_P, S["pi_R"], S["pi_P"],
+                                      S["saved"], S["dx"], dG_R, dG_P, S["ws"]))
+        else:
+            var = B.POETX_MEM if sps[0].variant == "mem" else B.POETX_FAST
+            gd = B.group_desc(T, sps[0].n, b, k, B.POETX_BF16, var, [sp.m for sp in sps])
+            Wt = torch.cat([S["Wt"] for S in sts]).contiguous()
+            pi_R = torch.cat([S["pi_R"] for S in sts]).contiguous()
+            pi_P = torch.cat([S["pi_P"] for S in sts]).contiguous()
+            y = torch.empty((T, M), dtype=torch.bfloat16, device="cuda")
+            dy = torch.cat([S["dy"] for S in sts], dim=1).contiguous()
+            dx = torch.empty_like(x)
+            saved = B.workspace(B.poetx_group_saved_bytes(gd)) if var == B.POETX_FAST else None
+            ws = B.workspace(max(B.poetx_group_fwd_workspace_bytes(gd), B.poetx_group_bwd_workspace_bytes(gd)))
+            fwd = (lambda gd=gd, x=x, Wt=Wt, G_R=G_R, G_P=G_P, pi_R=pi_R, pi_P=pi_P, y=y, saved=saved, ws=ws:
+                   B.poetx_group_fwd(gd, x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws))
+            bwd = (lambda gd=gd, dy=dy, x=x, Wt=Wt, G_R=G_R, G_P=G_P, pi_R=pi_R, pi_P=pi_P, saved=saved, dx=dx,
+                   dG_R=dG_R, dG_P=dG_P, ws=ws:
+                   B.poetx_group_bwd(gd, dy, x, Wt, G_R, G_P, pi_R, pi_P, saved, dx, dG_R, dG_P, ws))
+        calls.append((fwd, bwd))
+
+    def step():
+        B.poetx_cnp_fwd_save(q_all, nall, b, k, G_all, cnp_saved, cnp_ws)
+        for fwd, _ in calls:
+            fwd()
+        for _, bwd in reversed(calls):
+            bwd()
+        B.poetx_cnp_bwd_saved(q_all, dG_all, nall, b, k, dq_all, B.POETX_BF16, cnp_saved, cnp_ws)
+    return _time_steps(step, args.steps, args.warmup)
 
 
 def run_cnp_13b(args):

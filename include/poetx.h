@@ -209,6 +209,53 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,
                      const int32_t* pi_P, const void* saved, void* dx, float* dG_R,
                      float* dG_P, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- groups of linears */
+/* Linears that read the same input (a decoder layer's q, k and v projections,
+ * or its gate and up projections) as one chain, so that each stage is one
+ * launch over the whole group instead of one per linear (review Summary: the
+ * batch-parallel block products; a layer's linears batched into grouped
+ * launches).  Every linear keeps its own W0, R, P and permutations: linear g
+ * computes y_g = R_g W0_g P_g x exactly as poetx_linear_fwd does, and the group
+ * computes all of them from one read of x.
+ *
+ * With off_g = m_0 + ... + m_{g-1} and M = off_count:
+ *   Wt   dtype [M, n]           the pre-permuted weights stacked by rows (linear g
+ *                               in rows [off_g, off_g + m_g));
+ *   G_R  dtype [M/b, b, b]      linear g's R blocks from block off_g / b;
+ *   G_P  dtype [count n/b, b, b] linear g's P blocks from block g n / b;
+ *   pi_R int32 [M]              linear g's own permutation of [0, m_g) at off_g;
+ *   pi_P int32 [count n]        linear g's own permutation of [0, n) at g n;
+ *   y, dy dtype [T, M]          linear g's output in columns [off_g, off_g + m_g);
+ *   dx   dtype [T, n]           sum over the group of the input gradients
+ *                               (float32 sum, one rounding);
+ *   dG_R float32 [M/b, b, b], dG_P float32 [count n/b, b, b], in the G layout.
+ * FAST saves the dense products' outputs [T, M] and the gathered inputs [T, count n]
+ * (at the next 256-byte boundary); MEM saves nothing.  The dense products of
+ * a bf16 group whose m_g and n are multiples of 128 run as one launch. */
+#define POETX_MAX_GROUP 8
+typedef struct poetx_group_desc {
+    int64_t T;        /* tokens, >= 0 */
+    int64_t n;        /* width of the shared input (d_in of every linear) */
+    int64_t b;        /* block size of every R and P */
+    int32_t k;        /* Neumann order */
+    int32_t dtype;    /* POETX_F32 or POETX_BF16 */
+    int32_t variant;  /* POETX_FAST or POETX_MEM */
+    int32_t count;    /* linears in the group, 1 .. POETX_MAX_GROUP */
+    int32_t reserved; /* must be 0 */
+    int32_t pad;      /* ignored */
+    int64_t m[POETX_MAX_GROUP]; /* d_out of each linear (the first `count`); b | m_g */
+} poetx_group_desc;
+size_t poetx_group_saved_bytes(const poetx_group_desc* g);
+size_t poetx_group_fwd_workspace_bytes(const poetx_group_desc* g);
+int poetx_group_fwd(const poetx_group_desc* g, const void* x, const void* Wt, const void* G_R,
+                    const void* G_P, const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved,
+                    void* ws, size_t ws_bytes, void* stream);
+size_t poetx_group_bwd_workspace_bytes(const poetx_group_desc* g);
+int poetx_group_bwd(const poetx_group_desc* g, const void* dy, const void* x, const void* Wt,
+                    const void* G_R, const void* G_P, const int32_t* pi_R, const int32_t* pi_P,
+                    const void* saved, void* dx, float* dG_R, float* dG_P, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* ------------------------------------------------------------------ merge */
 /* Merge-then-reinitialize (agidaily.cc article; review "merge_then_reinitialize"):
  * with G from q_R / q_P (k = d->k, products in d->dtype),

@@ -30,6 +30,8 @@ EXPORTS = [
     "poetx_check_perm_workspace_bytes", "poetx_check_perm",
     "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd",
     "poetx_linear_bwd_workspace_bytes", "poetx_linear_bwd",
+    "poetx_group_saved_bytes", "poetx_group_fwd_workspace_bytes", "poetx_group_fwd",
+    "poetx_group_bwd_workspace_bytes", "poetx_group_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
     "poetx_gemm", "poetx_block_apply", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
     "poetx_adamw_step", "poetx_adamw_reset",
@@ -47,6 +49,15 @@ class LinearDesc(C.Structure):
                 ("k", C.c_int32), ("dtype", C.c_int32), ("variant", C.c_int32), ("reserved", C.c_int32)]
 
 
+POETX_MAX_GROUP = 8
+
+
+class GroupDesc(C.Structure):
+    _fields_ = [("T", C.c_int64), ("n", C.c_int64), ("b", C.c_int64), ("k", C.c_int32), ("dtype", C.c_int32),
+                ("variant", C.c_int32), ("count", C.c_int32), ("reserved", C.c_int32), ("pad", C.c_int32),
+                ("m", C.c_int64 * POETX_MAX_GROUP)]
+
+
 class AdamwParams(C.Structure):
     _fields_ = [("lr", C.c_double), ("gamma", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double)]
@@ -55,6 +66,7 @@ class AdamwParams(C.Structure):
 _lib: Optional[C.CDLL] = None
 _VP, _I64, _I32, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
 _DP = C.POINTER(LinearDesc)
+_GP = C.POINTER(GroupDesc)
 
 _SIGS = {
     "poetx_version": ([], C.c_char_p),
@@ -78,6 +90,11 @@ _SIGS = {
     "poetx_linear_fwd": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_linear_bwd_workspace_bytes": ([_DP], _SZ),
     "poetx_linear_bwd": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
+    "poetx_group_saved_bytes": ([_GP], _SZ),
+    "poetx_group_fwd_workspace_bytes": ([_GP], _SZ),
+    "poetx_group_fwd": ([_GP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
+    "poetx_group_bwd_workspace_bytes": ([_GP], _SZ),
+    "poetx_group_bwd": ([_GP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_merge_workspace_bytes": ([_DP], _SZ),
     "poetx_merge": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_gemm": ([_I32, _I32, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64,
@@ -234,6 +251,40 @@ def poetx_linear_fwd(d: LinearDesc, x, Wt, G_R, G_P, pi_R, pi_P, y, saved=None, 
     _check("poetx_linear_fwd", load().poetx_linear_fwd(C.byref(d), _ptr(x), _ptr(Wt), _ptr(G_R), _ptr(G_P),
                                                        _ptr(pi_R), _ptr(pi_P), _ptr(y), _ptr(saved), p, nbytes,
                                                        _stream(stream)))
+
+
+def group_desc(T, n, b, k, dtype, variant, ms) -> GroupDesc:
+    ms = [int(v) for v in ms]
+    if not 1 <= len(ms) <= POETX_MAX_GROUP:
+        raise ValueError(f"a group holds 1 to {POETX_MAX_GROUP} linears, got {len(ms)}")
+    m = (C.c_int64 * POETX_MAX_GROUP)(*(ms + [0] * (POETX_MAX_GROUP - len(ms))))
+    return GroupDesc(int(T), int(n), int(b), int(k), int(dtype), int(variant), len(ms), 0, 0, m)
+
+
+def poetx_group_saved_bytes(g: GroupDesc) -> int:
+    return load().poetx_group_saved_bytes(C.byref(g))
+
+
+def poetx_group_fwd_workspace_bytes(g: GroupDesc) -> int:
+    return load().poetx_group_fwd_workspace_bytes(C.byref(g))
+
+
+def poetx_group_fwd(g: GroupDesc, x, Wt, G_R, G_P, pi_R, pi_P, y, saved=None, ws=None, stream=None):
+    p, nbytes = _ws(ws)
+    _check("poetx_group_fwd", load().poetx_group_fwd(C.byref(g), _ptr(x), _ptr(Wt), _ptr(G_R), _ptr(G_P),
+                                                     _ptr(pi_R), _ptr(pi_P), _ptr(y), _ptr(saved), p, nbytes,
+                                                     _stream(stream)))
+
+
+def poetx_group_bwd_workspace_bytes(g: GroupDesc) -> int:
+    return load().poetx_group_bwd_workspace_bytes(C.byref(g))
+
+
+def poetx_group_bwd(g: GroupDesc, dy, x, Wt, G_R, G_P, pi_R, pi_P, saved, dx, dG_R, dG_P, ws=None, stream=None):
+    p, nbytes = _ws(ws)
+    _check("poetx_group_bwd", load().poetx_group_bwd(C.byref(g), _ptr(dy), _ptr(x), _ptr(Wt), _ptr(G_R),
+                                                     _ptr(G_P), _ptr(pi_R), _ptr(pi_P), _ptr(saved), _ptr(dx),
+                                                     _ptr(dG_R), _ptr(dG_P), p, nbytes, _stream(stream)))
 
 
 def poetx_linear_bwd_workspace_bytes(d: LinearDesc) -> int:

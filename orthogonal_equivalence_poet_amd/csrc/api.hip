@@ -749,6 +749,147 @@ int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, co
     return POETX_OK;
 }
 
+// ------------------------------------------------------ groups of linears
+// A group of `count` linears reading the same input x [T, n] runs as one chain
+// of width m = sum m_g (outputs concatenated) and n' = count n (one gathered
+// copy of x per linear), so every stage is one launch: see poetx.h.
+struct GroupPlan {
+    poetx_linear_desc lin{};   // the chain: m = sum m_g, n = count n
+    int count = 0;
+    int64_t n = 0;             // width of the shared input
+    PermSegments seg;
+};
+
+int check_group(const poetx_group_desc* g, GroupPlan& P) {
+    if (!g) return POETX_ERR_INVALID_ARG;
+    if (g->count < 1 || g->count > POETX_MAX_GROUP) return POETX_ERR_SHAPE;
+    if (g->variant != POETX_FAST && g->variant != POETX_MEM) return POETX_ERR_INVALID_ARG;
+    if (g->n <= 0 || g->n > kMaxExtent / g->count) return POETX_ERR_SHAPE;
+    int64_t M = 0;
+    P.seg.count = g->count;
+    P.seg.n = g->n;
+    for (int i = 0; i < g->count; ++i) {
+        if (g->m[i] <= 0 || g->m[i] > kMaxExtent - M) return POETX_ERR_SHAPE;
+        P.seg.off[i] = M;
+        M += g->m[i];
+    }
+    P.seg.off[g->count] = M;
+    P.count = g->count;
+    P.n = g->n;
+    P.lin = poetx_linear_desc{g->T, M, g->count * g->n, g->b, g->k, g->dtype, g->variant, g->reserved};
+    POETX_TRY(check_desc(&P.lin));
+    for (int i = 0; i < g->count; ++i)
+        if (g->m[i] % g->b) return POETX_ERR_SHAPE;
+    if (g->n % g->b) return POETX_ERR_SHAPE;
+    return POETX_OK;
+}
+
+inline const char* byte_off(const void* p, int64_t elems, size_t es) {
+    return static_cast<const char*>(p) + (size_t)elems * es;
+}
+inline char* byte_off(void* p, int64_t elems, size_t es) { return static_cast<char*>(p) + (size_t)elems * es; }
+
+// The dense products of a group.  Forward (nn = false): H2[:, seg g] = H1[:, g n
+// .. (g+1) n) . Wt_g^T.  Backward (nn = true): dH1[:, g n .. (g+1) n) =
+// dH2[:, seg g] . Wt_g.  Wt is the row-stacked [sum m_g, n] weight.  bf16 with
+// 128-column-aligned segments runs as grouped launches of the pipelined
+// kernel: the forward products all have k = n and form one launch; backward
+// products share a launch only with neighbours of the same k = m_g, so that a
+// launch's tiles take equal time (q, k and v: q alone, k with v).  Otherwise
+// one dense product per linear.
+hipError_t group_dense(const GroupPlan& P, bool nn, const void* A, const void* Wt, void* C, hipStream_t s) {
+    const bool bf = P.lin.dtype == POETX_BF16;
+    const size_t es = esize(P.lin.dtype);
+    const int64_t T = P.lin.T, M = P.lin.m, n = P.n, G = P.count;
+    const int64_t lda = nn ? M : G * n, ldc = nn ? G * n : M;
+    bool grouped = bf && G > 1 && n % 128 == 0;
+    for (int g = 0; g < G && grouped; ++g) {
+        const int64_t m_g = P.seg.off[g + 1] - P.seg.off[g];
+        grouped = m_g % 128 == 0 && pipe_gemm_supported(false, nn, T, nn ? n : m_g, nn ? m_g : n, lda, n, 0, 0);
+    }
+    if (grouped) {
+        auto m_of = [&](int g) { return P.seg.off[g + 1] - P.seg.off[g]; };
+        for (int g0 = 0; g0 < G;) {
+            int g1 = g0 + 1;
+            if (!nn) g1 = (int)G;
+            else
+                while (g1 < G && m_of(g1) == m_of(g0)) ++g1;
+            // linears [g0, g1): output columns from c0, relative group table
+            const int64_t c0 = nn ? g0 * n : P.seg.off[g0];
+            PipeArgs p;
+            p.A = A; p.lda = lda;
+            p.B = Wt; p.ldb = n;
+            p.C = byte_off(C, c0, es); p.ldc = ldc;
+            p.M = (int)T;
+            p.N = (int)(nn ? (g1 - g0) * n : P.seg.off[g1] - P.seg.off[g0]);
+            p.ngroups = g1 - g0;
+            int kmax = 0;
+            for (int g = g0; g < g1; ++g) {
+                const int64_t off = P.seg.off[g];
+                PipeGroup& e = p.grp[g - g0];
+                if (!nn) {
+                    e.n_begin = (int)(off - c0); e.k = (int)n; e.a_off = g * n; e.b_off = off * n - (off - c0) * n;
+                } else {
+                    e.n_begin = (int)((g - g0) * n); e.k = (int)m_of(g); e.a_off = off; e.b_off = off * n - (g - g0) * n;
+                }
+                kmax = std::max(kmax, e.k);
+            }
+            p.K = kmax;
+            p.k_per_split = kmax;
+            auto tiles = [&](int bm) { return ((T + bm - 1) / bm) * ((p.N + 127) / 128); };
+            const PipeTile t = tiles(256) >= 256   ? PipeTile::Tall
+                               : tiles(128) >= 256 ? PipeTile::Square
+                                                   : PipeTile::Slim;
+            const hipError_t e = pipe_gemm(false, nn, false, p, s, t);
+            if (e != hipSuccess) return e;
+            g0 = g1;
+        }
+        return hipSuccess;
+    }
+    for (int g = 0; g < G; ++g) {
+        const int64_t off = P.seg.off[g], m_g = P.seg.off[g + 1] - off;
+        const void* Wg = byte_off(Wt, off * n, es);
+        hipError_t e;
+        if (!nn)
+            e = dense_gemm(GemmLayout::NT, bf, T, m_g, n, byte_off(A, g * n, es), lda, Wg, n, byte_off(C, off, es),
+                           ldc, s);
+        else
+            e = dense_gemm(GemmLayout::NN, bf, T, n, m_g, byte_off(A, off, es), lda, Wg, n, byte_off(C, g * n, es),
+                           ldc, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Index tables in the workspace: pi_R with each linear's output offset added,
+// and each P permutation inverted in place of its slice (for the dx sum).
+struct GroupIdx {
+    int32_t* pi_R = nullptr;
+    int32_t* inv_P = nullptr;
+};
+
+void plan_group_idx(Carver& cv, const GroupPlan& P, GroupIdx& I) {
+    I.pi_R = cv.take_n<int32_t>(P.lin.m);
+    I.inv_P = cv.take_n<int32_t>(P.lin.n);
+}
+
+int group_forward(const GroupPlan& P, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                  const int32_t* pi_P, const int32_t* pi_R_cat, void* y, void* h2, void* a, void* buf,
+                  hipStream_t s) {
+    const poetx_linear_desc* d = &P.lin;
+    const bool bf = d->dtype == POETX_BF16;
+    const int64_t T = d->T, M = d->m, nn = d->n, b = d->b;
+    // a = [x gathered by pi_P,g for every g];  h1 = a . blockdiag(G_P)^T
+    HIP_TRY(gather_sum(x, a, bf, T, P.n, nn, pi_P, 1, s));
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, nn, b, a, G_P, buf, s));
+    // h2[:, seg g] = h1_g . Wt_g^T
+    HIP_TRY(group_dense(P, false, buf, Wt, h2, s));
+    // z = h2 . blockdiag(G_R)^T ; y = z scattered by the offset pi_R
+    HIP_TRY(block_apply(GemmLayout::NT, bf, T, M, b, h2, G_R, buf, s));
+    HIP_TRY(permute_2d(buf, y, bf, T, M, nullptr, pi_R_cat, true, s));
+    return POETX_OK;
+}
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -1055,6 +1196,110 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     // da = dh1 . blockdiag(G_P) ; dx = da scattered by pi_P
     HIP_TRY(block_apply(GemmLayout::NN, bf, T, n, b, bufB, G_P, bufC, s));
     HIP_TRY(permute_2d(bufC, dx, bf, T, n, nullptr, pi_P, true, s));
+    return POETX_OK;
+}
+
+size_t poetx_group_saved_bytes(const poetx_group_desc* g) {
+    GroupPlan P;
+    if (check_group(g, P) != POETX_OK) return 0;
+    return poetx_linear_saved_bytes(&P.lin);
+}
+
+size_t poetx_group_fwd_workspace_bytes(const poetx_group_desc* g) {
+    GroupPlan P;
+    if (check_group(g, P) != POETX_OK) return 0;
+    Carver cv(nullptr);
+    LinearBufs L;
+    plan_linear(cv, &P.lin, false, L);
+    if (P.lin.variant == POETX_MEM) cv.take(esize(P.lin.dtype) * (size_t)(P.lin.T * P.lin.m));
+    GroupIdx I;
+    plan_group_idx(cv, P, I);
+    return cv.off;
+}
+
+int poetx_group_fwd(const poetx_group_desc* g, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
+                    void* stream) {
+    GroupPlan P;
+    POETX_TRY(check_group(g, P));
+    if (P.lin.T == 0) return POETX_OK;
+    if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
+    if (P.lin.variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (ws_bytes < poetx_group_fwd_workspace_bytes(g)) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    const hipStream_t s = as_stream(stream);
+    Carver cv(ws);
+    LinearBufs L;
+    plan_linear(cv, &P.lin, false, L);
+    void* h2 = saved;
+    void* a = L.buf[0];
+    if (P.lin.variant == POETX_MEM) h2 = cv.take(esize(P.lin.dtype) * (size_t)(P.lin.T * P.lin.m));
+    else a = static_cast<char*>(saved) + fast_saved_a_offset(&P.lin);
+    GroupIdx I;
+    plan_group_idx(cv, P, I);
+    HIP_TRY(group_perms(pi_R, pi_P, I.pi_R, I.inv_P, P.seg, s));
+    return group_forward(P, x, Wt, G_R, G_P, pi_P, I.pi_R, y, h2, a, L.buf[1], s);
+}
+
+size_t poetx_group_bwd_workspace_bytes(const poetx_group_desc* g) {
+    GroupPlan P;
+    if (check_group(g, P) != POETX_OK) return 0;
+    Carver cv(nullptr);
+    LinearBufs L;
+    plan_linear(cv, &P.lin, true, L);
+    GroupIdx I;
+    plan_group_idx(cv, P, I);
+    return cv.off;
+}
+
+int poetx_group_bwd(const poetx_group_desc* g, const void* dy, const void* x, const void* Wt, const void* G_R,
+                    const void* G_P, const int32_t* pi_R, const int32_t* pi_P, const void* saved, void* dx,
+                    float* dG_R, float* dG_P, void* ws, size_t ws_bytes, void* stream) {
+    GroupPlan P;
+    POETX_TRY(check_group(g, P));
+    if (!dG_R || !dG_P) return POETX_ERR_INVALID_ARG;
+    const hipStream_t s = as_stream(stream);
+    const poetx_linear_desc* d = &P.lin;
+    const int64_t T = d->T, M = d->m, nn = d->n, b = d->b;
+    if (T == 0) {
+        HIP_TRY(fill_zero(dG_R, sizeof(float) * (size_t)(M * b), s));
+        HIP_TRY(fill_zero(dG_P, sizeof(float) * (size_t)(nn * b), s));
+        return POETX_OK;
+    }
+    if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
+    if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (ws_bytes < poetx_group_bwd_workspace_bytes(g)) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    Carver cv(ws);
+    LinearBufs L;
+    plan_linear(cv, d, true, L);
+    GroupIdx I;
+    plan_group_idx(cv, P, I);
+    HIP_TRY(group_perms(pi_R, pi_P, I.pi_R, I.inv_P, P.seg, s));
+    const bool bf = d->dtype == POETX_BF16;
+    const void* bufA = L.buf[0];
+    void* bufB = L.buf[1];
+    void* bufC = L.buf[2];
+    const void* h2 = saved;
+    if (d->variant == POETX_FAST) {
+        bufA = static_cast<const char*>(saved) + fast_saved_a_offset(d);
+    } else {
+        // recompute a, h1 and h2 from x
+        HIP_TRY(gather_sum(x, L.buf[0], bf, T, P.n, nn, pi_P, 1, s));
+        HIP_TRY(block_apply(GemmLayout::NT, bf, T, nn, b, bufA, G_P, bufB, s));
+        HIP_TRY(group_dense(P, false, bufB, Wt, bufC, s));
+        h2 = bufC;
+    }
+    // dz = dy gathered by the offset pi_R;  dG_R = dz_j^T h2_j;  dh2 = dz . blockdiag(G_R)
+    HIP_TRY(permute_2d(dy, bufB, bf, T, M, nullptr, I.pi_R, false, s));
+    POETX_TRY(block_grad(bf, T, M, b, bufB, h2, dG_R, L.splits_R, L.kps_R, L.part, s));
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, M, b, bufB, G_R, bufC, s));
+    // dh1[:, g n .. (g+1) n) = dh2[:, seg g] . Wt_g;  dG_P = dh1_j^T a_j;  da = dh1 . blockdiag(G_P)
+    HIP_TRY(group_dense(P, true, bufC, Wt, bufB, s));
+    POETX_TRY(block_grad(bf, T, nn, b, bufB, bufA, dG_P, L.splits_P, L.kps_P, L.part, s));
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, nn, b, bufB, G_P, bufC, s));
+    // dx = sum over the linears of da_g scattered by pi_P,g
+    HIP_TRY(gather_sum(bufC, dx, bf, T, nn, P.n, I.inv_P, P.count, s));
     return POETX_OK;
 }
 

@@ -8,6 +8,17 @@
 
 namespace poetx {
 
+// One product of a grouped launch (pipe_gemm with ngroups > 0): output columns
+// [n_begin, next n_begin) use A + a_off and B + b_off (element offsets) and run
+// k over [0, k).
+struct PipeGroup {
+    int n_begin = 0;
+    int k = 0;
+    int64_t a_off = 0;
+    int64_t b_off = 0;
+};
+constexpr int kMaxPipeGroups = 8;
+
 struct PipeArgs {
     const void* A = nullptr;   // bf16
     int64_t lda = 0, strideA = 0;
@@ -40,6 +51,11 @@ struct PipeArgs {
     int64_t lda2 = 0, strideA2 = 0;
     const void* B2 = nullptr;
     int64_t ldb2 = 0, strideB2 = 0;
+    // Grouped product (plain epilogue, batch 1, no split): ngroups entries with
+    // ascending n_begin, grp[0].n_begin == 0, each a multiple of the tile's
+    // column extent; K must be the largest group k.
+    int ngroups = 0;
+    PipeGroup grp[kMaxPipeGroups];
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead

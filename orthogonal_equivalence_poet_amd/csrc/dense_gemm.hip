@@ -605,13 +605,31 @@ pipe_gemm_kernel(const PipeArgs p) {
     const int wm = wave / NWN, wn = wave % NWN;
     const int M = p.M, N = p.N;
     const int kb = blockIdx.z * p.k_per_split;
-    const int ke = min(p.K, kb + p.k_per_split);
+    int ke = min(p.K, kb + p.k_per_split);
     int tm, tn;
     int z;
     batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
+    if constexpr (EPI == kEpiPlain && DUAL == 0) {
+        if (p.ngroups > 0) {
+            // grouped product: the group whose column range holds n0 (ranges
+            // start at multiples of BN, so a tile never spans two groups)
+            int64_t a_off = p.grp[0].a_off, b_off = p.grp[0].b_off;
+            int gk = p.grp[0].k;
+#pragma unroll
+            for (int i = 1; i < kMaxPipeGroups; ++i)
+                if (i < p.ngroups && n0 >= p.grp[i].n_begin) {
+                    a_off = p.grp[i].a_off;
+                    b_off = p.grp[i].b_off;
+                    gk = p.grp[i].k;
+                }
+            A += a_off;
+            B += b_off;
+            ke = min(gk, kb + p.k_per_split);
+        }
+    }
     f32x16_t acc[MI][NJ], acc2[MI][NJ];
     EpiAddends<BM, BN, G::kThreads> pre;
     if constexpr (EPI == kEpiGeneral && EpiAddends<BM, BN, G::kThreads>::kOn) load_addends(p, m0, n0, z, tid, pre);

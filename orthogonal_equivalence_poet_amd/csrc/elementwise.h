@@ -20,6 +20,21 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int* sigma, int64_t len,
                         hipStream_t s);
 hipError_t check_perm(const int* pi, int64_t len, int* ok, int* counts, int* bad, hipStream_t s);
+// dst[r][c] = sum_{g < nsum} src[r][idx[g dst_cols + c]] (float32 sum, one rounding);
+// src [rows, src_cols], dst [rows, dst_cols], both 16-byte rows.
+hipError_t gather_sum(const void* src, void* dst, bool bf16, int64_t rows, int64_t src_cols, int64_t dst_cols,
+                      const int* idx, int nsum, hipStream_t s);
+// The index tables of a group of `count` linears sharing an input of width n,
+// the linear g owning output rows [off[g], off[g + 1]):
+// out_R[i] = pi_R[i] + off[g] (its R permutation in the concatenated outputs) and
+// inv_P[g n + pi_P[g n + j]] = g n + j (its P permutation inverted, offset by g n).
+struct PermSegments {
+    int count = 0;
+    int64_t n = 0;
+    int64_t off[9] = {};
+};
+hipError_t group_perms(const int* pi_R, const int* pi_P, int* out_R, int* inv_P, const PermSegments& seg,
+                       hipStream_t s);
 // inv[pi[i]] = i.
 hipError_t invert_perm(const int* pi, int* inv, int64_t len, hipStream_t s);
 // out (d x d, 16-byte aligned, d % b == 0) = Pi^T diag(G) Pi as a dense matrix, given

@@ -343,6 +343,82 @@ __global__ void finish_check_kernel(const int* __restrict__ bad, int* __restrict
     if (threadIdx.x == 0 && blockIdx.x == 0) ok[0] = bad[0] ? 0 : 1;
 }
 
+// ------------------------------------------------- grouped column gathers
+// dst[r][c] = sum_{g < nsum} src[r][idx[g * dst_cols + c]] (float32 sum, one
+// rounding), src [rows, src_cols], dst [rows, dst_cols].  With nsum = 1 this
+// is a gather between rows of different widths (one input into the gathered
+// copies of several linears); with nsum > 1 it adds several gathered slices
+// (the input gradient of linears that share that input).  A workgroup stages
+// rows_per_wg source rows in LDS, as the permutation kernel does.
+template <typename T>
+__global__ void __launch_bounds__(256) gather_sum_lds(const T* __restrict__ src, T* __restrict__ dst, int64_t rows,
+                                                      int src_cols, int dst_cols, const int* __restrict__ idx,
+                                                      int nsum, int rows_per_wg) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T* buf = reinterpret_cast<T*>(smem_raw);
+    constexpr int V = ElemTraits<T>::kVec;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)min<int64_t>(rows_per_wg, rows - row0);
+    const int src_chunks = src_cols / V;
+    for (int u = threadIdx.x; u < nrows * src_chunks; u += 256) {
+        const int r = u / src_chunks;
+        const int c = (u % src_chunks) * V;
+        *reinterpret_cast<uint4*>(buf + r * src_cols + c) =
+            *reinterpret_cast<const uint4*>(src + (row0 + r) * src_cols + c);
+    }
+    __syncthreads();
+    const int dst_chunks = dst_cols / V;
+    for (int u = threadIdx.x; u < nrows * dst_chunks; u += 256) {
+        const int r = u / dst_chunks;
+        const int c = (u % dst_chunks) * V;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+        for (int g = 0; g < nsum; ++g) {
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] += load_f32(buf + r * src_cols + idx[g * dst_cols + c + i]);
+        }
+        T v[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) store_f32(&v[i], acc[i]);
+        uint4 w;
+        __builtin_memcpy(&w, v, sizeof(w));
+        *reinterpret_cast<uint4*>(dst + (row0 + r) * dst_cols + c) = w;
+    }
+}
+
+// Rows too long for LDS: the same from global memory, one output per thread.
+template <typename T>
+__global__ void gather_sum_direct(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int src_cols,
+                                  int dst_cols, const int* __restrict__ idx, int nsum) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * dst_cols) return;
+    const int64_t r = i / dst_cols;
+    const int c = (int)(i % dst_cols);
+    float acc = 0.f;
+    for (int g = 0; g < nsum; ++g) acc += load_f32(src + r * src_cols + idx[g * dst_cols + c]);
+    store_f32(dst + i, acc);
+}
+
+// Offsets for a group of linears: out_R[i] = pi_R[i] + off[g] for i in segment
+// g of [0, off[count]); inv_P[g n + pi_P[j]] = j for j in [g n, (g + 1) n).
+__global__ void group_perms_kernel(const int* __restrict__ pi_R, const int* __restrict__ pi_P,
+                                   int* __restrict__ out_R, int* __restrict__ inv_P, PermSegments seg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nR = seg.off[seg.count];
+    if (i < nR) {
+        int64_t o = 0;
+        for (int g = 1; g < seg.count; ++g)
+            if (i >= seg.off[g]) o = seg.off[g];
+        out_R[i] = pi_R[i] + (int)o;
+    }
+    const int64_t nP = seg.count * seg.n;
+    if (i < nP) {
+        const int64_t g = i / seg.n;
+        inv_P[g * seg.n + pi_P[i]] = (int)i;
+    }
+}
+
 // ------------------------------------------- dense block-diagonal transforms
 // out (d x d) = Pi^T diag(G_0, G_1, ...) Pi as a dense matrix, inv the inverse
 // of pi: out[a][c] = G[i / b][i % b][j % b] with i = inv[a], j = inv[c] when i
@@ -508,6 +584,44 @@ hipError_t compose_perm(const int* pi_old, const int* pi_new, int* inv_tmp, int*
     hipLaunchKernelGGL(invert_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi_old, inv_tmp, len);
     hipLaunchKernelGGL(compose_perm_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, inv_tmp, pi_new, sigma,
                        len);
+    return hipGetLastError();
+}
+
+hipError_t gather_sum(const void* src, void* dst, bool bf16, int64_t rows, int64_t src_cols, int64_t dst_cols,
+                      const int* idx, int nsum, hipStream_t s) {
+    if (rows <= 0 || dst_cols <= 0) return hipSuccess;
+    const int esz = bf16 ? 2 : 4;
+    const int V = 16 / esz;
+    const int64_t row_bytes = src_cols * esz;
+    if (row_bytes <= (int64_t)permute_lds_row_limit_bytes() && src_cols % V == 0 && dst_cols % V == 0) {
+        int rpw = (int)std::max<int64_t>(1, (4 * 1024 + row_bytes - 1) / row_bytes);
+        rpw = (int)std::min<int64_t>({rpw, rows, (int64_t)permute_lds_row_limit_bytes() / row_bytes});
+        const size_t smem = (size_t)rpw * row_bytes;
+        const unsigned grid = (unsigned)((rows + rpw - 1) / rpw);
+        if (bf16)
+            hipLaunchKernelGGL(gather_sum_lds<bf16_t>, dim3(grid), dim3(256), smem, s, (const bf16_t*)src,
+                               (bf16_t*)dst, rows, (int)src_cols, (int)dst_cols, idx, nsum, rpw);
+        else
+            hipLaunchKernelGGL(gather_sum_lds<float>, dim3(grid), dim3(256), smem, s, (const float*)src,
+                               (float*)dst, rows, (int)src_cols, (int)dst_cols, idx, nsum, rpw);
+    } else {
+        const int64_t total = rows * dst_cols;
+        if (bf16)
+            hipLaunchKernelGGL(gather_sum_direct<bf16_t>, dim3(blocks_for(total, 256)), dim3(256), 0, s,
+                               (const bf16_t*)src, (bf16_t*)dst, rows, (int)src_cols, (int)dst_cols, idx, nsum);
+        else
+            hipLaunchKernelGGL(gather_sum_direct<float>, dim3(blocks_for(total, 256)), dim3(256), 0, s,
+                               (const float*)src, (float*)dst, rows, (int)src_cols, (int)dst_cols, idx, nsum);
+    }
+    return hipGetLastError();
+}
+
+hipError_t group_perms(const int* pi_R, const int* pi_P, int* out_R, int* inv_P, const PermSegments& seg,
+                       hipStream_t s) {
+    const int64_t len = std::max<int64_t>(seg.off[seg.count], (int64_t)seg.count * seg.n);
+    if (len <= 0) return hipSuccess;
+    hipLaunchKernelGGL(group_perms_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi_R, pi_P, out_R, inv_P,
+                       seg);
     return hipGetLastError();
 }
 

@@ -122,6 +122,54 @@ def test_comparison_variant_sizes_and_merge_rejection(B):
                                None) == B.POETX_ERR_UNSUPPORTED
 
 
+def test_group_desc_layout_sizes_and_validation(B):
+    lib = B.load()
+    assert C.sizeof(B.GroupDesc) == 3 * 8 + 6 * 4 + 8 * 8
+    T, n, b = 2048, 4096, 256
+    ms = [4096, 1024, 1024]
+    g = B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, ms)
+    # FAST keeps the dense outputs [T, sum m] and the gathered inputs [T, count n]
+    assert lib.poetx_group_saved_bytes(C.byref(g)) == 2 * T * sum(ms) + 2 * T * 3 * n
+    # the same buffers as one chain of that width, plus two index tables
+    chain = B.desc(T, sum(ms), 3 * n, b, 3, B.POETX_BF16, B.POETX_FAST)
+    assert lib.poetx_group_fwd_workspace_bytes(C.byref(g)) >= lib.poetx_linear_fwd_workspace_bytes(C.byref(chain))
+    assert lib.poetx_group_bwd_workspace_bytes(C.byref(g)) >= lib.poetx_linear_bwd_workspace_bytes(C.byref(chain))
+    mem = B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_MEM, ms)
+    assert lib.poetx_group_saved_bytes(C.byref(mem)) == 0
+
+    def fwd(gd, ws_bytes=1 << 40, saved=FAKE):
+        return lib.poetx_group_fwd(C.byref(gd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, saved, FAKE, ws_bytes,
+                                   None)
+
+    bad = B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, ms)
+    bad.count = 0
+    assert fwd(bad) == B.POETX_ERR_SHAPE
+    bad.count = 9
+    assert fwd(bad) == B.POETX_ERR_SHAPE
+    assert fwd(B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, [4096, 1000])) == B.POETX_ERR_SHAPE
+    assert fwd(B.group_desc(T, 4000, b, 3, B.POETX_BF16, B.POETX_FAST, ms)) == B.POETX_ERR_SHAPE
+    assert fwd(B.group_desc(T, n, 24, 3, B.POETX_BF16, B.POETX_FAST, ms)) == B.POETX_ERR_UNSUPPORTED
+    for v in (B.POETX_FOUR_PERM, B.POETX_WEIGHT_CENTRIC, 7):
+        assert fwd(B.group_desc(T, n, b, 3, B.POETX_BF16, v, ms)) == B.POETX_ERR_INVALID_ARG
+    bad = B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, ms)
+    bad.reserved = 1
+    assert fwd(bad) == B.POETX_ERR_INVALID_ARG
+    assert fwd(g, saved=None) == B.POETX_ERR_INVALID_ARG
+    assert fwd(g, ws_bytes=lib.poetx_group_fwd_workspace_bytes(C.byref(g)) - 1) == B.POETX_ERR_WORKSPACE
+    assert lib.poetx_group_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               None) == B.POETX_ERR_INVALID_ARG
+    nb = lib.poetx_group_bwd_workspace_bytes(C.byref(g))
+    assert lib.poetx_group_bwd(C.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               nb, None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_group_bwd(C.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               nb - 1, None) == B.POETX_ERR_WORKSPACE
+    empty = B.group_desc(0, n, b, 3, B.POETX_BF16, B.POETX_FAST, ms)
+    assert lib.poetx_group_fwd(C.byref(empty), None, None, None, None, None, None, None, None, None, 0,
+                               None) == B.POETX_OK
+    with pytest.raises(ValueError):
+        B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, [256] * 9)
+
+
 def test_cnp_and_skew_validation(B):
     lib = B.load()
     assert lib.poetx_cnp_fwd(FAKE, 4, 24, 3, FAKE, 0, FAKE, 1 << 30, None) == 3

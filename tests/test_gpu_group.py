@@ -1,0 +1,159 @@
+"""GPU parity of groups of linears that share an input (poetx_group_fwd /
+poetx_group_bwd): every linear of the group against the float64 oracle on its
+own, the summed input gradient against the sum of the oracle's, and the group
+against the same linears run one by one through poetx_linear_fwd / _bwd
+(bitwise for y and the block gradients: both run the same products in the same
+order).  Bars: relative Frobenius error 1e-5 (float32) and 1.5e-2 (bf16)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import poet_oracle as O
+from orthogonal_equivalence_poet_amd import binding as B
+from orthogonal_equivalence_poet_amd import inputs as I
+from tests.gpu_helpers import DEV, GpuLayer, cnp_fwd, code, dev, dev_i32, host, rel_fro, tdtype, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _lib(gpu_lib):
+    yield
+    torch.cuda.synchronize()
+
+
+def _specs(ms, n, b, k, T, dtype, variant, key):
+    return [I.LinearSpec(f"grp{g}_{m}x{n}", m=m, n=n, b=b, k=k, T=T, dtype=dtype, q_std=0.02, variant=variant,
+                         key=(key, len(ms), g)) for g, m in enumerate(ms)]
+
+
+class GpuGroup:
+    """Device state of one group: the linears' tensors stacked as the group
+    entry points take them, one shared input x (the first linear's)."""
+
+    def __init__(self, specs, inps):
+        s0 = specs[0]
+        self.specs, self.inps = specs, inps
+        self.dtype = s0.dtype
+        self.x = dev(inps[0]["x"], s0.dtype)
+        self.layers = [GpuLayer(sp, dict(inp, x=inps[0]["x"])) for sp, inp in zip(specs, inps)]
+        L = self.layers
+        self.Wt = torch.cat([l.Wt for l in L]).contiguous()
+        self.pi_R = torch.cat([l.pi_R for l in L]).contiguous()
+        self.pi_P = torch.cat([l.pi_P for l in L]).contiguous()
+        self.G_R = torch.cat([cnp_fwd(l.q_R, sp.nblk_R, sp.b, sp.k, sp.dtype) for l, sp in zip(L, specs)])
+        self.G_P = torch.cat([cnp_fwd(l.q_P, sp.nblk_P, sp.b, sp.k, sp.dtype) for l, sp in zip(L, specs)])
+        self.dy = torch.cat([l.dy for l in L], dim=1).contiguous()
+        self.M = sum(sp.m for sp in specs)
+        var = B.POETX_MEM if s0.variant == "mem" else B.POETX_FAST
+        self.desc = B.group_desc(s0.T, s0.n, s0.b, s0.k, code(s0.dtype), var, [sp.m for sp in specs])
+
+    def run(self):
+        s0 = self.specs[0]
+        T, n, b = s0.T, s0.n, s0.b
+        self.y = torch.empty((T, self.M), dtype=tdtype(self.dtype), device=DEV)
+        self.saved = B.workspace(B.poetx_group_saved_bytes(self.desc))
+        ws = B.workspace(max(B.poetx_group_fwd_workspace_bytes(self.desc),
+                             B.poetx_group_bwd_workspace_bytes(self.desc)))
+        B.poetx_group_fwd(self.desc, self.x, self.Wt, self.G_R, self.G_P, self.pi_R, self.pi_P, self.y, self.saved,
+                          ws)
+        self.dx = torch.empty((T, n), dtype=tdtype(self.dtype), device=DEV)
+        self.dG_R = torch.empty((self.M // b, b, b), dtype=torch.float32, device=DEV)
+        self.dG_P = torch.empty((len(self.specs) * n // b, b, b), dtype=torch.float32, device=DEV)
+        B.poetx_group_bwd(self.desc, self.dy, self.x, self.Wt, self.G_R, self.G_P, self.pi_R, self.pi_P, self.saved,
+                          self.dx, self.dG_R, self.dG_P, ws)
+        torch.cuda.synchronize()
+
+    def slices(self):
+        """Per linear: (column range of y, R-block range, P-block range)."""
+        out, off, offP = [], 0, 0
+        for sp in self.specs:
+            out.append((slice(off, off + sp.m), slice(off // sp.b, (off + sp.m) // sp.b),
+                        slice(offP, offP + sp.nblk_P)))
+            off += sp.m
+            offP += sp.nblk_P
+        return out
+
+
+def _oracle(specs, inps):
+    x = inps[0]["x"]
+    refs, dx = [], 0.0
+    for sp, inp in zip(specs, inps):
+        G_R = O.blocks_from_params(inp["q_R"], sp.b, sp.k)
+        G_P = O.blocks_from_params(inp["q_P"], sp.b, sp.k)
+        args = (inp["W0"], G_R, G_P, inp["pi_R"], inp["pi_P"])
+        y = O.forward_from_blocks(x, *args)
+        dx_g, dG_R, dG_P = O.backward_from_blocks(inp["dy"], x, *args)
+        refs.append(dict(y=y, dG_R=dG_R, dG_P=dG_P))
+        dx = dx + dx_g
+    return refs, dx
+
+
+GROUPS = [
+    # linear outputs, n, b, k, T, dtype, variant
+    ([512, 256, 256], 512, 128, 3, 300, "bf16", "fast"),   # q/k/v-shaped, grouped dense launches
+    ([512, 256, 256], 512, 128, 3, 300, "bf16", "mem"),
+    ([768, 768], 256, 256, 4, 257, "bf16", "fast"),         # gate/up-shaped
+    ([96, 32, 64], 160, 32, 2, 77, "f32", "fast"),           # per-linear dense products, fp32
+    ([64, 48], 48, 16, 3, 33, "bf16", "mem"),                # segments not 128-aligned
+    ([256], 512, 128, 3, 64, "bf16", "fast"),               # a group of one
+    ([128] * 8, 256, 64, 3, 130, "bf16", "fast"),            # the largest group
+]
+
+
+@pytest.mark.parametrize("ms,n,b,k,T,dtype,variant", GROUPS)
+def test_group_parity(ms, n, b, k, T, dtype, variant):
+    specs = _specs(ms, n, b, k, T, dtype, variant, 30)
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    g = GpuGroup(specs, inps)
+    g.run()
+    refs, dx_ref = _oracle(specs, inps)
+    t = tol(dtype)
+    y, dG_R, dG_P = host(g.y), host(g.dG_R), host(g.dG_P)
+    errs = {"dx": rel_fro(host(g.dx), dx_ref)}
+    for i, ((ys, rs, ps), ref) in enumerate(zip(g.slices(), refs)):
+        errs[f"y{i}"] = rel_fro(y[:, ys], ref["y"])
+        errs[f"dG_R{i}"] = rel_fro(dG_R[rs], ref["dG_R"])
+        errs[f"dG_P{i}"] = rel_fro(dG_P[ps], ref["dG_P"])
+    bad = {key: e for key, e in errs.items() if not e <= t}
+    assert not bad, errs
+
+
+@pytest.mark.parametrize("ms,n,b,k,T,dtype,variant", [GROUPS[0], GROUPS[2], GROUPS[3]])
+def test_group_matches_linears_one_by_one(ms, n, b, k, T, dtype, variant):
+    specs = _specs(ms, n, b, k, T, dtype, variant, 31)
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    g = GpuGroup(specs, inps)
+    g.run()
+    dx_sum = 0.0
+    for l, (ys, rs, ps) in zip(g.layers, g.slices()):
+        l.G_R, l.G_P = g.G_R[rs], g.G_P[ps]
+        l.y = torch.empty_like(g.y[:, ys])
+        l.saved = B.workspace(B.poetx_linear_saved_bytes(l.desc))
+        ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(l.desc), B.poetx_linear_bwd_workspace_bytes(l.desc)))
+        B.poetx_linear_fwd(l.desc, l.x, l.Wt, l.G_R, l.G_P, l.pi_R, l.pi_P, l.y, l.saved, ws)
+        l.dx = torch.empty_like(l.x)
+        l.dG_R, l.dG_P = torch.empty_like(g.dG_R[rs]), torch.empty_like(g.dG_P[ps])
+        B.poetx_linear_bwd(l.desc, l.dy, l.x, l.Wt, l.G_R, l.G_P, l.pi_R, l.pi_P, l.saved, l.dx, l.dG_R, l.dG_P, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(l.y, g.y[:, ys])
+        assert torch.equal(l.dG_R, g.dG_R[rs]) and torch.equal(l.dG_P, g.dG_P[ps])
+        dx_sum = dx_sum + host(l.dx)
+    # the group adds the float32 input gradients once; one by one each is rounded first
+    assert rel_fro(host(g.dx), dx_sum) <= tol(dtype)
+
+
+def test_group_empty_batch_and_repeat_is_bitwise():
+    specs = _specs([256, 128], 256, 64, 3, 0, "bf16", "fast", 32)
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    g = GpuGroup(specs, inps)
+    g.run()
+    assert not g.dG_R.any() and not g.dG_P.any()
+    specs = _specs([256, 128], 256, 64, 3, 100, "bf16", "fast", 33)
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    g = GpuGroup(specs, inps)
+    g.run()
+    first = [t.clone() for t in (g.y, g.dx, g.dG_R, g.dG_P)]
+    g.run()
+    for a, c in zip(first, (g.y, g.dx, g.dG_R, g.dG_P)):
+        assert torch.equal(a, c)
