@@ -212,9 +212,10 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x,
 /* ------------------------------------------------------- groups of linears */
 /* Linears that read the same input (a decoder layer's q, k and v projections,
  * or its gate and up projections) as one chain, so that each stage is one
- * launch over the whole group instead of one per linear (review Summary: the
- * batch-parallel block products; a layer's linears batched into grouped
- * launches).  Every linear keeps its own W0, R, P and permutations: linear g
+ * launch over the whole group instead of one per linear.  This extends the
+ * review's batch-parallel block products (Summary: all blocks of a transform
+ * in one batched product) across the linears of a group; the pages do not
+ * describe it.  Every linear keeps its own W0, R, P and permutations: linear g
  * computes y_g = R_g W0_g P_g x exactly as poetx_linear_fwd does, and the group
  * computes all of them from one read of x.
  *

@@ -51,9 +51,9 @@ struct PipeArgs {
     int64_t lda2 = 0, strideA2 = 0;
     const void* B2 = nullptr;
     int64_t ldb2 = 0, strideB2 = 0;
-    // Grouped product (plain epilogue, batch 1, no split): ngroups entries with
-    // ascending n_begin, grp[0].n_begin == 0, each a multiple of the tile's
-    // column extent; K must be the largest group k.
+    // Grouped product (pipe_gemm with k-major A, bf16 output, tile Tall, Square
+    // or Slim; batch 1, no split): ngroups entries with ascending n_begin,
+    // grp[0].n_begin == 0, each a multiple of 128; K must be the largest group k.
     int ngroups = 0;
     PipeGroup grp[kMaxPipeGroups];
 };

@@ -590,7 +590,10 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
 
 // DUAL = 1: acc = op(A) op(B) + A2^T B2 (second product with m/n-major A2, B2);
 // DUAL = 2: the second product goes to its own accumulator (general epilogue mode 2).
-template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2, int DUAL = 0>
+// GRP: a grouped product (PipeArgs::grp), a separate instantiation so that the
+// plain kernels carry no group lookup.
+template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2, int DUAL = 0,
+          bool GRP = false>
 __global__ void __launch_bounds__(64 * NWM * NWN)
 __attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
 pipe_gemm_kernel(const PipeArgs p) {
@@ -612,8 +615,8 @@ pipe_gemm_kernel(const PipeArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
-    if constexpr (EPI == kEpiPlain && DUAL == 0) {
-        if (p.ngroups > 0) {
+    if constexpr (GRP) {
+        {
             // grouped product: the group whose column range holds n0 (ranges
             // start at multiples of BN, so a tile never spans two groups)
             int64_t a_off = p.grp[0].a_off, b_off = p.grp[0].b_off;
@@ -760,7 +763,7 @@ cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 }
 
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
-          int DUAL = 0>
+          int DUAL = 0, bool GRP = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -776,7 +779,7 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
         if (p.A2) q.A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)y0 * p.strideA2;
         if (p.B2) q.B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)y0 * p.strideB2;
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN, DUAL>),
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN, DUAL, GRP>),
                            dim3(tiles, q.batch, p.splits), dim3(64 * NWM * NWN), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1221,6 +1224,19 @@ hipError_t pipe_gemm(bool a_mn, bool b_mn, bool out_f32, const PipeArgs& p, hipS
     if (p.M <= 0 || p.N <= 0 || p.batch <= 0 || p.splits <= 0) return hipSuccess;
     // instantiated combinations: dense / block products (k-major A, bf16 out),
     // block gradients (m/n-major A and B, float32 out) and the two below
+    if (p.ngroups > 0) {
+        // grouped dense products (k-major A, bf16 out, 128-column tiles)
+        if (a_mn || out_f32 || p.batch != 1 || p.splits != 1 || p.ngroups > kMaxPipeGroups) return hipErrorInvalidValue;
+        if (tile == PipeTile::Square)
+            return b_mn ? launch<128, 128, false, true, false, kEpiPlain, 4, 2, 2, 0, true>(p, stream)
+                        : launch<128, 128, false, false, false, kEpiPlain, 4, 2, 2, 0, true>(p, stream);
+        if (tile == PipeTile::Slim)
+            return b_mn ? launch<64, 128, false, true, false, kEpiPlain, 4, 2, 2, 0, true>(p, stream)
+                        : launch<64, 128, false, false, false, kEpiPlain, 4, 2, 2, 0, true>(p, stream);
+        if (tile != PipeTile::Tall) return hipErrorInvalidValue;
+        return b_mn ? launch<256, 128, false, true, false, kEpiPlain, 3, 4, 2, 0, true>(p, stream)
+                    : launch<256, 128, false, false, false, kEpiPlain, 3, 4, 2, 0, true>(p, stream);
+    }
     if (!a_mn && !out_f32) {
         if (tile == PipeTile::Square)
             return b_mn ? launch<128, 128, false, true, false, kEpiPlain, 4>(p, stream)
