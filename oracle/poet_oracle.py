@@ -27,7 +27,11 @@ taken where the pages are silent (all listed in the design notes):
     and R = Pi_R^T D_R Pi_R with D_R = blockdiag(G_R,0, G_R,1, ...);
   * the absorbed permutations are the two next to W0:  Wt = Pi_R W0 Pi_P^T;
   * merge folds R W0 P into the weight, resamples both permutations and sets
-    q to zero.
+    q to zero;
+  * the quantized variant (the review's POET-XQ, Summary and Strengths: the
+    checkpointed variant never keeps a dequantized weight, and the comparison
+    is with 8-bit methods) stores the pre-permuted weight as symmetric int8
+    per output row; the pages give no format, this is the plainest 8-bit one.
 
 All functions take and return numpy float64 arrays (float32 inputs are widened
 losslessly); permutations are integer arrays.
@@ -43,7 +47,7 @@ __all__ = [
     "forward", "forward_from_blocks", "backward", "backward_from_blocks",
     "cnp_vjp", "merge", "effective_weight",
     "input_grad", "block_grad_entries", "block_grad_blocks", "merge_entries",
-    "adamw_step", "train_steps",
+    "adamw_step", "train_steps", "quantize_rows_int8", "dequantize_rows",
 ]
 
 
@@ -258,6 +262,30 @@ def backward(dy, x, W0, q_R, q_P, pi_R, pi_P, b: int, k: int):
     dq_R = params_grad_from_skew_grad(cnp_vjp(Q_R, dG_R, k))
     dq_P = params_grad_from_skew_grad(cnp_vjp(Q_P, dG_P, k))
     return dx, dq_R, dq_P, dG_R, dG_P
+
+
+# -------------------------------------------------------------- POET-XQ
+def quantize_rows_int8(W):
+    """Symmetric 8-bit storage of a weight, one scale per row (output channel):
+    scale_i = max_j |W_ij| / 127 and q_ij = the integer nearest W_ij / scale_i
+    (ties to even), in [-127, 127]; a row of zeros has scale 0 and codes 0.
+    The codes are integers decided by floating point, so they are decided in
+    float32, the precision the stored weight has (review Summary / Strengths,
+    POET-XQ; the format itself is this library's reading).
+    Returns (q int8 [m, n], scale float32 [m])."""
+    W32 = np.asarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W32), axis=1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(W32 / safe[:, None])
+    q = np.where(scale[:, None] > 0, q, 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, scale
+
+
+def dequantize_rows(q, scale) -> np.ndarray:
+    """The weight the quantized storage stands for: q_ij * scale_i (exact in float64)."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
 # ------------------------------------------------------------------- merge

@@ -511,3 +511,47 @@ def test_train_after_merge_starts_afresh():
     second = O.train_steps(xs[M:], dys[M:], W0_1, qR1, qP1, piR1, piP1, b, k, _OPT, M, iter(perms[1:]))
     for a, c in zip(full, second):
         assert np.allclose(a, c, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- POET-XQ storage
+def test_quantize_rows_hand_example():
+    # row 0: amax 1.27 -> scale 0.01 (float32); 0.5 / 0.01 = 50, -0.333 / 0.01 = -33.3 -> -33
+    # row 1: all zeros -> scale 0, codes 0;  row 2: a single nonzero maps to +-127
+    W = np.array([[1.27, 0.5, -0.333, 0.0], [0.0, 0.0, 0.0, 0.0], [0.0, -3.0, 0.0, 0.0]], dtype=np.float32)
+    q, s = O.quantize_rows_int8(W)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert q[0].tolist() == [127, 50, -33, 0]
+    assert s[1] == 0 and q[1].tolist() == [0, 0, 0, 0]
+    assert q[2].tolist() == [0, -127, 0, 0] and s[2] == np.float32(3.0) / np.float32(127.0)
+
+
+def test_quantize_rows_is_nearest_grid_point_by_brute_force():
+    rng = np.random.default_rng(41)
+    W = (rng.standard_normal((6, 40)) * rng.uniform(0.01, 3.0, (6, 1))).astype(np.float32)
+    q, s = O.quantize_rows_int8(W)
+    ks = np.arange(-127, 128, dtype=np.float64)
+    for i in range(W.shape[0]):
+        grid = ks * np.float64(s[i])
+        for j in range(W.shape[1]):
+            d = np.abs(W[i, j] - grid)
+            best = d.min()
+            # the code is a nearest grid point (a float32 tie may go either way)
+            assert abs(W[i, j] - q[i, j] * np.float64(s[i])) <= best + 1e-6 * s[i]
+        assert np.abs(q[i]).max() == 127   # the largest entry sits on the end of the grid
+    err = np.abs(O.dequantize_rows(q, s) - W)
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-5))
+
+
+def test_quantize_rows_round_trips_values_on_the_grid():
+    rng = np.random.default_rng(42)
+    codes = rng.integers(-127, 128, (5, 33)).astype(np.int8)
+    codes[:, 0] = 127
+    scale = rng.uniform(0.001, 0.1, 5).astype(np.float32)
+    # the scale is recomputed from the row maximum: amax = 127 * s exactly in float32 when
+    # 127 * s is representable; take s = amax / 127 as the quantizer does
+    amax = (np.float32(127.0) * scale).astype(np.float32)
+    s2 = (amax / np.float32(127.0)).astype(np.float32)
+    W = (codes.astype(np.float32) * s2[:, None]).astype(np.float32)
+    q, s = O.quantize_rows_int8(W)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(q, codes)
