@@ -23,7 +23,8 @@ timed on the host cores as a baseline, and, as context outside the timed step,
 the vendor library (torch.matmul, i.e. hipBLASLt) on the same dense shapes and a
 plain device copy (`vendor_reference`), and the same step with every variant
 of the linear (`variants`: fast, mem, all four permutations on the
-activations, and the original weight-centric POET with dense R and P).
+activations, the original weight-centric POET with dense R and P, and mem on
+the int8-stored weight).
 
   --pmc-dir DIR   parse a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run of this
                   script and record the dense GEMM's HBM traffic in
@@ -391,11 +392,13 @@ def variant_steps(spec, S, steps=10, warmup=5):
     from orthogonal_equivalence_poet_amd import binding as B
     nblk = spec.nblk_R + spec.nblk_P
     out = {}
+    Wq = B.workspace(B.poetx_qweight_bytes(spec.m, spec.n))
+    B.poetx_quantize_weight(S["Wt"], spec.m, spec.n, Wq)
     for name, var in (("fast", B.POETX_FAST), ("mem", B.POETX_MEM), ("four_perm", B.POETX_FOUR_PERM),
-                      ("weight_centric", B.POETX_WEIGHT_CENTRIC)):
+                      ("weight_centric", B.POETX_WEIGHT_CENTRIC), ("mem_q8", B.POETX_MEM_Q8)):
         d = B.desc(spec.T, spec.m, spec.n, spec.b, spec.k, B.POETX_BF16, var)
-        weight = S["Wt"] if var in (B.POETX_FAST, B.POETX_MEM) else S["W0"]
-        saved = B.workspace(B.poetx_linear_saved_bytes(d)) if var != B.POETX_MEM else None
+        weight = {B.POETX_FAST: S["Wt"], B.POETX_MEM: S["Wt"], B.POETX_MEM_Q8: Wq}.get(var, S["W0"])
+        saved = B.workspace(B.poetx_linear_saved_bytes(d)) if var not in (B.POETX_MEM, B.POETX_MEM_Q8) else None
         ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d), B.poetx_linear_bwd_workspace_bytes(d),
                              B.poetx_cnp_fwd_workspace_bytes(nblk, spec.b, spec.k, B.POETX_BF16),
                              B.poetx_cnp_bwd_workspace_bytes(nblk, spec.b, spec.k, B.POETX_BF16)))
@@ -410,6 +413,7 @@ def variant_steps(spec, S, steps=10, warmup=5):
         out[f"{name}_ms"] = round(_time_steps(step, steps, warmup), 4)
     out["weight_centric_over_fast"] = round(out["weight_centric_ms"] / out["fast_ms"], 2)
     out["four_perm_over_fast"] = round(out["four_perm_ms"] / out["fast_ms"], 3)
+    out["mem_q8_over_mem"] = round(out["mem_q8_ms"] / out["mem_ms"], 3)
     return out
 
 

@@ -88,7 +88,16 @@ enum { POETX_F32 = 0, POETX_BF16 = 1 };
  * With either of them the weight argument of poetx_linear_fwd / _bwd is W0
  * [m, n] itself, not the pre-permuted Wt, and poetx_merge does not apply
  * (POETX_ERR_UNSUPPORTED). */
-enum { POETX_FAST = 0, POETX_MEM = 1, POETX_FOUR_PERM = 2, POETX_WEIGHT_CENTRIC = 3 };
+enum { POETX_FAST = 0, POETX_MEM = 1, POETX_FOUR_PERM = 2, POETX_WEIGHT_CENTRIC = 3, POETX_MEM_Q8 = 4 };
+
+/* mem_q8 (the review's POET-XQ, Summary and Strengths: quantized training
+ * through the checkpointed variant, which never keeps a dequantized weight):
+ * the stored weight is the quantized buffer of poetx_quantize_weight (int8 per
+ * output row, see below) and every poetx_linear_fwd / _bwd call expands it into
+ * its own workspace, runs the mem chain on it and drops it; bf16 only.  The
+ * pages give no format: symmetric int8 with one float32 scale per row of Wt is
+ * this library's reading of their 8-bit setting.  poetx_merge on a mem_q8
+ * descriptor merges in bf16 and stores the result quantized again. */
 
 typedef struct poetx_linear_desc {
     int64_t T;       /* tokens (rows of x and y), >= 0 */
@@ -97,7 +106,7 @@ typedef struct poetx_linear_desc {
     int64_t b;       /* block size of R and P */
     int32_t k;       /* Neumann order (highest power of Q kept) */
     int32_t dtype;   /* POETX_F32 or POETX_BF16 */
-    int32_t variant; /* POETX_FAST, POETX_MEM, POETX_FOUR_PERM or POETX_WEIGHT_CENTRIC */
+    int32_t variant; /* POETX_FAST, POETX_MEM, POETX_FOUR_PERM, POETX_WEIGHT_CENTRIC or POETX_MEM_Q8 */
     int32_t reserved;/* must be 0 */
 } poetx_linear_desc;
 
@@ -266,12 +275,25 @@ int poetx_group_bwd(const poetx_group_desc* g, const void* dy, const void* x, co
  * Wt is updated in place (dtype [m, n]); the caller draws pi_new (no RNG in
  * the library) and uses it from then on.  Passing pi_new == pi_old gives a
  * pure fold; with q == 0 as well the call leaves Wt bit-identical.
- * d->T is ignored; d->variant must be POETX_FAST or POETX_MEM (the stored
- * weight of the other two is W0 itself; POETX_ERR_UNSUPPORTED). */
+ * d->T is ignored.  With POETX_MEM_Q8, Wt is the quantized buffer: the merge
+ * runs on its bf16 expansion and writes the merged weight back quantized.
+ * POETX_FOUR_PERM and POETX_WEIGHT_CENTRIC keep W0 itself, not Wt:
+ * POETX_ERR_UNSUPPORTED. */
 size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d);
 int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P,
                 const int32_t* pi_R_old, const int32_t* pi_P_old, const int32_t* pi_R_new,
                 const int32_t* pi_P_new, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------- quantized weight (mem_q8) */
+/* Wq layout: int8 codes [m, n] row-major, then float32 scales [m] at the next
+ * 256-byte boundary; poetx_qweight_bytes gives the size (0 for bad sizes).
+ * Quantize (W float32 or bf16 [m, n], n % 16 == 0, Wq 16-byte aligned):
+ *   scale_i = max_j |W_ij| / 127,  q_ij = nearest integer to W_ij / scale_i (ties
+ *   to even) in [-127, 127], computed in float32; a zero row gets scale 0.
+ * Dequantize: W (bf16 [m, n]) = bf16(q_ij * scale_i). */
+size_t poetx_qweight_bytes(int64_t m, int64_t n);
+int poetx_quantize_weight(const void* W, int dtype, int64_t m, int64_t n, void* Wq, void* stream);
+int poetx_dequantize_weight(const void* Wq, int64_t m, int64_t n, void* W, void* stream);
 
 /* ------------------------------------------------- building blocks (stages) */
 /* The MFMA GEMM every stage of the layer runs on, exposed for composition and

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpoetx.so")
 
 POETX_OK, POETX_ERR_INVALID_ARG, POETX_ERR_SHAPE, POETX_ERR_UNSUPPORTED, POETX_ERR_WORKSPACE, POETX_ERR_HIP = range(6)
 POETX_F32, POETX_BF16 = 0, 1
-POETX_FAST, POETX_MEM, POETX_FOUR_PERM, POETX_WEIGHT_CENTRIC = 0, 1, 2, 3
+POETX_FAST, POETX_MEM, POETX_FOUR_PERM, POETX_WEIGHT_CENTRIC, POETX_MEM_Q8 = 0, 1, 2, 3, 4
 POETX_GEMM_NT, POETX_GEMM_NN, POETX_GEMM_TN = 0, 1, 2
 
 EXPORTS = [
@@ -33,6 +33,7 @@ EXPORTS = [
     "poetx_group_saved_bytes", "poetx_group_fwd_workspace_bytes", "poetx_group_fwd",
     "poetx_group_bwd_workspace_bytes", "poetx_group_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
+    "poetx_qweight_bytes", "poetx_quantize_weight", "poetx_dequantize_weight",
     "poetx_gemm", "poetx_block_apply", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
     "poetx_adamw_step", "poetx_adamw_reset",
 ]
@@ -96,6 +97,9 @@ _SIGS = {
     "poetx_group_bwd_workspace_bytes": ([_GP], _SZ),
     "poetx_group_bwd": ([_GP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_merge_workspace_bytes": ([_DP], _SZ),
+    "poetx_qweight_bytes": ([_I64, _I64], _SZ),
+    "poetx_quantize_weight": ([_VP, _I32, _I64, _I64, _VP, _VP], _I32),
+    "poetx_dequantize_weight": ([_VP, _I64, _I64, _VP, _VP], _I32),
     "poetx_merge": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_gemm": ([_I32, _I32, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64,
                     _VP], _I32),
@@ -308,6 +312,19 @@ def poetx_merge(d: LinearDesc, Wt, q_R, q_P, pi_R_old, pi_P_old, pi_R_new, pi_P_
     _check("poetx_merge", load().poetx_merge(C.byref(d), _ptr(Wt), _ptr(q_R), _ptr(q_P), _ptr(pi_R_old),
                                              _ptr(pi_P_old), _ptr(pi_R_new), _ptr(pi_P_new), p, nbytes,
                                              _stream(stream)))
+
+
+def poetx_qweight_bytes(m, n) -> int:
+    return load().poetx_qweight_bytes(m, n)
+
+
+def poetx_quantize_weight(W, m, n, Wq, stream=None):
+    _check("poetx_quantize_weight", load().poetx_quantize_weight(_ptr(W), _dtype_code(W), m, n, _ptr(Wq),
+                                                                 _stream(stream)))
+
+
+def poetx_dequantize_weight(Wq, m, n, W, stream=None):
+    _check("poetx_dequantize_weight", load().poetx_dequantize_weight(_ptr(Wq), m, n, _ptr(W), _stream(stream)))
 
 
 def poetx_gemm(layout, A, B, C, M, N, K, batch=1, lda=None, ldb=None, ldc=None, strideA=0, strideB=0, strideC=0,

@@ -71,8 +71,9 @@ int check_nblk(int64_t nblk, int64_t b) {
 
 int check_desc(const poetx_linear_desc* d) {
     if (!d) return POETX_ERR_INVALID_ARG;
-    if (!dtype_ok(d->dtype) || d->variant < POETX_FAST || d->variant > POETX_WEIGHT_CENTRIC || d->reserved != 0)
+    if (!dtype_ok(d->dtype) || d->variant < POETX_FAST || d->variant > POETX_MEM_Q8 || d->reserved != 0)
         return POETX_ERR_INVALID_ARG;
+    if (d->variant == POETX_MEM_Q8 && d->dtype != POETX_BF16) return POETX_ERR_UNSUPPORTED;
     POETX_TRY(check_block(d->b));
     POETX_TRY(check_k(d->k));
     if (d->T < 0 || d->m <= 0 || d->n <= 0) return POETX_ERR_SHAPE;
@@ -733,6 +734,17 @@ int wc_backward(const poetx_linear_desc* d, const void* dy, const void* x, const
     return POETX_OK;
 }
 
+// The mem chain (MEM, and MEM_Q8 on its dequantized weight) recomputes h1 and h2.
+inline bool mem_chain(const poetx_linear_desc* d) { return d->variant == POETX_MEM || d->variant == POETX_MEM_Q8; }
+
+// Quantized weight buffer: int8 codes [m, n], then float32 row scales [m] at the
+// next 256-byte boundary.
+inline size_t qscale_offset(int64_t m, int64_t n) { return ((size_t)(m * n) + 255) & ~size_t(255); }
+inline const int8_t* qcodes(const void* Wq) { return static_cast<const int8_t*>(Wq); }
+inline const float* qscales(const void* Wq, int64_t m, int64_t n) {
+    return reinterpret_cast<const float*>(static_cast<const char*>(Wq) + qscale_offset(m, n));
+}
+
 int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
                    hipStream_t s) {
@@ -1063,7 +1075,7 @@ int poetx_check_perm(const int32_t* pi, int64_t len, int32_t* ok, void* ws, size
 }
 
 size_t poetx_linear_saved_bytes(const poetx_linear_desc* d) {
-    if (check_desc(d) != POETX_OK || d->variant == POETX_MEM) return 0;
+    if (check_desc(d) != POETX_OK || mem_chain(d)) return 0;
     if (d->variant == POETX_WEIGHT_CENTRIC) {
         Carver cv(nullptr);
         WcSaved S;
@@ -1082,9 +1094,10 @@ size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
         cv.take_n<int32_t>(d->n);                          // pi_P^-1
         return cv.off;
     }
+    if (d->variant == POETX_MEM_Q8) cv.take(2 * (size_t)(d->m * d->n));  // the dequantized weight
     LinearBufs L;
     plan_linear(cv, d, false, L);
-    if (d->variant == POETX_MEM) cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
+    if (mem_chain(d)) cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
     return cv.off;
 }
 
@@ -1094,7 +1107,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
     POETX_TRY(check_desc(d));
     if (d->T == 0) return POETX_OK;
     if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
-    if (d->variant != POETX_MEM && !saved) return POETX_ERR_INVALID_ARG;
+    if (!mem_chain(d) && !saved) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_fwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
@@ -1108,6 +1121,12 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
         int32_t* inv_P = cv.take_n<int32_t>(d->n);
         return wc_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, S, Pd, inv_R, inv_P, as_stream(stream));
     }
+    if (d->variant == POETX_MEM_Q8) {
+        // the quantized weight is expanded into the workspace for this call only
+        void* Wd = cv.take(2 * (size_t)(d->m * d->n));
+        HIP_TRY(dequantize_rows(qcodes(Wt), qscales(Wt, d->m, d->n), Wd, d->m, d->n, as_stream(stream)));
+        Wt = Wd;
+    }
     LinearBufs L;
     plan_linear(cv, d, false, L);
     if (d->variant == POETX_FOUR_PERM)
@@ -1116,7 +1135,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
                                  as_stream(stream));
     void* h2 = saved;
     void* a = L.buf[0];
-    if (d->variant == POETX_MEM) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
+    if (mem_chain(d)) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
     else a = static_cast<char*>(saved) + fast_saved_a_offset(d);
     return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, a, L.buf[1], as_stream(stream));
 }
@@ -1129,6 +1148,7 @@ size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {
         plan_wc_bwd(cv, d, B);
         return cv.off;
     }
+    if (d->variant == POETX_MEM_Q8) cv.take(2 * (size_t)(d->m * d->n));  // the dequantized weight
     LinearBufs L;
     plan_linear(cv, d, true, L);
     return cv.off;
@@ -1147,7 +1167,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
         return POETX_OK;
     }
     if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
-    if (d->variant != POETX_MEM && !saved) return POETX_ERR_INVALID_ARG;
+    if (!mem_chain(d) && !saved) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_bwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
@@ -1159,6 +1179,11 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
         WcBufs B;
         plan_wc_bwd(cv, d, B);
         return wc_backward(d, dy, x, Wt, pi_R, pi_P, S, dx, dG_R, dG_P, B, s);
+    }
+    if (d->variant == POETX_MEM_Q8) {
+        void* Wd = cv.take(2 * (size_t)(m * n));
+        HIP_TRY(dequantize_rows(qcodes(Wt), qscales(Wt, m, n), Wd, m, n, s));
+        Wt = Wd;
     }
     LinearBufs L;
     plan_linear(cv, d, true, L);
@@ -1177,7 +1202,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
         // a = x gathered by pi_P again (kept for dG_P)
         HIP_TRY(permute_2d(x, L.buf[0], bf, T, n, nullptr, pi_P, false, s));
     }
-    if (d->variant == POETX_MEM) {
+    if (mem_chain(d)) {
         // recompute h1 and h2 from x
         HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, bufA, G_P, bufB, s));
         HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, bufB, n, Wt, n, bufC, m, s));
@@ -1304,10 +1329,11 @@ int poetx_group_bwd(const poetx_group_desc* g, const void* dy, const void* x, co
 }
 
 size_t poetx_merge_workspace_bytes(const poetx_linear_desc* d) {
-    if (check_desc(d) != POETX_OK || (d->variant != POETX_FAST && d->variant != POETX_MEM)) return 0;
+    if (check_desc(d) != POETX_OK || d->variant == POETX_FOUR_PERM || d->variant == POETX_WEIGHT_CENTRIC) return 0;
     const bool bf = d->dtype == POETX_BF16;
     Carver cv(nullptr);
     const size_t es = esize(d->dtype);
+    if (d->variant == POETX_MEM_Q8) cv.take(2 * (size_t)(d->m * d->n));  // the dequantized weight
     cv.take(es * (size_t)(d->m * d->b));  // G_R
     cv.take(es * (size_t)(d->n * d->b));  // G_P
     cv.take(es * (size_t)(d->m * d->n));  // D_R Wt
@@ -1323,7 +1349,7 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
                 const int32_t* pi_P_old, const int32_t* pi_R_new, const int32_t* pi_P_new, void* ws,
                 size_t ws_bytes, void* stream) {
     POETX_TRY(check_desc(d));
-    if (d->variant != POETX_FAST && d->variant != POETX_MEM) return POETX_ERR_UNSUPPORTED;
+    if (d->variant == POETX_FOUR_PERM || d->variant == POETX_WEIGHT_CENTRIC) return POETX_ERR_UNSUPPORTED;
     if (!Wt || !q_R || !q_P || !pi_R_old || !pi_P_old || !pi_R_new || !pi_P_new) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_merge_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
@@ -1333,6 +1359,13 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
     const int64_t m = d->m, n = d->n, b = d->b;
     const size_t es = esize(d->dtype);
     Carver cv(ws);
+    void* Wq = nullptr;
+    if (d->variant == POETX_MEM_Q8) {
+        // merge in bf16 on the expanded weight, then store it quantized again
+        Wq = Wt;
+        Wt = cv.take(2 * (size_t)(m * n));
+        HIP_TRY(dequantize_rows(qcodes(Wq), qscales(Wq, m, n), Wt, m, n, s));
+    }
     void* G_R = cv.take(es * (size_t)(m * b));
     void* G_P = cv.take(es * (size_t)(n * b));
     void* W1 = cv.take(es * (size_t)(m * n));
@@ -1360,8 +1393,32 @@ int poetx_merge(const poetx_linear_desc* d, void* Wt, float* q_R, float* q_P, co
     HIP_TRY(compose_perm(pi_R_old, pi_R_new, inv, sig_R, m, s));
     HIP_TRY(compose_perm(pi_P_old, pi_P_new, inv, sig_P, n, s));
     HIP_TRY(permute_2d(W2, Wt, bf, m, n, sig_R, sig_P, false, s));
+    if (Wq)
+        HIP_TRY(quantize_rows(Wt, true, m, n, static_cast<int8_t*>(Wq),
+                              const_cast<float*>(qscales(Wq, m, n)), s));
     HIP_TRY(fill_zero(q_R, sizeof(float) * (size_t)(m / b) * (size_t)(b * (b - 1) / 2), s));
     HIP_TRY(fill_zero(q_P, sizeof(float) * (size_t)(n / b) * (size_t)(b * (b - 1) / 2), s));
+    return POETX_OK;
+}
+
+size_t poetx_qweight_bytes(int64_t m, int64_t n) {
+    if (m <= 0 || n <= 0 || m > kMaxExtent || n > kMaxExtent) return 0;
+    return qscale_offset(m, n) + sizeof(float) * (size_t)m;
+}
+
+int poetx_quantize_weight(const void* W, int dtype, int64_t m, int64_t n, void* Wq, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    if (m <= 0 || n <= 0 || m > kMaxExtent || n > kMaxExtent || n % 16) return POETX_ERR_SHAPE;
+    if (!W || !Wq || ((uintptr_t)Wq & 15)) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(quantize_rows(W, dtype == POETX_BF16, m, n, static_cast<int8_t*>(Wq),
+                          const_cast<float*>(qscales(Wq, m, n)), as_stream(stream)));
+    return POETX_OK;
+}
+
+int poetx_dequantize_weight(const void* Wq, int64_t m, int64_t n, void* W, void* stream) {
+    if (m <= 0 || n <= 0 || m > kMaxExtent || n > kMaxExtent || n % 16) return POETX_ERR_SHAPE;
+    if (!Wq || !W || ((uintptr_t)Wq & 15) || ((uintptr_t)W & 15)) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(dequantize_rows(qcodes(Wq), qscales(Wq, m, n), W, m, n, as_stream(stream)));
     return POETX_OK;
 }
 

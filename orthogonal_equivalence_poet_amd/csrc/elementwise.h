@@ -35,6 +35,11 @@ struct PermSegments {
 };
 hipError_t group_perms(const int* pi_R, const int* pi_P, int* out_R, int* inv_P, const PermSegments& seg,
                        hipStream_t s);
+// Symmetric int8 storage per row: scale[i] = max_j |W[i][j]| / 127, q[i][j] = nearest
+// integer to W[i][j] / scale[i] (ties to even) in [-127, 127]; zero rows: scale 0, codes 0.
+hipError_t quantize_rows(const void* W, bool bf16, int64_t m, int64_t n, int8_t* q, float* scale, hipStream_t s);
+// out (bf16 [m, n], 16-byte aligned, n % 16 == 0) = q[i][j] * scale[i].
+hipError_t dequantize_rows(const int8_t* q, const float* scale, void* out, int64_t m, int64_t n, hipStream_t s);
 // inv[pi[i]] = i.
 hipError_t invert_perm(const int* pi, int* inv, int64_t len, hipStream_t s);
 // out (d x d, 16-byte aligned, d % b == 0) = Pi^T diag(G) Pi as a dense matrix, given

@@ -419,6 +419,54 @@ __global__ void group_perms_kernel(const int* __restrict__ pi_R, const int* __re
     }
 }
 
+// ------------------------------------------------------ int8 weight storage
+// One workgroup per row: scale = max |w| / 127, q = the integer nearest w /
+// scale (ties to even) in [-127, 127], all in float32 with correctly rounded
+// divisions; a row of zeros gets scale 0 and codes 0.
+template <typename T>
+__global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict__ W, int64_t n,
+                                                            int8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float red[256];
+    const int64_t row = blockIdx.x;
+    const T* __restrict__ w = W + row * n;
+    float amax = 0.f;
+    for (int64_t j = threadIdx.x; j < n; j += 256) amax = fmaxf(amax, fabsf(load_f32(w + j)));
+    red[threadIdx.x] = amax;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    const float sc = red[0] / 127.0f;
+    if (threadIdx.x == 0) scale[row] = sc;
+    for (int64_t j = threadIdx.x; j < n; j += 256) {
+        float v = 0.f;
+        if (sc > 0.f) v = fminf(fmaxf(rintf(load_f32(w + j) / sc), -127.f), 127.f);
+        q[row * n + j] = static_cast<int8_t>(v);
+    }
+}
+
+// out[i][j] = bf16(q[i][j] * scale[i]); one thread per 16 codes (n % 16 == 0).
+__global__ void __launch_bounds__(256) dequantize_rows_kernel(const int8_t* __restrict__ q,
+                                                              const float* __restrict__ scale,
+                                                              bf16_t* __restrict__ out, int64_t m, int64_t n) {
+    const int64_t chunks = n / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= m * chunks) return;
+    const int64_t row = idx / chunks;
+    const int64_t c0 = (idx % chunks) * 16;
+    const uint4 v = *reinterpret_cast<const uint4*>(q + row * n + c0);
+    const float sc = scale[row];
+    int8_t e[16];
+    __builtin_memcpy(e, &v, sizeof(e));
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = pack_bf16x2((float)e[2 * i] * sc, (float)e[2 * i + 1] * sc);
+    uint4* dst = reinterpret_cast<uint4*>(out + row * n + c0);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // ------------------------------------------- dense block-diagonal transforms
 // out (d x d) = Pi^T diag(G_0, G_1, ...) Pi as a dense matrix, inv the inverse
 // of pi: out[a][c] = G[i / b][i % b][j % b] with i = inv[a], j = inv[c] when i
@@ -622,6 +670,26 @@ hipError_t group_perms(const int* pi_R, const int* pi_P, int* out_R, int* inv_P,
     if (len <= 0) return hipSuccess;
     hipLaunchKernelGGL(group_perms_kernel, dim3(blocks_for(len, 256)), dim3(256), 0, s, pi_R, pi_P, out_R, inv_P,
                        seg);
+    return hipGetLastError();
+}
+
+hipError_t quantize_rows(const void* W, bool bf16, int64_t m, int64_t n, int8_t* q, float* scale, hipStream_t s) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    if (m > 0x7fffffff) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(quantize_rows_kernel<bf16_t>, dim3((unsigned)m), dim3(256), 0, s, (const bf16_t*)W, n, q,
+                           scale);
+    else
+        hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)m), dim3(256), 0, s, (const float*)W, n, q,
+                           scale);
+    return hipGetLastError();
+}
+
+hipError_t dequantize_rows(const int8_t* q, const float* scale, void* out, int64_t m, int64_t n, hipStream_t s) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    if (n % 16 || ((uintptr_t)q & 15) || ((uintptr_t)out & 15)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dequantize_rows_kernel, dim3(blocks_for(m * (n / 16), 256)), dim3(256), 0, s, q, scale,
+                       (bf16_t*)out, m, n);
     return hipGetLastError();
 }
 

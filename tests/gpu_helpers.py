@@ -52,7 +52,7 @@ def cnp_bwd(q: torch.Tensor, dG: torch.Tensor, nblk: int, b: int, k: int, dtype:
 
 
 VARIANTS = {"fast": B.POETX_FAST, "mem": B.POETX_MEM, "four_perm": B.POETX_FOUR_PERM,
-            "weight_centric": B.POETX_WEIGHT_CENTRIC}
+            "weight_centric": B.POETX_WEIGHT_CENTRIC, "mem_q8": B.POETX_MEM_Q8}
 
 
 class GpuLayer:
@@ -73,8 +73,12 @@ class GpuLayer:
         self.dy = dev(inp["dy"], s.dtype) if "dy" in inp else None
         var = VARIANTS[self.variant]
         self.desc = B.desc(s.T, s.m, s.n, s.b, s.k, code(s.dtype), var)
-        # the chain variants take the pre-permuted weight, the comparison ones W0 itself
+        # the chain variants take the pre-permuted weight, the comparison ones W0 itself,
+        # the quantized one the int8 storage of the pre-permuted weight
         self.weight = self.Wt if var in (B.POETX_FAST, B.POETX_MEM) else self.W0
+        if var == B.POETX_MEM_Q8:
+            self.weight = B.workspace(B.poetx_qweight_bytes(s.m, s.n))
+            B.poetx_quantize_weight(self.Wt, s.m, s.n, self.weight)
 
     def forward(self):
         s = self.spec

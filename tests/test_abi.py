@@ -107,9 +107,9 @@ def test_comparison_variant_sizes_and_merge_rejection(B):
     assert lib.poetx_linear_saved_bytes(C.byref(wc)) == 2 * (m * m + 2 * m * n)
     assert lib.poetx_linear_bwd_workspace_bytes(C.byref(wc)) == 2 * 2 * m * n + 4 * m * m + 4 * n * n
     assert lib.poetx_linear_fwd_workspace_bytes(C.byref(wc)) >= 2 * n * n + 4 * (m + n)
-    # the four variant values are accepted, a fifth is not
-    assert lib.poetx_linear_saved_bytes(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 4))) == 0
-    assert lib.poetx_linear_fwd(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 4)), FAKE, FAKE, FAKE, FAKE, FAKE,
+    # the five variant values are accepted, a sixth is not
+    assert lib.poetx_linear_saved_bytes(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 5))) == 0
+    assert lib.poetx_linear_fwd(C.byref(B.desc(T, m, n, b, 3, B.POETX_BF16, 5)), FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.POETX_ERR_INVALID_ARG
     # saved is required by every variant but mem
     for d in (four, wc):
@@ -149,7 +149,7 @@ def test_group_desc_layout_sizes_and_validation(B):
     assert fwd(B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, [4096, 1000])) == B.POETX_ERR_SHAPE
     assert fwd(B.group_desc(T, 4000, b, 3, B.POETX_BF16, B.POETX_FAST, ms)) == B.POETX_ERR_SHAPE
     assert fwd(B.group_desc(T, n, 24, 3, B.POETX_BF16, B.POETX_FAST, ms)) == B.POETX_ERR_UNSUPPORTED
-    for v in (B.POETX_FOUR_PERM, B.POETX_WEIGHT_CENTRIC, 7):
+    for v in (B.POETX_FOUR_PERM, B.POETX_WEIGHT_CENTRIC, B.POETX_MEM_Q8, 7):
         assert fwd(B.group_desc(T, n, b, 3, B.POETX_BF16, v, ms)) == B.POETX_ERR_INVALID_ARG
     bad = B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, ms)
     bad.reserved = 1
@@ -168,6 +168,32 @@ def test_group_desc_layout_sizes_and_validation(B):
                                None) == B.POETX_OK
     with pytest.raises(ValueError):
         B.group_desc(T, n, b, 3, B.POETX_BF16, B.POETX_FAST, [256] * 9)
+
+
+def test_quantized_weight_layout_and_validation(B):
+    lib = B.load()
+    assert lib.poetx_qweight_bytes(4096, 4096) == 4096 * 4096 + 4 * 4096
+    assert lib.poetx_qweight_bytes(3, 16) == 256 + 12
+    assert lib.poetx_qweight_bytes(0, 16) == 0
+    assert lib.poetx_quantize_weight(FAKE, B.POETX_BF16, 8, 40, FAKE, None) == B.POETX_ERR_SHAPE   # n % 16
+    assert lib.poetx_quantize_weight(FAKE, 9, 8, 48, FAKE, None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_quantize_weight(None, B.POETX_BF16, 8, 48, FAKE, None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_quantize_weight(FAKE, B.POETX_BF16, 8, 48, FAKE + 8, None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_dequantize_weight(FAKE, -1, 48, FAKE, None) == B.POETX_ERR_SHAPE
+    # mem_q8: bf16 only, saves nothing, the mem workspace plus one bf16 weight
+    q8 = B.desc(2048, 4096, 1024, 256, 3, B.POETX_BF16, B.POETX_MEM_Q8)
+    mem = B.desc(2048, 4096, 1024, 256, 3, B.POETX_BF16, B.POETX_MEM)
+    assert lib.poetx_linear_saved_bytes(C.byref(q8)) == 0
+    for f in (lib.poetx_linear_fwd_workspace_bytes, lib.poetx_linear_bwd_workspace_bytes,
+              lib.poetx_merge_workspace_bytes):
+        assert f(C.byref(q8)) == f(C.byref(mem)) + 2 * 4096 * 1024
+    f32 = B.desc(2048, 4096, 1024, 256, 3, B.POETX_F32, B.POETX_MEM_Q8)
+    assert lib.poetx_linear_fwd(C.byref(f32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == B.POETX_ERR_UNSUPPORTED
+    # no saved buffer needed
+    need = lib.poetx_linear_fwd_workspace_bytes(C.byref(q8))
+    assert lib.poetx_linear_fwd(C.byref(q8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1,
+                                None) == B.POETX_ERR_WORKSPACE
 
 
 def test_cnp_and_skew_validation(B):
