@@ -6,7 +6,9 @@ Summary; the agidaily.cc article): R and P are block-diagonal orthogonal
 transforms in random permuted bases, every block a Cayley-Neumann series of a
 skew-symmetric Q kept as its upper triangle (the trainable parameters q_R, q_P).
 The review's Summary names the pieces this module exposes: the fast and the
-checkpointed mem variant (``mem_efficient_mode``) and merge-then-reinitialize
+checkpointed mem variant (``mem_efficient_mode``), the quantized variant on top
+of it (``quantized``: POET-XQ, the weight kept as int8 per output row and
+expanded inside each library call) and merge-then-reinitialize
 (``merge_then_reinitialize``).
 
 Everything the layer computes runs in libpoetx (``binding``): this module only
@@ -77,9 +79,9 @@ class _PoetLinearFn(torch.autograd.Function):
         T = x.shape[0]
         d = layer._desc(T)
         nR, nblk, b, k = layer.nblk_R, layer.nblk, layer.block_size, layer.k
-        code = _code(layer.Wt.dtype)
+        code = _code(layer.dtype)
         q = torch.cat([q_R.detach(), q_P.detach()]).contiguous()   # one flat batch of blocks
-        G = torch.empty((nblk, b, b), dtype=layer.Wt.dtype, device=x.device)
+        G = torch.empty((nblk, b, b), dtype=layer.dtype, device=x.device)
         cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), x.device)
         ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d), B.poetx_linear_bwd_workspace_bytes(d),
                              B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code),
@@ -87,7 +89,7 @@ class _PoetLinearFn(torch.autograd.Function):
         saved = B.workspace(B.poetx_linear_saved_bytes(d), x.device)
         y = torch.empty((T, layer.out_features), dtype=x.dtype, device=x.device)
         B.poetx_cnp_fwd_save(q, nblk, b, k, G, cnp_saved, ws)
-        B.poetx_linear_fwd(d, x, layer.Wt, G[:nR], G[nR:], layer.pi_R, layer.pi_P, y, saved, ws)
+        B.poetx_linear_fwd(d, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, y, saved, ws)
         ctx.save_for_backward(x)
         ctx.stash = (layer, d, q, G, cnp_saved, saved, ws)
         return y
@@ -101,9 +103,9 @@ class _PoetLinearFn(torch.autograd.Function):
         dx = torch.empty_like(x)
         dG = torch.empty((nblk, b, b), dtype=torch.float32, device=x.device)
         dq = torch.empty_like(q)
-        B.poetx_linear_bwd(d, dy, x, layer.Wt, G[:nR], G[nR:], layer.pi_R, layer.pi_P, saved, dx, dG[:nR], dG[nR:],
-                           ws)
-        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, _code(layer.Wt.dtype), cnp_saved, ws)
+        B.poetx_linear_bwd(d, dy, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, saved, dx, dG[:nR],
+                           dG[nR:], ws)
+        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, _code(layer.dtype), cnp_saved, ws)
         ctx.stash = None
         return dx, dq[:nR], dq[nR:], None
 
@@ -114,11 +116,13 @@ class POETLinear(torch.nn.Module):
     W0: [out_features, in_features] float32 or bfloat16 on a GPU; its dtype is the
     layer's compute dtype (activations must match).  block_size must divide both
     feature counts and be a multiple of 16; k is the Neumann order.  q_R and q_P
-    start at zero (R = P = I), so the layer starts as x W0^T.
+    start at zero (R = P = I), so the layer starts as x W0^T.  quantized=True
+    (bfloat16 only, implies the mem variant) keeps the pre-permuted weight as
+    int8 codes with one scale per output row instead of the weight itself.
     """
 
     def __init__(self, W0: torch.Tensor, block_size: int, k: int = 3, mem_efficient_mode: bool = False,
-                 generator: Optional[torch.Generator] = None):
+                 generator: Optional[torch.Generator] = None, quantized: bool = False):
         super().__init__()
         B.load()
         m, n = W0.shape
@@ -126,7 +130,11 @@ class POETLinear(torch.nn.Module):
         if m % b or n % b:
             raise ValueError(f"block size {b} must divide both {m} and {n}")
         self.out_features, self.in_features, self.block_size, self.k = m, n, b, int(k)
-        self.mem_efficient_mode = bool(mem_efficient_mode)
+        self.quantized = bool(quantized)
+        if self.quantized and W0.dtype != torch.bfloat16:
+            raise TypeError("the quantized layer computes in bfloat16")
+        self.mem_efficient_mode = bool(mem_efficient_mode) or self.quantized
+        self.dtype = W0.dtype
         self.nblk_R, self.nblk_P = m // b, n // b
         self.nblk = self.nblk_R + self.nblk_P
         ntri = b * (b - 1) // 2
@@ -134,8 +142,15 @@ class POETLinear(torch.nn.Module):
         self.register_buffer("pi_R", _perm(m, generator, dev))
         self.register_buffer("pi_P", _perm(n, generator, dev))
         W0 = W0.detach().contiguous()
-        self.register_buffer("Wt", torch.empty_like(W0))
-        B.poetx_prepermute(W0, self.Wt, m, n, self.pi_R, self.pi_P)
+        Wt = torch.empty_like(W0)
+        B.poetx_prepermute(W0, Wt, m, n, self.pi_R, self.pi_P)
+        if self.quantized:
+            # int8 codes [m, n] then float32 row scales, one byte buffer (the library's layout)
+            self.register_buffer("Wq", B.workspace(B.poetx_qweight_bytes(m, n), dev))
+            B.poetx_quantize_weight(Wt, m, n, self.Wq)
+            del Wt
+        else:
+            self.register_buffer("Wt", Wt)
         self.q_R = torch.nn.Parameter(torch.zeros((self.nblk_R, ntri), dtype=torch.float32, device=dev))
         self.q_P = torch.nn.Parameter(torch.zeros((self.nblk_P, ntri), dtype=torch.float32, device=dev))
         # AdamW moments over the flat (q_R, q_P) batch and the updates since the last reset
@@ -143,13 +158,19 @@ class POETLinear(torch.nn.Module):
         self.register_buffer("adam_v", torch.zeros((self.nblk, ntri), dtype=torch.float32, device=dev))
         self.adam_t = 0
 
+    @property
+    def weight(self) -> torch.Tensor:
+        """What the library reads as the stored weight: Wt, or the int8 buffer Wq."""
+        return self.Wq if self.quantized else self.Wt
+
     def _desc(self, T: int) -> B.LinearDesc:
-        variant = B.POETX_MEM if self.mem_efficient_mode else B.POETX_FAST
-        return B.desc(T, self.out_features, self.in_features, self.block_size, self.k, _code(self.Wt.dtype), variant)
+        variant = (B.POETX_MEM_Q8 if self.quantized else B.POETX_MEM if self.mem_efficient_mode
+                   else B.POETX_FAST)
+        return B.desc(T, self.out_features, self.in_features, self.block_size, self.k, _code(self.dtype), variant)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
-        x2 = x.reshape(-1, self.in_features).to(self.Wt.dtype).contiguous()
+        x2 = x.reshape(-1, self.in_features).to(self.dtype).contiguous()
         y = _PoetLinearFn.apply(x2, self.q_R, self.q_P, self)
         return y.reshape(*lead, self.out_features)
 
@@ -173,12 +194,12 @@ class POETLinear(torch.nn.Module):
         """Fold R W0 P into the stored weight, draw new permutations, set q to zero
         and reset the optimizer moments and count."""
         d = self._desc(0)
-        pi_R_new = _perm(self.out_features, generator, self.Wt.device)
-        pi_P_new = _perm(self.in_features, generator, self.Wt.device)
-        ws = B.workspace(B.poetx_merge_workspace_bytes(d), self.Wt.device)
+        pi_R_new = _perm(self.out_features, generator, self.weight.device)
+        pi_P_new = _perm(self.in_features, generator, self.weight.device)
+        ws = B.workspace(B.poetx_merge_workspace_bytes(d), self.weight.device)
         q_R = self.q_R.detach().contiguous()
         q_P = self.q_P.detach().contiguous()
-        B.poetx_merge(d, self.Wt, q_R, q_P, self.pi_R, self.pi_P, pi_R_new, pi_P_new, ws)
+        B.poetx_merge(d, self.weight, q_R, q_P, self.pi_R, self.pi_P, pi_R_new, pi_P_new, ws)
         self.q_R.copy_(q_R)
         self.q_P.copy_(q_P)
         self.pi_R.copy_(pi_R_new)

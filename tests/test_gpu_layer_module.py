@@ -104,3 +104,38 @@ def test_cayley_neumann_operator(b, k, dtype):
     assert rel_fro(host(G), O.blocks_from_params(q_np, b, k)) < tol
     ref = O.params_grad_from_skew_grad(O.cnp_vjp(O.skew_from_params(q_np, b), dG_np, k))
     assert rel_fro(host(q.grad), ref) < tol
+
+
+def test_quantized_module_forward_backward_and_merge():
+    m, n, b, k = 256, 128, 64, 3
+    W0 = I.gaussian((m, n), 0.02, "bf16", 15, 99, 0)
+    gen = torch.Generator().manual_seed(99)
+    lay = POETLinear(torch.from_numpy(W0).to(DEV).to(torch.bfloat16), b, k, generator=gen, quantized=True)
+    assert lay.mem_efficient_mode and not hasattr(lay, "Wt") and lay.Wq.dtype == torch.uint8
+    with torch.no_grad():
+        lay.q_R.copy_(torch.from_numpy(I.gaussian(tuple(lay.q_R.shape), 0.02, "f32", 15, 99, 1)))
+        lay.q_P.copy_(torch.from_numpy(I.gaussian(tuple(lay.q_P.shape), 0.02, "f32", 15, 99, 2)))
+    x_np = I.gaussian((40, n), 1.0, "bf16", 16, m, n)
+    dy_np = I.gaussian((40, m), 1.0, "bf16", 17, m, n)
+    x = torch.from_numpy(x_np).to(DEV).to(torch.bfloat16).requires_grad_(True)
+    y = lay(x)
+    (y.float() * torch.from_numpy(dy_np).to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    pi_R, pi_P = host(lay.pi_R).astype(np.int64), host(lay.pi_P).astype(np.int64)
+    q_R, q_P = host(lay.q_R), host(lay.q_P)
+    # the oracle on the weight the int8 storage stands for, back in W0's basis
+    qc, sc = O.quantize_rows_int8(O.prepermute(W0, pi_R, pi_P))
+    W0q = np.empty((m, n))
+    W0q[np.ix_(pi_R, pi_P)] = O.dequantize_rows(qc, sc)
+    y_ref = O.forward(x_np, W0q, q_R, q_P, pi_R, pi_P, b, k)
+    dx_ref, dq_R, dq_P, _, _ = O.backward(dy_np, x_np, W0q, q_R, q_P, pi_R, pi_P, b, k)
+    assert rel_fro(host(y), y_ref) < 1.5e-2
+    assert rel_fro(host(x.grad), dx_ref) < 1.5e-2
+    assert rel_fro(host(lay.q_R.grad), dq_R) < 1.5e-2 and rel_fro(host(lay.q_P.grad), dq_P) < 1.5e-2
+    # a merge keeps the function up to the new quantization of the merged weight
+    with torch.no_grad():
+        y0 = lay(x)
+        lay.merge_then_reinitialize(torch.Generator().manual_seed(100))
+        y1 = lay(x)
+    assert not lay.q_R.any() and not lay.q_P.any()
+    assert rel_fro(host(y1), host(y0)) < 1.5e-2
