@@ -157,3 +157,29 @@ def test_group_empty_batch_and_repeat_is_bitwise():
     g.run()
     for a, c in zip(first, (g.y, g.dx, g.dG_R, g.dG_P)):
         assert torch.equal(a, c)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("names", [("q_proj", "k_proj", "v_proj"), ("gate_proj", "up_proj")])
+def test_llama8b_layer_groups_full_size_sampled(names):
+    """The groups the layer bench times (mem variant, 2048 tokens), sampled rows and blocks."""
+    specs = [sp for sp in I.llama8b_layer() if sp.name.split("_", 1)[1] in names]
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    g = GpuGroup(specs, inps)
+    g.run()
+    rows = [0, 1, 999, specs[0].T - 1]
+    x = inps[0]["x"]
+    dx_ref = 0.0
+    errs = {}
+    for i, (sp, inp, (ys, rs, ps)) in enumerate(zip(specs, inps, g.slices())):
+        G_R = O.blocks_from_params(inp["q_R"], sp.b, sp.k)
+        G_P = O.blocks_from_params(inp["q_P"], sp.b, sp.k)
+        args = (inp["W0"], G_R, G_P, inp["pi_R"], inp["pi_P"])
+        errs[f"y{i}"] = rel_fro(host(g.y[rows][:, ys]), O.forward_from_blocks(x[rows], *args))
+        dx_ref = dx_ref + O.input_grad(inp["dy"][rows], *args)
+        jR, jP = [0, sp.nblk_R - 1], [0, sp.nblk_P - 1]
+        errs[f"dG_R{i}"] = rel_fro(host(g.dG_R[rs][jR]), O.block_grad_blocks(inp["dy"], x, *args, "R", jR))
+        errs[f"dG_P{i}"] = rel_fro(host(g.dG_P[ps][jP]), O.block_grad_blocks(inp["dy"], x, *args, "P", jP))
+    errs["dx"] = rel_fro(host(g.dx[rows]), dx_ref)
+    assert all(e <= tol("bf16") for e in errs.values()), errs
