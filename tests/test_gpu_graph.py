@@ -20,7 +20,9 @@ def _lib(gpu_lib):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("dtype,variant", [("f32", B.POETX_FAST), ("bf16", B.POETX_MEM), ("bf16", B.POETX_FAST)])
+@pytest.mark.parametrize("dtype,variant", [("f32", B.POETX_FAST), ("bf16", B.POETX_MEM), ("bf16", B.POETX_FAST),
+                                           ("bf16", B.POETX_MEM_Q8), ("bf16", B.POETX_FOUR_PERM),
+                                           ("bf16", B.POETX_WEIGHT_CENTRIC)])
 def test_step_graph_replays_match_eager(dtype, variant):
     T, m, n, b, k = 96, 256, 128, 64, 3
     spec = I.LinearSpec("graph", m=m, n=n, b=b, k=k, T=T, dtype=dtype, q_std=0.02, key=(13, m, n))
@@ -33,6 +35,12 @@ def test_step_graph_replays_match_eager(dtype, variant):
     pi_R, pi_P = dev_i32(inp["pi_R"]), dev_i32(inp["pi_P"])
     Wt = torch.empty((m, n), dtype=td, device=DEV)
     B.poetx_prepermute(dev(inp["W0"], dtype), Wt, m, n, pi_R, pi_P)
+    if variant == B.POETX_MEM_Q8:        # the int8 storage of the pre-permuted weight
+        Wq = B.workspace(B.poetx_qweight_bytes(m, n))
+        B.poetx_quantize_weight(Wt, m, n, Wq)
+        Wt = Wq
+    elif variant in (B.POETX_FOUR_PERM, B.POETX_WEIGHT_CENTRIC):   # these take W0 itself
+        Wt = dev(inp["W0"], dtype)
     q0 = torch.cat([dev(inp["q_R"]), dev(inp["q_P"])]).contiguous()
     q = q0.clone()
     G = torch.empty((nblk, b, b), dtype=td, device=DEV)
@@ -90,4 +98,68 @@ def test_step_graph_replays_match_eager(dtype, variant):
         step()   # eager work between the replays
         torch.cuda.synchronize()
         assert torch.equal(q, ref[4])
+    assert np.isfinite(ref[3].cpu().numpy()).all()
+
+
+def test_group_step_graph_replays_match_eager():
+    """q/k/v-shaped group (grouped dense launches), mem variant, captured and replayed."""
+    T, n, b, k = 130, 256, 64, 3
+    ms = [256, 128, 128]
+    specs = [I.LinearSpec(f"ggraph{i}", m=m, n=n, b=b, k=k, T=T, dtype="bf16", q_std=0.02, key=(14, i, m))
+             for i, m in enumerate(ms)]
+    inps = [I.make_linear_inputs(sp) for sp in specs]
+    M = sum(ms)
+    x = dev(inps[0]["x"], "bf16")
+    dy = torch.cat([dev(inp["dy"], "bf16") for inp in inps], dim=1).contiguous()
+    pi_R = torch.cat([dev_i32(inp["pi_R"]) for inp in inps]).contiguous()
+    pi_P = torch.cat([dev_i32(inp["pi_P"]) for inp in inps]).contiguous()
+    Wt = torch.empty((M, n), dtype=torch.bfloat16, device=DEV)
+    o = 0
+    for m, inp, pr, pp in zip(ms, inps, pi_R.split(ms), pi_P.split(n)):
+        B.poetx_prepermute(dev(inp["W0"], "bf16"), Wt[o:o + m], m, n, pr, pp)
+        o += m
+    qR = torch.cat([dev(inp["q_R"]) for inp in inps])
+    qP = torch.cat([dev(inp["q_P"]) for inp in inps])
+    q = torch.cat([qR, qP]).contiguous()
+    nR, nblk = M // b, M // b + len(ms) * n // b
+    G = torch.empty((nblk, b, b), dtype=torch.bfloat16, device=DEV)
+    dG = torch.empty((nblk, b, b), dtype=torch.float32, device=DEV)
+    dq = torch.empty_like(q)
+    y = torch.empty((T, M), dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty((T, n), dtype=torch.bfloat16, device=DEV)
+    gd = B.group_desc(T, n, b, k, B.POETX_BF16, B.POETX_MEM, ms)
+    ws = B.workspace(max(B.poetx_group_fwd_workspace_bytes(gd), B.poetx_group_bwd_workspace_bytes(gd),
+                         B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, B.POETX_BF16),
+                         B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, B.POETX_BF16)))
+    cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, B.POETX_BF16))
+
+    def step():
+        B.poetx_cnp_fwd_save(q, nblk, b, k, G, cnp_saved, ws)
+        B.poetx_group_fwd(gd, x, Wt, G[:nR], G[nR:], pi_R, pi_P, y, None, ws)
+        B.poetx_group_bwd(gd, dy, x, Wt, G[:nR], G[nR:], pi_R, pi_P, None, dx, dG[:nR], dG[nR:], ws)
+        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, B.POETX_BF16, cnp_saved, ws)
+
+    outs = (y, dx, dG, dq)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want)
+        step()   # eager work between the replays
+        torch.cuda.synchronize()
     assert np.isfinite(ref[3].cpu().numpy()).all()
