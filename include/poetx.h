@@ -28,7 +28,10 @@
  * Memory and execution model (all entry points):
  *   - every tensor pointer is a caller-owned DEVICE pointer, contiguous
  *     row-major, 16-byte aligned; the library never allocates or frees device
- *     memory and keeps no pointer after the call returns;
+ *     memory and keeps no pointer after the call returns.  The layer and group
+ *     calls (poetx_linear_*, poetx_group_*) check the alignment of every
+ *     pointer they take and return POETX_ERR_INVALID_ARG for one that is not
+ *     16-byte aligned (a contiguous view at an odd element offset, say);
  *   - work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*, NULL = the null stream); results are ready when the stream is;
  *   - scratch memory comes from the caller's workspace `ws` of `ws_bytes`

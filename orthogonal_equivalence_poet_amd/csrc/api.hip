@@ -52,6 +52,13 @@ struct Carver {
 };
 
 inline bool dtype_ok(int d) { return d == POETX_F32 || d == POETX_BF16; }
+
+// Every tensor the layer entry points take is read or written with 16-byte
+// vector accesses (and the direct-to-LDS operand loads): a pointer off that
+// alignment is an argument error, not a misaligned access.
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... P>
+inline bool all_al16(const P*... p) { return (al16(p) && ...); }
 inline size_t esize(int d) { return d == POETX_BF16 ? 2 : 4; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -1108,6 +1115,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
     if (d->T == 0) return POETX_OK;
     if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
     if (!mem_chain(d) && !saved) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws)) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_fwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
@@ -1168,6 +1176,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     }
     if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
     if (!mem_chain(d) && !saved) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(dy, x, Wt, G_R, G_P, pi_R, pi_P, saved, dx, dG_R, dG_P, ws)) return POETX_ERR_INVALID_ARG;
     const size_t need = poetx_linear_bwd_workspace_bytes(d);
     if (ws_bytes < need) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
@@ -1250,6 +1259,7 @@ int poetx_group_fwd(const poetx_group_desc* g, const void* x, const void* Wt, co
     if (P.lin.T == 0) return POETX_OK;
     if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
     if (P.lin.variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws)) return POETX_ERR_INVALID_ARG;
     if (ws_bytes < poetx_group_fwd_workspace_bytes(g)) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
     const hipStream_t s = as_stream(stream);
@@ -1293,6 +1303,7 @@ int poetx_group_bwd(const poetx_group_desc* g, const void* dy, const void* x, co
     }
     if (!dy || !x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !dx) return POETX_ERR_INVALID_ARG;
     if (d->variant == POETX_FAST && !saved) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(dy, x, Wt, G_R, G_P, pi_R, pi_P, saved, dx, dG_R, dG_P, ws)) return POETX_ERR_INVALID_ARG;
     if (ws_bytes < poetx_group_bwd_workspace_bytes(g)) return POETX_ERR_WORKSPACE;
     if (!ws) return POETX_ERR_INVALID_ARG;
     Carver cv(ws);

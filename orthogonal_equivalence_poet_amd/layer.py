@@ -47,19 +47,19 @@ class _CayleyNeumannFn(torch.autograd.Function):
         code = _code(dtype)
         q = q.detach().contiguous()
         G = torch.empty((nblk, b, b), dtype=dtype, device=q.device)
-        ws = B.workspace(max(B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code),
-                             B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, code)), q.device)
+        ws = B.workspace(B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code), q.device)
         saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), q.device)
         B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
-        ctx.stash = (q, b, k, code, saved, ws)
+        ctx.stash = (q, b, k, code, saved)
         return G
 
     @staticmethod
     def backward(ctx, dG):
-        q, b, k, code, saved, ws = ctx.stash
-        dq = torch.empty_like(q)
-        B.poetx_cnp_bwd_saved(q, dG.float().contiguous(), q.shape[0], b, k, dq, code, saved, ws)
+        q, b, k, code, saved = ctx.stash
         ctx.stash = None
+        dq = torch.empty_like(q)
+        ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(q.shape[0], b, k, code), q.device)
+        B.poetx_cnp_bwd_saved(q, dG.float().contiguous(), q.shape[0], b, k, dq, code, saved, ws)
         return dq, None, None, None
 
 
@@ -72,7 +72,16 @@ def cayley_neumann(q: torch.Tensor, b: int, k: int = 3, dtype: torch.dtype = tor
 
 
 class _PoetLinearFn(torch.autograd.Function):
-    """y = R W0 P x for x [T, n]; gradients for x, q_R and q_P (none for W0)."""
+    """y = R W0 P x for x [T, n]; gradients for x, q_R and q_P (none for W0).
+
+    What lives from the forward to the backward is exactly what the variant
+    saves (the review's Summary and Reproducibility & code: POET-X_fast keeps
+    intermediates, the checkpointed POET-X_mem recomputes them):
+      fast: the blocks G, the transform's saved Q / Q^2 terms and the chain's
+            saved h2 and gathered input (poetx_linear_saved_bytes);
+      mem (and the quantized layer): nothing beyond x and the parameters; the
+            backward forms G again from q.
+    Workspaces are taken inside each call and released before it returns."""
 
     @staticmethod
     def forward(ctx, x, q_R, q_P, layer):
@@ -82,31 +91,45 @@ class _PoetLinearFn(torch.autograd.Function):
         code = _code(layer.dtype)
         q = torch.cat([q_R.detach(), q_P.detach()]).contiguous()   # one flat batch of blocks
         G = torch.empty((nblk, b, b), dtype=layer.dtype, device=x.device)
-        cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), x.device)
-        ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d), B.poetx_linear_bwd_workspace_bytes(d),
-                             B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code),
-                             B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, code)), x.device)
-        saved = B.workspace(B.poetx_linear_saved_bytes(d), x.device)
         y = torch.empty((T, layer.out_features), dtype=x.dtype, device=x.device)
-        B.poetx_cnp_fwd_save(q, nblk, b, k, G, cnp_saved, ws)
-        B.poetx_linear_fwd(d, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, y, saved, ws)
-        ctx.save_for_backward(x)
-        ctx.stash = (layer, d, q, G, cnp_saved, saved, ws)
+        ws = B.workspace(max(B.poetx_linear_fwd_workspace_bytes(d),
+                             B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code)), x.device)
+        if layer.mem_efficient_mode:
+            B.poetx_cnp_fwd(q, nblk, b, k, G, ws)
+            B.poetx_linear_fwd(d, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, y, None, ws)
+            ctx.stash = (layer, d, None, None, None)
+        else:
+            cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), x.device)
+            saved = B.workspace(B.poetx_linear_saved_bytes(d), x.device)
+            B.poetx_cnp_fwd_save(q, nblk, b, k, G, cnp_saved, ws)
+            B.poetx_linear_fwd(d, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, y, saved, ws)
+            ctx.stash = (layer, d, G, cnp_saved, saved)
+        ctx.save_for_backward(x, q_R, q_P)
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        (x,) = ctx.saved_tensors
-        layer, d, q, G, cnp_saved, saved, ws = ctx.stash
+        x, q_R, q_P = ctx.saved_tensors
+        layer, d, G, cnp_saved, saved = ctx.stash
+        ctx.stash = None
         nR, nblk, b, k = layer.nblk_R, layer.nblk, layer.block_size, layer.k
+        code = _code(layer.dtype)
+        q = torch.cat([q_R.detach(), q_P.detach()]).contiguous()
         dy = dy.to(x.dtype).contiguous()
         dx = torch.empty_like(x)
         dG = torch.empty((nblk, b, b), dtype=torch.float32, device=x.device)
         dq = torch.empty_like(q)
+        ws = B.workspace(max(B.poetx_linear_bwd_workspace_bytes(d),
+                             B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, code),
+                             B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, code)), x.device)
+        if G is None:
+            # mem: the blocks again from q, keeping the transform's terms for its backward
+            G = torch.empty((nblk, b, b), dtype=layer.dtype, device=x.device)
+            cnp_saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, code), x.device)
+            B.poetx_cnp_fwd_save(q, nblk, b, k, G, cnp_saved, ws)
         B.poetx_linear_bwd(d, dy, x, layer.weight, G[:nR], G[nR:], layer.pi_R, layer.pi_P, saved, dx, dG[:nR],
                            dG[nR:], ws)
-        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, _code(layer.dtype), cnp_saved, ws)
-        ctx.stash = None
+        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, code, cnp_saved, ws)
         return dx, dq[:nR], dq[nR:], None
 
 

@@ -30,11 +30,36 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def rel_fro(got, ref) -> float:
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+def _rel(got, ref) -> float:
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def rel_fro(got, ref) -> float:
+    """Relative Frobenius error, taken over the whole tensor AND over every
+    slice along the leading axis (a token row of an activation [T, d], a block
+    of G / dG [nblk, b, b] or of dq [nblk, b(b-1)/2], a row of a weight), and
+    the largest of these returned: a tolerance on it bounds every row or block
+    on its own, so an error confined to one row, one ragged tail tile or one
+    block cannot hide in the aggregate.  A slice whose reference is zero is
+    measured by its absolute norm."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = _rel(got, ref)
+    if got.ndim >= 2 and got.shape[0] > 1:
+        g2 = got.reshape(got.shape[0], -1)
+        r2 = ref.reshape(ref.shape[0], -1)
+        num = np.linalg.norm(g2 - r2, axis=1)
+        den = np.linalg.norm(r2, axis=1)
+        err = max(err, float(np.max(num / np.where(den > 0, den, 1.0))))
+    return err
+
+
+def rel_fro_whole(got, ref) -> float:
+    """The whole-tensor relative Frobenius error alone (for comparisons that are
+    not oracle parity, e.g. a layer's output before and after a merge)."""
+    return _rel(np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64))
 
 
 def cnp_fwd(q: torch.Tensor, nblk: int, b: int, k: int, dtype: str) -> torch.Tensor:

@@ -87,6 +87,36 @@ def test_null_pointers_and_small_workspace(B):
     assert lib.poetx_linear_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
 
 
+def test_misaligned_pointers_are_rejected(B):
+    """A contiguous view at an odd element offset is an argument error in the
+    layer and group calls (their kernels use 16-byte vector and direct-to-LDS
+    accesses), reported before any HIP call."""
+    lib = B.load()
+    d = _d(B, dtype=B.POETX_BF16)
+    nf = lib.poetx_linear_fwd_workspace_bytes(C.byref(d))
+    nb = lib.poetx_linear_bwd_workspace_bytes(C.byref(d))
+    odd = FAKE + 2   # one bf16 element past an aligned address
+    for i in range(9):
+        args = [FAKE] * 9
+        args[i] = odd
+        assert lib.poetx_linear_fwd(C.byref(d), *args, nf, None) == B.POETX_ERR_INVALID_ARG, i
+    for i in range(12):
+        args = [FAKE] * 12
+        args[i] = odd
+        assert lib.poetx_linear_bwd(C.byref(d), *args, nb, None) == B.POETX_ERR_INVALID_ARG, i
+    g = B.group_desc(32, 64, 16, 3, B.POETX_BF16, B.POETX_FAST, [64, 32])
+    gf = lib.poetx_group_fwd_workspace_bytes(C.byref(g))
+    gb = lib.poetx_group_bwd_workspace_bytes(C.byref(g))
+    for i in range(9):
+        args = [FAKE] * 9
+        args[i] = odd
+        assert lib.poetx_group_fwd(C.byref(g), *args, gf, None) == B.POETX_ERR_INVALID_ARG, i
+    for i in range(12):
+        args = [FAKE] * 12
+        args[i] = odd
+        assert lib.poetx_group_bwd(C.byref(g), *args, gb, None) == B.POETX_ERR_INVALID_ARG, i
+
+
 def test_empty_batch_forward_is_a_no_op(B):
     lib = B.load()
     d = _d(B, T=0)

@@ -139,3 +139,48 @@ def test_quantized_module_forward_backward_and_merge():
         y1 = lay(x)
     assert not lay.q_R.any() and not lay.q_P.any()
     assert rel_fro(host(y1), host(y0)) < 1.5e-2
+
+
+def _rnd(nbytes):
+    """Bytes torch's caching allocator books for one tensor of nbytes (512-byte granules)."""
+    return (max(int(nbytes), 1) + 511) // 512 * 512
+
+
+@pytest.mark.parametrize("mem,quantized", [(False, False), (True, False), (True, True)])
+def test_module_keeps_only_what_the_variant_saves(mem, quantized):
+    """Device memory held from the forward to the backward is exactly what the
+    variant saves: fast keeps the blocks G, the transform's saved terms and the
+    chain's saved h2 and gathered input; mem and the quantized layer keep
+    nothing beyond the caller's x and the parameters (no workspace, no dequantized
+    weight).  After the backward only the gradients remain."""
+    from orthogonal_equivalence_poet_amd import binding as B
+    m, n, b, k, T = 1024, 512, 128, 3, 300
+    W0 = I.gaussian((m, n), 0.02, "bf16", 25, m, n)
+    lay = POETLinear(torch.from_numpy(W0).to(DEV).to(torch.bfloat16), b, k, mem_efficient_mode=mem,
+                     generator=torch.Generator().manual_seed(25), quantized=quantized)
+    with torch.no_grad():
+        lay.q_R.copy_(torch.from_numpy(I.gaussian(tuple(lay.q_R.shape), 0.02, "f32", 25, 1)))
+        lay.q_P.copy_(torch.from_numpy(I.gaussian(tuple(lay.q_P.shape), 0.02, "f32", 25, 2)))
+    x = torch.from_numpy(I.gaussian((T, n), 1.0, "bf16", 26, 0)).to(DEV).to(torch.bfloat16).requires_grad_(True)
+    dy = torch.from_numpy(I.gaussian((T, m), 1.0, "bf16", 27, 0)).to(DEV).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    y = lay(x)
+    torch.cuda.synchronize()
+    kept = torch.cuda.memory_allocated() - before - _rnd(2 * T * m)
+    d = lay._desc(T)
+    nblk = lay.nblk
+    if mem:
+        want = 0
+    else:
+        want = (_rnd(2 * nblk * b * b) + _rnd(B.poetx_cnp_saved_bytes(nblk, b, k, B.POETX_BF16))
+                + _rnd(B.poetx_linear_saved_bytes(d)))
+    assert kept == want, (kept, want)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    # x.grad, and q_R.grad / q_P.grad either as their own tensors or as the two
+    # views of the one dq buffer the backward returns (autograd may keep either)
+    dq_bytes = 4 * (lay.q_R.numel() + lay.q_P.numel())
+    grads = {_rnd(2 * T * n) + _rnd(lay.q_R.numel() * 4) + _rnd(lay.q_P.numel() * 4),
+             _rnd(2 * T * n) + _rnd(dq_bytes)}
+    assert torch.cuda.memory_allocated() - before - _rnd(2 * T * m) in grads

@@ -139,8 +139,15 @@ def test_cnp_fwd_parity(b, k, dtype, std, norm):
     ref = O.neumann_cayley(O.skew_from_params(q, b), k)
     assert rel_fro(G, ref) <= tol(dtype)
     eye = np.eye(b)
-    # the informative part G - I (small for small q) is checked on its own
+    # the informative part G - I (small for small q) is checked on its own.
+    # Against the exact G, bf16 storage alone costs up to 1.62e-2 here (at
+    # b = 256, q ~ N(0, 1e-3^2) the diagonal 1 - 2.6e-4 rounds to 1.0, and G - I
+    # loses its diagonal), so that check is held to 3e-2; against the oracle's G
+    # rounded to bf16 once (the best a bf16 output can be) it meets the bf16 bar.
     assert rel_fro(G - eye, ref - eye) <= (1e-4 if dtype == "f32" else 3e-2)
+    if dtype == "bf16":
+        ref_bf = I.round_to_bf16(ref.astype(np.float32)).astype(np.float64)
+        assert rel_fro(G - eye, ref_bf - eye) <= tol(dtype)
 
 
 @pytest.mark.parametrize("b,k,dtype,std,norm", CNP_CASES)
