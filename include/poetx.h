@@ -208,6 +208,29 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt,
                      const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* poetx_linear_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same forward, same arguments and results, bit for bit, but without a
+ * workspace argument.  Its scratch is a device array of the library's own,
+ * POETX_NOALLOC_SCRATCH_BYTES bytes, one copy on each GPU the library runs on,
+ * held from the first call on that GPU until the process ends.  The caller
+ * still passes x, y, saved and the weights.
+ *   - a descriptor whose poetx_linear_fwd_workspace_bytes exceeds
+ *     POETX_NOALLOC_SCRATCH_BYTES returns POETX_ERR_WORKSPACE before any HIP
+ *     call (at bf16 that admits, e.g., the fast forward at T * max(m, n) up to
+ *     16 Mi elements: 2048 tokens of a 4096-wide layer);
+ *   - the call allocates and frees nothing (no hipMalloc, hipFree or
+ *     allocating library routine); on a device's first call it looks up the
+ *     array's address once (hipGetSymbolAddress);
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (different streams or threads without ordering) race; calls ordered
+ *     on one stream do not.  Nothing in the array needs to start at zero.
+ * Other errors as for poetx_linear_fwd. */
+#define POETX_NOALLOC_SCRATCH_BYTES (64u << 20)
+int poetx_linear_fwd_noalloc(const poetx_linear_desc* d, const void* x, const void* Wt,
+                             const void* G_R, const void* G_P, const int32_t* pi_R,
+                             const int32_t* pi_P, void* y, void* saved, void* stream);
+
 /* Backward of the chain for L = <dy, y>; W0 is frozen, so there is no dW0.
  *   dx  = dy R W0 P                              dtype [T, n]
  *   dG_R[j] = (Pi_R dR Pi_R^T) block j, dR = dy^T x P^T W0^T     float32 [m/b, b, b]

@@ -28,7 +28,7 @@ EXPORTS = [
     "poetx_cnp_saved_bytes", "poetx_cnp_fwd_save", "poetx_cnp_bwd_saved",
     "poetx_permute", "poetx_prepermute",
     "poetx_check_perm_workspace_bytes", "poetx_check_perm",
-    "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd",
+    "poetx_linear_saved_bytes", "poetx_linear_fwd_workspace_bytes", "poetx_linear_fwd", "poetx_linear_fwd_noalloc",
     "poetx_linear_bwd_workspace_bytes", "poetx_linear_bwd",
     "poetx_group_saved_bytes", "poetx_group_fwd_workspace_bytes", "poetx_group_fwd",
     "poetx_group_bwd_workspace_bytes", "poetx_group_bwd",
@@ -89,6 +89,7 @@ _SIGS = {
     "poetx_linear_saved_bytes": ([_DP], _SZ),
     "poetx_linear_fwd_workspace_bytes": ([_DP], _SZ),
     "poetx_linear_fwd": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
+    "poetx_linear_fwd_noalloc": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "poetx_linear_bwd_workspace_bytes": ([_DP], _SZ),
     "poetx_linear_bwd": ([_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_group_saved_bytes": ([_GP], _SZ),
@@ -271,6 +272,15 @@ def poetx_group_saved_bytes(g: GroupDesc) -> int:
 
 def poetx_group_fwd_workspace_bytes(g: GroupDesc) -> int:
     return load().poetx_group_fwd_workspace_bytes(C.byref(g))
+
+
+def poetx_linear_fwd_noalloc(d: LinearDesc, x, Wt, G_R, G_P, pi_R, pi_P, y, saved=None, stream=None):
+    _check("poetx_linear_fwd_noalloc", load().poetx_linear_fwd_noalloc(C.byref(d), _ptr(x), _ptr(Wt), _ptr(G_R),
+                                                                       _ptr(G_P), _ptr(pi_R), _ptr(pi_P), _ptr(y),
+                                                                       _ptr(saved), _stream(stream)))
+
+
+POETX_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def poetx_group_fwd(g: GroupDesc, x, Wt, G_R, G_P, pi_R, pi_P, y, saved=None, ws=None, stream=None):

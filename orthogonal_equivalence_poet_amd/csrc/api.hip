@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "dense_gemm.h"
@@ -911,6 +912,38 @@ int group_forward(const GroupPlan& P, const void* x, const void* Wt, const void*
 
 }  // namespace
 
+// ----------------------------------------------- no-allocation forward scratch
+// The workspace of poetx_linear_fwd_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  Host
+// code never uses the name itself (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, once per device, and is
+// kept below.
+static __device__ __align__(256) unsigned char scratch[POETX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (looked up on that device's first call).
+int scratch_address(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxScratchDevices) return POETX_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return POETX_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return POETX_OK;
+}
+
+}  // namespace
+
 // ======================================================================= ABI
 extern "C" {
 
@@ -1108,17 +1141,24 @@ size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
     return cv.off;
 }
 
-int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
-                     const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
-                     void* stream) {
-    POETX_TRY(check_desc(d));
-    if (d->T == 0) return POETX_OK;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the layer forward that need no workspace (both entry points).
+int check_linear_fwd_args(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R,
+                          const void* G_P, const int32_t* pi_R, const int32_t* pi_P, const void* y,
+                          const void* saved) {
     if (!x || !Wt || !G_R || !G_P || !pi_R || !pi_P || !y) return POETX_ERR_INVALID_ARG;
     if (!mem_chain(d) && !saved) return POETX_ERR_INVALID_ARG;
-    if (!all_al16(x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws)) return POETX_ERR_INVALID_ARG;
-    const size_t need = poetx_linear_fwd_workspace_bytes(d);
-    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
-    if (!ws) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(x, Wt, G_R, G_P, pi_R, pi_P, y, saved)) return POETX_ERR_INVALID_ARG;
+    return POETX_OK;
+}
+
+// The layer forward after validation, on a workspace of at least
+// poetx_linear_fwd_workspace_bytes(d) bytes at ws.
+int linear_fwd_run(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                   const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved, void* ws, void* stream) {
     Carver cv(ws);
     if (d->variant == POETX_WEIGHT_CENTRIC) {
         Carver sv(saved);
@@ -1146,6 +1186,35 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, 
     if (mem_chain(d)) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
     else a = static_cast<char*>(saved) + fast_saved_a_offset(d);
     return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, a, L.buf[1], as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
+                     const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved, void* ws, size_t ws_bytes,
+                     void* stream) {
+    POETX_TRY(check_desc(d));
+    if (d->T == 0) return POETX_OK;
+    POETX_TRY(check_linear_fwd_args(d, x, Wt, G_R, G_P, pi_R, pi_P, y, saved));
+    if (!al16(ws)) return POETX_ERR_INVALID_ARG;
+    const size_t need = poetx_linear_fwd_workspace_bytes(d);
+    if (ws_bytes < need) return POETX_ERR_WORKSPACE;
+    if (!ws) return POETX_ERR_INVALID_ARG;
+    return linear_fwd_run(d, x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws, stream);
+}
+
+int poetx_linear_fwd_noalloc(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R,
+                             const void* G_P, const int32_t* pi_R, const int32_t* pi_P, void* y, void* saved,
+                             void* stream) {
+    POETX_TRY(check_desc(d));
+    if (d->T == 0) return POETX_OK;
+    POETX_TRY(check_linear_fwd_args(d, x, Wt, G_R, G_P, pi_R, pi_P, y, saved));
+    if (poetx_linear_fwd_workspace_bytes(d) > (size_t)POETX_NOALLOC_SCRATCH_BYTES) return POETX_ERR_WORKSPACE;
+    void* ws = nullptr;
+    POETX_TRY(scratch_address(&ws));
+    return linear_fwd_run(d, x, Wt, G_R, G_P, pi_R, pi_P, y, saved, ws, stream);
 }
 
 size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {

@@ -117,6 +117,26 @@ def test_misaligned_pointers_are_rejected(B):
         assert lib.poetx_group_bwd(C.byref(g), *args, gb, None) == B.POETX_ERR_INVALID_ARG, i
 
 
+def test_noalloc_forward_validation(B):
+    """The forward without a workspace refuses a descriptor whose workspace
+    exceeds its scratch array, and bad arguments, before any HIP call."""
+    lib = B.load()
+    big = B.desc(8192, 14336, 4096, 512, 4, B.POETX_BF16, B.POETX_MEM)
+    assert lib.poetx_linear_fwd_workspace_bytes(C.byref(big)) > B.POETX_NOALLOC_SCRATCH_BYTES
+    assert lib.poetx_linear_fwd_noalloc(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                        None) == B.POETX_ERR_WORKSPACE
+    d = _d(B)
+    assert lib.poetx_linear_fwd_noalloc(C.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_linear_fwd_noalloc(C.byref(d), FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        None) == B.POETX_ERR_INVALID_ARG
+    assert lib.poetx_linear_fwd_noalloc(C.byref(_d(B, b=24)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        None) == B.POETX_ERR_UNSUPPORTED
+    # an empty batch returns before anything else
+    assert lib.poetx_linear_fwd_noalloc(C.byref(_d(B, T=0)), None, None, None, None, None, None, None, None,
+                                        None) == B.POETX_OK
+
+
 def test_empty_batch_forward_is_a_no_op(B):
     lib = B.load()
     d = _d(B, T=0)
