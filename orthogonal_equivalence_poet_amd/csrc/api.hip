@@ -345,34 +345,14 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
     const bool dual = cbf16 && b % 64 == 0 && pipe_gemm_supported(false, false, b, b, b, b, b, bb, bb) &&
                       pipe_gemm_supported(true, true, b, b, b, b, b, bb, bb);
     if (k == 3 && dual) {
-        // Same schedule as below with the products paired per launch:
-        // dA = dG + dG S and dS = 2 dG + dG S + T^T dG from one launch,
-        // dQ = 2 dA + dS Q^T + Q^T dS from a second.
-        PipeArgs d;
-        d.A = dGc; d.lda = b; d.strideA = bb;
-        d.B = B.Sc; d.ldb = b; d.strideB = bb;
-        d.A2 = B.Tc; d.lda2 = b; d.strideA2 = bb;
-        d.B2 = dGc; d.ldb2 = b; d.strideB2 = bb;
-        d.C = B.a32; d.ldc = b; d.strideC = bb;
-        d.C2 = B.c_c; d.ldc2 = b; d.strideC2 = bb;
-        d.Cin1 = dG; d.ldcin1 = b; d.strideCin1 = bb;
-        d.beta1 = 1.f; d.beta2 = 2.f;
-        d.M = d.N = d.K = ib;
-        d.batch = (int)nblk;
-        d.k_per_split = ib;
-        HIP_TRY(pipe_gemm_dual(true, true, d, s));
-        PipeArgs e;
-        e.A = B.c_c; e.lda = b; e.strideA = bb;
-        e.B = B.Qc; e.ldb = b; e.strideB = bb;
-        e.A2 = B.Qc; e.lda2 = b; e.strideA2 = bb;
-        e.B2 = B.c_c; e.ldb2 = b; e.strideB2 = bb;
-        e.C = dQ; e.ldc = b; e.strideC = bb;
-        e.Cin1 = B.a32; e.ldcin1 = b; e.strideCin1 = bb; e.beta1 = 2.f;
-        e.M = e.N = e.K = ib;
-        e.batch = (int)nblk;
-        e.k_per_split = ib;
-        // the skew pack rides on the second launch (mirrored tile pairs)
-        HIP_TRY(cnp_pack_pair(e, dq, ib, s));
+        // Only the skew part of dQ reaches dq: with X1 = dG S, X2 = T^T dG,
+        // dS = 2 dG + X1 + X2 and Sigma = dS + dS^T (symmetric),
+        // dQ - dQ^T = 2 (dA - dA^T) - (P - P^T) with dA = dG + X1, P = Sigma Q,
+        // since Q Sigma = -(Sigma Q)^T.  Pass 1 writes Sigma and the packed
+        // 2 (dA - dA^T); pass 2 adds the packed -(P - P^T).  Three products
+        // instead of four; the pack rides on both passes.
+        HIP_TRY(cnp_bwd_sym(dGc, dG, B.Sc, B.Tc, B.c_c, dq, nblk, ib, s));
+        HIP_TRY(cnp_bwd_sigq(B.c_c, B.Qc, dq, nblk, ib, s));
         packed = true;
     } else if (k == 3) {
         // G = A B with A = I + T, B = I + S (T = 2Q + S, S symmetric):

@@ -95,6 +95,16 @@ int pipe_tile_cols(PipeTile t);
 // dq[idx(r, c)] = dQ[r][c] - dQ[c][r] for r < c (row-major upper triangle).
 hipError_t cnp_pack_pair(const PipeArgs& p, float* dq, int b, hipStream_t stream);
 
+// The k = 3 Cayley-Neumann backward in two passes over mirrored tile pairs (bf16
+// operands, b % 64 == 0, all [nblk, b, b] row-major): with X1 = dG S,
+// X2 = T^T dG, dS = 2 dG + X1 + X2, Sigma = dS + dS^T,
+//   cnp_bwd_sym:  sigma = Sigma (bf16), dq = 2 (dA - dA^T) packed (dA = dG + X1);
+//   cnp_bwd_sigq: dq += pack(-(P - P^T)), P = Sigma Q.
+// dGc is dG in bf16, dG the float32 original (the exact leading terms).
+hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const void* T, void* sigma, float* dq,
+                       int64_t nblk, int b, hipStream_t stream);
+hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nblk, int b, hipStream_t stream);
+
 // Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
 // kernel): packed float32 parameters q [nblk, b(b-1)/2] -> G bf16 [nblk, b, b];
 // with Qc given also Q in bf16, with S and T given (k >= 2) also S = Q Q and

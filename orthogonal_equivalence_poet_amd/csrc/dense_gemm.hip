@@ -42,6 +42,7 @@
 // stored.  K-contiguous operands need K % 64 == 0; for m/n-major operands a
 // ragged last k-tile is loaded from clamped rows and its rows past K are zeroed
 // in LDS before use.
+#include <algorithm>
 #include <type_traits>
 
 #include "dense_gemm.h"
@@ -762,6 +763,180 @@ cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
     }
 }
 
+// ------------------------------------------- Cayley-Neumann backward, k = 3
+// G = (I + T)(I + S) with S = Q Q (symmetric) and T = 2Q + S.  The pack keeps
+// only the skew part of dQ, dq[idx(r, c)] = dQ[r][c] - dQ[c][r], and with
+//   X1 = dG S,  X2 = T^T dG,  dA = dG + X1,  dS = 2 dG + X1 + X2,
+//   Sigma = dS + dS^T (symmetric),  P = Sigma Q
+// that part is 2 (dA - dA^T) - (P - P^T): Q Sigma = -(Sigma Q)^T for a skew Q
+// and a symmetric Sigma, so the two products dS Q^T and Q^T dS of the full dQ
+// become the one product P.  Two passes over mirrored pairs of 64 x 64 tiles
+// (I, J) and (J, I), I <= J, one per group of four waves (a diagonal pair
+// computes its tile twice, so that both groups pass the same barriers):
+//   pass 1 (cnp_bwd_sym_kernel): X1 and X2 of both tiles; writes Sigma (bf16,
+//     both tiles) and dq[idx(r, c)] = 2 (dA[r][c] - dA[c][r]) for the pair's
+//     upper-triangle entries;
+//   pass 2 (cnp_bwd_sigq_kernel): -P = Sigma Q^T of both tiles (Q^T = -Q);
+//     dq[idx(r, c)] += P[c][r] - P[r][c], in place (each entry has one owner).
+__device__ __forceinline__ int64_t tri_index(int r, int c, int b) {
+    return (int64_t)r * b - (int64_t)r * (r + 1) / 2 + (c - r - 1);
+}
+
+// A 64 x 64 float32 tile in LDS, element (r, c) at r * 64 + (c ^ 4 ((r >> 2) & 15)):
+// four consecutive columns of a row stay one 16-byte access, and a column read
+// by 64 lanes (16 groups of four columns x four rows) meets 64 different banks.
+__device__ __forceinline__ int t64(int r, int c) { return r * 64 + (c ^ (((r >> 2) & 15) << 2)); }
+
+// Tile pair of launch slot blockIdx.x: (ti, tj), ti <= tj, of nt x nt tiles.
+__device__ __forceinline__ void pair_of(int nt, int& ti, int& tj) {
+    int i = 0, t = blockIdx.x;
+    while (t >= nt - i) {
+        t -= nt - i;
+        ++i;
+    }
+    ti = i;
+    tj = i + t;
+}
+
+// Accumulator of a 2 x 2-wave 64 x 64 tile into a t64 tile (lane holds rows
+// 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 of its 32 x 32 wave tile).
+__device__ __forceinline__ void stage_acc(float* __restrict__ tile, const f32x16_t& acc, int wm, int wn, int lane) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = wn * 32 + (lane & 31);
+        tile[t64(row, col)] = acc[r];
+    }
+}
+
+template <int S>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 4)))
+cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restrict__ sig, int b) {
+    using G = Geo<64, 64, 2, 2>;
+    constexpr int kRing = S * G::kStageBytes;
+    static_assert(2 * 64 * 64 * 4 <= kRing, "two staged tiles exceed a group's ring");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kRing];
+    const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
+    const int lane = tid & 63, w4 = (tid >> 6) & 3;
+    const int wm = w4 >> 1, wn = w4 & 1;
+    int ti, tj;
+    pair_of(b / 64, ti, tj);
+    const int z = blockIdx.y;
+    // group 0: tile (ti, tj); group 1: tile (tj, ti)
+    const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
+    const int64_t bb = (int64_t)b * b;
+    // A = dG (bf16, k-major), B = S (k-major, S = S^T), A2 = T ([K][M]), B2 = dG ([K][N])
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + z * bb;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + z * bb;
+    const uint16_t* A2 = reinterpret_cast<const uint16_t*>(p.A2) + z * bb;
+    const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.B2) + z * bb;
+    unsigned char* ring = lds + grp * kRing;
+    EpiAddends<64, 64, 256> pre;   // dG (float32) of this group's tile, Cin1
+    load_addends(p, m0, n0, z, gtid, pre);
+    f32x16_t x1[1][1], x2[1][1];
+    main_loop<G, false, false, S>(ring, A, b, B, b, m0, n0, b, b, 0, b, gtid, x1);
+    block_barrier();   // the second product reuses the LDS ring
+    main_loop<G, true, true, S>(ring, A2, b, B2, b, m0, n0, b, b, 0, b, gtid, x2);
+    block_barrier();   // every wave is done reading the operand stages
+    float* E = reinterpret_cast<float*>(ring);   // 2 dG + X1 + X2 (= dS)
+    float* F = E + 64 * 64;                      // dG + X1 (= dA)
+    {
+        f32x16_t e = x1[0][0] + x2[0][0];
+        stage_acc(E, e, wm, wn, lane);
+        stage_acc(F, x1[0][0], wm, wn, lane);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EpiAddends<64, 64, 256>::kPer; ++k) {
+        const int u = k * 256 + gtid;
+        const int row = u >> 4, c = (u & 15) * 4;
+        float4 e = *reinterpret_cast<const float4*>(E + t64(row, c));
+        float4 f = *reinterpret_cast<const float4*>(F + t64(row, c));
+        const float4 a = pre.a1[k];
+        e.x += 2.f * a.x; e.y += 2.f * a.y; e.z += 2.f * a.z; e.w += 2.f * a.w;
+        f.x += a.x; f.y += a.y; f.z += a.z; f.w += a.w;
+        *reinterpret_cast<float4*>(E + t64(row, c)) = e;
+        *reinterpret_cast<float4*>(F + t64(row, c)) = f;
+    }
+    __syncthreads();
+    const float* E0 = reinterpret_cast<const float*>(lds);
+    const float* F0 = E0 + 64 * 64;
+    const float* E1 = ti == tj ? E0 : reinterpret_cast<const float*>(lds + kRing);
+    const float* F1 = E1 + 64 * 64;
+    // Sigma of this group's tile: Sigma[r][c] = dS[r][c] + dS[c][r]
+    if (grp == 0 || ti != tj) {
+        const float* Eo = grp ? E1 : E0;
+        const float* Ex = grp ? E0 : E1;
+        uint16_t* sz = sig + z * bb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = k * 256 + gtid;
+            const int row = u >> 4, c = (u & 15) * 4;
+            const float4 v = *reinterpret_cast<const float4*>(Eo + t64(row, c));
+            const float s0 = v.x + Ex[t64(c, row)], s1 = v.y + Ex[t64(c + 1, row)];
+            const float s2 = v.z + Ex[t64(c + 2, row)], s3 = v.w + Ex[t64(c + 3, row)];
+            *reinterpret_cast<uint2*>(sz + (int64_t)(m0 + row) * b + n0 + c) =
+                make_uint2(pack_bf16x2(s0, s1), pack_bf16x2(s2, s3));
+        }
+    }
+    // dq = 2 (dA - dA^T) on the pair's upper-triangle entries
+    float* out = dq + (int64_t)z * ((int64_t)b * (b - 1) / 2);
+#pragma unroll
+    for (int k = 0; k < 64 * 64 / 512; ++k) {
+        const int u = k * 512 + tid;
+        const int rl = u >> 6, cl = u & 63;
+        const int r = 64 * ti + rl, c = 64 * tj + cl;
+        if (r < c) out[tri_index(r, c, b)] = 2.f * (F0[t64(rl, cl)] - F1[t64(cl, rl)]);
+    }
+}
+
+template <int S>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 4)))
+cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
+    using G = Geo<64, 64, 2, 2>;
+    constexpr int kRing = S * G::kStageBytes;
+    static_assert(64 * 64 * 4 <= kRing, "staged tile exceeds a group's ring");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kRing];
+    const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
+    const int lane = tid & 63, w4 = (tid >> 6) & 3;
+    const int wm = w4 >> 1, wn = w4 & 1;
+    int ti, tj;
+    pair_of(b / 64, ti, tj);
+    const int z = blockIdx.y;
+    const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
+    const int64_t bb = (int64_t)b * b;
+    // A = Sigma (bf16, symmetric), B = Q (rows of Q as [N][K]): acc = Sigma Q^T = -P
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + z * bb;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + z * bb;
+    unsigned char* ring = lds + grp * kRing;
+    // the partial dq this pass adds to, read before the main loop (its latency
+    // hides behind the products); every thread owns fixed entries
+    float* out = dq + (int64_t)z * ((int64_t)b * (b - 1) / 2);
+    float part[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = k * 512 + tid;
+        const int rl = u >> 6, cl = u & 63;
+        const int r = 64 * ti + rl, c = 64 * tj + cl;
+        part[k] = r < c ? out[tri_index(r, c, b)] : 0.f;
+    }
+    f32x16_t acc[1][1];
+    main_loop<G, false, false, S>(ring, A, b, B, b, m0, n0, b, b, 0, b, gtid, acc);
+    block_barrier();   // every wave is done reading the operand stages
+    stage_acc(reinterpret_cast<float*>(ring), acc[0][0], wm, wn, lane);
+    __syncthreads();
+    const float* N0 = reinterpret_cast<const float*>(lds);
+    const float* N1 = ti == tj ? N0 : reinterpret_cast<const float*>(lds + kRing);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = k * 512 + tid;
+        const int rl = u >> 6, cl = u & 63;
+        const int r = 64 * ti + rl, c = 64 * tj + cl;
+        // -P[r][c] + P[c][r] = acc(I, J)[rl][cl] - acc(J, I)[cl][rl]
+        if (r < c) out[tri_index(r, c, b)] = part[k] + (N0[t64(rl, cl)] - N1[t64(cl, rl)]);
+    }
+}
+
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
           int DUAL = 0, bool GRP = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
@@ -1363,6 +1538,59 @@ hipError_t cnp_pack_pair(const PipeArgs& p_in, float* dq, int b, hipStream_t str
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Launch helper of the two k = 3 backward passes: pairs of 64 x 64 tiles of
+// every block, batch entries in chunks of at most 65535 (grid.y).
+template <class Fn>
+hipError_t launch_pairs(int64_t nblk, int b, Fn&& fn) {
+    const int nt = b / 64;
+    constexpr int kMaxY = 65535;
+    for (int64_t y0 = 0; y0 < nblk; y0 += kMaxY) {
+        const int ny = (int)std::min<int64_t>(kMaxY, nblk - y0);
+        fn(y0, dim3(nt * (nt + 1) / 2, ny));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const void* T, void* sigma, float* dq,
+                       int64_t nblk, int b, hipStream_t stream) {
+    if (nblk <= 0) return hipSuccess;
+    if (b % 64 != 0 || b > 1024) return hipErrorInvalidValue;
+    const int64_t bb = (int64_t)b * b, ntri = (int64_t)b * (b - 1) / 2;
+    return launch_pairs(nblk, b, [&](int64_t y0, dim3 grid) {
+        PipeArgs p;
+        p.A = static_cast<const uint16_t*>(dGc) + y0 * bb;
+        p.B = static_cast<const uint16_t*>(S) + y0 * bb;
+        p.A2 = static_cast<const uint16_t*>(T) + y0 * bb;
+        p.B2 = static_cast<const uint16_t*>(dGc) + y0 * bb;
+        p.Cin1 = dG + y0 * bb; p.ldcin1 = b; p.strideCin1 = bb;
+        p.M = p.N = p.K = b;
+        p.epi_vec = (reinterpret_cast<uintptr_t>(dG) & 15) == 0;   // 16-byte addend loads
+        uint16_t* sg = static_cast<uint16_t*>(sigma) + y0 * bb;
+        if (b <= 256)
+            hipLaunchKernelGGL(cnp_bwd_sym_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
+        else
+            hipLaunchKernelGGL(cnp_bwd_sym_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
+    });
+}
+
+hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nblk, int b, hipStream_t stream) {
+    if (nblk <= 0) return hipSuccess;
+    if (b % 64 != 0 || b > 1024) return hipErrorInvalidValue;
+    const int64_t bb = (int64_t)b * b, ntri = (int64_t)b * (b - 1) / 2;
+    return launch_pairs(nblk, b, [&](int64_t y0, dim3 grid) {
+        PipeArgs p;
+        p.A = static_cast<const uint16_t*>(sigma) + y0 * bb;
+        p.B = static_cast<const uint16_t*>(Q) + y0 * bb;
+        p.M = p.N = p.K = b;
+        if (b <= 256)
+            hipLaunchKernelGGL(cnp_bwd_sigq_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
+        else
+            hipLaunchKernelGGL(cnp_bwd_sigq_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
+    });
 }
 
 int pipe_tile_rows(PipeTile t) {
