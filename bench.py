@@ -26,10 +26,19 @@ of the linear (`variants`: fast, mem, all four permutations on the
 activations, the original weight-centric POET with dense R and P, and mem on
 the int8-stored weight).
 
+The default line also nests, under "configs", the other Llama-shaped workloads
+timed the same way (K steps after W warm-up steps): the up_proj-shaped linear in
+the fast and mem variants, all 7 linears of a Llama-8B and of a Llama-13B
+decoder layer (mem), and the 15280-block Cayley-Neumann launch; each with its
+step time and the aggregate MFMA rate of its block and dense products
+(--no-configs leaves them out).  The roofline object describes the longer of the
+two dense products (the backward's, Wt read n-major) and lists both.
+
   --pmc-dir DIR   parse a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run of this
-                  script and record the dense GEMM's HBM traffic in
+                  script and record the two dense products' HBM traffic in
                   profiles/traffic_dense_gemm.json (scaled by a plain copy of
-                  known size that every run performs).
+                  known size that every run performs); prints every kernel's
+                  mean counter values per dispatch.
   --workload W    other workloads, same line format (the default is the one
                   the metric is quoted on): up_proj / up_proj_mem (Llama-8B
                   MLP up_proj shape, b=512, k=4, 4096 tokens), llama8b_layer
@@ -60,7 +69,6 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 256 << 20      # plain copy every run performs (counter scale reference)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_gemm.json")
 GEMM_SRC = os.path.join(ROOT, "orthogonal_equivalence_poet_amd", "csrc", "dense_gemm.hip")
-DENSE_KERNEL_TAG = "pipe_gemm_kernel<256, 128, false, false, false,"   # dense NT (forward), demangled prefix
 COPY_KERNEL_TAG = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 
@@ -167,11 +175,12 @@ def make_step(spec, S):
     return step
 
 
-def stage_timings(spec, S, reps):
+def stage_timings(spec, S, reps, gemm_only=False, only=None):
     """Every stage of the step alone, through the C ABI, same shapes and
     launch configurations as inside poetx_linear_fwd / _bwd (the mem variant
     repeats the input gather, the P-side block product and the dense forward in
-    its backward; the fast variant keeps their outputs)."""
+    its backward; the fast variant keeps their outputs).  gemm_only: only the
+    block, dense and block-gradient products, warm, for the nested records."""
     import torch
     from orthogonal_equivalence_poet_amd import binding as B
     T, m, n, b, k = spec.T, spec.m, spec.n, spec.b, spec.k
@@ -231,7 +240,12 @@ def stage_timings(spec, S, reps):
         ("aux_adamw", lambda: B.poetx_adamw_step(q_opt, S["dq"], m_opt, v_opt, nblk * ntri, 1, opt_p), 0,
          28 * nblk * ntri),
     ]
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    if gemm_only:
+        stages = [st_ for st_ in stages if st_[0].startswith(GEMM_STAGES)]
+    if only is not None:
+        stages = [st_ for st_ in stages if st_[0] in only]
+    quick = gemm_only or only is not None
+    flush = None if quick else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     for name, fn, flops, nbytes in stages:
         us = _time_events(fn, reps)
         tf = flops / us / 1e6 if flops else None
@@ -242,12 +256,24 @@ def stage_timings(spec, S, reps):
         st[name] = {"us": round(us, 2), "tflops": round(tf, 1) if tf else None, "gbs": round(gbs, 1),
                     "bound": "mfma" if mfma else "hbm",
                     "frac": round((tf / PEAK_BF16_TFLOPS) if mfma else (gbs / PEAK_HBM_GBS), 4)}
-        if not mfma:   # the memory-bound stages also cold: nothing of theirs left in L2 / MALL
+        if not mfma and flush is not None:   # memory-bound stages also cold: nothing left in L2 / MALL
             cold = _time_cold(fn, 5, flush)
             st[name]["cold_us"] = round(cold, 2)
             st[name]["cold_gbs"] = round(nbytes / cold / 1e3, 1)
         st[name]["_flops"] = flops
     return st
+
+
+GEMM_STAGES = ("blk", "dense", "grad")   # the block, dense and block-gradient products
+
+
+def gemm_aggregate(st):
+    """Aggregate MFMA rate of the block and dense products of a stage table:
+    their algorithmic FLOPs over the sum of their kernel times."""
+    names = [nm for nm in st if nm.startswith(GEMM_STAGES)]
+    flops = sum(st[nm]["_flops"] for nm in names)
+    us = sum(st[nm]["us"] for nm in names)
+    return flops, us
 
 
 def cpu_baseline(spec, inp, budget_s=12.0, max_reps=3):
@@ -291,38 +317,55 @@ def read_traffic():
     return rec
 
 
+# The dense products of the q_proj-shaped step (2048 x 4096 x 4096): 256
+# workgroups of 512 lanes of the 256 x 128 tile, Wt read k-major (forward) or
+# n-major (backward).  Dispatches of the same kernel at other shapes (the
+# comparison variants) are told apart by their grid size.
+DENSE_KERNELS = {"dense_fwd": ("pipe_gemm_kernel<256, 128, false, false, false,", 256 * 512),
+                 "dense_bwd": ("pipe_gemm_kernel<256, 128, false, true, false,", 256 * 512)}
+
+
 def parse_pmc(pmc_dir):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dense NT GEMM and of the
-    reference copy, from rocprofv3 counter CSVs; writes TRAFFIC_FILE."""
-    vals = {}
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the two dense products and
+    of the reference copy, from rocprofv3 counter CSVs; writes TRAFFIC_FILE.
+    Also prints every kernel's mean per dispatch (for the profile summaries)."""
+    vals, every = {}, {}
     for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for row in csv.DictReader(f):
                 name = row.get("Kernel_Name", "")
                 cn = row.get("Counter_Name", "")
                 v = float(row.get("Counter_Value", "nan"))
-                if DENSE_KERNEL_TAG in name:
-                    key = "gemm"
-                elif COPY_KERNEL_TAG in name:
+                grid = int(float(row.get("Grid_Size", "0") or 0))
+                every.setdefault((name, grid, cn), []).append(v)
+                key = None
+                for nm, (tag, g) in DENSE_KERNELS.items():
+                    if tag in name and grid == g:
+                        key = nm
+                if COPY_KERNEL_TAG in name:
                     key = "copy"
-                else:
-                    continue
-                vals.setdefault((key, cn), []).append(v)
+                if key:
+                    vals.setdefault((key, cn), []).append(v)
     rec = {"gemm_source_sha256_16": gemm_source_hash(), "copy_bytes": COPY_BYTES}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        g = vals.get(("gemm", cn))
         c = vals.get(("copy", cn))
-        if not g or not c:
+        if not c:
             continue
-        g_kib = sum(g) / len(g)
         c_kib = max(c)   # the 256 MiB copy is the largest copy dispatch
         scale = COPY_BYTES / (c_kib * 1024.0)
-        rec[cn] = {"gemm_kib_per_dispatch": g_kib, "copy_kib": c_kib, "scale": scale,
-                   "gemm_bytes_per_dispatch": g_kib * 1024.0 * scale}
+        for nm in DENSE_KERNELS:
+            g = vals.get((nm, cn))
+            if not g:
+                continue
+            g_kib = sum(g) / len(g)
+            rec.setdefault(nm, {})[cn] = {"kib_per_dispatch": g_kib, "dispatches": len(g), "copy_kib": c_kib,
+                                          "scale": scale, "bytes_per_dispatch": g_kib * 1024.0 * scale}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+    for (name, grid, cn), v in sorted(every.items()):
+        print(f"{cn}\t{grid}\t{len(v)}\t{sum(v) / len(v):.1f}\t{name[:150]}")
 
 
 def _products(k):
@@ -451,22 +494,30 @@ def run_linear(args, spec, label):
     ms_graph = _time_steps(graph.replay, args.steps, args.warmup)
 
     st = stage_timings(spec, S, args.stage_reps)
-    gemm_names = [nm for nm in st if nm.startswith(("blk", "dense", "grad"))]
-    g_flops = sum(st[nm]["_flops"] for nm in gemm_names)
-    g_us = sum(st[nm]["us"] for nm in gemm_names)
+    g_flops, g_us = gemm_aggregate(st)
     gemm_tflops = g_flops / g_us / 1e6
-    dense = st["dense_fwd"]
-    dense_flops = dense["_flops"]
     traffic = read_traffic() if label == "q_proj" else None
-    tr = None
-    if traffic and "FETCH_SIZE" in traffic and "WRITE_SIZE" in traffic:
-        tr = round(traffic["FETCH_SIZE"]["gemm_bytes_per_dispatch"] + traffic["WRITE_SIZE"]["gemm_bytes_per_dispatch"])
-    roof = {"kernel": f"dense Wt GEMM, forward (h2 = h1 Wt^T, {spec.T} x {spec.m} x {spec.n}, bf16, fp32 accumulate)",
-            "bound": "mfma", "achieved": round(dense_flops / dense["us"] / 1e6, 1),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(dense_flops / dense["us"] / 1e6 / PEAK_BF16_TFLOPS, 4),
-            "traffic": tr, "avg_launch_us": dense["us"],
-            "algorithmic_flops_per_launch": dense_flops}
+    shapes = {"dense_fwd": f"forward, h2 = h1 Wt^T ({spec.T} x {spec.m} x {spec.n}, Wt read k-major)",
+              "dense_bwd": f"backward, dh1 = dh2 Wt ({spec.T} x {spec.n} x {spec.m}, Wt read n-major)"}
+    kernels = {}
+    for nm in ("dense_fwd", "dense_bwd"):
+        flops = st[nm]["_flops"]
+        tr = None
+        rec = (traffic or {}).get(nm)
+        if rec and "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
+            tr = round(rec["FETCH_SIZE"]["bytes_per_dispatch"] + rec["WRITE_SIZE"]["bytes_per_dispatch"])
+        kernels[nm] = {"kernel": f"dense Wt GEMM, {shapes[nm]}, bf16, fp32 accumulate",
+                       "achieved": round(flops / st[nm]["us"] / 1e6, 1),
+                       "frac": round(flops / st[nm]["us"] / 1e6 / PEAK_BF16_TFLOPS, 4),
+                       "traffic": tr, "avg_launch_us": st[nm]["us"], "algorithmic_flops_per_launch": flops}
+    # the roofline object describes the longer of the two dense products (the
+    # step's dominant kernel); both are listed under "kernels"
+    dom = max(kernels, key=lambda nm: kernels[nm]["avg_launch_us"])
+    roof = {"kernel": kernels[dom]["kernel"], "bound": "mfma", "achieved": kernels[dom]["achieved"],
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+            "traffic": kernels[dom]["traffic"], "avg_launch_us": kernels[dom]["avg_launch_us"],
+            "algorithmic_flops_per_launch": kernels[dom]["algorithmic_flops_per_launch"], "stage": dom,
+            "kernels": kernels}
     for v in st.values():
         v.pop("_flops", None)
     nR, nP = spec.nblk_R, spec.nblk_P
@@ -489,6 +540,59 @@ def run_linear(args, spec, label):
     out["variants"] = variant_steps(spec, S)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp)
+    return out
+
+
+def nested_linear(args, spec, label):
+    """A linear's step (as in the main line) and the aggregate MFMA rate of its
+    block and dense products, each timed alone (warm), for the nested records."""
+    S, _ = build_state(spec)
+    step = make_step(spec, S)
+    per = {}
+    ms = _time_steps(step, args.steps, args.warmup, per)
+    st = stage_timings(spec, S, 20, gemm_only=True)
+    flops, us = gemm_aggregate(st)
+    nR, nP = spec.nblk_R, spec.nblk_P
+    rec = {"workload": f"llama8b_{label}: W0 {spec.m}x{spec.n} bf16, b={spec.b} ({nR}+{nP} blocks), k={spec.k}, "
+                       f"{spec.T // 2048} x 2048 tokens, {spec.variant} variant"
+                       + (f", every Q block at spectral norm {spec.q_block_norm}" if spec.q_block_norm else ""),
+           "tokens_per_s": round(spec.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "ms_per_step_median": round(per["median"], 4), "ms_per_step_min": round(per["min"], 4),
+           "gemm_pct_peak": round(100 * flops / us / 1e6 / PEAK_BF16_TFLOPS, 2),
+           "gemm_tflops": round(flops / us / 1e6, 1), "gemm_gflop_per_step": round(flops / 1e9, 2),
+           "stages_us": {nm: v["us"] for nm, v in st.items()},
+           "dense_frac": {nm: v["frac"] for nm, v in st.items() if nm.startswith("dense")}}
+    return rec
+
+
+_TOP_KEYS = ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "dtype", "data")
+
+
+def _nest(line):
+    """A workload's line as a nested record: without the keys the main line holds."""
+    rec = {k: v for k, v in line.items() if k not in _TOP_KEYS}
+    cfg = rec.pop("config", {})
+    rec["workload"] = cfg.get("workload")
+    return rec
+
+
+def nested_configs(args):
+    """The other Llama-8B / 13B workloads, each timed the same way as the main
+    line (K steps after W warm-up steps) and nested in it."""
+    import torch
+    from orthogonal_equivalence_poet_amd import inputs as I
+    out = {}
+    jobs = [("up_proj_fast", lambda: nested_linear(args, I.llama8b_up_proj("fast"), "up_proj")),
+            ("up_proj_mem", lambda: nested_linear(args, I.llama8b_up_proj("mem"), "up_proj")),
+            ("llama8b_layer", lambda: _nest(run_layer(args, I.llama8b_layer(), "llama8b_layer", merge=True))),
+            ("llama13b_layer", lambda: _nest(run_layer(args, I.llama13b_layer(), "llama13b_layer", merge=False))),
+            ("cnp_13b", lambda: _nest(run_cnp_13b(args)))]
+    for name, fn in jobs:
+        t0 = time.perf_counter()
+        out[name] = fn()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        print(f"bench: {name} done in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     return out
 
 
@@ -541,6 +645,15 @@ def run_layer(args, specs, label, merge):
                      "linear_fwd + 7 x linear_bwd + cnp_bwd_saved over the same blocks", T)
     out["ms_per_step_median"] = round(per["median"], 4)
     out["ms_per_step_min"] = round(per["min"], 4)
+    # the block and dense products of every linear alone (warm, same launches
+    # as inside the step): their algorithmic FLOPs over their kernel time
+    kf, ku = 0, 0.0
+    for sp, S in zip(specs, states):
+        f_, u_ = gemm_aggregate(stage_timings(sp, S, 20, gemm_only=True))
+        kf, ku = kf + f_, ku + u_
+    out["gemm_pct_peak"] = round(100 * kf / ku / 1e6 / PEAK_BF16_TFLOPS, 2)
+    out["gemm_tflops"] = round(kf / ku / 1e6, 1)
+    out["gemm_kernel_us"] = round(ku, 1)
     out["step_gemm_tflops"] = round(g_flops / (ms * 1e-3) / 1e12, 1)
     out["step_pct_peak"] = round(100 * g_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     out["gemm_gflop_per_step"] = round(g_flops / 1e9, 2)
@@ -677,6 +790,27 @@ def run_cnp_13b(args):
     return out
 
 
+def profile_stages(args):
+    """Only the named stages of the workload's step, each --stage-reps times
+    (warm), through the same entry points and launch shapes as stage_timings."""
+    from orthogonal_equivalence_poet_amd import inputs as I
+    w = args.workload
+    spec = (I.llama8b_q_proj() if w == "q_proj"
+            else I.llama8b_up_proj("mem" if w == "up_proj_mem" else "fast") if w.startswith("up_proj") else None)
+    if spec is None:
+        print(f"--profile-stages supports the single-linear workloads, not {w}", file=sys.stderr)
+        return 2
+    S, _ = build_state(spec)
+    want = [nm for nm in args.profile_stages.split(",") if nm]
+    st = stage_timings(spec, S, args.stage_reps, only=want)
+    missing = set(want) - set(st)
+    if missing:
+        print(f"unknown stages: {sorted(missing)}", file=sys.stderr)
+        return 2
+    print(json.dumps({nm: {"us": v["us"], "frac": v["frac"]} for nm, v in st.items()}))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,7 +818,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the nested records of the other workloads in the default line")
     ap.add_argument("--pmc-dir", default=None)
+    ap.add_argument("--profile-stages", default=None,
+                    help="comma-separated stage names (see stage_timings): build the workload's state, "
+                         "run only those stages --stage-reps times each and print their mean times "
+                         "(for rocprofv3 counter and trace passes on chosen kernels)")
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "up_proj", "up_proj_mem", "llama8b_layer", "llama13b_layer", "cnp_13b"])
     args = ap.parse_args()
@@ -703,8 +843,13 @@ def main():
     B.load()
     torch.cuda.set_device(0)
     w = args.workload
+    if args.profile_stages:
+        return profile_stages(args)
     if w == "q_proj":
         out = run_linear(args, I.llama8b_q_proj(), "q_proj")
+        print("bench: q_proj done", file=sys.stderr, flush=True)
+        if not args.no_configs:
+            out["configs"] = nested_configs(args)
     elif w in ("up_proj", "up_proj_mem"):
         spec = I.llama8b_up_proj("mem" if w == "up_proj_mem" else "fast")
         out = run_linear(args, spec, "up_proj")
