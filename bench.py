@@ -325,33 +325,48 @@ DENSE_KERNELS = {"dense_fwd": ("pipe_gemm_kernel<256, 128, false, false, false,"
                  "dense_bwd": ("pipe_gemm_kernel<256, 128, false, true, false,", 256 * 512)}
 
 
+def _pmc_rows(pmc_dir):
+    """(kernel name, grid size, counter, value per dispatch) from every rocprofv3
+    counter output under pmc_dir: CSV files or rocpd SQLite databases."""
+    import sqlite3
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                yield (row.get("Kernel_Name", ""), int(float(row.get("Grid_Size", "0") or 0)),
+                       row.get("Counter_Name", ""), float(row.get("Counter_Value", "nan")))
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*_results.db"), recursive=True):
+        con = sqlite3.connect(path)
+        try:
+            yield from con.execute("select kernel_name, grid_size, counter_name, value from counters_collection")
+        finally:
+            con.close()
+
+
 def parse_pmc(pmc_dir):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the two dense products and
     of the reference copy, from rocprofv3 counter CSVs; writes TRAFFIC_FILE.
     Also prints every kernel's mean per dispatch (for the profile summaries)."""
-    vals, every = {}, {}
-    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                name = row.get("Kernel_Name", "")
-                cn = row.get("Counter_Name", "")
-                v = float(row.get("Counter_Value", "nan"))
-                grid = int(float(row.get("Grid_Size", "0") or 0))
-                every.setdefault((name, grid, cn), []).append(v)
-                key = None
-                for nm, (tag, g) in DENSE_KERNELS.items():
-                    if tag in name and grid == g:
-                        key = nm
-                if COPY_KERNEL_TAG in name:
-                    key = "copy"
-                if key:
-                    vals.setdefault((key, cn), []).append(v)
+    vals, every, copies = {}, {}, {}
+    for name, grid, cn, v in _pmc_rows(pmc_dir):
+        every.setdefault((name, grid, cn), []).append(v)
+        key = None
+        for nm, (tag, g) in DENSE_KERNELS.items():
+            if tag in name and grid == g:
+                key = nm
+        if key:
+            vals.setdefault((key, cn), []).append(v)
+        if COPY_KERNEL_TAG in name:
+            copies.setdefault((cn, grid), []).append(v)
     rec = {"gemm_source_sha256_16": gemm_source_hash(), "copy_bytes": COPY_BYTES}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        c = vals.get(("copy", cn))
-        if not c:
+        # the runtime may split the 256 MiB reference copy into several
+        # dispatches: sum those of the largest copy grid (the run's other
+        # copies are small)
+        grids = [g for (c, g) in copies if c == cn]
+        if not grids:
             continue
-        c_kib = max(c)   # the 256 MiB copy is the largest copy dispatch
+        c = copies[(cn, max(grids))]
+        c_kib = sum(c)
         scale = COPY_BYTES / (c_kib * 1024.0)
         for nm in DENSE_KERNELS:
             g = vals.get((nm, cn))
@@ -359,7 +374,8 @@ def parse_pmc(pmc_dir):
                 continue
             g_kib = sum(g) / len(g)
             rec.setdefault(nm, {})[cn] = {"kib_per_dispatch": g_kib, "dispatches": len(g), "copy_kib": c_kib,
-                                          "scale": scale, "bytes_per_dispatch": g_kib * 1024.0 * scale}
+                                          "copy_dispatches": len(c), "scale": scale,
+                                          "bytes_per_dispatch": g_kib * 1024.0 * scale}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -800,7 +816,11 @@ def profile_stages(args):
     if spec is None:
         print(f"--profile-stages supports the single-linear workloads, not {w}", file=sys.stderr)
         return 2
+    import torch
     S, _ = build_state(spec)
+    # a plain device copy of known size: the scale for the HBM byte counters
+    cs = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    torch.empty_like(cs).copy_(cs)
     want = [nm for nm in args.profile_stages.split(",") if nm]
     st = stage_timings(spec, S, args.stage_reps, only=want)
     missing = set(want) - set(st)

@@ -684,6 +684,27 @@ pipe_gemm_kernel(const PipeArgs p) {
     }
 }
 
+// Tile pair (ti, tj), ti <= tj, of nt x nt tiles and batch entry z of this
+// workgroup (grid: pairs of a block along x, blocks along y).  Launch slots are
+// dealt round-robin to the 8 XCDs, so slot ids are regrouped to give each XCD
+// a contiguous run of work: whole blocks, whose operands are then fetched into
+// one L2 only (dealt as they come, the pairs of one block spread over several
+// XCDs and each of their L2s fetched the block again).
+__device__ __forceinline__ void pair_of(int nt, int& ti, int& tj, int& z) {
+    const int pairs = (int)gridDim.x;
+    const int total = pairs * (int)gridDim.y;
+    int id = (int)blockIdx.x + pairs * (int)blockIdx.y;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+    z = id / pairs;
+    int i = 0, t = id - z * pairs;
+    while (t >= nt - i) {
+        t -= nt - i;
+        ++i;
+    }
+    ti = i;
+    tj = i + t;
+}
+
 // The last product pair of the Cayley-Neumann backward with the skew pack
 // folded in: dQ = A B^T + A2^T B2 + beta1 Cin1 + beta2 Cin2 over b x b blocks,
 // and dq[idx(r, c)] = dQ[r][c] - dQ[c][r] (r < c) written straight from the
@@ -708,14 +729,8 @@ cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
     const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
     const int lane = tid & 63, w4 = (tid >> 6) & 3;
     const int wm = w4 >> 1, wn = w4 & 1;
-    const int nt = b / 64;
-    int ti = 0, t = blockIdx.x;
-    while (t >= nt - ti) {
-        t -= nt - ti;
-        ++ti;
-    }
-    const int tj = ti + t;
-    const int z = blockIdx.y;
+    int ti, tj, z;
+    pair_of(b / 64, ti, tj, z);
     // group 0: tile (ti, tj); group 1: tile (tj, ti)
     const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
@@ -778,25 +793,11 @@ cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 //     upper-triangle entries;
 //   pass 2 (cnp_bwd_sigq_kernel): -P = Sigma Q^T of both tiles (Q^T = -Q);
 //     dq[idx(r, c)] += P[c][r] - P[r][c], in place (each entry has one owner).
-__device__ __forceinline__ int64_t tri_index(int r, int c, int b) {
-    return (int64_t)r * b - (int64_t)r * (r + 1) / 2 + (c - r - 1);
-}
 
 // A 64 x 64 float32 tile in LDS, element (r, c) at r * 64 + (c ^ 4 ((r >> 2) & 15)):
 // four consecutive columns of a row stay one 16-byte access, and a column read
 // by 64 lanes (16 groups of four columns x four rows) meets 64 different banks.
 __device__ __forceinline__ int t64(int r, int c) { return r * 64 + (c ^ (((r >> 2) & 15) << 2)); }
-
-// Tile pair of launch slot blockIdx.x: (ti, tj), ti <= tj, of nt x nt tiles.
-__device__ __forceinline__ void pair_of(int nt, int& ti, int& tj) {
-    int i = 0, t = blockIdx.x;
-    while (t >= nt - i) {
-        t -= nt - i;
-        ++i;
-    }
-    ti = i;
-    tj = i + t;
-}
 
 // Accumulator of a 2 x 2-wave 64 x 64 tile into a t64 tile (lane holds rows
 // 8 (r/4) + 4 (lane/32) + r%4 of column lane%32 of its 32 x 32 wave tile).
@@ -819,9 +820,8 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
     const int lane = tid & 63, w4 = (tid >> 6) & 3;
     const int wm = w4 >> 1, wn = w4 & 1;
-    int ti, tj;
-    pair_of(b / 64, ti, tj);
-    const int z = blockIdx.y;
+    int ti, tj, z;
+    pair_of(b / 64, ti, tj, z);
     // group 0: tile (ti, tj); group 1: tile (tj, ti)
     const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
     const int64_t bb = (int64_t)b * b;
@@ -886,7 +886,7 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
         const int u = k * 512 + tid;
         const int rl = u >> 6, cl = u & 63;
         const int r = 64 * ti + rl, c = 64 * tj + cl;
-        if (r < c) out[tri_index(r, c, b)] = 2.f * (F0[t64(rl, cl)] - F1[t64(cl, rl)]);
+        if (r < c) out[upper_index(r, c, b)] = 2.f * (F0[t64(rl, cl)] - F1[t64(cl, rl)]);
     }
 }
 
@@ -900,9 +900,8 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
     const int tid = threadIdx.x, grp = tid >> 8, gtid = tid & 255;
     const int lane = tid & 63, w4 = (tid >> 6) & 3;
     const int wm = w4 >> 1, wn = w4 & 1;
-    int ti, tj;
-    pair_of(b / 64, ti, tj);
-    const int z = blockIdx.y;
+    int ti, tj, z;
+    pair_of(b / 64, ti, tj, z);
     const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
     const int64_t bb = (int64_t)b * b;
     // A = Sigma (bf16, symmetric), B = Q (rows of Q as [N][K]): acc = Sigma Q^T = -P
@@ -918,7 +917,7 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
         const int u = k * 512 + tid;
         const int rl = u >> 6, cl = u & 63;
         const int r = 64 * ti + rl, c = 64 * tj + cl;
-        part[k] = r < c ? out[tri_index(r, c, b)] : 0.f;
+        part[k] = r < c ? out[upper_index(r, c, b)] : 0.f;
     }
     f32x16_t acc[1][1];
     main_loop<G, false, false, S>(ring, A, b, B, b, m0, n0, b, b, 0, b, gtid, acc);
@@ -933,7 +932,7 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
         const int rl = u >> 6, cl = u & 63;
         const int r = 64 * ti + rl, c = 64 * tj + cl;
         // -P[r][c] + P[c][r] = acc(I, J)[rl][cl] - acc(J, I)[cl][rl]
-        if (r < c) out[tri_index(r, c, b)] = part[k] + (N0[t64(rl, cl)] - N1[t64(cl, rl)]);
+        if (r < c) out[upper_index(r, c, b)] = part[k] + (N0[t64(rl, cl)] - N1[t64(cl, rl)]);
     }
 }
 
