@@ -96,11 +96,16 @@ enum { POETX_FAST = 0, POETX_MEM = 1, POETX_FOUR_PERM = 2, POETX_WEIGHT_CENTRIC 
 /* mem_q8 (the review's POET-XQ, Summary and Strengths: quantized training
  * through the checkpointed variant, which never keeps a dequantized weight):
  * the stored weight is the quantized buffer of poetx_quantize_weight (int8 per
- * output row, see below) and every poetx_linear_fwd / _bwd call expands it into
- * its own workspace, runs the mem chain on it and drops it; bf16 only.  The
- * pages give no format: symmetric int8 with one float32 scale per row of Wt is
- * this library's reading of their 8-bit setting.  poetx_merge on a mem_q8
- * descriptor merges in bf16 and stores the result quantized again. */
+ * output row, see below) and poetx_linear_fwd / _bwd run the mem chain with the
+ * int8 codes read straight into the dense products: the codes are widened to
+ * bf16 inside the product (exact), the row scales are applied in float32 (to
+ * the output columns of h2 in the forward, to the columns of dh2 in the
+ * backward), so the weight the chain computes with is code * scale and no
+ * dequantized copy of it is made; bf16 only, b % 64 == 0 (POETX_ERR_SHAPE
+ * otherwise).  The pages give no format: symmetric int8 with one float32 scale
+ * per row of Wt is this library's reading of their 8-bit setting.  poetx_merge
+ * on a mem_q8 descriptor expands the weight into its workspace, merges in bf16
+ * and stores the result quantized again. */
 
 typedef struct poetx_linear_desc {
     int64_t T;       /* tokens (rows of x and y), >= 0 */

@@ -83,6 +83,8 @@ int check_desc(const poetx_linear_desc* d) {
         return POETX_ERR_INVALID_ARG;
     if (d->variant == POETX_MEM_Q8 && d->dtype != POETX_BF16) return POETX_ERR_UNSUPPORTED;
     POETX_TRY(check_block(d->b));
+    // the int8 weight feeds products tiled in 64-k steps over both m and n
+    if (d->variant == POETX_MEM_Q8 && d->b % 64 != 0) return POETX_ERR_SHAPE;
     POETX_TRY(check_k(d->k));
     if (d->T < 0 || d->m <= 0 || d->n <= 0) return POETX_ERR_SHAPE;
     if (d->m % d->b != 0 || d->n % d->b != 0) return POETX_ERR_SHAPE;
@@ -524,8 +526,10 @@ void plan_linear(Carver& cv, const poetx_linear_desc* d, bool backward, LinearBu
 // Batched block product over the feature axis of a [T, d] activation:
 // out[:, jb:(j+1)b] = in[:, jb:(j+1)b] . G_j^T (NT) or . G_j (NN).
 hipError_t block_apply(GemmLayout layout, bool bf16, int64_t T, int64_t d, int64_t b, const void* in,
-                       const void* G, void* out, hipStream_t s) {
+                       const void* G, void* out, hipStream_t s, const float* colscale = nullptr) {
     const bool nn = layout == GemmLayout::NN;
+    if (colscale && !(bf16 && nn && pipe_gemm_supported(false, nn, T, b, b, d, b, b, b * b)))
+        return hipErrorInvalidValue;
     if (bf16 && pipe_gemm_supported(false, nn, T, b, b, d, b, b, b * b)) {
         PipeArgs p;
         p.A = in; p.lda = d; p.strideA = b;
@@ -541,6 +545,12 @@ hipError_t block_apply(GemmLayout layout, bool bf16, int64_t T, int64_t d, int64
         PipeTile t = PipeTile::Tall;
         if (b >= 256)
             t = tiles(256, 256) >= 256 ? PipeTile::Big : tiles(128, 256) >= 256 ? PipeTile::Wide : PipeTile::Slim;
+        if (colscale) {
+            // out[:, c] *= colscale[c]: block j's columns start at j b
+            p.colscale = colscale;
+            p.strideScale = b;
+            return pipe_gemm_colscale(p, s, t);
+        }
         return pipe_gemm(false, nn, false, p, s, t);
     }
     return gemm(layout, bf16, bf16, T, b, b, d / b, Mat{in, d, b}, Mat{G, b, b * b}, out, d, b, s);
@@ -733,6 +743,23 @@ inline const float* qscales(const void* Wq, int64_t m, int64_t n) {
     return reinterpret_cast<const float*>(static_cast<const char*>(Wq) + qscale_offset(m, n));
 }
 
+// The dense products of the chain on the stored weight: Wt itself, or for
+// MEM_Q8 its int8 codes with the row scales applied in float32 (forward: per
+// output column of h2 in the product's epilogue; backward: on dh2's columns by
+// the block product that makes dh2, see poetx_linear_bwd).
+hipError_t dense_fwd(const poetx_linear_desc* d, const void* h1, const void* Wt, void* h2, hipStream_t s) {
+    const int64_t T = d->T, m = d->m, n = d->n;
+    if (d->variant == POETX_MEM_Q8)
+        return dense_gemm_q8(false, h1, n, qcodes(Wt), n, qscales(Wt, m, n), h2, m, (int)T, (int)m, (int)n, s);
+    return dense_gemm(GemmLayout::NT, d->dtype == POETX_BF16, T, m, n, h1, n, Wt, n, h2, m, s);
+}
+hipError_t dense_bwd(const poetx_linear_desc* d, const void* dh2, const void* Wt, void* dh1, hipStream_t s) {
+    const int64_t T = d->T, m = d->m, n = d->n;
+    if (d->variant == POETX_MEM_Q8)
+        return dense_gemm_q8(true, dh2, m, qcodes(Wt), n, nullptr, dh1, n, (int)T, (int)n, (int)m, s);
+    return dense_gemm(GemmLayout::NN, d->dtype == POETX_BF16, T, n, m, dh2, m, Wt, n, dh1, n, s);
+}
+
 int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
                    hipStream_t s) {
@@ -741,8 +768,8 @@ int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, co
     // a = x gathered by pi_P;  h1 = a . blockdiag(G_P)^T
     HIP_TRY(permute_2d(x, buf_a, bf, T, n, nullptr, pi_P, false, s));
     HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, buf_a, G_P, buf_b, s));
-    // h2 = h1 . Wt^T
-    HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, buf_b, n, Wt, n, h2_out, m, s));
+    // h2 = h1 . Wt^T (the int8 weight: h1 . codes^T, output column i scaled by scale_i)
+    HIP_TRY(dense_fwd(d, buf_b, Wt, h2_out, s));
     // z = h2 . blockdiag(G_R)^T ; y = z scattered by pi_R
     HIP_TRY(block_apply(GemmLayout::NT, bf, T, m, b, h2_out, G_R, buf_b, s));
     HIP_TRY(permute_2d(buf_b, y, bf, T, m, nullptr, pi_R, true, s));
@@ -1114,7 +1141,6 @@ size_t poetx_linear_fwd_workspace_bytes(const poetx_linear_desc* d) {
         cv.take_n<int32_t>(d->n);                          // pi_P^-1
         return cv.off;
     }
-    if (d->variant == POETX_MEM_Q8) cv.take(2 * (size_t)(d->m * d->n));  // the dequantized weight
     LinearBufs L;
     plan_linear(cv, d, false, L);
     if (mem_chain(d)) cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
@@ -1148,12 +1174,6 @@ int linear_fwd_run(const poetx_linear_desc* d, const void* x, const void* Wt, co
         int32_t* inv_R = cv.take_n<int32_t>(d->m);
         int32_t* inv_P = cv.take_n<int32_t>(d->n);
         return wc_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, S, Pd, inv_R, inv_P, as_stream(stream));
-    }
-    if (d->variant == POETX_MEM_Q8) {
-        // the quantized weight is expanded into the workspace for this call only
-        void* Wd = cv.take(2 * (size_t)(d->m * d->n));
-        HIP_TRY(dequantize_rows(qcodes(Wt), qscales(Wt, d->m, d->n), Wd, d->m, d->n, as_stream(stream)));
-        Wt = Wd;
     }
     LinearBufs L;
     plan_linear(cv, d, false, L);
@@ -1205,7 +1225,6 @@ size_t poetx_linear_bwd_workspace_bytes(const poetx_linear_desc* d) {
         plan_wc_bwd(cv, d, B);
         return cv.off;
     }
-    if (d->variant == POETX_MEM_Q8) cv.take(2 * (size_t)(d->m * d->n));  // the dequantized weight
     LinearBufs L;
     plan_linear(cv, d, true, L);
     return cv.off;
@@ -1238,11 +1257,6 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
         plan_wc_bwd(cv, d, B);
         return wc_backward(d, dy, x, Wt, pi_R, pi_P, S, dx, dG_R, dG_P, B, s);
     }
-    if (d->variant == POETX_MEM_Q8) {
-        void* Wd = cv.take(2 * (size_t)(m * n));
-        HIP_TRY(dequantize_rows(qcodes(Wt), qscales(Wt, m, n), Wd, m, n, s));
-        Wt = Wd;
-    }
     LinearBufs L;
     plan_linear(cv, d, true, L);
     if (d->variant == POETX_FOUR_PERM)
@@ -1263,17 +1277,19 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* dy, const void* x, 
     if (mem_chain(d)) {
         // recompute h1 and h2 from x
         HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, bufA, G_P, bufB, s));
-        HIP_TRY(dense_gemm(GemmLayout::NT, bf, T, m, n, bufB, n, Wt, n, bufC, m, s));
+        HIP_TRY(dense_fwd(d, bufB, Wt, bufC, s));
         h2 = bufC;
     }
     // dz = dy gathered by pi_R
     HIP_TRY(permute_2d(dy, bufB, bf, T, m, nullptr, pi_R, false, s));
     // dG_R[j] = dz_j^T h2_j
     POETX_TRY(block_grad(bf, T, m, b, bufB, h2, dG_R, L.splits_R, L.kps_R, L.part, s));
-    // dh2 = dz . blockdiag(G_R)
-    HIP_TRY(block_apply(GemmLayout::NN, bf, T, m, b, bufB, G_R, bufC, s));
+    // dh2 = dz . blockdiag(G_R) (MEM_Q8: column i scaled by the weight's row
+    // scale_i, so that the next product can take the int8 codes as they are)
+    HIP_TRY(block_apply(GemmLayout::NN, bf, T, m, b, bufB, G_R, bufC, s,
+                        d->variant == POETX_MEM_Q8 ? qscales(Wt, m, n) : nullptr));
     // dh1 = dh2 . Wt
-    HIP_TRY(dense_gemm(GemmLayout::NN, bf, T, n, m, bufC, m, Wt, n, bufB, n, s));
+    HIP_TRY(dense_bwd(d, bufC, Wt, bufB, s));
     // dG_P[j] = dh1_j^T a_j
     POETX_TRY(block_grad(bf, T, n, b, bufB, bufA, dG_P, L.splits_P, L.kps_P, L.part, s));
     // da = dh1 . blockdiag(G_P) ; dx = da scattered by pi_P

@@ -56,6 +56,10 @@ struct PipeArgs {
     // grp[0].n_begin == 0, each a multiple of 128; K must be the largest group k.
     int ngroups = 0;
     PipeGroup grp[kMaxPipeGroups];
+    // Column scale of the plain epilogue (int8 dense forward, scaled block
+    // product): C[r][c] = acc * colscale[c] (batch entry z: colscale + z strideScale).
+    const float* colscale = nullptr;
+    int64_t strideScale = 0;
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead
@@ -112,6 +116,21 @@ hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nbl
 bool cnp_fused_supported(int64_t b, int k);
 hipError_t cnp_fused_fwd(const float* q, void* G, void* Qc, void* S, void* T, int64_t nblk, int64_t b, int k,
                          hipStream_t stream);
+
+// Dense products with an int8 B operand (the quantized weight: codes [N][K]
+// k-major for b_nn = false, [K][N] n-major for b_nn = true; int8, ld in
+// elements): the codes travel global -> LDS as bytes and are widened to bf16 in
+// LDS (exact: |code| <= 127), a tile ahead of their use.  b_nn = false scales
+// output column c by colscale[c]; b_nn = true applies no scale (the caller folds
+// the row scales of the weight into A's columns).  Needs K % 64 == 0 for
+// b_nn = false, N % 16 == 0, lda % 8 == 0, ldb % 16 == 0, 16-byte aligned operands.
+bool dense_gemm_q8_supported(bool b_nn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
+hipError_t dense_gemm_q8(bool b_nn, const void* A, int64_t lda, const int8_t* B, int64_t ldb, const float* colscale,
+                         void* C, int64_t ldc, int M, int N, int K, hipStream_t stream);
+// The block product of pipe_gemm (k-major A, bf16 out, n-major B: out = in . G)
+// with its output columns scaled: out[:, c] *= colscale[c] over the whole
+// [T, d] activation (tiles as block_apply picks them).
+hipError_t pipe_gemm_colscale(const PipeArgs& p, hipStream_t stream, PipeTile tile);
 
 // Dense convenience wrappers (batch 1, no split).
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);

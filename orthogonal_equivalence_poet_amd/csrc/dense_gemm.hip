@@ -56,17 +56,23 @@ constexpr int BK = 64;
 
 // Workgroup tile BM x BN (x 64 k), NWM x NWN waves, each owning a WTM x WTN
 // sub-tile of MI x NJ 32 x 32 MFMA tiles.
-template <int BM_, int BN_, int NWM_ = 2, int NWN_ = 2>
+// Q8: B is an int8 operand.  A stage then holds A and the int8 B tile (BN x 64
+// bytes); the bf16 B tile the fragments read lives in a double buffer after the
+// ring, widened from the int8 tile one k-tile ahead.
+template <int BM_, int BN_, int NWM_ = 2, int NWN_ = 2, bool Q8_ = false>
 struct Geo {
     static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+    static constexpr bool Q8 = Q8_;
     static constexpr int NW = NWM * NWN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int kABytes = BM * BK * 2;
-    static constexpr int kBBytes = BN * BK * 2;
-    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int kBBytes = BN * BK * 2;    // bf16 B tile
+    static constexpr int kB8Bytes = BN * BK;       // int8 B tile
+    static constexpr int kStageBytes = kABytes + (Q8 ? kB8Bytes : kBBytes);
+    static constexpr int kExtraBytes = Q8 ? 2 * kBBytes : 0;   // the widened double buffer
     static constexpr int WTM = BM / NWM, WTN = BN / NWN, MI = WTM / 32, NJ = WTN / 32;
-    static constexpr int kLoadsPerTile = (kABytes + kBBytes) / (kThreads * 16);
-    static_assert(MI >= 1 && NJ >= 1 && (kABytes + kBBytes) % (kThreads * 16) == 0, "tile geometry");
+    static constexpr int kLoadsPerTile = kStageBytes / (kThreads * 16);
+    static_assert(MI >= 1 && NJ >= 1 && kStageBytes % (kThreads * 16) == 0, "tile geometry");
 };
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -139,7 +145,39 @@ __device__ __forceinline__ void dma_one(int j, uint32_t dst, const uint16_t* __r
     }
 }
 
+// Loads of an int8 operand tile (unswizzled in LDS: it is only read by the
+// widening pass, one 16-byte chunk per thread).
+//   k-major: ROWS rows x 64 k bytes from src[row][k], rows clamped to rows_total;
+//   n-major: 64 k-rows x ROWS bytes from src[k][col], k clamped to k_end,
+//   columns clamped to rows_total (a multiple of 16).
+template <int ROWS, int NW>
+struct OperandLoads8 {
+    static constexpr int runs = ROWS * BK / 1024;
+    static constexpr int n = runs / NW;
+    static_assert(runs % NW == 0, "int8 runs per wave");
+};
+
+template <int ROWS, bool MN, int NW>
+__device__ __forceinline__ void dma_one8(int j, uint32_t dst, const int8_t* __restrict__ src, int64_t ld, int r0,
+                                         int rows_total, int k0, int k_end, int wave, int lane) {
+    const int g = j * NW + wave;
+    if constexpr (!MN) {
+        const int r = 16 * g + (lane >> 2);             // 16 rows of 64 bytes per run
+        const int row = min(r0 + r, rows_total - 1);
+        dma16(src + (int64_t)row * ld + k0 + (lane & 3) * 16, __builtin_amdgcn_readfirstlane(dst + g * 1024));
+    } else {
+        constexpr int kSlots = ROWS / 16;               // 16-byte chunks per k-row
+        constexpr int kRowsPerRun = 1024 / ROWS;
+        const int kr = kRowsPerRun * g + lane / kSlots;
+        const int col = min(r0 + (lane % kSlots) * 16, rows_total - 16);
+        const int k = min(k0 + kr, k_end - 1);
+        dma16(src + (int64_t)k * ld + col, __builtin_amdgcn_readfirstlane(dst + g * 1024));
+    }
+}
+
 // Everything needed to issue the loads of one k-tile into one LDS stage.
+// Q8 jobs load the int8 B tile of the NEXT k-tile (k0_b) into stage_b, so that
+// it can be widened while the current tile computes.
 struct DmaJob {
     uint32_t stage;
     const uint16_t* A;
@@ -147,22 +185,109 @@ struct DmaJob {
     const uint16_t* B;
     int64_t ldb;
     int m0, n0, M, N, k0, k_end, wave, lane;
+    uint32_t stage_b = 0;
+    int k0_b = 0;
 };
 
 // Part PART of NPARTS of a k-tile's loads (A's loads first, then B's), so the
 // loads can be spread over the MFMA work of the tile being computed.
 template <class G, bool A_MN, bool B_MN, int PART, int NPARTS>
 __device__ __forceinline__ void dma_part(const DmaJob& d) {
-    constexpr int NA = OperandLoads<G::BM, A_MN, G::NW>::n, NB = OperandLoads<G::BN, B_MN, G::NW>::n;
+    constexpr int NA = OperandLoads<G::BM, A_MN, G::NW>::n;
+    constexpr int NB = G::Q8 ? OperandLoads8<G::BN, G::NW>::n : OperandLoads<G::BN, B_MN, G::NW>::n;
     constexpr int L = NA + NB;
     constexpr int lo = PART * L / NPARTS, hi = (PART + 1) * L / NPARTS;
 #pragma unroll
     for (int idx = lo; idx < hi; ++idx) {
         if (idx < NA)
             dma_one<G::BM, A_MN, G::NW>(idx, d.stage, d.A, d.lda, d.m0, d.M, d.k0, d.k_end, d.wave, d.lane);
+        else if constexpr (G::Q8)
+            dma_one8<G::BN, B_MN, G::NW>(idx - NA, d.stage_b, reinterpret_cast<const int8_t*>(d.B), d.ldb, d.n0, d.N,
+                                         d.k0_b, d.k_end, d.wave, d.lane);
         else
             dma_one<G::BN, B_MN, G::NW>(idx - NA, d.stage + G::kABytes, d.B, d.ldb, d.n0, d.N, d.k0, d.k_end,
                                         d.wave, d.lane);
+    }
+}
+
+// Widening of an int8 B tile into the bf16 B layout the fragment reads use
+// (k-major: rows of 64 k, chunk c of row r at slot c ^ swz_k(r); n-major:
+// k-rows of BN, chunk c of k-row k at slot c ^ swz_mn(k)).  A thread owns
+// kPer 16-byte int8 chunks (16 values); widen_load reads them into registers,
+// widen_part<P> turns the P-th quarter of their dwords (4 values each) into
+// 8-byte bf16 runs, so that the work can ride between a tile's four MFMA
+// groups.  n-major k-rows at or past `valid` become zero (a ragged last k-tile
+// was loaded from clamped rows).
+template <class G>
+struct Widen8 {
+    static constexpr int kPer = G::BN * BK / 16 / G::kThreads;
+    static_assert(kPer >= 1 && (G::BN * BK / 16) % G::kThreads == 0, "widening chunks per thread");
+    uint4 w[kPer];
+};
+
+template <class G>
+__device__ __forceinline__ void widen_load(const unsigned char* __restrict__ src8, int tid, Widen8<G>& r) {
+#pragma unroll
+    for (int c = 0; c < Widen8<G>::kPer; ++c)
+        r.w[c] = *reinterpret_cast<const uint4*>(src8 + (c * G::kThreads + tid) * 16);
+}
+
+// 4 int8 values -> 4 bf16 (exact for |v| <= 128), element 0 in the low half.
+__device__ __forceinline__ uint2 widen4(uint32_t d) {
+    const uint32_t x = d ^ 0x80808080u;
+    const float f0 = (float)(x & 0xffu) - 128.f;
+    const float f1 = (float)((x >> 8) & 0xffu) - 128.f;
+    const float f2 = (float)((x >> 16) & 0xffu) - 128.f;
+    const float f3 = (float)(x >> 24) - 128.f;
+    return make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
+}
+
+template <class G, bool B_MN, int PART>
+__device__ __forceinline__ void widen_part(unsigned char* __restrict__ dst, int valid, int tid, const Widen8<G>& r) {
+    constexpr int BN = G::BN;
+    constexpr int D = Widen8<G>::kPer * 4;   // dwords per thread
+    static_assert(D % 4 == 0, "quarters");
+#pragma unroll
+    for (int q = PART * D / 4; q < (PART + 1) * D / 4; ++q) {
+        const int c = q >> 2, dw = q & 3;
+        const int u = c * G::kThreads + tid;
+        const uint4& w = r.w[c];
+        const uint32_t word = dw == 0 ? w.x : dw == 1 ? w.y : dw == 2 ? w.z : w.w;
+        uint2 v = widen4(word);
+        int off;
+        if constexpr (!B_MN) {
+            const int row = u >> 2, ch = 2 * (u & 3) + (dw >> 1);
+            off = row * 128 + ((ch ^ swz_k(row)) << 4) + (dw & 1) * 8;
+        } else {
+            constexpr int kPerRow = BN / 16;
+            const int k = u / kPerRow, ch = 2 * (u % kPerRow) + (dw >> 1);
+            if (k >= valid) v = make_uint2(0, 0);
+            off = k * (BN * 2) + ((ch ^ swz_mn<BN>(k)) << 4) + (dw & 1) * 8;
+        }
+        *reinterpret_cast<uint2*>(dst + off) = v;
+    }
+}
+
+template <class G, bool B_MN>
+__device__ __forceinline__ void widen_all(const unsigned char* __restrict__ src8, unsigned char* __restrict__ dst,
+                                          int valid, int tid) {
+    Widen8<G> r;
+    widen_load<G>(src8, tid, r);
+    widen_part<G, B_MN, 0>(dst, valid, tid, r);
+    widen_part<G, B_MN, 1>(dst, valid, tid, r);
+    widen_part<G, B_MN, 2>(dst, valid, tid, r);
+    widen_part<G, B_MN, 3>(dst, valid, tid, r);
+}
+
+// The k-step ks share of a tile's widening (Q8), after that step's MFMAs.
+template <class G, bool B_MN>
+__device__ __forceinline__ void widen_step(int ks, unsigned char* __restrict__ dst, int valid, int tid,
+                                           const Widen8<G>& r) {
+    switch (ks) {
+        case 0: widen_part<G, B_MN, 0>(dst, valid, tid, r); break;
+        case 1: widen_part<G, B_MN, 1>(dst, valid, tid, r); break;
+        case 2: widen_part<G, B_MN, 2>(dst, valid, tid, r); break;
+        default: widen_part<G, B_MN, 3>(dst, valid, tid, r); break;
     }
 }
 
@@ -201,28 +326,48 @@ __device__ __forceinline__ uint4 load_frag(const unsigned char* __restrict__ bas
 }
 
 // Fragments of k-step ks for one wave (MI A fragments, NJ B fragments).
+// A from stage st, B from bst (the stage's B tile, or the widened buffer for Q8).
 template <class G, bool A_MN, bool B_MN>
-__device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st, int wm, int wn, int ks, int lane,
-                                           uint4 (&af)[G::MI], uint4 (&bfr)[G::NJ]) {
+__device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st, const unsigned char* __restrict__ bst,
+                                           int wm, int wn, int ks, int lane, uint4 (&af)[G::MI],
+                                           uint4 (&bfr)[G::NJ]) {
 #pragma unroll
     for (int i = 0; i < G::MI; ++i) af[i] = load_frag<A_MN, G::BM>(st, wm * G::WTM + i * 32, ks, lane);
 #pragma unroll
-    for (int j = 0; j < G::NJ; ++j) bfr[j] = load_frag<B_MN, G::BN>(st + G::kABytes, wn * G::WTN + j * 32, ks, lane);
+    for (int j = 0; j < G::NJ; ++j) bfr[j] = load_frag<B_MN, G::BN>(bst, wn * G::WTN + j * 32, ks, lane);
+}
+template <class G, bool A_MN, bool B_MN>
+__device__ __forceinline__ void load_frags(const unsigned char* __restrict__ st, int wm, int wn, int ks, int lane,
+                                           uint4 (&af)[G::MI], uint4 (&bfr)[G::NJ]) {
+    load_frags<G, A_MN, B_MN>(st, st + G::kABytes, wm, wn, ks, lane, af, bfr);
 }
 
 // One k-tile (four k-steps of 16) with register double-buffered fragments:
 // the LDS reads of step ks+1 are issued before the MFMAs of step ks, and
 // scheduling barriers keep the compiler from sinking them; a quarter of the
 // next tile's loads goes out with each k-step.
+// The widening of the next k-tile's int8 B operand (Q8), spread over a tile's
+// four k-steps (a quarter after each step's MFMAs are issued).
+struct WidenJob {
+    const unsigned char* src = nullptr;
+    unsigned char* dst = nullptr;
+    int valid = 0;
+    bool on = false;
+};
+
 template <class G, bool A_MN, bool B_MN>
-__device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, int wm, int wn, int lane,
-                                             f32x16_t (&acc)[G::MI][G::NJ], const DmaJob& next, bool load_next) {
+__device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, const unsigned char* __restrict__ bst,
+                                             int wm, int wn, int lane, f32x16_t (&acc)[G::MI][G::NJ],
+                                             const DmaJob& next, bool load_next, const WidenJob& wj, int tid) {
     uint4 af[2][G::MI], bfr[2][G::NJ];
-    load_frags<G, A_MN, B_MN>(st, wm, wn, 0, lane, af[0], bfr[0]);
+    Widen8<G> w8;
+    if constexpr (G::Q8)
+        if (wj.on) widen_load<G>(wj.src, tid, w8);
+    load_frags<G, A_MN, B_MN>(st, bst, wm, wn, 0, lane, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
         const int cur = ks & 1;
-        if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(st, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+        if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(st, bst, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
         if (load_next) {
             switch (ks) {
                 case 0: dma_part<G, A_MN, B_MN, 0, 4>(next); break;
@@ -237,7 +382,17 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ s
 #pragma unroll
             for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (G::Q8) {
+            if (wj.on) widen_step<G, B_MN>(ks, wj.dst, wj.valid, tid, w8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+}
+
+template <class G, bool A_MN, bool B_MN>
+__device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ st, int wm, int wn, int lane,
+                                             f32x16_t (&acc)[G::MI][G::NJ], const DmaJob& next, bool load_next) {
+    compute_tile<G, A_MN, B_MN>(st, st + G::kABytes, wm, wn, lane, acc, next, load_next, WidenJob{}, 0);
 }
 
 // Zero the k-rows >= valid of an m/n-major tile (ragged last k-tile).
@@ -474,12 +629,37 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
     }
 }
 
+// Wait until at most `jobs` k-tiles of this thread's loads are in flight
+// (0 <= jobs <= S - 1): everything issued before them has landed.
+template <int LPT, int S>
+__device__ __forceinline__ void wait_jobs(int jobs) {
+    static_assert(S >= 2 && S <= 8 && LPT * (S - 1) < 64, "vmcnt range");
+    switch (jobs) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<LPT>(); break;
+        case 2: if constexpr (S > 2) wait_vmcnt<2 * LPT>(); break;
+        case 3: if constexpr (S > 3) wait_vmcnt<3 * LPT>(); break;
+        case 4: if constexpr (S > 4) wait_vmcnt<4 * LPT>(); break;
+        case 5: if constexpr (S > 5) wait_vmcnt<5 * LPT>(); break;
+        default: if constexpr (S > 6) wait_vmcnt<6 * LPT>(); break;
+    }
+}
+
 // S-stage LDS ring: S - 1 k-tiles are requested before the first one is used,
 // so a product with K <= 64 (S - 1) waits for memory once.
-// Epilogue kinds: plain store, general (see PipeArgs).
-constexpr int kEpiPlain = 0, kEpiGeneral = 1;
+// Epilogue kinds: plain store, general (see PipeArgs), plain store with the
+// output columns scaled by PipeArgs::colscale.
+constexpr int kEpiPlain = 0, kEpiGeneral = 1, kEpiColScale = 2;
 
 // The k loop of one output tile at (m0, n0) into acc (zeroed here).
+// Q8 (G::Q8): B is int8.  Job t loads A(t) into stage t % S and the int8 B of
+// tile t + 1 into the int8 area of stage (t + 1) % S (that area's previous
+// tile was widened before tile t began); tile t widens the int8 B of tile t + 1
+// into the bf16 buffer (t + 1) & 1 while it computes from buffer t & 1, and the
+// barrier that opens tile t + 1 publishes it.  The int8 B of tile 0 is loaded
+// and widened before the loop.  Past the last tile, job nk - 1 loads a clamped,
+// unused int8 tile, so that every job issues the same loads and the vmcnt
+// arithmetic stays exact.
 template <class G, bool A_MN, bool B_MN, int S>
 __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __restrict__ A, int64_t lda,
                                           const uint16_t* __restrict__ B, int64_t ldb, int m0, int n0, int M, int N,
@@ -493,6 +673,7 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     const int wm = wave / G::NWN, wn = wave % G::NWN;
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const uint32_t base = lds_offset(lds);
+    unsigned char* const bbf = lds + S * kStageBytes;   // Q8: widened B, two tiles
     if (zero) {
 #pragma unroll
         for (int i = 0; i < G::MI; ++i)
@@ -505,29 +686,75 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     if (nk == 0) return;
 
     DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
+    // Q8: where job t puts the int8 B of tile t + 1, and its k (k-major tiles
+    // past K are clamped to the last one; n-major rows are clamped per row)
+    auto set_b8 = [&](int t, int stage_of_t) {
+        if constexpr (G::Q8) {
+            const int sb = stage_of_t == S - 1 ? 0 : stage_of_t + 1;
+            job.stage_b = base + sb * kStageBytes + kABytes;
+            job.k0_b = B_MN ? kb + (t + 1) * BK : min(kb + (t + 1) * BK, ke - BK);
+        }
+    };
+    if constexpr (G::Q8) {
+        // the int8 B of tile 0, ahead of every job
+        DmaJob j0 = job;
+        j0.stage_b = base + kABytes;
+        j0.k0_b = kb;
+        constexpr int NA = OperandLoads<BM, A_MN, G::NW>::n, NB = OperandLoads8<BN, G::NW>::n;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            dma_one8<BN, B_MN, G::NW>(j, j0.stage_b, reinterpret_cast<const int8_t*>(B), ldb, n0, N, kb, ke, wave,
+                                      lane);
+        (void)NA;
+    }
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) {
         if (t < nk) {
             job.stage = base + t * kStageBytes;
             job.k0 = kb + t * BK;
+            set_b8(t, t);
             dma_tile<G, A_MN, B_MN>(job);
         }
+    }
+    if constexpr (G::Q8) {
+        // tile 0's int8 B landed (only the jobs may still be in flight) for every
+        // thread: widen it into buffer 0
+        wait_jobs<kLoadsPerTile, S>(min(S - 1, nk));
+        block_barrier();
+        widen_all<G, B_MN>(lds + kABytes, bbf, ke - kb, tid);
     }
     // Tile kt becomes readable once this thread's loads of it are done (at most
     // those of the tiles after it, up to kt + S - 2, remain) and every wave has
     // passed the barrier; a ragged last m/n-major tile then gets its rows past K
-    // zeroed (they were loaded from clamped rows).
+    // zeroed (they were loaded from clamped rows; Q8 B tiles are zeroed when widened).
     auto enter = [&](int kt, int stage) {
         wait_tiles<kLoadsPerTile, S>(min(nk, kt + S - 1) - kt - 1);
         block_barrier();
-        if constexpr (A_MN || B_MN) {
+        constexpr bool zb = B_MN && !G::Q8;
+        if constexpr (A_MN || zb) {
             const int valid = ke - (kb + kt * BK);
             if (valid < BK) {
                 if constexpr (A_MN) zero_rows_mn<BM, G::kThreads>(lds + stage * kStageBytes, valid, tid);
-                if constexpr (B_MN) zero_rows_mn<BN, G::kThreads>(lds + stage * kStageBytes + kABytes, valid, tid);
+                if constexpr (zb) zero_rows_mn<BN, G::kThreads>(lds + stage * kStageBytes + kABytes, valid, tid);
                 __syncthreads();
             }
         }
+    };
+    // the B tile that tile kt reads, and the widening tile kt does for tile kt + 1
+    auto b_tile = [&](int kt, int stage) -> const unsigned char* {
+        if constexpr (G::Q8) return bbf + (kt & 1) * G::kBBytes;
+        else return lds + stage * kStageBytes + kABytes;
+    };
+    auto widen_job = [&](int kt, int stage) {
+        WidenJob w;
+        if constexpr (G::Q8) {
+            const int sn = stage == S - 1 ? 0 : stage + 1;
+            w.src = lds + sn * kStageBytes + kABytes;
+            w.dst = bbf + ((kt + 1) & 1) * G::kBBytes;
+            w.valid = ke - (kb + (kt + 1) * BK);
+            w.on = kt + 1 < nk;
+        }
+        return w;
     };
     int st = 0;            // stage of tile kt
     int st_load = S - 1;   // stage that receives tile kt + S - 1
@@ -542,7 +769,9 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
             enter(kt, st);
             job.stage = base + st_load * kStageBytes;
             job.k0 = kb + (kt + S - 1) * BK;
-            compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, wm, wn, lane, acc, job, kt + S - 1 < nk);
+            set_b8(kt + S - 1, st_load);
+            compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, b_tile(kt, st), wm, wn, lane, acc, job,
+                                        kt + S - 1 < nk, widen_job(kt, st), tid);
             st = st == S - 1 ? 0 : st + 1;
             st_load = st_load == S - 1 ? 0 : st_load + 1;
         }
@@ -550,17 +779,24 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     }
     uint4 af[2][G::MI], bfr[2][G::NJ];
     enter(0, 0);
-    load_frags<G, A_MN, B_MN>(lds, wm, wn, 0, lane, af[0], bfr[0]);
+    load_frags<G, A_MN, B_MN>(lds, b_tile(0, 0), wm, wn, 0, lane, af[0], bfr[0]);
     for (int kt = 0; kt < nk; ++kt) {
         job.stage = base + st_load * kStageBytes;
         job.k0 = kb + (kt + S - 1) * BK;
+        set_b8(kt + S - 1, st_load);
         const bool load_next = kt + S - 1 < nk;
         const unsigned char* cur_st = lds + st * kStageBytes;
+        const unsigned char* cur_b = b_tile(kt, st);
         const int st_next = st == S - 1 ? 0 : st + 1;
+        const WidenJob wj = widen_job(kt, st);
+        Widen8<G> w8;
+        if constexpr (G::Q8)
+            if (wj.on) widen_load<G>(wj.src, tid, w8);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int cur = ks & 1;
-            if (ks + 1 < BK / 16) load_frags<G, A_MN, B_MN>(cur_st, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            if (ks + 1 < BK / 16)
+                load_frags<G, A_MN, B_MN>(cur_st, cur_b, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
             if (load_next) {
                 switch (ks) {
                     case 0: dma_part<G, A_MN, B_MN, 0, 4>(job); break;
@@ -571,7 +807,8 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
             }
             if (ks == BK / 16 - 1 && kt + 1 < nk) {
                 enter(kt + 1, st_next);
-                load_frags<G, A_MN, B_MN>(lds + st_next * kStageBytes, wm, wn, 0, lane, af[cur ^ 1], bfr[cur ^ 1]);
+                load_frags<G, A_MN, B_MN>(lds + st_next * kStageBytes, b_tile(kt + 1, st_next), wm, wn, 0, lane,
+                                          af[cur ^ 1], bfr[cur ^ 1]);
             }
             // The MFMAs run at raised wave priority, so the arbiter favours the
             // waves that keep the matrix cores busy over those issuing loads.
@@ -583,6 +820,14 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
                 for (int j = 0; j < G::NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (G::Q8) {
+                // every quarter must land before the barrier that opens tile
+                // kt + 1 (taken at the last k-step, before its MFMAs): the
+                // third k-step does the last two quarters
+                if (wj.on && ks < BK / 16 - 1) widen_step<G, B_MN>(ks, wj.dst, wj.valid, tid, w8);
+                if (wj.on && ks == BK / 16 - 2) widen_step<G, B_MN>(ks + 1, wj.dst, wj.valid, tid, w8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         st = st_next;
         st_load = st_load == S - 1 ? 0 : st_load + 1;
@@ -593,16 +838,18 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
 // DUAL = 2: the second product goes to its own accumulator (general epilogue mode 2).
 // GRP: a grouped product (PipeArgs::grp), a separate instantiation so that the
 // plain kernels carry no group lookup.
+// Q8: B is int8 (the quantized weight), see main_loop.
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI, int S, int NWM = 2, int NWN = 2, int DUAL = 0,
-          bool GRP = false>
+          bool GRP = false, bool Q8 = false>
 __global__ void __launch_bounds__(64 * NWM * NWN)
 __attribute__((amdgpu_waves_per_eu(PipeWaves<BM, BN, NWM * NWN>::lo, PipeWaves<BM, BN, NWM * NWN>::hi)))
 pipe_gemm_kernel(const PipeArgs p) {
-    using G = Geo<BM, BN, NWM, NWN>;
+    using G = Geo<BM, BN, NWM, NWN, Q8>;
     constexpr int kStageBytes = G::kStageBytes;
     constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
-    static_assert(S * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes];
+    static_assert(S * kStageBytes + G::kExtraBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
+    static_assert(!Q8 || (!A_MN && DUAL == 0 && EPI != kEpiGeneral), "int8 B: k-major A, single product");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes + G::kExtraBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -660,15 +907,27 @@ pipe_gemm_kernel(const PipeArgs p) {
         return;
     }
     OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
+    // column scales of this lane's NJ columns (kEpiColScale), 1 otherwise
+    float csc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if constexpr (EPI == kEpiColScale) {
+            const float* sc = p.colscale + (int64_t)z * p.strideScale;
+            csc[j] = col0 + j * 32 < N ? sc[col0 + j * 32] : 0.f;
+        } else {
+            csc[j] = 1.f;
+        }
+    }
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    store_f32(C + (int64_t)(row0 + i * 32 + (r >> 2) * 8 + (r & 3)) * p.ldc + col0 + j * 32,
-                              acc[i][j][r]);
+                for (int r = 0; r < 16; ++r) {
+                    const float v = EPI == kEpiColScale ? acc[i][j][r] * csc[j] : acc[i][j][r];
+                    store_f32(C + (int64_t)(row0 + i * 32 + (r >> 2) * 8 + (r & 3)) * p.ldc + col0 + j * 32, v);
+                }
     } else {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -678,7 +937,8 @@ pipe_gemm_kernel(const PipeArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = row0 + i * 32 + (r >> 2) * 8 + (r & 3);
-                    if (row < M && col < N) store_f32(C + (int64_t)row * p.ldc + col, acc[i][j][r]);
+                    const float v = EPI == kEpiColScale ? acc[i][j][r] * csc[j] : acc[i][j][r];
+                    if (row < M && col < N) store_f32(C + (int64_t)row * p.ldc + col, v);
                 }
             }
     }
@@ -937,7 +1197,7 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 }
 
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
-          int DUAL = 0, bool GRP = false>
+          int DUAL = 0, bool GRP = false, bool Q8 = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
@@ -953,7 +1213,8 @@ hipError_t launch(const PipeArgs& p, hipStream_t stream) {
         if (p.Cin2) q.Cin2 = p.Cin2 + (int64_t)y0 * p.strideCin2;
         if (p.A2) q.A2 = reinterpret_cast<const uint16_t*>(p.A2) + (int64_t)y0 * p.strideA2;
         if (p.B2) q.B2 = reinterpret_cast<const uint16_t*>(p.B2) + (int64_t)y0 * p.strideB2;
-        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN, DUAL, GRP>),
+        if (p.colscale) q.colscale = p.colscale + (int64_t)y0 * p.strideScale;
+        hipLaunchKernelGGL((pipe_gemm_kernel<BM, BN, A_MN, B_MN, OUT_F32, EPI, S, NWM, NWN, DUAL, GRP, Q8>),
                            dim3(tiles, q.batch, p.splits), dim3(64 * NWM * NWN), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1619,6 +1880,52 @@ hipError_t dense_gemm_bf16(bool b_nn, const void* A, int64_t lda, const void* B,
                        : tiles(128, 128) >= 256 ? PipeTile::Square
                                                 : PipeTile::Slim;
     return pipe_gemm(false, b_nn, false, p, stream, t);
+}
+
+bool dense_gemm_q8_supported(bool b_nn, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    (void)b_nn;
+    // A is k-major bf16 (whole 64-k tiles); int8 B chunks are 16 bytes
+    return M > 0 && N >= 16 && N % 16 == 0 && K >= BK && K % BK == 0 && lda % 8 == 0 && ldb % 16 == 0;
+}
+
+hipError_t dense_gemm_q8(bool b_nn, const void* A, int64_t lda, const int8_t* B, int64_t ldb, const float* colscale,
+                         void* C, int64_t ldc, int M, int N, int K, hipStream_t stream) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (!dense_gemm_q8_supported(b_nn, M, N, K, lda, ldb) || (!b_nn && !colscale)) return hipErrorInvalidValue;
+    PipeArgs p;
+    p.A = A; p.lda = lda;
+    p.B = B; p.ldb = ldb;
+    p.C = C; p.ldc = ldc;
+    p.M = M; p.N = N; p.K = K;
+    p.k_per_split = K;
+    p.colscale = b_nn ? nullptr : colscale;
+    // tiles as for the bf16 dense products
+    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (!b_nn) {
+        if (tiles(256, 256) >= 256)
+            return launch<256, 256, false, false, false, kEpiColScale, 2, 2, 4, 0, false, true>(p, stream);
+        if (tiles(256, 128) >= 256)
+            return launch<256, 128, false, false, false, kEpiColScale, 3, 4, 2, 0, false, true>(p, stream);
+        if (tiles(128, 128) >= 256)
+            return launch<128, 128, false, false, false, kEpiColScale, 4, 2, 2, 0, false, true>(p, stream);
+        return launch<64, 128, false, false, false, kEpiColScale, 4, 2, 2, 0, false, true>(p, stream);
+    }
+    if (tiles(256, 256) >= 256) return launch<256, 256, false, true, false, kEpiPlain, 2, 2, 4, 0, false, true>(p, stream);
+    if (tiles(256, 128) >= 256) return launch<256, 128, false, true, false, kEpiPlain, 3, 4, 2, 0, false, true>(p, stream);
+    if (tiles(128, 128) >= 256) return launch<128, 128, false, true, false, kEpiPlain, 4, 2, 2, 0, false, true>(p, stream);
+    return launch<64, 128, false, true, false, kEpiPlain, 4, 2, 2, 0, false, true>(p, stream);
+}
+
+hipError_t pipe_gemm_colscale(const PipeArgs& p, hipStream_t stream, PipeTile tile) {
+    if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+    if (!p.colscale || p.splits != 1) return hipErrorInvalidValue;
+    switch (tile) {
+        case PipeTile::Big: return launch<256, 256, false, true, false, kEpiColScale, 2, 2, 4>(p, stream);
+        case PipeTile::Wide: return launch<128, 256, false, true, false, kEpiColScale, 3, 2, 4>(p, stream);
+        case PipeTile::Slim: return launch<64, 128, false, true, false, kEpiColScale, 4>(p, stream);
+        case PipeTile::Tall: return launch<256, 128, false, true, false, kEpiColScale, 3, 4, 2>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }

@@ -156,6 +156,8 @@ class POETLinear(torch.nn.Module):
         self.quantized = bool(quantized)
         if self.quantized and W0.dtype != torch.bfloat16:
             raise TypeError("the quantized layer computes in bfloat16")
+        if self.quantized and b % 64:
+            raise ValueError("the quantized layer needs a block size that is a multiple of 64")
         self.mem_efficient_mode = bool(mem_efficient_mode) or self.quantized
         self.dtype = W0.dtype
         self.nblk_R, self.nblk_P = m // b, n // b

@@ -230,13 +230,22 @@ def test_quantized_weight_layout_and_validation(B):
     assert lib.poetx_quantize_weight(None, B.POETX_BF16, 8, 48, FAKE, None) == B.POETX_ERR_INVALID_ARG
     assert lib.poetx_quantize_weight(FAKE, B.POETX_BF16, 8, 48, FAKE + 8, None) == B.POETX_ERR_INVALID_ARG
     assert lib.poetx_dequantize_weight(FAKE, -1, 48, FAKE, None) == B.POETX_ERR_SHAPE
-    # mem_q8: bf16 only, saves nothing, the mem workspace plus one bf16 weight
+    # mem_q8: bf16 only, saves nothing; the layer calls need the mem workspace
+    # only (the int8 codes go straight into the dense products), the merge also
+    # one bf16 expansion of the weight
     q8 = B.desc(2048, 4096, 1024, 256, 3, B.POETX_BF16, B.POETX_MEM_Q8)
     mem = B.desc(2048, 4096, 1024, 256, 3, B.POETX_BF16, B.POETX_MEM)
     assert lib.poetx_linear_saved_bytes(C.byref(q8)) == 0
-    for f in (lib.poetx_linear_fwd_workspace_bytes, lib.poetx_linear_bwd_workspace_bytes,
-              lib.poetx_merge_workspace_bytes):
-        assert f(C.byref(q8)) == f(C.byref(mem)) + 2 * 4096 * 1024
+    for f in (lib.poetx_linear_fwd_workspace_bytes, lib.poetx_linear_bwd_workspace_bytes):
+        assert f(C.byref(q8)) == f(C.byref(mem))
+    assert lib.poetx_merge_workspace_bytes(C.byref(q8)) == lib.poetx_merge_workspace_bytes(C.byref(mem)) + \
+        2 * 4096 * 1024
+    # the int8 products run in 64-k steps over m and n: b % 64 == 0
+    for bad_b in (16, 32, 48, 80):
+        dbad = B.desc(64, 4 * bad_b, 2 * bad_b, bad_b, 3, B.POETX_BF16, B.POETX_MEM_Q8)
+        assert lib.poetx_linear_fwd_workspace_bytes(C.byref(dbad)) == 0
+        assert lib.poetx_linear_fwd(C.byref(dbad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                    None) == B.POETX_ERR_SHAPE
     f32 = B.desc(2048, 4096, 1024, 256, 3, B.POETX_F32, B.POETX_MEM_Q8)
     assert lib.poetx_linear_fwd(C.byref(f32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
                                 None) == B.POETX_ERR_UNSUPPORTED

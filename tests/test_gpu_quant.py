@@ -3,9 +3,11 @@ with int8 per-row storage as this library's reading of its 8-bit setting).
 
 The int8 codes and scales are integers / float32 values decided in float32 on
 both sides and must match the oracle bit for bit; the layer on the quantized
-weight is held to the bf16 bar (relative Frobenius 1.5e-2) against the oracle's
-layer on the dequantized weight, and must equal the mem chain run on the
-library's own dequantized weight bit for bit."""
+weight (its dense products read the int8 codes and apply the row scales in
+float32) is held to the bf16 bar (relative Frobenius 1.5e-2, every row and
+block) against the oracle's layer on the weight the storage stands for,
+code * scale, and stays within that bar of the mem chain run on the library's
+own bf16 expansion of the same storage."""
 import numpy as np
 import pytest
 import torch
@@ -67,8 +69,8 @@ def _oracle_q8(spec, inp):
     return dict(y=y, dx=dx, dG_R=dG_R, dG_P=dG_P), W0q
 
 
-@pytest.mark.parametrize("m,n,b,k,T", [(768, 512, 128, 3, 300), (512, 1024, 256, 3, 257), (64, 48, 16, 3, 40),
-                                       (1024, 512, 256, 4, 2048)])
+@pytest.mark.parametrize("m,n,b,k,T", [(768, 512, 128, 3, 300), (512, 1024, 256, 3, 257), (128, 192, 64, 3, 40),
+                                       (1024, 512, 256, 4, 2048), (4096, 1024, 256, 3, 77)])
 def test_mem_q8_layer_parity(m, n, b, k, T):
     spec = I.LinearSpec(f"q8_{m}x{n}", m=m, n=n, b=b, k=k, T=T, dtype="bf16", q_std=0.02, key=(61, m, T))
     inp = I.make_linear_inputs(spec)
@@ -79,14 +81,31 @@ def test_mem_q8_layer_parity(m, n, b, k, T):
     got = dict(y=host(g.y), dx=host(g.dx), dG_R=host(g.dG_R), dG_P=host(g.dG_P))
     errs = {key: rel_fro(got[key], ref[key]) for key in ref}
     assert all(e <= tol("bf16") for e in errs.values()), errs
-    # the same step on the library's own expansion of the quantized weight, mem chain
+    # the same step on the library's own bf16 expansion of the storage, mem chain:
+    # the same function up to that expansion's rounding
     mem = GpuLayer(spec, inp, "mem")
     B.poetx_dequantize_weight(g.weight, m, n, mem.Wt)
     mem.weight = mem.Wt
     mem.forward()
     mem.backward()
     for a, c in ((g.y, mem.y), (g.dx, mem.dx), (g.dG_R, mem.dG_R), (g.dG_P, mem.dG_P)):
-        assert torch.equal(a, c)
+        assert rel_fro(host(a), host(c)) <= tol("bf16")
+    # runs are bitwise repeatable
+    y0, dx0 = g.y.clone(), g.dx.clone()
+    g.forward()
+    g.backward()
+    assert torch.equal(g.y, y0) and torch.equal(g.dx, dx0)
+
+
+def test_mem_q8_keeps_no_dequantized_weight():
+    """The quantized variant's workspaces are those of the mem variant: the
+    int8 codes go straight into the dense products, no bf16 copy of the weight
+    is made (the merge, once per reset gap, still expands it)."""
+    for (T, m, n, b) in ((2048, 4096, 4096, 256), (4096, 14336, 4096, 512), (40, 128, 192, 64)):
+        dq = B.desc(T, m, n, b, 3, B.POETX_BF16, B.POETX_MEM_Q8)
+        dm = B.desc(T, m, n, b, 3, B.POETX_BF16, B.POETX_MEM)
+        assert B.poetx_linear_fwd_workspace_bytes(dq) == B.poetx_linear_fwd_workspace_bytes(dm)
+        assert B.poetx_linear_bwd_workspace_bytes(dq) == B.poetx_linear_bwd_workspace_bytes(dm)
 
 
 def test_mem_q8_merge():
@@ -141,3 +160,42 @@ def test_q_proj_shape_mem_q8_sampled():
                dG_P=O.block_grad_blocks(inp["dy"], inp["x"], *args, "P", jP))
     errs = {key: rel_fro(got[key], ref[key]) for key in ref}
     assert all(e <= tol("bf16") for e in errs.values()), errs
+
+
+def _pow2_scaled_weight(m, n, seed):
+    """A weight whose int8 row storage is exact: integer codes in [-127, 127]
+    times a power-of-two scale per row, each row holding a +-127 (so the
+    quantizer's scale is exactly that power of two).  bf16 holds every entry."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-127, 128, size=(m, n))
+    codes[np.arange(m), rng.integers(0, n, size=m)] = 127 * rng.choice([-1, 1], size=m)
+    scale = 2.0 ** rng.integers(-9, -5, size=m)
+    return (codes * scale[:, None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("m,n,b,T", [(4096, 4096, 256, 2048),     # 256 x 128 product tiles
+                                     (14336, 4096, 512, 4096),    # 256 x 256
+                                     (2048, 2048, 256, 2048),     # 128 x 128
+                                     (1024, 4096, 256, 2048),     # 64 x 128
+                                     (768, 512, 128, 300)])       # 64 x 128, ragged rows
+def test_mem_q8_equals_mem_bitwise_on_an_exactly_stored_weight(m, n, b, T):
+    """On a weight the int8 storage holds exactly with power-of-two row scales,
+    scaling in float32 after the products (forward) or before them (dh2) equals
+    using the bf16 weight itself: the quantized chain must equal the mem chain
+    bit for bit, through every tile shape of the int8 products."""
+    spec = I.LinearSpec(f"q8x_{m}x{n}", m=m, n=n, b=b, k=3, T=T, dtype="bf16", q_std=0.01, key=(63, m, T))
+    inp = I.make_linear_inputs(spec)
+    W = _pow2_scaled_weight(m, n, 64 + m)
+    Wt_perm = np.empty_like(W)
+    Wt_perm[np.ix_(inp["pi_R"], inp["pi_P"])] = W    # so that the pre-permuted weight is W
+    inp["W0"] = Wt_perm
+    g = GpuLayer(spec, inp, "mem_q8")
+    mem = GpuLayer(spec, inp, "mem")
+    assert torch.equal(mem.Wt, dev(W, "bf16"))
+    q, s = _split(g.weight, m, n)
+    assert np.all(np.log2(s) == np.round(np.log2(s)))   # the scales are powers of two
+    for lay in (g, mem):
+        lay.forward()
+        lay.backward()
+    for a, c in ((g.y, mem.y), (g.dx, mem.dx), (g.dG_R, mem.dG_R), (g.dG_P, mem.dG_P)):
+        assert torch.equal(a, c)
