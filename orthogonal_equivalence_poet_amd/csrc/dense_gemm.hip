@@ -89,6 +89,14 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
                  : "memory", "m0");
 }
 
+// The same load with a wave-uniform 64-bit base (SGPR pair) and a 32-bit
+// per-lane byte offset: the base moves with the k-tile, the offsets stay
+// fixed, so the loop issues no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -175,9 +183,32 @@ __device__ __forceinline__ void dma_one8(int j, uint32_t dst, const int8_t* __re
     }
 }
 
+// Byte offset of the j-th 1 KB run's 16 bytes for this lane, relative to the
+// operand's k-tile base (k-major: src + k0; m/n-major: src + k0 ld), with the
+// row / column clamps of dma_one; k needs no clamp (whole k-tiles only).
+template <int ROWS, bool MN, int NW>
+__device__ __forceinline__ uint32_t dma_voff(int j, int64_t ld, int r0, int rows_total, int wave, int lane) {
+    const int g = j * NW + wave;
+    if constexpr (!MN) {
+        const int r = 8 * g + (lane >> 3);
+        const int c = (lane & 7) ^ swz_k(r);
+        const int row = min(r0 + r, rows_total - 1);
+        return (uint32_t)(2 * ((int64_t)row * ld + c * 8));
+    } else {
+        constexpr int kRowBytes = ROWS * 2;
+        constexpr int kRowsPerRun = 1024 / kRowBytes;
+        constexpr int kSlots = kRowBytes / 16;
+        const int kr = kRowsPerRun * g + lane / kSlots;
+        const int c = (lane % kSlots) ^ swz_mn<ROWS>(kr);
+        const int col = min(r0 + c * 8, rows_total - 8);
+        return (uint32_t)(2 * ((int64_t)kr * ld + col));
+    }
+}
+
 // Everything needed to issue the loads of one k-tile into one LDS stage.
 // Q8 jobs load the int8 B tile of the NEXT k-tile (k0_b) into stage_b, so that
-// it can be widened while the current tile computes.
+// it can be widened while the current tile computes.  Products with a k-major
+// A (SADDR) carry fixed per-lane offsets and move only the two uniform bases.
 struct DmaJob {
     uint32_t stage;
     const uint16_t* A;
@@ -187,18 +218,32 @@ struct DmaJob {
     int m0, n0, M, N, k0, k_end, wave, lane;
     uint32_t stage_b = 0;
     int k0_b = 0;
+    const char* a_k = nullptr;   // SADDR: A + k0 (bytes), B + k0 or B + k0 ldb
+    const char* b_k = nullptr;
+    uint32_t voff[16] = {};      // SADDR: per-lane offsets of the tile's loads (A's, then B's)
 };
 
 // Part PART of NPARTS of a k-tile's loads (A's loads first, then B's), so the
 // loads can be spread over the MFMA work of the tile being computed.
+template <class G, bool A_MN>
+constexpr bool kSaddr = !A_MN && !G::Q8;
+
 template <class G, bool A_MN, bool B_MN, int PART, int NPARTS>
 __device__ __forceinline__ void dma_part(const DmaJob& d) {
     constexpr int NA = OperandLoads<G::BM, A_MN, G::NW>::n;
     constexpr int NB = G::Q8 ? OperandLoads8<G::BN, G::NW>::n : OperandLoads<G::BN, B_MN, G::NW>::n;
     constexpr int L = NA + NB;
     constexpr int lo = PART * L / NPARTS, hi = (PART + 1) * L / NPARTS;
+    static_assert(!kSaddr<G, A_MN> || L <= 16, "per-lane offsets");
 #pragma unroll
     for (int idx = lo; idx < hi; ++idx) {
+        if constexpr (kSaddr<G, A_MN>) {
+            const bool is_a = idx < NA;
+            const int g = (is_a ? idx : idx - NA) * G::NW + d.wave;
+            const uint32_t m0 = d.stage + (is_a ? 0u : (uint32_t)G::kABytes) + g * 1024;
+            dma16s(is_a ? d.a_k : d.b_k, d.voff[idx], __builtin_amdgcn_readfirstlane(m0));
+            continue;
+        }
         if (idx < NA)
             dma_one<G::BM, A_MN, G::NW>(idx, d.stage, d.A, d.lda, d.m0, d.M, d.k0, d.k_end, d.wave, d.lane);
         else if constexpr (G::Q8)
@@ -686,6 +731,20 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     if (nk == 0) return;
 
     DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
+    if constexpr (kSaddr<G, A_MN>) {
+        constexpr int NA = OperandLoads<BM, A_MN, G::NW>::n, NB = OperandLoads<BN, B_MN, G::NW>::n;
+#pragma unroll
+        for (int j = 0; j < NA; ++j) job.voff[j] = dma_voff<BM, false, G::NW>(j, lda, m0, M, wave, lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) job.voff[NA + j] = dma_voff<BN, B_MN, G::NW>(j, ldb, n0, N, wave, lane);
+    }
+    // the uniform bases of job k0 (SADDR)
+    auto set_bases = [&]() {
+        if constexpr (kSaddr<G, A_MN>) {
+            job.a_k = reinterpret_cast<const char*>(A) + 2 * (int64_t)job.k0;
+            job.b_k = reinterpret_cast<const char*>(B) + 2 * (B_MN ? (int64_t)job.k0 * ldb : (int64_t)job.k0);
+        }
+    };
     // Q8: where job t puts the int8 B of tile t + 1, and its k (k-major tiles
     // past K are clamped to the last one; n-major rows are clamped per row)
     auto set_b8 = [&](int t, int stage_of_t) {
@@ -713,6 +772,7 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
             job.stage = base + t * kStageBytes;
             job.k0 = kb + t * BK;
             set_b8(t, t);
+            set_bases();
             dma_tile<G, A_MN, B_MN>(job);
         }
     }
@@ -770,6 +830,7 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
             job.stage = base + st_load * kStageBytes;
             job.k0 = kb + (kt + S - 1) * BK;
             set_b8(kt + S - 1, st_load);
+            set_bases();
             compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, b_tile(kt, st), wm, wn, lane, acc, job,
                                         kt + S - 1 < nk, widen_job(kt, st), tid);
             st = st == S - 1 ? 0 : st + 1;
@@ -784,6 +845,7 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
         job.stage = base + st_load * kStageBytes;
         job.k0 = kb + (kt + S - 1) * BK;
         set_b8(kt + S - 1, st_load);
+        set_bases();
         const bool load_next = kt + S - 1 < nk;
         const unsigned char* cur_st = lds + st * kStageBytes;
         const unsigned char* cur_b = b_tile(kt, st);
@@ -1199,6 +1261,11 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
           int DUAL = 0, bool GRP = false, bool Q8 = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
+    if constexpr (!A_MN && !Q8) {
+        // the loads address each operand k-tile by 32-bit per-lane byte offsets
+        const int64_t span_a = (int64_t)p.M * p.lda * 2, span_b = (int64_t)(B_MN ? p.K : p.N) * p.ldb * 2;
+        if (span_a >= (int64_t(1) << 32) || span_b >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    }
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     constexpr int kMaxY = 65535;
     for (int y0 = 0; y0 < p.batch; y0 += kMaxY) {
