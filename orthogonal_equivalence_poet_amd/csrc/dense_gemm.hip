@@ -714,7 +714,9 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     constexpr int kLoadsPerTile = G::kLoadsPerTile;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform: held in a scalar register, the LDS destinations
+    // of the loads (M0) are formed without per-lane arithmetic
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / G::NWN, wn = wave % G::NWN;
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const uint32_t base = lds_offset(lds);
@@ -790,7 +792,9 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     auto enter = [&](int kt, int stage) {
         wait_tiles<kLoadsPerTile, S>(min(nk, kt + S - 1) - kt - 1);
         block_barrier();
-        constexpr bool zb = B_MN && !G::Q8;
+        // a k-major A means whole 64-k tiles (no ragged tile); Q8 B tiles are
+        // zeroed when widened
+        constexpr bool zb = B_MN && A_MN;
         if constexpr (A_MN || zb) {
             const int valid = ke - (kb + kt * BK);
             if (valid < BK) {
