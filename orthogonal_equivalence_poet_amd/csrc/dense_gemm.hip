@@ -789,8 +789,10 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     // those of the tiles after it, up to kt + S - 2, remain) and every wave has
     // passed the barrier; a ragged last m/n-major tile then gets its rows past K
     // zeroed (they were loaded from clamped rows; Q8 B tiles are zeroed when widened).
-    auto enter = [&](int kt, int stage) {
-        wait_tiles<kLoadsPerTile, S>(min(nk, kt + S - 1) - kt - 1);
+    // pending: this thread's k-tiles of loads that may stay in flight, S - 2 in
+    // the steady part of the loop (a constant the wait folds to one s_waitcnt)
+    auto enter = [&](int kt, int stage, int pending) {
+        wait_tiles<kLoadsPerTile, S>(pending);
         block_barrier();
         // a k-major A means whole 64-k tiles (no ragged tile); Q8 B tiles are
         // zeroed when widened
@@ -828,33 +830,46 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     // first LDS reads of the next tile; the same barrier frees tile kt's stage,
     // as every wave holds tile kt's last fragments in registers by then.  Other
     // tiles hand over at the top of each tile.
+    // The loop runs in two parts: a steady one, where every tile issues the
+    // loads of tile kt + S - 1 and waits with a fixed count, and the last
+    // S - 1 tiles, which issue none and wait for what is left.
     if constexpr (!(S >= 3 && BM == 256 && BN == 128)) {
-        for (int kt = 0; kt < nk; ++kt) {
-            enter(kt, st);
+        auto tile = [&](int kt, auto steady_c) {
+            constexpr bool STEADY = decltype(steady_c)::value;
+            enter(kt, st, STEADY ? S - 2 : min(nk, kt + S - 1) - kt - 1);
             job.stage = base + st_load * kStageBytes;
             job.k0 = kb + (kt + S - 1) * BK;
             set_b8(kt + S - 1, st_load);
             set_bases();
+            WidenJob wj = widen_job(kt, st);
+            if constexpr (STEADY && G::Q8) wj.on = true;
             compute_tile<G, A_MN, B_MN>(lds + st * kStageBytes, b_tile(kt, st), wm, wn, lane, acc, job,
-                                        kt + S - 1 < nk, widen_job(kt, st), tid);
+                                        STEADY || kt + S - 1 < nk, wj, tid);
             st = st == S - 1 ? 0 : st + 1;
             st_load = st_load == S - 1 ? 0 : st_load + 1;
-        }
+        };
+        int kt = 0;
+        for (; kt + S - 1 < nk; ++kt) tile(kt, std::true_type{});
+        for (; kt < nk; ++kt) tile(kt, std::false_type{});
         return;
     }
     uint4 af[2][G::MI], bfr[2][G::NJ];
-    enter(0, 0);
+    enter(0, 0, min(nk, S - 1) - 1);
     load_frags<G, A_MN, B_MN>(lds, b_tile(0, 0), wm, wn, 0, lane, af[0], bfr[0]);
-    for (int kt = 0; kt < nk; ++kt) {
+    // steady: tile kt + S - 1 exists (so does tile kt + 1, and kt + S <= nk)
+    auto tile = [&](int kt, auto steady_c) {
+        constexpr bool STEADY = decltype(steady_c)::value;
         job.stage = base + st_load * kStageBytes;
         job.k0 = kb + (kt + S - 1) * BK;
         set_b8(kt + S - 1, st_load);
         set_bases();
-        const bool load_next = kt + S - 1 < nk;
+        const bool load_next = STEADY || kt + S - 1 < nk;
+        const bool has_next = STEADY || kt + 1 < nk;
         const unsigned char* cur_st = lds + st * kStageBytes;
         const unsigned char* cur_b = b_tile(kt, st);
         const int st_next = st == S - 1 ? 0 : st + 1;
-        const WidenJob wj = widen_job(kt, st);
+        WidenJob wj = widen_job(kt, st);
+        if constexpr (STEADY && G::Q8) wj.on = true;
         Widen8<G> w8;
         if constexpr (G::Q8)
             if (wj.on) widen_load<G>(wj.src, tid, w8);
@@ -871,8 +886,8 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
                     default: dma_part<G, A_MN, B_MN, 3, 4>(job); break;
                 }
             }
-            if (ks == BK / 16 - 1 && kt + 1 < nk) {
-                enter(kt + 1, st_next);
+            if (ks == BK / 16 - 1 && has_next) {
+                enter(kt + 1, st_next, STEADY ? S - 2 : min(nk, kt + S) - kt - 2);
                 load_frags<G, A_MN, B_MN>(lds + st_next * kStageBytes, b_tile(kt + 1, st_next), wm, wn, 0, lane,
                                           af[cur ^ 1], bfr[cur ^ 1]);
             }
@@ -897,7 +912,10 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
         }
         st = st_next;
         st_load = st_load == S - 1 ? 0 : st_load + 1;
-    }
+    };
+    int kt = 0;
+    for (; kt + S - 1 < nk; ++kt) tile(kt, std::true_type{});
+    for (; kt < nk; ++kt) tile(kt, std::false_type{});
 }
 
 // DUAL = 1: acc = op(A) op(B) + A2^T B2 (second product with m/n-major A2, B2);
