@@ -104,6 +104,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
 __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -205,6 +208,23 @@ __device__ __forceinline__ uint32_t dma_voff(int j, int64_t ld, int r0, int rows
     }
 }
 
+// The same for an int8 operand tile (dma_one8's addressing), in bytes.
+template <int ROWS, bool MN, int NW>
+__device__ __forceinline__ uint32_t dma_voff8(int j, int64_t ld, int r0, int rows_total, int wave, int lane) {
+    const int g = j * NW + wave;
+    if constexpr (!MN) {
+        const int r = 16 * g + (lane >> 2);
+        const int row = min(r0 + r, rows_total - 1);
+        return (uint32_t)((int64_t)row * ld + (lane & 3) * 16);
+    } else {
+        constexpr int kSlots = ROWS / 16;
+        constexpr int kRowsPerRun = 1024 / ROWS;
+        const int kr = kRowsPerRun * g + lane / kSlots;
+        const int col = min(r0 + (lane % kSlots) * 16, rows_total - 16);
+        return (uint32_t)((int64_t)kr * ld + col);
+    }
+}
+
 // Everything needed to issue the loads of one k-tile into one LDS stage.
 // Q8 jobs load the int8 B tile of the NEXT k-tile (k0_b) into stage_b, so that
 // it can be widened while the current tile computes.  Products with a k-major
@@ -226,7 +246,7 @@ struct DmaJob {
 // Part PART of NPARTS of a k-tile's loads (A's loads first, then B's), so the
 // loads can be spread over the MFMA work of the tile being computed.
 template <class G, bool A_MN>
-constexpr bool kSaddr = !A_MN && !G::Q8;
+constexpr bool kSaddr = !A_MN;
 
 template <class G, bool A_MN, bool B_MN, int PART, int NPARTS>
 __device__ __forceinline__ void dma_part(const DmaJob& d) {
@@ -240,7 +260,7 @@ __device__ __forceinline__ void dma_part(const DmaJob& d) {
         if constexpr (kSaddr<G, A_MN>) {
             const bool is_a = idx < NA;
             const int g = (is_a ? idx : idx - NA) * G::NW + d.wave;
-            const uint32_t m0 = d.stage + (is_a ? 0u : (uint32_t)G::kABytes) + g * 1024;
+            const uint32_t m0 = (is_a ? d.stage : G::Q8 ? d.stage_b : d.stage + (uint32_t)G::kABytes) + g * 1024;
             dma16s(is_a ? d.a_k : d.b_k, d.voff[idx], __builtin_amdgcn_readfirstlane(m0));
             continue;
         }
@@ -297,7 +317,10 @@ __device__ __forceinline__ void widen_part(unsigned char* __restrict__ dst, int 
         const int c = q >> 2, dw = q & 3;
         const int u = c * G::kThreads + tid;
         const uint4& w = r.w[c];
-        const uint32_t word = dw == 0 ? w.x : dw == 1 ? w.y : dw == 2 ? w.z : w.w;
+        uint32_t word = dw == 0 ? w.x : dw == 1 ? w.y : dw == 2 ? w.z : w.w;
+        // an ordered no-op on the input: the conversion cannot be hoisted
+        // above the scheduling barrier of the k-step it belongs to
+        asm volatile("" : "+v"(word));
         uint2 v = widen4(word);
         int off;
         if constexpr (!B_MN) {
@@ -734,26 +757,32 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
 
     DmaJob job{base, A, lda, B, ldb, m0, n0, M, N, kb, ke, wave, lane};
     if constexpr (kSaddr<G, A_MN>) {
-        constexpr int NA = OperandLoads<BM, A_MN, G::NW>::n, NB = OperandLoads<BN, B_MN, G::NW>::n;
+        constexpr int NA = OperandLoads<BM, A_MN, G::NW>::n;
+        constexpr int NB = G::Q8 ? OperandLoads8<BN, G::NW>::n : OperandLoads<BN, B_MN, G::NW>::n;
 #pragma unroll
         for (int j = 0; j < NA; ++j) job.voff[j] = dma_voff<BM, false, G::NW>(j, lda, m0, M, wave, lane);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) job.voff[NA + j] = dma_voff<BN, B_MN, G::NW>(j, ldb, n0, N, wave, lane);
+        for (int j = 0; j < NB; ++j)
+            job.voff[NA + j] = G::Q8 ? dma_voff8<BN, B_MN, G::NW>(j, ldb, n0, N, wave, lane)
+                                     : dma_voff<BN, B_MN, G::NW>(j, ldb, n0, N, wave, lane);
     }
     // the uniform bases of job k0 (SADDR)
     auto set_bases = [&]() {
         if constexpr (kSaddr<G, A_MN>) {
             job.a_k = reinterpret_cast<const char*>(A) + 2 * (int64_t)job.k0;
-            job.b_k = reinterpret_cast<const char*>(B) + 2 * (B_MN ? (int64_t)job.k0 * ldb : (int64_t)job.k0);
+            if constexpr (G::Q8)   // int8 B of tile k0_b
+                job.b_k = reinterpret_cast<const char*>(B) + (B_MN ? (int64_t)job.k0_b * ldb : (int64_t)job.k0_b);
+            else
+                job.b_k = reinterpret_cast<const char*>(B) + 2 * (B_MN ? (int64_t)job.k0 * ldb : (int64_t)job.k0);
         }
     };
-    // Q8: where job t puts the int8 B of tile t + 1, and its k (k-major tiles
-    // past K are clamped to the last one; n-major rows are clamped per row)
+    // Q8: where job t puts the int8 B of tile t + 1, and its k (a tile past K
+    // is clamped to the last one; K is whole 64-k tiles)
     auto set_b8 = [&](int t, int stage_of_t) {
         if constexpr (G::Q8) {
             const int sb = stage_of_t == S - 1 ? 0 : stage_of_t + 1;
             job.stage_b = base + sb * kStageBytes + kABytes;
-            job.k0_b = B_MN ? kb + (t + 1) * BK : min(kb + (t + 1) * BK, ke - BK);
+            job.k0_b = min(kb + (t + 1) * BK, ke - BK);
         }
     };
     if constexpr (G::Q8) {
@@ -793,6 +822,10 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     // the steady part of the loop (a constant the wait folds to one s_waitcnt)
     auto enter = [&](int kt, int stage, int pending) {
         wait_tiles<kLoadsPerTile, S>(pending);
+        // Q8: the widening's LDS writes (read by other waves past the barrier)
+        // and this wave's reads of the widened buffer the next tile rewrites
+        // must be done: a barrier does not wait for LDS operations
+        if constexpr (G::Q8) wait_lgkm0();
         block_barrier();
         // a k-major A means whole 64-k tiles (no ragged tile); Q8 B tiles are
         // zeroed when widened
@@ -1283,9 +1316,10 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
           int DUAL = 0, bool GRP = false, bool Q8 = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
-    if constexpr (!A_MN && !Q8) {
+    if constexpr (!A_MN) {
         // the loads address each operand k-tile by 32-bit per-lane byte offsets
-        const int64_t span_a = (int64_t)p.M * p.lda * 2, span_b = (int64_t)(B_MN ? p.K : p.N) * p.ldb * 2;
+        const int64_t span_a = (int64_t)p.M * p.lda * 2,
+                      span_b = (int64_t)(B_MN ? p.K : p.N) * p.ldb * (Q8 ? 1 : 2);
         if (span_a >= (int64_t(1) << 32) || span_b >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     }
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);

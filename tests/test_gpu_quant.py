@@ -194,8 +194,12 @@ def test_mem_q8_equals_mem_bitwise_on_an_exactly_stored_weight(m, n, b, T):
     assert torch.equal(mem.Wt, dev(W, "bf16"))
     q, s = _split(g.weight, m, n)
     assert np.all(np.log2(s) == np.round(np.log2(s)))   # the scales are powers of two
-    for lay in (g, mem):
-        lay.forward()
-        lay.backward()
-    for a, c in ((g.y, mem.y), (g.dx, mem.dx), (g.dG_R, mem.dG_R), (g.dG_P, mem.dG_P)):
-        assert torch.equal(a, c)
+    mem.forward()
+    mem.backward()
+    # repeated: a missing wait between the widening of the int8 tiles and
+    # their readers shows as a few differing elements in some runs only
+    for _ in range(8):
+        g.forward()
+        g.backward()
+        for a, c in ((g.y, mem.y), (g.dx, mem.dx), (g.dG_R, mem.dG_R), (g.dG_P, mem.dG_P)):
+            assert torch.equal(a, c)
