@@ -206,9 +206,22 @@ def stage_timings(spec, S, reps, gemm_only=False, only=None):
          4 * nblk * b * (b - 1) // 2 + 2 * nblk * b * b),
         ("perm_gather_x", lambda: B.poetx_permute(S["x"], a, T, n, None, S["pi_P"], False), 0, 2 * 2 * T * n),
         ("blk_fwd_P", blk(NT, a, S["G_P"], h1, n), 2 * T * n * b, 2 * (2 * T * n + n * b)),
-        ("dense_fwd", lambda: B.poetx_gemm(NT, h1, S["Wt"], h2, T, m, n, dense=True), 2 * T * m * n,
-         2 * (T * n + m * n + T * m)),
-        ("blk_fwd_R", blk(NT, h2, S["G_R"], z, m), 2 * T * m * b, 2 * (2 * T * m + m * b)),
+    ]
+    dense_fwd = ("dense_fwd", lambda: B.poetx_gemm(NT, h1, S["Wt"], h2, T, m, n, dense=True), 2 * T * m * n,
+                 2 * (T * n + m * n + T * m))
+    tiles = -(-T // 128) * (m // 256)
+    if b == 256 and (tiles % 256 == 0 or tiles >= 1024):
+        # the forward's dense product with the R-side block product folded in
+        # (poetx_linear_fwd's path for b = 256 on such grids); FAST also writes h2
+        keep = spec.variant != "mem"
+        stages.append(("dense_fwd_fold_R",
+                       lambda: B.poetx_dense_fold_r(h1, S["Wt"], S["G_R"], z, T, m, n, b, h2=h2 if keep else None),
+                       2 * T * m * n + 2 * T * m * b,
+                       2 * (T * n + m * n + T * m + m * b) + (2 * T * m if keep else 0)))
+    else:
+        stages += [dense_fwd,
+                   ("blk_fwd_R", blk(NT, h2, S["G_R"], z, m), 2 * T * m * b, 2 * (2 * T * m + m * b))]
+    stages += [
         ("perm_scatter_y", lambda: B.poetx_permute(z, S["y"], T, m, None, S["pi_R"], True), 0, 2 * 2 * T * m),
         ("perm_gather_dy", lambda: B.poetx_permute(S["dy"], z, T, m, None, S["pi_R"], False), 0, 2 * 2 * T * m),
         ("grad_R", lambda: B.poetx_block_grad(z, h2, dG, T, m, b, gws), 2 * T * m * b, 2 * 2 * T * m + 4 * m * b),
@@ -223,7 +236,7 @@ def stage_timings(spec, S, reps, gemm_only=False, only=None):
          _products(k)[1] * 2 * b ** 3 * nblk, 4 * nblk * b * b + 4 * nblk * b * (b - 1) // 2),
     ]
     if spec.variant == "mem":   # recomputed in the backward, same kernels (fast keeps a and h2)
-        stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages
+        stages += [(nm + "_recompute", fn, fl, nb) for nm, fn, fl, nb in stages + [dense_fwd]
                    if nm in ("perm_gather_x", "blk_fwd_P", "dense_fwd")]
     # the standalone skew unpack (to bf16) and pack of the same blocks; not part of the
     # step (the fused forward unpacks on chip, the backward's pack is inside cnp_bwd)
@@ -318,10 +331,11 @@ def read_traffic():
 
 
 # The dense products of the q_proj-shaped step (2048 x 4096 x 4096): 256
-# workgroups of 512 lanes of the 256 x 128 tile, Wt read k-major (forward) or
-# n-major (backward).  Dispatches of the same kernel at other shapes (the
+# workgroups of 512 lanes, the forward on the 128 x 256 tile with the R-side
+# block product folded in (Wt read k-major), the backward on the 256 x 128 tile
+# (Wt read n-major).  Dispatches of the same kernel at other shapes (the
 # comparison variants) are told apart by their grid size.
-DENSE_KERNELS = {"dense_fwd": ("pipe_gemm_kernel<256, 128, false, false, false,", 256 * 512),
+DENSE_KERNELS = {"dense_fwd_fold_R": ("pipe_gemm_kernel<128, 256, false, false, false, 3,", 256 * 512),
                  "dense_bwd": ("pipe_gemm_kernel<256, 128, false, true, false,", 256 * 512)}
 
 
@@ -513,16 +527,19 @@ def run_linear(args, spec, label):
     g_flops, g_us = gemm_aggregate(st)
     gemm_tflops = g_flops / g_us / 1e6
     traffic = read_traffic() if label == "q_proj" else None
-    shapes = {"dense_fwd": f"forward, h2 = h1 Wt^T ({spec.T} x {spec.m} x {spec.n}, Wt read k-major)",
-              "dense_bwd": f"backward, dh1 = dh2 Wt ({spec.T} x {spec.n} x {spec.m}, Wt read n-major)"}
+    shapes = {"dense_fwd": f"dense Wt GEMM, forward, h2 = h1 Wt^T ({spec.T} x {spec.m} x {spec.n}, Wt read k-major)",
+              "dense_fwd_fold_R": f"dense Wt GEMM with the R-side block product folded in, forward, "
+                                  f"z = (h1 Wt^T) blockdiag(G_R)^T ({spec.T} x {spec.m} x {spec.n}, then "
+                                  f"{spec.m // spec.b} blocks of {spec.b}; Wt read k-major)",
+              "dense_bwd": f"dense Wt GEMM, backward, dh1 = dh2 Wt ({spec.T} x {spec.n} x {spec.m}, Wt read n-major)"}
     kernels = {}
-    for nm in ("dense_fwd", "dense_bwd"):
+    for nm in ("dense_fwd_fold_R" if "dense_fwd_fold_R" in st else "dense_fwd", "dense_bwd"):
         flops = st[nm]["_flops"]
         tr = None
         rec = (traffic or {}).get(nm)
         if rec and "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
             tr = round(rec["FETCH_SIZE"]["bytes_per_dispatch"] + rec["WRITE_SIZE"]["bytes_per_dispatch"])
-        kernels[nm] = {"kernel": f"dense Wt GEMM, {shapes[nm]}, bf16, fp32 accumulate",
+        kernels[nm] = {"kernel": f"{shapes[nm]}, bf16, fp32 accumulate",
                        "achieved": round(flops / st[nm]["us"] / 1e6, 1),
                        "frac": round(flops / st[nm]["us"] / 1e6 / PEAK_BF16_TFLOPS, 4),
                        "traffic": tr, "avg_launch_us": st[nm]["us"], "algorithmic_flops_per_launch": flops}
@@ -803,7 +820,46 @@ def run_cnp_13b(args):
     out["fwd_tflops"] = round(pf * 2 * b ** 3 * nblk / us_f / 1e6, 1)
     out["bwd_tflops"] = round(pb * 2 * b ** 3 * nblk / us_b / 1e6, 1)
     out["fwd_gbs"] = round((4 * ntri + 2 * b * b) * nblk / us_f / 1e3, 1)
+    # the standalone skew unpack (q -> bf16 Q) and pack (float32 dQ -> dq) over the
+    # same blocks, in the buffers of the backward (not part of the step)
+    del G
+    Qb = torch.empty((nblk, b, b), dtype=torch.bfloat16, device="cuda")
+    us_u = _time_events(lambda: B.poetx_skew_unpack(q, Qb, nblk, b), 5, warm=1)
+    del Qb
+    us_p = _time_events(lambda: B.poetx_skew_pack(dG, dq, nblk, b), 5, warm=1)
+    out["skew_unpack_us"] = round(us_u, 1)
+    out["skew_unpack_gbs"] = round((4 * ntri + 2 * b * b) * nblk / us_u / 1e3, 1)
+    out["skew_pack_us"] = round(us_p, 1)
+    out["skew_pack_gbs"] = round((4 * b * b + 4 * ntri) * nblk / us_p / 1e3, 1)
     return out
+
+
+def profile_cnp_13b(args):
+    """The 15280-block Cayley-Neumann forward and backward and the skew passes,
+    each --stage-reps times, for counter passes (no timing of the whole step)."""
+    import torch
+    from orthogonal_equivalence_poet_amd import binding as B
+    from orthogonal_equivalence_poet_amd import inputs as I
+    b, k = 256, 3
+    nblk = I.llama13b_cnp_blocks()
+    q = torch.from_numpy(I.cnp_params(nblk, b, 1e-3, 5, 1, 0)).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dG = torch.randn((nblk, b, b), device="cuda", generator=gen)
+    G = torch.empty((nblk, b, b), dtype=torch.bfloat16, device="cuda")
+    dq = torch.empty_like(q)
+    saved = B.workspace(B.poetx_cnp_saved_bytes(nblk, b, k, B.POETX_BF16))
+    ws = B.workspace(B.poetx_cnp_bwd_workspace_bytes(nblk, b, k, B.POETX_BF16))
+    cs = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    torch.empty_like(cs).copy_(cs)
+    del cs
+    for _ in range(args.stage_reps):
+        B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
+        B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, B.POETX_BF16, saved, ws)
+    B.poetx_skew_unpack(q, G, nblk, b)
+    B.poetx_skew_pack(dG, dq, nblk, b)
+    torch.cuda.synchronize()
+    print(json.dumps({"cnp_13b_profiled": nblk, "reps": args.stage_reps}))
+    return 0
 
 
 def profile_stages(args):
@@ -863,6 +919,8 @@ def main():
     B.load()
     torch.cuda.set_device(0)
     w = args.workload
+    if args.profile_stages and w == "cnp_13b":
+        return profile_cnp_13b(args)
     if args.profile_stages:
         return profile_stages(args)
     if w == "q_proj":

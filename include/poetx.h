@@ -350,6 +350,20 @@ int poetx_gemm(int layout, int dtype, int dense, int64_t M, int64_t N, int64_t K
 int poetx_block_apply(int dtype, int transpose_G, int64_t T, int64_t d, int64_t b, const void* in, const void* G,
                       void* out, void* stream);
 
+/* The layer forward's dense product with its R-side block product folded
+ * into the same launch (review Summary: the input-centric chain as a few
+ * fused products; agidaily article, the operator fusion of the W_RP section):
+ *   h2 = h1 . Wt^T,   z[:, jb:(j+1)b] = h2[:, jb:(j+1)b] . G_R[j]^T
+ * h1: bf16 [T, n]; Wt: bf16 [m, n]; G_R: bf16 [m/b, b, b]; z: bf16 [T, m];
+ * h2: bf16 [T, m], written when not NULL.  b must be 256 and n a multiple of
+ * 64 (else POETX_ERR_UNSUPPORTED); dtype must be POETX_BF16.  h2 is rounded to
+ * bf16 before the block product, so z equals poetx_gemm (dense NT) followed by
+ * poetx_block_apply bit for bit.  z and h2 must not overlap h1 or Wt.
+ * poetx_linear_fwd takes this path for bf16 chains with b = 256 whose grid of
+ * ceil(T / 128) * m / 256 tiles is a multiple of 256 or at least 1024. */
+int poetx_dense_fold_r(int dtype, int64_t T, int64_t m, int64_t n, int64_t b, const void* h1, const void* Wt,
+                       const void* G_R, void* h2, void* z, void* stream);
+
 /* Block gradients of the batch-wise block products (the backward of the
  * review's "batch-wise block-diagonal matmul"): for j < d/b
  *   dG[j] = A[:, jb:(j+1)b]^T B[:, jb:(j+1)b]      (sum over the T rows)

@@ -34,7 +34,7 @@ EXPORTS = [
     "poetx_group_bwd_workspace_bytes", "poetx_group_bwd",
     "poetx_merge_workspace_bytes", "poetx_merge",
     "poetx_qweight_bytes", "poetx_quantize_weight", "poetx_dequantize_weight",
-    "poetx_gemm", "poetx_block_apply", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
+    "poetx_gemm", "poetx_block_apply", "poetx_dense_fold_r", "poetx_block_grad_workspace_bytes", "poetx_block_grad",
     "poetx_adamw_step", "poetx_adamw_reset",
 ]
 
@@ -105,6 +105,7 @@ _SIGS = {
     "poetx_gemm": ([_I32, _I32, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _I64,
                     _VP], _I32),
     "poetx_block_apply": ([_I32, _I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP], _I32),
+    "poetx_dense_fold_r": ([_I32, _I64, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "poetx_block_grad_workspace_bytes": ([_I64, _I64, _I64, _I32], _SZ),
     "poetx_block_grad": ([_I32, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP], _I32),
     "poetx_adamw_step": ([_VP, _VP, _VP, _VP, _I64, _I64, C.POINTER(AdamwParams), _VP], _I32),
@@ -349,6 +350,11 @@ def poetx_gemm(layout, A, B, C, M, N, K, batch=1, lda=None, ldb=None, ldc=None, 
 def poetx_block_apply(inp, G, out, T, d, b, transpose_G=True, stream=None):
     _check("poetx_block_apply", load().poetx_block_apply(_dtype_code(out), int(bool(transpose_G)), T, d, b, _ptr(inp),
                                                          _ptr(G), _ptr(out), _stream(stream)))
+
+
+def poetx_dense_fold_r(h1, Wt, G_R, z, T, m, n, b, h2=None, stream=None):
+    _check("poetx_dense_fold_r", load().poetx_dense_fold_r(_dtype_code(z), T, m, n, b, _ptr(h1), _ptr(Wt), _ptr(G_R),
+                                                           _ptr(h2), _ptr(z), _stream(stream)))
 
 
 def poetx_block_grad_workspace_bytes(T, d, b, dtype) -> int:

@@ -760,14 +760,41 @@ hipError_t dense_bwd(const poetx_linear_desc* d, const void* dh2, const void* Wt
     return dense_gemm(GemmLayout::NN, d->dtype == POETX_BF16, T, n, m, dh2, m, Wt, n, dh1, n, s);
 }
 
+// The dense product and the R-side block product of the forward as one launch
+// (dense_fold_r): bf16 chains with b = 256, whose 128 x 256 dense tiles are
+// whole R blocks, when that tile grid runs in whole waves over the 256 CUs or in
+// at least four (same-process timings of fold against dense + block product:
+// 2048 x 4096 x 4096 69.0 / 67.6 against 69.3 us with / without h2 kept,
+// 8192 x 5120 x 5120 405.7 / 392.2 against 442.1 us; a grid of 3.5 waves,
+// 2048 x 14336 x 4096, lost 1-5%, and 64 tiles, 2048 x 1024 x 4096, 48.5
+// against 28.1 us).
+bool fold_r(const poetx_linear_desc* d) {
+    const int64_t T = d->T, m = d->m, n = d->n;
+    const int64_t tiles = ((T + 127) / 128) * (m / 256);
+    return d->dtype == POETX_BF16 && d->b == 256 &&
+           (d->variant == POETX_FAST || d->variant == POETX_MEM || d->variant == POETX_MEM_Q8) &&
+           (tiles % 256 == 0 || tiles >= 1024) && dense_fold_r_supported(T, m, n, n, n, m, m, 256);
+}
+
+// h2_out receives h2 when the chain keeps it (FAST); z_buf ([T, m], not aliasing
+// h1 or a) receives z on the folded path.
 int linear_forward(const poetx_linear_desc* d, const void* x, const void* Wt, const void* G_R, const void* G_P,
                    const int32_t* pi_R, const int32_t* pi_P, void* y, void* h2_out, void* buf_a, void* buf_b,
-                   hipStream_t s) {
+                   void* z_buf, hipStream_t s) {
     const bool bf = d->dtype == POETX_BF16;
     const int64_t T = d->T, m = d->m, n = d->n, b = d->b;
     // a = x gathered by pi_P;  h1 = a . blockdiag(G_P)^T
     HIP_TRY(permute_2d(x, buf_a, bf, T, n, nullptr, pi_P, false, s));
     HIP_TRY(block_apply(GemmLayout::NT, bf, T, n, b, buf_a, G_P, buf_b, s));
+    if (fold_r(d)) {
+        // z = (h1 . Wt^T) . blockdiag(G_R)^T in one launch; h2 leaves the chip for FAST only
+        const bool q8 = d->variant == POETX_MEM_Q8;
+        HIP_TRY(dense_fold_r(q8, buf_b, n, q8 ? static_cast<const void*>(qcodes(Wt)) : Wt, n,
+                             q8 ? qscales(Wt, m, n) : nullptr, G_R, mem_chain(d) ? nullptr : h2_out, m, z_buf, m,
+                             (int)T, (int)m, (int)n, (int)b, s));
+        HIP_TRY(permute_2d(z_buf, y, bf, T, m, nullptr, pi_R, true, s));
+        return POETX_OK;
+    }
     // h2 = h1 . Wt^T (the int8 weight: h1 . codes^T, output column i scaled by scale_i)
     HIP_TRY(dense_fwd(d, buf_b, Wt, h2_out, s));
     // z = h2 . blockdiag(G_R)^T ; y = z scattered by pi_R
@@ -1183,9 +1210,14 @@ int linear_fwd_run(const poetx_linear_desc* d, const void* x, const void* Wt, co
                                  as_stream(stream));
     void* h2 = saved;
     void* a = L.buf[0];
-    if (mem_chain(d)) h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
-    else a = static_cast<char*>(saved) + fast_saved_a_offset(d);
-    return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, a, L.buf[1], as_stream(stream));
+    void* z = L.buf[0];   // FAST: free (a is kept in saved); MEM: h2's buffer, which the folded path skips
+    if (mem_chain(d)) {
+        h2 = cv.take(esize(d->dtype) * (size_t)(d->T * d->m));
+        z = h2;
+    } else {
+        a = static_cast<char*>(saved) + fast_saved_a_offset(d);
+    }
+    return linear_forward(d, x, Wt, G_R, G_P, pi_R, pi_P, y, h2, a, L.buf[1], z, as_stream(stream));
 }
 
 }  // namespace
@@ -1537,6 +1569,22 @@ int poetx_block_apply(int dtype, int transpose_G, int64_t T, int64_t d, int64_t 
     if (!in || !G || !out) return POETX_ERR_INVALID_ARG;
     HIP_TRY(block_apply(transpose_G ? GemmLayout::NT : GemmLayout::NN, dtype == POETX_BF16, T, d, b, in, G, out,
                         as_stream(stream)));
+    return POETX_OK;
+}
+
+int poetx_dense_fold_r(int dtype, int64_t T, int64_t m, int64_t n, int64_t b, const void* h1, const void* Wt,
+                       const void* G_R, void* h2, void* z, void* stream) {
+    if (!dtype_ok(dtype)) return POETX_ERR_INVALID_ARG;
+    POETX_TRY(check_block(b));
+    if (T < 0 || m <= 0 || n <= 0 || m % b || n % b || T > kMaxExtent || m > kMaxExtent || n > kMaxExtent)
+        return POETX_ERR_SHAPE;
+    if (dtype != POETX_BF16 || b != 256 || !dense_fold_r_supported(std::max<int64_t>(T, 1), m, n, n, n, m, m, 256))
+        return POETX_ERR_UNSUPPORTED;
+    if (T == 0) return POETX_OK;
+    if (!h1 || !Wt || !G_R || !z) return POETX_ERR_INVALID_ARG;
+    if (!all_al16(h1, Wt, G_R, z, h2)) return POETX_ERR_INVALID_ARG;
+    HIP_TRY(dense_fold_r(false, h1, n, Wt, n, nullptr, G_R, h2, m, z, m, (int)T, (int)m, (int)n, (int)b,
+                         as_stream(stream)));
     return POETX_OK;
 }
 

@@ -60,6 +60,9 @@ struct PipeArgs {
     // product): C[r][c] = acc * colscale[c] (batch entry z: colscale + z strideScale).
     const float* colscale = nullptr;
     int64_t strideScale = 0;
+    // The R blocks of the folded forward (dense_fold_r): b x b bf16 blocks, block
+    // j for output columns [256 j, 256 j + 256).
+    const void* Gfold = nullptr;
 };
 
 // a_mn: A is [K][M] (m contiguous) instead of [M][K]; b_mn: B is [K][N] instead
@@ -131,6 +134,18 @@ hipError_t dense_gemm_q8(bool b_nn, const void* A, int64_t lda, const int8_t* B,
 // with its output columns scaled: out[:, c] *= colscale[c] over the whole
 // [T, d] activation (tiles as block_apply picks them).
 hipError_t pipe_gemm_colscale(const PipeArgs& p, hipStream_t stream, PipeTile tile);
+
+// The layer forward's dense product with its R-side block product folded in
+// (b = 256): z = (A B^T) blockdiag(G)^T for A = h1 [M][K], B = Wt [N][K] (bf16,
+// or int8 codes with q8 and output column c of A B^T scaled by colscale[c]
+// first), G [N / 256][256][256] bf16; h2 = A B^T (bf16) is also written when h2
+// is given.  z equals the dense product, bf16 rounding of h2 and block product
+// run one after another, bit for bit.  N % 256 == 0, K % 64 == 0.
+bool dense_fold_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldc2,
+                            int b);
+hipError_t dense_fold_r(bool q8, const void* A, int64_t lda, const void* B, int64_t ldb, const float* colscale,
+                        const void* G, void* h2, int64_t ldh2, void* z, int64_t ldz, int M, int N, int K, int b,
+                        hipStream_t stream);
 
 // Dense convenience wrappers (batch 1, no split).
 bool dense_gemm_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);

@@ -717,7 +717,9 @@ __device__ __forceinline__ void wait_jobs(int jobs) {
 // so a product with K <= 64 (S - 1) waits for memory once.
 // Epilogue kinds: plain store, general (see PipeArgs), plain store with the
 // output columns scaled by PipeArgs::colscale.
-constexpr int kEpiPlain = 0, kEpiGeneral = 1, kEpiColScale = 2;
+// kEpiFoldR: the R-side block product of the layer forward applied to the tile
+// (fold_r_epilogue).
+constexpr int kEpiPlain = 0, kEpiGeneral = 1, kEpiColScale = 2, kEpiFoldR = 3;
 
 // The k loop of one output tile at (m0, n0) into acc (zeroed here).
 // Q8 (G::Q8): B is int8.  Job t loads A(t) into stage t % S and the int8 B of
@@ -951,6 +953,100 @@ __device__ __forceinline__ void main_loop(unsigned char* lds, const uint16_t* __
     for (; kt < nk; ++kt) tile(kt, std::false_type{});
 }
 
+// The R-side block product of the layer forward, folded into the dense
+// product's epilogue: a 128 x 256 tile of h2 = h1 Wt^T is one token tile of one
+// R block (b = 256), so z = h2 G_j^T for that tile needs only G_j (b x b,
+// k-major rows).  h2 is rounded to bf16 as the unfused chain stores it (for an
+// int8 weight after its column scale), stored when the caller keeps it (C2),
+// and kept in LDS as four k-major 128 x 64 A tiles; G_j streams through a
+// three-stage ring of 256 x 64 tiles behind it.  The second product runs the
+// tiles, k-steps and MFMAs of the 128 x 256 block product in the same order,
+// so z equals the unfused chain's bit for bit.
+template <class G>
+__device__ __forceinline__ void fold_r_epilogue(const PipeArgs& p, f32x16_t (&acc)[G::MI][G::NJ],
+                                                unsigned char* lds, int m0, int n0, int tid, const float (&csc)[G::NJ]) {
+    static_assert(G::BM == 128 && G::BN == 256 && G::NWM == 2 && G::NWN == 4, "fold tile");
+    constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
+    constexpr int kATile = 128 * BK * 2;        // 16 KB: h2 columns [64 kt, 64 kt + 64)
+    constexpr int kPanel = 4 * kATile;          // the tile's h2, 64 KB
+    constexpr int kBTile = 256 * BK * 2;        // 32 KB: one k-tile of G_j
+    constexpr int kRing = 3;
+    static_assert(kPanel + kRing * kBTile <= 160 * 1024, "fold LDS");
+    constexpr int NB = OperandLoads<256, false, G::NW>::n;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / G::NWN, wn = wave % G::NWN;
+    const uint32_t base = lds_offset(lds);
+    const uint16_t* Gj = reinterpret_cast<const uint16_t*>(p.Gfold) + (int64_t)(n0 / 256) * (256 * 256);
+    auto load_g = [&](int kt, int stage) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            dma_one<256, false, G::NW>(j, base + kPanel + stage * kBTile, Gj, 256, 0, 256, kt * BK, 256, wave, lane);
+    };
+    block_barrier();   // every wave is done reading the operand stages
+#pragma unroll
+    for (int kt = 0; kt < kRing; ++kt) load_g(kt, kt);
+    // h2 in bf16: stored (C2) and staged; element (row, col) of the tile goes to
+    // A tile col / 64, row `row`, k = col % 64 (the k-major swizzle of the ring)
+    bf16_t* C2 = reinterpret_cast<bf16_t*>(p.C2);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int col = wn * WTN + j * 32 + (lane & 31);
+                const bf16_t h = ElemTraits<bf16_t>::from_f32(G::Q8 ? acc[i][j][r] * csc[j] : acc[i][j][r]);
+                if (C2 && m0 + row < p.M) C2[(int64_t)(m0 + row) * p.ldc2 + n0 + col] = h;
+                const int kk = col & 63;
+                *reinterpret_cast<bf16_t*>(lds + (col >> 6) * kATile + row * 128 +
+                                           (((kk >> 3) ^ swz_k(row)) << 4) + (kk & 7) * 2) = h;
+            }
+    f32x16_t z[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[i][j][r] = 0.f;
+    wait_vmcnt<0>();
+    __syncthreads();   // the h2 panel and G's first three k-tiles are in LDS
+    auto compute = [&](int kt, int stage) {
+        const unsigned char* at = lds + kt * kATile;
+        const unsigned char* bt = lds + kPanel + stage * kBTile;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            uint4 af[MI], bfr[NJ];
+            load_frags<G, false, false>(at, bt, wm, wn, ks, lane, af, bfr);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[i], bfr[j], z[i][j]);
+        }
+    };
+    compute(0, 0);
+    __syncthreads();   // stage 0 is free
+    load_g(3, 0);
+    compute(1, 1);
+    compute(2, 2);
+    wait_vmcnt<0>();
+    __syncthreads();
+    compute(3, 0);
+    bf16_t* C = reinterpret_cast<bf16_t*>(p.C);
+    const int col0 = n0 + wn * WTN + (lane & 31);
+    const int row0 = m0 + wm * WTM + (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                if (row < p.M) store_f32(C + (int64_t)row * p.ldc + col0 + j * 32, z[i][j][r]);
+            }
+}
+
 // DUAL = 1: acc = op(A) op(B) + A2^T B2 (second product with m/n-major A2, B2);
 // DUAL = 2: the second product goes to its own accumulator (general epilogue mode 2).
 // GRP: a grouped product (PipeArgs::grp), a separate instantiation so that the
@@ -966,7 +1062,9 @@ pipe_gemm_kernel(const PipeArgs p) {
     constexpr int MI = G::MI, NJ = G::NJ, WTM = G::WTM, WTN = G::WTN;
     static_assert(S * kStageBytes + G::kExtraBytes <= 160 * 1024, "LDS ring exceeds 160 KB");
     static_assert(!Q8 || (!A_MN && DUAL == 0 && EPI != kEpiGeneral), "int8 B: k-major A, single product");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * kStageBytes + G::kExtraBytes];
+    static_assert(EPI != kEpiFoldR || (!A_MN && !B_MN && !OUT_F32 && DUAL == 0 && !GRP), "fold: the NT forward");
+    constexpr int kLds = EPI == kEpiFoldR ? 160 * 1024 : S * kStageBytes + G::kExtraBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1024,16 +1122,21 @@ pipe_gemm_kernel(const PipeArgs p) {
         return;
     }
     OutT* C = reinterpret_cast<OutT*>(p.C) + (int64_t)z * p.strideC + (int64_t)blockIdx.z * p.strideSplit;
-    // column scales of this lane's NJ columns (kEpiColScale), 1 otherwise
+    // column scales of this lane's NJ columns (kEpiColScale, or the fold on an
+    // int8 weight), 1 otherwise
     float csc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        if constexpr (EPI == kEpiColScale) {
+        if constexpr (EPI == kEpiColScale || (EPI == kEpiFoldR && Q8)) {
             const float* sc = p.colscale + (int64_t)z * p.strideScale;
             csc[j] = col0 + j * 32 < N ? sc[col0 + j * 32] : 0.f;
         } else {
             csc[j] = 1.f;
         }
+    }
+    if constexpr (EPI == kEpiFoldR) {
+        fold_r_epilogue<G>(p, acc, lds, m0, n0, tid, csc);
+        return;
     }
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
@@ -1974,6 +2077,33 @@ hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nbl
         else
             hipLaunchKernelGGL(cnp_bwd_sigq_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
     });
+}
+
+bool dense_fold_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldc2,
+                            int b) {
+    return b == 256 && M > 0 && N > 0 && N % 256 == 0 && K >= BK && K % BK == 0 && lda % 8 == 0 && ldb % 8 == 0 &&
+           ldc % 8 == 0 && ldc2 % 8 == 0 && ldc >= N && ldc2 >= N && M <= 0x7fffffff && N <= 0x7fffffff &&
+           K <= 0x7fffffff;
+}
+
+hipError_t dense_fold_r(bool q8, const void* A, int64_t lda, const void* B, int64_t ldb, const float* colscale,
+                        const void* G, void* h2, int64_t ldh2, void* z, int64_t ldz, int M, int N, int K, int b,
+                        hipStream_t stream) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (!dense_fold_r_supported(M, N, K, lda, ldb, ldz, h2 ? ldh2 : ldz, b) || !G || !z || (q8 && !colscale))
+        return hipErrorInvalidValue;
+    if (q8 && ldb % 16 != 0) return hipErrorInvalidValue;
+    PipeArgs p;
+    p.A = A; p.lda = lda;
+    p.B = B; p.ldb = ldb;
+    p.C = z; p.ldc = ldz;
+    p.C2 = h2; p.ldc2 = ldh2;
+    p.Gfold = G;
+    p.colscale = colscale;
+    p.M = M; p.N = N; p.K = K;
+    p.k_per_split = K;
+    if (q8) return launch<128, 256, false, false, false, kEpiFoldR, 3, 2, 4, 0, false, true>(p, stream);
+    return launch<128, 256, false, false, false, kEpiFoldR, 3, 2, 4>(p, stream);
 }
 
 int pipe_tile_rows(PipeTile t) {

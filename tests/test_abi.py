@@ -117,6 +117,30 @@ def test_misaligned_pointers_are_rejected(B):
         assert lib.poetx_group_bwd(C.byref(g), *args, gb, None) == B.POETX_ERR_INVALID_ARG, i
 
 
+def test_dense_fold_r_validation(B):
+    """The folded dense + R-side product takes bf16 chains with b = 256 only and
+    checks shapes and pointers before any HIP call."""
+    lib = B.load()
+    bf, f32 = B.POETX_BF16, B.POETX_F32
+    ok = (2048, 4096, 4096, 256)
+    args = [FAKE] * 5 + [None]
+    assert lib.poetx_dense_fold_r(f32, *ok, *args) == B.POETX_ERR_UNSUPPORTED
+    assert lib.poetx_dense_fold_r(bf, 2048, 4096, 4096, 128, *args) == B.POETX_ERR_UNSUPPORTED
+    assert lib.poetx_dense_fold_r(bf, 2048, 4096, 4096, 512, *args) == B.POETX_ERR_UNSUPPORTED
+    assert lib.poetx_dense_fold_r(bf, 2048, 4096 + 256, 4096 + 8, 256, *args) == B.POETX_ERR_SHAPE
+    assert lib.poetx_dense_fold_r(bf, -1, 4096, 4096, 256, *args) == B.POETX_ERR_SHAPE
+    assert lib.poetx_dense_fold_r(bf, 0, 4096, 4096, 256, *args) == B.POETX_OK
+    assert lib.poetx_dense_fold_r(7, *ok, *args) == B.POETX_ERR_INVALID_ARG
+    for i in range(5):
+        a = [FAKE] * 5 + [None]
+        a[i] = FAKE + 2
+        assert lib.poetx_dense_fold_r(bf, *ok, *a) == B.POETX_ERR_INVALID_ARG, i
+    for i in (0, 1, 2, 4):
+        a = [FAKE] * 5 + [None]
+        a[i] = None
+        assert lib.poetx_dense_fold_r(bf, *ok, *a) == B.POETX_ERR_INVALID_ARG, i
+
+
 def test_noalloc_forward_validation(B):
     """The forward without a workspace refuses a descriptor whose workspace
     exceeds its scratch array, and bad arguments, before any HIP call."""
