@@ -864,10 +864,10 @@ hipError_t group_dense(const GroupPlan& P, bool nn, const void* A, const void* W
     if (grouped) {
         auto m_of = [&](int g) { return P.seg.off[g + 1] - P.seg.off[g]; };
         for (int g0 = 0; g0 < G;) {
-            int g1 = g0 + 1;
-            if (!nn) g1 = (int)G;
-            else
-                while (g1 < G && m_of(g1) == m_of(g0)) ++g1;
+            // one launch for the whole group; in the backward the linears may
+            // differ in k (q/k/v: m_g = 4096, 1024, 1024), whose tiles the
+            // launch deals longest k first and evenly over the XCDs
+            const int g1 = (int)G;
             // linears [g0, g1): output columns from c0, relative group table
             const int64_t c0 = nn ? g0 * n : P.seg.off[g0];
             PipeArgs p;

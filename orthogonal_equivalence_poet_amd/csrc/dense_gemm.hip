@@ -508,6 +508,61 @@ __device__ __forceinline__ void batch_tile_coords(int tiles_m, int tiles_n, int&
     tn = t / tiles_m;
 }
 
+// Grouped launches (PipeArgs::grp) whose groups differ in k: the groups' tiles
+// are taken longest k first (ties in table order) and dealt to the XCDs the way
+// the hardware deals launch slots, round-robin, so every XCD gets an equal share
+// of every group and starts its long tiles first; within an XCD a group's share
+// is one contiguous run in the four-M-panel-deep order of single products, so
+// the panels it reads stay in that XCD's L2.  With one k for every group the
+// whole grid takes the order of a single product (tile_coords).
+__device__ __forceinline__ void grp_tile_coords(const PipeArgs& p, int bn, int tiles_m, int tiles_n, int& tm,
+                                                int& tn) {
+    constexpr int NG = kMaxPipeGroups;
+    const int ng = p.ngroups;
+    int k[NG], c0[NG], cols[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        k[i] = i < ng ? p.grp[i].k : -1;
+        c0[i] = p.grp[i].n_begin / bn;
+        int c1 = tiles_n;
+        if (i + 1 < NG && i + 1 < ng) c1 = p.grp[i + 1].n_begin / bn;
+        cols[i] = i < ng ? c1 - c0[i] : 0;
+    }
+    bool mixed = false;
+#pragma unroll
+    for (int i = 1; i < NG; ++i) mixed = mixed || (i < ng && k[i] != k[0]);
+    if (!mixed) {
+        tile_coords((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+        return;
+    }
+    const int x = (int)blockIdx.x & 7;   // the XCD this slot is dealt to
+    const int u = (int)blockIdx.x;       // position in the longest-k-first deal
+    tm = tiles_m;                         // past every group: no tile
+    tn = tiles_n;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int cnt = tiles_m * cols[i];
+        int off = 0;   // tiles of the groups dealt before group i
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+            if (j != i && (k[j] > k[i] || (k[j] == k[i] && j < i))) off += tiles_m * cols[j];
+        if (i < ng && u >= off && u < off + cnt) {
+            // group i's tiles go to the XCDs in rotated order starting at XCD off % 8
+            const int rho = (x - off % 8 + 8) & 7;
+            const int u0 = off + rho;                     // first tile of group i dealt to XCD x
+            const int start = rho * (cnt >> 3) + min(rho, cnt & 7);
+            const int id = start + (u - u0) / 8;          // contiguous per XCD
+            constexpr int D = 4;                          // M panels deep
+            const int grp = id / (D * cols[i]);
+            const int first = grp * D;
+            const int gm = min(D, tiles_m - first);
+            const int r = id - grp * D * cols[i];
+            tm = first + r % gm;
+            tn = c0[i] + r / gm;
+        }
+    }
+}
+
 // Register budget: the 256 x 128 and 128 x 256 tiles hold 128 accumulators per
 // lane and their LDS ring allows one workgroup per CU, so they take the whole
 // register file; smaller tiles leave room for several workgroups per CU.
@@ -1074,7 +1129,13 @@ pipe_gemm_kernel(const PipeArgs p) {
     int ke = min(p.K, kb + p.k_per_split);
     int tm, tn;
     int z;
-    batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
+    if constexpr (GRP) {
+        z = 0;
+        grp_tile_coords(p, BN, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+        if (tm * BM >= M || tn * BN >= N) return;
+    } else {
+        batch_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, z, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (int64_t)z * p.strideA;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (int64_t)z * p.strideB;
