@@ -373,13 +373,13 @@ def parse_pmc(pmc_dir):
             copies.setdefault((cn, grid), []).append(v)
     rec = {"gemm_source_sha256_16": gemm_source_hash(), "copy_bytes": COPY_BYTES}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        # the runtime may split the 256 MiB reference copy into several
-        # dispatches: sum those of the largest copy grid (the run's other
-        # copies are small)
-        grids = [g for (c, g) in copies if c == cn]
-        if not grids:
+        # the 256 MiB reference copy: the largest copy dispatch of the run (plus
+        # any of at least a tenth of it, should the runtime split the copy);
+        # the run's other copies are small, some with the same grid size
+        c_all = [v for (c, g), vs in copies.items() if c == cn for v in vs]
+        if not c_all:
             continue
-        c = copies[(cn, max(grids))]
+        c = [v for v in c_all if v >= 0.1 * max(c_all)]
         c_kib = sum(c)
         scale = COPY_BYTES / (c_kib * 1024.0)
         for nm in DENSE_KERNELS:
