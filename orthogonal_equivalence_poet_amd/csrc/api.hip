@@ -331,12 +331,25 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
     return POETX_OK;
 }
 
+// Batches from which the k = 3, b = 256 backward takes one block per workgroup
+// instead of the two passes over tile pairs.  A lone workgroup takes about
+// 54 us on its block, the pair passes spread a few blocks over the whole chip
+// (32 blocks: 28 us); from a few hundred blocks on, the per-block kernel moves
+// fewer bytes and is ahead (256: 84 against 116 us; 15280: 4.8 against 7.7 ms).
+constexpr int64_t kBlockBwdMinBlocks = 256;
+
 // Adjoint schedules (reverse of the forward ones), ending with the skew pack.
 int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k, bool cbf16, float* dq,
                  CnpBufs& B, bool saved, hipStream_t s) {
     if (!saved) POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
     const int ib = (int)b;
     const int64_t bb = b * b;
+    if (cbf16 && k == 3 && b == 256 && nblk >= kBlockBwdMinBlocks) {
+        // one block per workgroup: every intermediate on chip, dG read as float32
+        // and kept as bf16 in the scratch of its compute copy
+        HIP_TRY(cnp_bwd_block(dG, B.Sc, B.Tc, B.Qc, B.dGc, dq, nblk, ib, s));
+        return POETX_OK;
+    }
     const void* dGc = dG;
     if (cbf16) {
         HIP_TRY(combine(nblk, ib, dG, 1.f, nullptr, 0, nullptr, 0, 0, nullptr, B.dGc, true, s));

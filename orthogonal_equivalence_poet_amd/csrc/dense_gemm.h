@@ -111,6 +111,12 @@ hipError_t cnp_pack_pair(const PipeArgs& p, float* dq, int b, hipStream_t stream
 hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const void* T, void* sigma, float* dq,
                        int64_t nblk, int b, hipStream_t stream);
 hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nblk, int b, hipStream_t stream);
+// The same k = 3 backward with one b = 256 block per workgroup (every
+// intermediate on chip, no Sigma or partial dq in memory): dq [nblk, b(b-1)/2]
+// from dG float32 and the bf16 S, T, Q of each block.  dGh [nblk, b, b] bf16 is
+// scratch (the kernel writes dG / 2 there once and reads it back).
+hipError_t cnp_bwd_block(const float* dG, const void* S, const void* T, const void* Q, void* dGh, float* dq,
+                         int64_t nblk, int b, hipStream_t stream);
 
 // Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
 // kernel): packed float32 parameters q [nblk, b(b-1)/2] -> G bf16 [nblk, b, b];

@@ -1477,6 +1477,353 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
     }
 }
 
+// The k = 3 backward of one b = 256 block per workgroup (large batches): the
+// same algebra as the two pair passes, with every intermediate kept on chip.
+// With X1 = dG S, X2 = T^T dG, dS = 2 dG + X1 + X2, Sigma = dS + dS^T, P = Sigma Q
+// and dA = dG + X1, the packed dq is E - E^T on the upper triangle for
+// E = 2 dA - P = 2 dG + 2 X1 - P.  Eight waves, wave (wm, wn) owning rows
+// [64 wm, 64 wm + 64) and columns [128 wn, 128 wn + 128) of the block, share one
+// set of accumulators (two waves per SIMD leave 256 registers a lane, room for
+// one 64 x 128 float32 set and the operands).  The float32 leading terms enter
+// as the accumulators' starting value, loaded straight from dG, and the
+// products carry halved operands, so that no phase adds dG element by element
+// (halving is exact in bf16 and float32):
+//   A. acc = dG + (dG / 2) S + T^T (dG / 2) = dS / 2, doubled: dS;
+//   B. dS to LDS in bf16, each lane adds the transposed entries of its own:
+//      Sigma (the transposed half rounded to bf16 twice, there and in Sigma);
+//      Sigma / 2, symmetric, goes back as the m-major A image of phase C;
+//   C. acc = dG + (Sigma / 2) Q^T = dG - P / 2, Q's rows by DMA;
+//   D. acc / 2 + (dG / 2) S = E / 4 for E = 2 dG + 2 X1 - P, times 4: E;
+//   E. dq[idx(r, c)] = E[r][c] - E[c][r] (r < c), the transposed entries through
+//      LDS in float32, one column half of the block at a time.
+// dG enters the products rounded to bf16 (as the pair passes' bf16 copy) and
+// the leading 2 dG terms in float32.  The products run two-stage rings (the next
+// tile's loads in flight over the current tile's MFMAs).  dG is read as float32
+// twice (the starting values of A and C) and once more for A's first product,
+// whose 64-column panels pass through registers: converted to bf16 (dG / 2)
+// there, they also go to a row-major scratch copy, from which the later
+// products take dG's rows (A's n-major B) and columns (D's k-major A) by DMA,
+// as they take S, T and Q.
+constexpr int kBlkB = 256;
+
+// LDS images read transposed: dS (bf16, 256 x 256) holds entry (r, c) at
+// element r * 256 + (c ^ 4 (r & 31)), a column half of E (float32, 256 x 128)
+// holds (r, cc) at element r * 128 + (cc ^ 4 (r & 15)).  The XOR moves whole
+// groups of four columns, so four consecutive columns of a row stay one aligned
+// 8- or 16-byte access, and 32 lanes reading one column of 32 consecutive rows
+// meet every bank.
+
+__global__ void __launch_bounds__(512, 1)
+cnp_bwd_block_kernel(const float* __restrict__ dG, const uint16_t* __restrict__ Sg, const uint16_t* __restrict__ Tg,
+                     const uint16_t* __restrict__ Qg, uint16_t* __restrict__ dGh, float* __restrict__ dq) {
+    using G = Geo<256, 256, 4, 2>;
+    constexpr int MI = G::MI, NJ = G::NJ;        // 2 x 4 tiles of 32 x 32 per wave
+    constexpr int kStage = 64 * 1024;            // A (32 KB) + B (32 KB)
+    constexpr int kQBuf = 128 * 1024;            // phase C's B tile
+    constexpr int NB = OperandLoads<256, false, G::NW>::n;   // DMA loads of a 256 x 64 tile per thread
+    static_assert(NB == OperandLoads<256, true, G::NW>::n && NB == 4, "tile loads");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[160 * 1024];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / G::NWN, wn = wave % G::NWN;
+    const int64_t z = blockIdx.x;
+    const float* __restrict__ g = dG + z * (kBlkB * kBlkB);
+    const uint16_t* __restrict__ S = Sg + z * (kBlkB * kBlkB);
+    const uint16_t* __restrict__ T = Tg + z * (kBlkB * kBlkB);
+    const uint16_t* __restrict__ Q = Qg + z * (kBlkB * kBlkB);
+    uint16_t* __restrict__ H = dGh + z * (kBlkB * kBlkB);   // dG / 2 in bf16, row-major
+    const uint32_t base = lds_offset(lds);
+
+    f32x16_t acc[MI][NJ];
+    // f(tile, first row, first column) for each 32 x 32 accumulator tile; the
+    // bounds are uniform over the wave.  A lane holds rows r0 + 8 q + u (q, u < 4,
+    // r0 = first row + 4 L) of column first column + l31 of its tile, the element
+    // in accumulator 4 q + u.
+    const int L = lane >> 5, l31 = lane & 31;
+    auto for_tiles = [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) f(acc[i][j], wm * 64 + 32 * i, wn * 128 + 32 * j);
+    };
+    // acc = dG, loaded straight into the accumulators (no arithmetic on the
+    // loaded values, so the loads stay in flight until the first MFMA needs them)
+    // The wave's 64 x 128 region from a uniform base and 32-bit per-lane byte
+    // offsets; the lane index passes through an ordered no-op first, so that no
+    // part of the offsets is kept (or spilled) from one call to the next.
+    auto init_dg = [&]() __attribute__((always_inline)) {
+        const char* gw = reinterpret_cast<const char*>(g + wm * 64 * kBlkB + wn * 128);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const uint32_t o = 4 * ((ln >> 5) * 4 * kBlkB + (ln & 31));
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const uint32_t c = 4 * ((i * 32 + (rr >> 2) * 8 + (rr & 3)) * kBlkB + j * 32);
+                    acc[i][j][rr] = *reinterpret_cast<const float*>(gw + (o + c));
+                }
+    };
+    auto scale_acc = [&](float f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) acc[i][j][rr] *= f;
+    };
+
+    float4 st[8];   // this thread's 32 floats of the next dG panel
+    // dG[:, 64 kt + 32 h .. + 32) of row r = tid / 2, h = tid % 2, times `scale` (k-major A)
+    auto load_cols = [&](int kt) __attribute__((always_inline)) {
+        const float4* src = reinterpret_cast<const float4*>(g + (tid >> 1) * kBlkB + kt * 64 + (tid & 1) * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] = src[i];
+    };
+    // the panel as bf16 (dG / 2) into the A stage and into its row-major copy H
+    auto put_cols = [&](int stage, int kt) __attribute__((always_inline)) {
+        const int r = tid >> 1, h = tid & 1;
+        unsigned char* dst = lds + stage * kStage + r * 128;
+        uint4* hrow = reinterpret_cast<uint4*>(H + r * kBlkB + kt * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * h + i;
+            const float4 u = st[2 * i], v = st[2 * i + 1];
+            const uint4 w = make_uint4(pack_bf16x2(0.5f * u.x, 0.5f * u.y), pack_bf16x2(0.5f * u.z, 0.5f * u.w),
+                                       pack_bf16x2(0.5f * v.x, 0.5f * v.y), pack_bf16x2(0.5f * v.z, 0.5f * v.w));
+            *reinterpret_cast<uint4*>(dst + ((c ^ swz_k(r)) << 4)) = w;
+            hrow[c] = w;
+        }
+    };
+    // S rows (k-major B), T rows (m-major A), H rows (n-major B) and columns
+    // (k-major A), Q rows (k-major B of phase C)
+    auto dma_rows = [&](auto mn_c, const uint16_t* src, int kt, uint32_t dst) __attribute__((always_inline)) {
+        constexpr bool MN = decltype(mn_c)::value;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) dma_one<256, MN, G::NW>(j, dst, src, kBlkB, 0, kBlkB, kt * 64, kBlkB, wave, lane);
+    };
+    // One k-tile: the fragments of step ks + 1 are read before the MFMAs of step
+    // ks (two sets live), and the fence keeps later reads from moving up.
+    auto compute = [&](auto amn_c, auto bmn_c, const unsigned char* at, const unsigned char* bt)
+                       __attribute__((always_inline)) {
+        constexpr bool AMN = decltype(amn_c)::value, BMN = decltype(bmn_c)::value;
+        uint4 af[2][MI], bfr[2][NJ];
+        load_frags<G, AMN, BMN>(at, bt, wm, wn, 0, lane, af[0], bfr[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 16) load_frags<G, AMN, BMN>(at, bt, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+        }
+    };
+    // acc += (dG / 2) S over the four k-tiles, dG's panels through registers
+    // (converted to bf16 into the A stage and into H).  Issue order per tile:
+    // the register loads (8), then the DMA (4), so a wait for the registers
+    // leaves the DMA in flight (vmcnt 4); the four stores of H follow, and a wait
+    // for the DMA leaves them in flight (memory operations report completion in
+    // issue order).  Tile kt + 1 goes to the stage tile kt - 1 used, once every
+    // wave has passed the barrier that opens tile kt.
+    // The first tile (stage 0), issued ahead.
+    auto x1_first = [&]() __attribute__((always_inline)) {
+        load_cols(0);
+        dma_rows(std::false_type{}, S, 0, base + G::kABytes);
+    };
+    // next_first(): the next phase's first loads, issued over this phase's last
+    // tile (stage 0 is free then: tile 2 is done everywhere) once every wave's
+    // stores of H have completed.
+    auto x1_loop = [&](auto&& next_first) __attribute__((always_inline)) {
+        wait_vmcnt<4>();
+        put_cols(0, 0);
+#pragma unroll 1
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt + 1 < 4) wait_vmcnt<4>();
+            else wait_vmcnt<0>();
+            wait_lgkm0();
+            block_barrier();
+            if (kt + 1 < 4) {
+                load_cols(kt + 1);
+                dma_rows(std::false_type{}, S, kt + 1, base + ((kt + 1) & 1) * kStage + G::kABytes);
+            } else {
+                next_first();
+            }
+            compute(std::false_type{}, std::false_type{}, lds + (kt & 1) * kStage, lds + (kt & 1) * kStage + G::kABytes);
+            if (kt + 1 < 4) {
+                wait_vmcnt<4>();
+                put_cols((kt + 1) & 1, kt + 1);
+            }
+        }
+    };
+    // acc += A B over the four k-tiles, both operands by DMA, in the same
+    // two-stage ring; the first tile is issued by the phase before.
+    auto dma_loop = [&](auto amn_c, auto bmn_c, const uint16_t* a_src, const uint16_t* b_src)
+                        __attribute__((always_inline)) {
+#pragma unroll 1
+        for (int kt = 0; kt < 4; ++kt) {
+            wait_vmcnt<0>();
+            wait_lgkm0();
+            block_barrier();
+            if (kt + 1 < 4) {
+                dma_rows(amn_c, a_src, kt + 1, base + ((kt + 1) & 1) * kStage);
+                dma_rows(bmn_c, b_src, kt + 1, base + ((kt + 1) & 1) * kStage + G::kABytes);
+            }
+            compute(amn_c, bmn_c, lds + (kt & 1) * kStage, lds + (kt & 1) * kStage + G::kABytes);
+        }
+    };
+
+    // ---- A. acc = dG + (dG / 2) S + T^T (dG / 2) = dS / 2 (halving is exact in
+    // bf16 and float32, so 2 acc is dS as 2 dG + X1 + X2); the first product
+    // leaves dG / 2 in bf16 in H, whose rows the second takes by DMA
+    init_dg();
+    x1_first();
+    x1_loop([&]() {   // T^T (dG / 2)'s first tile, over (dG / 2) S's last
+        dma_rows(std::true_type{}, T, 0, base);
+        dma_rows(std::true_type{}, H, 0, base + G::kABytes);
+    });
+    dma_loop(std::true_type{}, std::true_type{}, T, H);
+    scale_acc(2.f);    // dS
+    block_barrier();   // every wave is done reading the stages
+    dma_rows(std::false_type{}, Q, 0, base + kQBuf);   // Q's first k-tile, past the dS image
+
+    // ---- B. Sigma = dS + dS^T through LDS.  A lane holds four consecutive rows
+    // r..r+3 of a column c in each group of four accumulators, so it reads the
+    // transposed entries dS[c][r..r+3] as one 8-byte access, and writes Sigma,
+    // symmetric, as Sigma[c][r..r+3]: row c of the m-major A image of phase C
+    // (k-row c, m = r..r+3), again one 8-byte access.  Each tile's LDS addresses
+    // come from one per-lane base: the swizzle terms that vary with the
+    // accumulator index occupy bits of their own, so they enter as a constant
+    // XOR and a constant offset.
+    for_tiles([&](f32x16_t& t, int row_lo, int col_lo) {
+        const int r0 = row_lo + 4 * L, c = col_lo + l31;
+        uint32_t a = 512 * r0 + 2 * (c ^ (16 * L));     // dS (r0, c)
+        asm volatile("" : "+v"(a)::"memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<uint16_t*>(lds + ((a ^ (64 * q + 8 * u)) + 512 * (8 * q + u))) =
+                    ElemTraits<bf16_t>::from_f32(t[4 * q + u]).bits;
+    });
+    wait_lgkm0();
+    block_barrier();
+    for_tiles([&](f32x16_t& t, int row_lo, int col_lo) {
+        const int r0 = row_lo + 4 * L, c = col_lo + l31;
+        uint32_t a = 512 * c + 2 * (r0 ^ (4 * l31));    // dS (c, r0..r0+3)
+        asm volatile("" : "+v"(a)::"memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint2 v = *reinterpret_cast<const uint2*>(lds + (a ^ (16 * q)));
+            t[4 * q + 0] += bf16_to_f32((uint16_t)(v.x & 0xffff));
+            t[4 * q + 1] += bf16_to_f32((uint16_t)(v.x >> 16));
+            t[4 * q + 2] += bf16_to_f32((uint16_t)(v.y & 0xffff));
+            t[4 * q + 3] += bf16_to_f32((uint16_t)(v.y >> 16));
+        }
+    });
+    wait_lgkm0();
+    block_barrier();   // dS no longer read
+    for_tiles([&](f32x16_t& t, int row_lo, int col_lo) {
+        const int c = col_lo + l31;
+        // k-row c, m = r0 + 8 q .. + 3 of the m-major image (swz_mn<256> of k-row c)
+        uint32_t a = 512 * c + ((((row_lo >> 3)) ^ (4 * (c & 3))) << 4) + 8 * L;
+        asm volatile("" : "+v"(a)::"memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint2*>(lds + a + 16 * q) =
+                make_uint2(pack_bf16x2(0.5f * t[4 * q], 0.5f * t[4 * q + 1]),
+                           pack_bf16x2(0.5f * t[4 * q + 2], 0.5f * t[4 * q + 3]));
+    });
+    init_dg();   // phase C's starting value
+
+    // ---- C. acc += (Sigma / 2) Q^T = -P / 2 (one Q buffer)
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        block_barrier();   // Sigma complete; Q tile kt landed everywhere
+        if (kt == 3) {   // phase D's first tile: Sigma's tiles 0 and 1 (stage 0) are done
+            dma_rows(std::false_type{}, H, 0, base);
+            dma_rows(std::false_type{}, S, 0, base + G::kABytes);
+        }
+        compute(std::true_type{}, std::false_type{}, lds + kt * G::kABytes, lds + kQBuf);
+        if (kt + 1 < 4) {
+            block_barrier();   // every wave is done reading Q tile kt
+            dma_rows(std::false_type{}, Q, kt + 1, base + kQBuf);
+        }
+    }
+
+    // ---- D. acc / 2 + (dG / 2) S = E / 4, H's columns by DMA (its loop's
+    // barriers keep stage 1, Sigma's last tiles, untouched until every wave is
+    // done with them)
+    scale_acc(0.5f);
+    dma_loop(std::false_type{}, std::false_type{}, H, S);
+    scale_acc(4.f);    // E
+
+    // ---- E. dq = E - E^T on the upper triangle, by column halves: E[c][r..r+3]
+    // for a lane's rows r..r+3 of column c is one 16-byte read.  Only the part of
+    // E below the diagonal is read from LDS, so tiles wholly above it are not
+    // written, and tiles wholly below it store nothing.  The packed index of
+    // (r, c) steps by b - r - 2 from row r to row r + 1; the stores go through a
+    // buffer resource spanning the block's dq, where an entry on or below the
+    // diagonal takes an offset past its end and the store is dropped (no branch).
+    const __amdgpu_buffer_rsrc_t out =
+        __builtin_amdgcn_make_buffer_rsrc(dq + z * (kBlkB * (kBlkB - 1) / 2), 0, kBlkB * (kBlkB - 1) / 2 * 4, 0x00020000);
+    constexpr uint32_t kDrop = 0x80000000u;   // past the resource's end
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        wait_lgkm0();
+        block_barrier();   // the LDS is free (the ring, or the previous half, no longer read)
+        if (wn == h)
+            for_tiles([&](f32x16_t& t, int row_lo, int col_lo) {
+                if (row_lo < col_lo) return;   // wholly above the diagonal: never read
+                const int r0 = row_lo + 4 * L, cc = col_lo - 128 * h + l31;
+                uint32_t a = 512 * r0 + 4 * (cc ^ (16 * L));    // E (r0, cc)
+                asm volatile("" : "+v"(a)::"memory");
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        *reinterpret_cast<float*>(lds + ((a ^ (128 * (q & 1) + 16 * u)) + 512 * (8 * q + u))) =
+                            t[4 * q + u];
+            });
+        wait_lgkm0();
+        block_barrier();
+        // owners of (r, c), r < c, with r in this column half read E[c][r]
+        if ((wm >> 1) == h)
+            for_tiles([&](f32x16_t& t, int row_lo, int col_lo) {
+                if (row_lo > col_lo) return;   // wholly below the diagonal: nothing to store
+                const int r0 = row_lo + 4 * L, c = col_lo + l31;
+                uint32_t a = 512 * c + 4 * ((r0 - 128 * h) ^ (4 * (l31 & 15)));   // E[c][r0..r0+3]
+                // byte offset of dq[idx(r0, c)], its step to the next row, and the
+                // number of rows r0 + d above the diagonal (d < lim)
+                uint32_t j = 2 * r0 * (511 - r0) + 4 * (c - r0 - 1);
+                const uint32_t k4 = 4 * (254 - r0);
+                const int lim = c - r0;
+                asm volatile("" : "+v"(a), "+v"(j)::"memory");
+                // the four reads first (the buffer stores would otherwise order them)
+                float4 e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) e[q] = *reinterpret_cast<const float4*>(lds + (a ^ (32 * q)));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float ev[4] = {e[q].x, e[q].y, e[q].z, e[q].w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int d = 8 * q + u;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(t[4 * q + u] - ev[u]), out,
+                                                              d < lim ? j : kDrop, 0, 0);
+                        // to row r0 + d + 1, or from the quad's last row to the next quad's first
+                        j += u < 3 ? k4 - 4 * d : 5 * k4 - 4 * (5 * d + 10);
+                    }
+                }
+            });
+    }
+}
+
 template <int BM, int BN, bool A_MN, bool B_MN, bool OUT_F32, int EPI = kEpiPlain, int S = 3, int NWM = 2, int NWN = 2,
           int DUAL = 0, bool GRP = false, bool Q8 = false>
 hipError_t launch(const PipeArgs& p, hipStream_t stream) {
@@ -2138,6 +2485,24 @@ hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nbl
         else
             hipLaunchKernelGGL(cnp_bwd_sigq_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
     });
+}
+
+hipError_t cnp_bwd_block(const float* dG, const void* S, const void* T, const void* Q, void* dGh, float* dq,
+                         int64_t nblk, int b, hipStream_t stream) {
+    if (nblk <= 0) return hipSuccess;
+    if (b != kBlkB) return hipErrorInvalidValue;
+    const int64_t bb = (int64_t)b * b, ntri = (int64_t)b * (b - 1) / 2;
+    constexpr int64_t kMaxGrid = 0x7fffffff;
+    for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGrid) {
+        const int64_t nz = std::min<int64_t>(kMaxGrid, nblk - z0);
+        hipLaunchKernelGGL(cnp_bwd_block_kernel, dim3((unsigned)nz), dim3(512), 0, stream, dG + z0 * bb,
+                           static_cast<const uint16_t*>(S) + z0 * bb, static_cast<const uint16_t*>(T) + z0 * bb,
+                           static_cast<const uint16_t*>(Q) + z0 * bb, static_cast<uint16_t*>(dGh) + z0 * bb,
+                           dq + z0 * ntri);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool dense_fold_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldc2,

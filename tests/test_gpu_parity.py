@@ -160,6 +160,22 @@ def test_cnp_bwd_parity(b, k, dtype, std, norm):
     assert rel_fro(dq, ref) <= tol(dtype)
 
 
+# b = 256, k = 3, bf16 batches of 256 blocks or more take the one-block-per-
+# workgroup backward (below that, the pair passes); a sample of blocks, among
+# them the first and last of a ragged count, against the oracle
+@pytest.mark.parametrize("nblk,std,norm", [(256, 1e-3, None), (300, 1e-2, None), (517, 1e-2, 0.6)])
+def test_cnp_bwd_many_blocks(nblk, std, norm):
+    b, k = 256, 3
+    q = _q(nblk, b, std, 600 + nblk)
+    js = [0, 1, nblk // 2, nblk - 1]
+    if norm is not None:
+        q[js] = _scaled_q(len(js), b, std, norm, 601 + nblk)
+    dG = I.gaussian((nblk, b, b), 1.0, "f32", 602, nblk)
+    dq = host(cnp_bwd(dev(q), dev(dG), nblk, b, k, "bf16")[js])
+    ref = O.params_grad_from_skew_grad(O.cnp_vjp(O.skew_from_params(q[js], b), dG[js], k))
+    assert rel_fro(dq, ref) <= tol("bf16")    # every sampled block on its own, too
+
+
 # bf16 blocks of 128 or 256 take the fused per-panel forward (32-row panels for
 # a few blocks, as in the cases above; 64-row panels once there are 256 or more
 # of those); here many blocks, a sample of which is checked against the oracle.
