@@ -290,12 +290,25 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
     return POETX_OK;
 }
 
+// Batches from which the k = 3, b = 256 forward (bf16) takes one block per
+// workgroup instead of one 32- or 64-row panel per workgroup: one workgroup
+// takes about 24 us on its block, the panels spread a few blocks over more CUs
+// (64 blocks: 20 us against 27); from about a hundred blocks on, building each
+// block's Q image once wins (96: 28 against 33 us; 15280: 2.5 against 4.2 ms).
+constexpr int64_t kBlockFwdMinBlocks = 96;
+
 // Forward Cayley-Neumann schedules.  k = 3: G = I + 2Q + 2S + (2Q + S) S.
 // k = 4: E = (Q + S) + (Q + S) S, G = I + Q + E + Q E.  Other k: Horner,
 // D_1 = Q, D_{i+1} = Q + Q D_i, G = I + Q + D_k + Q D_k.  Every product is a
 // correction term; the leading terms are added in float32 by the epilogue.
 int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void* G, bool gbf16, CnpBufs& B,
                 bool save, hipStream_t s) {
+    if (cbf16 && gbf16 && k == 3 && b == 256 && nblk >= kBlockFwdMinBlocks && (reinterpret_cast<uintptr_t>(G) & 15) == 0) {
+        // one block per workgroup: Q built once per block, S and T through memory
+        // (the saving forward keeps them; otherwise the workspace holds them)
+        HIP_TRY(cnp_fwd_block(q, G, save ? B.Qc : nullptr, B.Sc, B.Tc, nblk, (int)b, s));
+        return POETX_OK;
+    }
     if (cbf16 && gbf16 && cnp_fused_supported(b, k) && (!save || k == 3) && (reinterpret_cast<uintptr_t>(G) & 15) == 0) {
         // bf16 blocks of 128 or 256: one kernel from the packed parameters to G,
         // every power of Q formed per panel on chip (the saving forward also
@@ -334,9 +347,10 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
 // Batches from which the k = 3, b = 256 backward takes one block per workgroup
 // instead of the two passes over tile pairs.  A lone workgroup takes about
 // 54 us on its block, the pair passes spread a few blocks over the whole chip
-// (32 blocks: 28 us); from a few hundred blocks on, the per-block kernel moves
-// fewer bytes and is ahead (256: 84 against 116 us; 15280: 4.8 against 7.7 ms).
-constexpr int64_t kBlockBwdMinBlocks = 256;
+// (32 blocks: 28 us, 96: 53 against 59 us); from about 128 blocks on, the
+// per-block kernel moves fewer bytes and is ahead (128: 63 against 66 us; 256:
+// 84 against 116 us; 15280: 4.8 against 7.7 ms).
+constexpr int64_t kBlockBwdMinBlocks = 128;
 
 // Adjoint schedules (reverse of the forward ones), ending with the skew pack.
 int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k, bool cbf16, float* dq,

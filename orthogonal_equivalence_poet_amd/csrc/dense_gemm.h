@@ -118,6 +118,12 @@ hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nbl
 hipError_t cnp_bwd_block(const float* dG, const void* S, const void* T, const void* Q, void* dGh, float* dq,
                          int64_t nblk, int b, hipStream_t stream);
 
+// The k = 3 Cayley-Neumann forward with one b = 256 block per workgroup, from
+// the packed parameters q [nblk, b(b-1)/2] to G [nblk, b, b] bf16, with S and T
+// (required) and Q (optional) kept in bf16 as the saving forward keeps them.
+hipError_t cnp_fwd_block(const float* q, void* G, void* Qc, void* S, void* T, int64_t nblk, int b,
+                         hipStream_t stream);
+
 // Fused Cayley-Neumann forward for bf16 blocks of b = 128 or 256 (see the
 // kernel): packed float32 parameters q [nblk, b(b-1)/2] -> G bf16 [nblk, b, b];
 // with Qc given also Q in bf16, with S and T given (k >= 2) also S = Q Q and

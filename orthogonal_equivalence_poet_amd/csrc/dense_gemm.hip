@@ -2070,31 +2070,20 @@ __device__ __forceinline__ uint4 img_frag(const unsigned char* __restrict__ tile
 
 typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int B, int PH>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, B == 256 ? 1 : 2)))
-cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t* __restrict__ Qc,
-                 uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv, int k, int total) {
-    using F = FusedCnp<B, PH>;
-    constexpr int KT = F::KT, QB = F::QB, XB = F::XB, MI = F::MI, NJ = F::NJ, NB8 = F::NB8;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS];
-    unsigned char* qs = lds;
-    unsigned char* xs = lds + KT * QB;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int id = blockIdx.x;
-    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
-    const int z = id / F::NP, p = id - z * F::NP;
-    const int64_t zoff = (int64_t)z * B * B;
-    const float* __restrict__ qz = q + (int64_t)z * F::NPAR;
-    const int r0 = PH * p;   // first row of the panel
-
-    // 1. the Q image.  Tasks: the strict upper sub-blocks (sub-rows R' and
-    // NB8 - 2 - R' sharing a run of NB8 tasks), then the diagonal ones; every
-    // thread issues the loads of all its tasks before it writes any.
-    constexpr int NTASK = (F::TASKS + 255) / 256;
+// Step 1 of the fused forward for one block: Q = U - U^T in LDS (bf16, the
+// k-tiled image described above) from the block's packed triangle qz, by NT
+// threads.  Tasks: the strict upper 8 x 8 sub-blocks (sub-rows R' and
+// NB8 - 2 - R' sharing a run of NB8 tasks), then the diagonal ones; every
+// thread issues the loads of all its tasks before it writes any.
+template <int B, int NT>
+__device__ __forceinline__ void build_q_image(const float* __restrict__ qz, unsigned char* __restrict__ qs, int tid) {
+    using F = FusedCnp<B, 64>;
+    constexpr int QB = F::QB, NB8 = F::NB8;
+    constexpr int NTASK = (F::TASKS + NT - 1) / NT;
     float u[NTASK][8][8];
 #pragma unroll
     for (int s = 0; s < NTASK; ++s) {
-        const int t = tid + 256 * s;
+        const int t = tid + NT * s;
         if (t < F::OFFDIAG) {
             const int Rp = t / NB8, cp = t - Rp * NB8;
             const bool first = cp < NB8 - 1 - Rp;
@@ -2126,7 +2115,7 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
     }
 #pragma unroll
     for (int s = 0; s < NTASK; ++s) {
-        const int t = tid + 256 * s;
+        const int t = tid + NT * s;
         if (t < F::OFFDIAG) {
             const int Rp = t / NB8, cp = t - Rp * NB8;
             const bool first = cp < NB8 - 1 - Rp;
@@ -2156,6 +2145,27 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
             }
         }
     }
+}
+
+template <int B, int PH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, B == 256 ? 1 : 2)))
+cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t* __restrict__ Qc,
+                 uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv, int k, int total) {
+    using F = FusedCnp<B, PH>;
+    constexpr int KT = F::KT, QB = F::QB, XB = F::XB, MI = F::MI, NJ = F::NJ, NB8 = F::NB8;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS];
+    unsigned char* qs = lds;
+    unsigned char* xs = lds + KT * QB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
+    const int z = id / F::NP, p = id - z * F::NP;
+    const int64_t zoff = (int64_t)z * B * B;
+    const float* __restrict__ qz = q + (int64_t)z * F::NPAR;
+    const int r0 = PH * p;   // first row of the panel
+
+    // 1. the Q image
+    build_q_image<B, 256>(qz, qs, tid);
     __syncthreads();
 
     // rows of an image as 16-byte chunks: PH rows x B/8 chunks over the workgroup
@@ -2273,6 +2283,193 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
             }
     __syncthreads();
     copy_rows(G, [&](int m, int c) { return *reinterpret_cast<const uint4*>(xs + img_off<XB>(m, c)); });
+}
+
+// The k = 3 Cayley-Neumann forward of one b = 256 block per workgroup (large
+// batches), keeping Q, S and T for the backward.  G = I + 2Q + 2S + T S with
+// S = Q Q and T = 2Q + S (the same factorization as the unfused products):
+//   1. the Q image in LDS from the packed triangle (the per-panel kernel's
+//      step 1, over the whole workgroup); Q's rows to Qc;
+//   2. acc = Q Q^T = -S from the image (both operands k-major rows of Q);
+//   3. S and T = 2Q + S to memory in bf16 (T from the bf16 Q and S, as the
+//      per-panel kernel forms it);
+//   4. acc = I + 2Q + 2S in float32 (2S from the accumulators, 2Q from the image);
+//   5. acc += S T^T, S's and T's rows back by DMA;
+//   6. G to memory in bf16.
+// S is symmetric, so the accumulator a lane holds for rows r..r+3 of column c,
+// (Q Q^T)(r.., c), is also S's row c at columns r..r+3, and the product of
+// step 5, (S T^T)(r.., c) = (T S)(c, r..), lands on G's row c at columns
+// r..r+3.  Eight waves, wave (wm, wn) owning rows [64 wm, 64 wm + 64) and
+// columns [128 wn, 128 wn + 128) of the accumulators, i.e. columns
+// [64 wm, 64 wm + 64) of rows [128 wn, 128 wn + 128) of S, T and G.  Each wave
+// passes its share through 4 KB of LDS of its own, 32 rows x 64 columns at a
+// time, so that the stores go out as whole 128-byte row segments.
+__global__ void __launch_bounds__(512, 1)
+cnp_fwd_block_kernel(const float* __restrict__ q, uint16_t* __restrict__ Gout, uint16_t* __restrict__ Qc,
+                     uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv) {
+    using F = FusedCnp<kBlkB, 64>;
+    using GE = Geo<256, 256, 4, 2>;
+    constexpr int MI = GE::MI, NJ = GE::NJ;     // 2 x 4 tiles of 32 x 32 per wave
+    constexpr int QB = F::QB;                   // one k-tile of the Q image, 32 KB
+    constexpr int kStage = 64 * 1024;           // step 5's A (32 KB) + B (32 KB)
+    constexpr int NB = OperandLoads<256, false, GE::NW>::n;
+    static_assert(4 * QB == 2 * kStage, "the ring takes the image's place");
+    constexpr int kStageOut = 4 * QB;           // the waves' 4 KB output stages
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * QB + 8 * 4096];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / GE::NWN, wn = wave % GE::NWN;
+    const int64_t z = blockIdx.x, zoff = z * (kBlkB * kBlkB);
+    const uint32_t base = lds_offset(lds);
+    const int L = lane >> 5, l31 = lane & 31;
+
+    // 1. the Q image, and Q's rows as 16-byte chunks
+    build_q_image<kBlkB, 512>(q + z * F::NPAR, lds, tid);
+    __syncthreads();
+    if (Qc)
+        for (int u = tid; u < kBlkB * (kBlkB / 8); u += 512) {
+            const int m = u / (kBlkB / 8), c = 8 * (u % (kBlkB / 8));
+            *reinterpret_cast<uint4*>(Qc + zoff + m * kBlkB + c) =
+                *reinterpret_cast<const uint4*>(lds + img_off<QB>(m, c));
+        }
+
+    // a lane holds rows r0 + 8 q + u (q, u < 4, r0 = first row + 4 L) of column
+    // first column + l31 of each 32 x 32 accumulator tile, in accumulator 4 q + u
+    f32x16_t acc[MI][NJ];
+
+    // 2. acc = Q Q^T, fragments straight from the image (two sets in flight)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    {
+        uint4 af[2][MI], bfr[2][NJ];
+        auto frags = [&](int ks, uint4 (&a)[MI], uint4 (&b)[NJ]) __attribute__((always_inline)) {
+            const unsigned char* t = lds + (ks >> 2) * QB;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) a[i] = img_frag(t, wm * 64 + 32 * i, ks & 3, lane);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) b[j] = img_frag(t, wn * 128 + 32 * j, ks & 3, lane);
+        };
+        frags(0, af[0], bfr[0]);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < 16) frags(ks + 1, af[cur ^ 1], bfr[cur ^ 1]);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+        }
+    }
+
+    // Rows [128 wn + 32 j, + 32) x columns [64 wm, + 64) of an output through the
+    // wave's stage: put(i, qd, half) gives the 8-byte run of row 128 wn + 32 j + l31
+    // at columns 64 wm + 32 i + 8 qd + 4 half; the stage holds (row, column) at
+    // row * 128 + 16 ((column / 8) ^ ((row / 2) & 7)) + 8 ((column / 4 & 1) ^ (row / 16 & 1))
+    // (32 lanes writing one column of 32 rows meet distinct banks), and each
+    // lane then stores 16-byte chunks, eight lanes to a row.
+    unsigned char* ostage = lds + kStageOut + wave * 4096;
+    auto out_rows = [&](uint16_t* __restrict__ dst, int j, auto&& put) __attribute__((always_inline)) {
+        const int rw = l31;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int ch = 4 * i + qd;
+                *reinterpret_cast<uint2*>(ostage + rw * 128 + 16 * (ch ^ ((rw >> 1) & 7)) + 8 * (L ^ ((rw >> 4) & 1))) =
+                    put(i, qd);
+            }
+        wait_lgkm0();
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+            const int row = 8 * ps + (lane >> 3), ch = lane & 7;
+            uint4 v = *reinterpret_cast<const uint4*>(ostage + row * 128 + 16 * (ch ^ ((row >> 1) & 7)));
+            if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+            *reinterpret_cast<uint4*>(dst + zoff + (wn * 128 + 32 * j + row) * kBlkB + wm * 64 + 8 * ch) = v;
+        }
+        wait_lgkm0();
+    };
+
+    // 3. S = -acc and T = 2Q + S, row c = 128 wn + 32 j + l31, columns
+    // r = 64 wm + 32 i + 4 L + 8 q + u; 4. acc = I + 2Q + 2S at the same entries
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int c = wn * 128 + 32 * j + l31;
+        uint2 sv[MI][4], tv[MI][4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            f32x16_t& t = acc[i][j];
+            const int r0 = wm * 64 + 32 * i + 4 * L;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const uint2 qv = *reinterpret_cast<const uint2*>(lds + img_off<QB>(c, r0 + 8 * qd));
+                const float qf[4] = {bf16_to_f32((uint16_t)(qv.x & 0xffff)), bf16_to_f32((uint16_t)(qv.x >> 16)),
+                                     bf16_to_f32((uint16_t)(qv.y & 0xffff)), bf16_to_f32((uint16_t)(qv.y >> 16))};
+                float sf[4], tf[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float sx = -t[4 * qd + u];
+                    sf[u] = bf16_to_f32(ElemTraits<bf16_t>::from_f32(sx).bits);
+                    tf[u] = 2.f * qf[u] + sf[u];
+                    t[4 * qd + u] = (c == r0 + 8 * qd + u ? 1.f : 0.f) + 2.f * qf[u] + 2.f * sx;
+                }
+                sv[i][qd] = make_uint2(pack_bf16x2(sf[0], sf[1]), pack_bf16x2(sf[2], sf[3]));
+                tv[i][qd] = make_uint2(pack_bf16x2(tf[0], tf[1]), pack_bf16x2(tf[2], tf[3]));
+            }
+        }
+        out_rows(Sv, j, [&](int i, int qd) { return sv[i][qd]; });
+        out_rows(Tv, j, [&](int i, int qd) { return tv[i][qd]; });
+    }
+
+    // 5. acc += S T^T over four k-tiles of 64, S's rows (A) and T's rows (B) by
+    // DMA into a two-stage ring over the image's place, tile kt + 1 issued
+    // over tile kt's products
+    const uint16_t* Sz = Sv + zoff;
+    const uint16_t* Tz = Tv + zoff;
+    auto dma_tile = [&](int kt) __attribute__((always_inline)) {
+        const uint32_t dst = base + (kt & 1) * kStage;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) dma_one<256, false, GE::NW>(j, dst, Sz, kBlkB, 0, kBlkB, kt * 64, kBlkB, wave, lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            dma_one<256, false, GE::NW>(j, dst + GE::kABytes, Tz, kBlkB, 0, kBlkB, kt * 64, kBlkB, wave, lane);
+    };
+    wait_vmcnt<0>();   // this thread's S and T stores have completed
+    wait_lgkm0();
+    block_barrier();   // everyone's have, and the image is no longer read
+    dma_tile(0);
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+        wait_vmcnt<0>();
+        block_barrier();   // tile kt landed everywhere; tile kt - 1's stage is free
+        if (kt + 1 < 4) dma_tile(kt + 1);
+        const unsigned char* at = lds + (kt & 1) * kStage;
+        uint4 af[2][MI], bfr[2][NJ];
+        load_frags<GE, false, false>(at, at + GE::kABytes, wm, wn, 0, lane, af[0], bfr[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 16)
+                load_frags<GE, false, false>(at, at + GE::kABytes, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Mfma32<bf16_t>::run(af[cur][i], bfr[cur][j], acc[i][j]);
+        }
+    }
+
+    // 6. G's rows through the stages
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        out_rows(Gout, j, [&](int i, int qd) {
+            const f32x16_t& t = acc[i][j];
+            return make_uint2(pack_bf16x2(t[4 * qd], t[4 * qd + 1]), pack_bf16x2(t[4 * qd + 2], t[4 * qd + 3]));
+        });
 }
 
 }  // namespace
@@ -2605,6 +2802,23 @@ hipError_t pipe_gemm_colscale(const PipeArgs& p, hipStream_t stream, PipeTile ti
         case PipeTile::Tall: return launch<256, 128, false, true, false, kEpiColScale, 3, 4, 2>(p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t cnp_fwd_block(const float* q, void* G, void* Qc, void* S, void* T, int64_t nblk, int b,
+                         hipStream_t stream) {
+    if (nblk <= 0) return hipSuccess;
+    if (b != kBlkB || !G || !S || !T) return hipErrorInvalidValue;
+    const int64_t bb = (int64_t)b * b, npar = (int64_t)b * (b - 1) / 2;
+    constexpr int64_t kMaxGrid = 0x7fffffff;
+    for (int64_t z0 = 0; z0 < nblk; z0 += kMaxGrid) {
+        const int64_t nz = std::min<int64_t>(kMaxGrid, nblk - z0);
+        hipLaunchKernelGGL(cnp_fwd_block_kernel, dim3((unsigned)nz), dim3(512), 0, stream, q + z0 * npar,
+                           static_cast<uint16_t*>(G) + z0 * bb, Qc ? static_cast<uint16_t*>(Qc) + z0 * bb : nullptr,
+                           static_cast<uint16_t*>(S) + z0 * bb, static_cast<uint16_t*>(T) + z0 * bb);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool cnp_fused_supported(int64_t b, int k) { return (b == 128 || b == 256) && k >= 1; }

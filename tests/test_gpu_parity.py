@@ -160,10 +160,11 @@ def test_cnp_bwd_parity(b, k, dtype, std, norm):
     assert rel_fro(dq, ref) <= tol(dtype)
 
 
-# b = 256, k = 3, bf16 batches of 256 blocks or more take the one-block-per-
+# b = 256, k = 3, bf16 batches of 128 blocks or more take the one-block-per-
 # workgroup backward (below that, the pair passes); a sample of blocks, among
 # them the first and last of a ragged count, against the oracle
-@pytest.mark.parametrize("nblk,std,norm", [(256, 1e-3, None), (300, 1e-2, None), (517, 1e-2, 0.6)])
+@pytest.mark.parametrize("nblk,std,norm", [(128, 1e-2, 0.5), (256, 1e-3, None), (300, 1e-2, None),
+                                           (517, 1e-2, 0.6)])
 def test_cnp_bwd_many_blocks(nblk, std, norm):
     b, k = 256, 3
     q = _q(nblk, b, std, 600 + nblk)
@@ -178,13 +179,15 @@ def test_cnp_bwd_many_blocks(nblk, std, norm):
 
 # bf16 blocks of 128 or 256 take the fused per-panel forward (32-row panels for
 # a few blocks, as in the cases above; 64-row panels once there are 256 or more
-# of those); here many blocks, a sample of which is checked against the oracle.
+# of those), except k = 3 at b = 256 from 96 blocks on, which takes one block
+# per workgroup; here many blocks, a sample of which is checked against the oracle.
 @pytest.mark.parametrize("b,k,std,norm,nblk", [(256, 3, 1e-3, None, 256), (256, 1, 0.05, None, 256),
                                                (256, 4, 1e-2, 0.5, 256), (256, 7, 1e-2, 0.6, 256),
                                                (128, 3, 0.05, None, 512), (128, 2, 1e-2, 0.5, 512),
-                                               (256, 3, 1e-3, None, 1024), (256, 4, 1e-2, 0.5, 1100)])
+                                               (256, 3, 1e-3, None, 1024), (256, 4, 1e-2, 0.5, 1100),
+                                               (256, 3, 1e-2, 0.6, 97), (256, 3, 1e-2, None, 95)])
 def test_cnp_fused_forward_many_blocks(b, k, std, norm, nblk):
-    # 64-row panels at many blocks, including ragged block counts
+    # many blocks, including ragged block counts on both sides of the k = 3 switch
     q = _q(nblk, b, std, 500 + b + k)
     js = [0, 1, nblk // 2, nblk - 1]
     if norm is not None:
@@ -212,9 +215,9 @@ def test_cnp_saved_variant_is_bitwise_identical(b, k, dtype, nblk):
     B.poetx_cnp_fwd_save(q, nblk, b, k, G, saved, ws)
     dq = torch.empty_like(dq_ref)
     B.poetx_cnp_bwd_saved(q, dG, nblk, b, k, dq, code(dtype), saved, ws)
-    # bf16 blocks of 128 / 256 take the fused per-panel forward; the saving
-    # forward does so only for k = 3 (for other k the backward needs the
-    # square's float32 companions)
+    # bf16 blocks of 128 / 256 take a fused forward (per panel, or per block for
+    # k = 3 at b = 256 from 96 blocks on); the saving forward does so only for
+    # k = 3 (for other k the backward needs the square's float32 companions)
     fused_plain = dtype == "bf16" and b in (128, 256)
     fused_save = fused_plain and k == 3
     js = [0, nblk - 1]
