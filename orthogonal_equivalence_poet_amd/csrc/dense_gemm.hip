@@ -1259,6 +1259,36 @@ __device__ __forceinline__ int64_t upper_index(int r, int c, int b) {
     return (int64_t)r * b - (int64_t)r * (r + 1) / 2 + (c - r - 1);
 }
 
+// The work units of one block of nt x nt 64 x 64 tiles for the k = 3 passes:
+// the nt (nt - 1) / 2 mirrored pairs (I, J), I < J, one tile per group of four
+// waves, then the diagonal tiles two at a time, one per group (diag; a lone
+// last one when nt is odd is computed by both groups and kept by group 0), so
+// that every unit carries two tiles of work.
+__host__ __device__ constexpr int units_per_block(int nt) { return nt * (nt - 1) / 2 + (nt + 1) / 2; }
+
+__device__ __forceinline__ void unit_of(int nt, int& ti, int& tj, int& z, bool& diag) {
+    const int units = (int)gridDim.x;
+    const int total = units * (int)gridDim.y;
+    int id = (int)blockIdx.x + units * (int)blockIdx.y;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);   // each XCD gets whole blocks
+    z = id / units;
+    int t = id - z * units;
+    const int npairs = nt * (nt - 1) / 2;
+    diag = t >= npairs;
+    if (diag) {
+        ti = 2 * (t - npairs);
+        tj = min(ti + 1, nt - 1);
+        return;
+    }
+    int i = 0;
+    while (t >= nt - 1 - i) {
+        t -= nt - 1 - i;
+        ++i;
+    }
+    ti = i;
+    tj = i + 1 + t;
+}
+
 template <int S>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 4)))
 cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
@@ -1326,11 +1356,11 @@ cnp_pack_pair_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
 //   Sigma = dS + dS^T (symmetric),  P = Sigma Q
 // that part is 2 (dA - dA^T) - (P - P^T): Q Sigma = -(Sigma Q)^T for a skew Q
 // and a symmetric Sigma, so the two products dS Q^T and Q^T dS of the full dQ
-// become the one product P.  Two passes over mirrored pairs of 64 x 64 tiles
-// (I, J) and (J, I), I <= J, one per group of four waves (a diagonal pair
-// computes its tile twice, so that both groups pass the same barriers):
+// become the one product P.  Two passes over units of two 64 x 64 tiles, one
+// per group of four waves (unit_of): a mirrored pair (I, J) and (J, I), I < J,
+// or two diagonal tiles, each its own mirror:
 //   pass 1 (cnp_bwd_sym_kernel): X1 and X2 of both tiles; writes Sigma (bf16,
-//     both tiles) and dq[idx(r, c)] = 2 (dA[r][c] - dA[c][r]) for the pair's
+//     both tiles) and dq[idx(r, c)] = 2 (dA[r][c] - dA[c][r]) for the unit's
 //     upper-triangle entries;
 //   pass 2 (cnp_bwd_sigq_kernel): -P = Sigma Q^T of both tiles (Q^T = -Q);
 //     dq[idx(r, c)] += P[c][r] - P[r][c], in place (each entry has one owner).
@@ -1362,9 +1392,12 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     const int lane = tid & 63, w4 = (tid >> 6) & 3;
     const int wm = w4 >> 1, wn = w4 & 1;
     int ti, tj, z;
-    pair_of(b / 64, ti, tj, z);
-    // group 0: tile (ti, tj); group 1: tile (tj, ti)
-    const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
+    bool diag;
+    unit_of(b / 64, ti, tj, z, diag);
+    // pair: group 0 tile (ti, tj), group 1 tile (tj, ti); diagonal unit: group 0
+    // tile (ti, ti), group 1 tile (tj, tj)
+    const int m0 = 64 * (grp ? tj : ti), n0 = diag ? m0 : 64 * (grp ? ti : tj);
+    const bool keep = !(diag && ti == tj && grp == 1);   // a lone diagonal tile: group 0's
     const int64_t bb = (int64_t)b * b;
     // A = dG (bf16, k-major), B = S (k-major, S = S^T), A2 = T ([K][M]), B2 = dG ([K][N])
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + z * bb;
@@ -1402,12 +1435,13 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     __syncthreads();
     const float* E0 = reinterpret_cast<const float*>(lds);
     const float* F0 = E0 + 64 * 64;
-    const float* E1 = ti == tj ? E0 : reinterpret_cast<const float*>(lds + kRing);
+    const float* E1 = reinterpret_cast<const float*>(lds + kRing);
     const float* F1 = E1 + 64 * 64;
-    // Sigma of this group's tile: Sigma[r][c] = dS[r][c] + dS[c][r]
-    if (grp == 0 || ti != tj) {
+    // Sigma of this group's tile: Sigma[r][c] = dS[r][c] + dS[c][r], the
+    // transposed entries from the mirrored tile (the own tile on the diagonal)
+    if (keep) {
         const float* Eo = grp ? E1 : E0;
-        const float* Ex = grp ? E0 : E1;
+        const float* Ex = diag ? Eo : (grp ? E0 : E1);
         uint16_t* sz = sig + z * bb;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1420,14 +1454,23 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
                 make_uint2(pack_bf16x2(s0, s1), pack_bf16x2(s2, s3));
         }
     }
-    // dq = 2 (dA - dA^T) on the pair's upper-triangle entries
+    // dq = 2 (dA - dA^T) on the unit's upper-triangle entries
     float* out = dq + (int64_t)z * ((int64_t)b * (b - 1) / 2);
+    if (!diag) {
 #pragma unroll
-    for (int k = 0; k < 64 * 64 / 512; ++k) {
-        const int u = k * 512 + tid;
-        const int rl = u >> 6, cl = u & 63;
-        const int r = 64 * ti + rl, c = 64 * tj + cl;
-        if (r < c) out[upper_index(r, c, b)] = 2.f * (F0[t64(rl, cl)] - F1[t64(cl, rl)]);
+        for (int k = 0; k < 64 * 64 / 512; ++k) {
+            const int u = k * 512 + tid;
+            const int rl = u >> 6, cl = u & 63;
+            out[upper_index(64 * ti + rl, 64 * tj + cl, b)] = 2.f * (F0[t64(rl, cl)] - F1[t64(cl, rl)]);
+        }
+    } else if (keep) {
+        const float* Fo = grp ? F1 : F0;
+#pragma unroll
+        for (int k = 0; k < 64 * 64 / 256; ++k) {
+            const int u = k * 256 + gtid;
+            const int rl = u >> 6, cl = u & 63;
+            if (rl < cl) out[upper_index(m0 + rl, m0 + cl, b)] = 2.f * (Fo[t64(rl, cl)] - Fo[t64(cl, rl)]);
+        }
     }
 }
 
@@ -1442,38 +1485,50 @@ cnp_bwd_sigq_kernel(const PipeArgs p, float* __restrict__ dq, int b) {
     const int lane = tid & 63, w4 = (tid >> 6) & 3;
     const int wm = w4 >> 1, wn = w4 & 1;
     int ti, tj, z;
-    pair_of(b / 64, ti, tj, z);
-    const int m0 = 64 * (grp ? tj : ti), n0 = 64 * (grp ? ti : tj);
+    bool diag;
+    unit_of(b / 64, ti, tj, z, diag);
+    const int m0 = 64 * (grp ? tj : ti), n0 = diag ? m0 : 64 * (grp ? ti : tj);
+    const bool keep = !(diag && ti == tj && grp == 1);
     const int64_t bb = (int64_t)b * b;
     // A = Sigma (bf16, symmetric), B = Q (rows of Q as [N][K]): acc = Sigma Q^T = -P
     const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + z * bb;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + z * bb;
     unsigned char* ring = lds + grp * kRing;
     // the partial dq this pass adds to, read before the main loop (its latency
-    // hides behind the products); every thread owns fixed entries
+    // hides behind the products); every thread owns fixed entries: the whole
+    // workgroup a pair's tile (ti, tj), each group its own diagonal tile
     float* out = dq + (int64_t)z * ((int64_t)b * (b - 1) / 2);
-    float part[8];
+    constexpr int kPer = 64 * 64 / 256;
+    auto entry = [&](int k, int& rl, int& cl) -> bool {
+        if (!diag) {
+            const int u = k * 512 + tid;
+            rl = u >> 6, cl = u & 63;
+            return k < 64 * 64 / 512;
+        }
+        const int u = k * 256 + gtid;
+        rl = u >> 6, cl = u & 63;
+        return keep && rl < cl;
+    };
+    const int r0 = diag ? m0 : 64 * ti, c0 = diag ? m0 : 64 * tj;
+    float part[kPer];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int u = k * 512 + tid;
-        const int rl = u >> 6, cl = u & 63;
-        const int r = 64 * ti + rl, c = 64 * tj + cl;
-        part[k] = r < c ? out[upper_index(r, c, b)] : 0.f;
+    for (int k = 0; k < kPer; ++k) {
+        int rl, cl;
+        part[k] = entry(k, rl, cl) ? out[upper_index(r0 + rl, c0 + cl, b)] : 0.f;
     }
     f32x16_t acc[1][1];
     main_loop<G, false, false, S>(ring, A, b, B, b, m0, n0, b, b, 0, b, gtid, acc);
     block_barrier();   // every wave is done reading the operand stages
     stage_acc(reinterpret_cast<float*>(ring), acc[0][0], wm, wn, lane);
     __syncthreads();
-    const float* N0 = reinterpret_cast<const float*>(lds);
-    const float* N1 = ti == tj ? N0 : reinterpret_cast<const float*>(lds + kRing);
+    // -P[r][c] + P[c][r] = acc(I, J)[rl][cl] - acc(J, I)[cl][rl] (a diagonal
+    // tile: its own transposed entries)
+    const float* N0 = reinterpret_cast<const float*>(diag ? ring : lds);
+    const float* N1 = reinterpret_cast<const float*>(diag ? ring : lds + kRing);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int u = k * 512 + tid;
-        const int rl = u >> 6, cl = u & 63;
-        const int r = 64 * ti + rl, c = 64 * tj + cl;
-        // -P[r][c] + P[c][r] = acc(I, J)[rl][cl] - acc(J, I)[cl][rl]
-        if (r < c) out[upper_index(r, c, b)] = part[k] + (N0[t64(rl, cl)] - N1[t64(cl, rl)]);
+    for (int k = 0; k < kPer; ++k) {
+        int rl, cl;
+        if (entry(k, rl, cl)) out[upper_index(r0 + rl, c0 + cl, b)] = part[k] + (N0[t64(rl, cl)] - N1[t64(cl, rl)]);
     }
 }
 
@@ -2634,12 +2689,12 @@ hipError_t cnp_pack_pair(const PipeArgs& p_in, float* dq, int b, hipStream_t str
 // Launch helper of the two k = 3 backward passes: pairs of 64 x 64 tiles of
 // every block, batch entries in chunks of at most 65535 (grid.y).
 template <class Fn>
-hipError_t launch_pairs(int64_t nblk, int b, Fn&& fn) {
+hipError_t launch_pairs(int64_t nblk, int b, Fn&& fn, bool units = false) {
     const int nt = b / 64;
     constexpr int kMaxY = 65535;
     for (int64_t y0 = 0; y0 < nblk; y0 += kMaxY) {
         const int ny = (int)std::min<int64_t>(kMaxY, nblk - y0);
-        fn(y0, dim3(nt * (nt + 1) / 2, ny));
+        fn(y0, dim3(units ? units_per_block(nt) : nt * (nt + 1) / 2, ny));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -2665,7 +2720,7 @@ hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const vo
             hipLaunchKernelGGL(cnp_bwd_sym_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
         else
             hipLaunchKernelGGL(cnp_bwd_sym_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
-    });
+    }, true);
 }
 
 hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nblk, int b, hipStream_t stream) {
@@ -2681,7 +2736,7 @@ hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nbl
             hipLaunchKernelGGL(cnp_bwd_sigq_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
         else
             hipLaunchKernelGGL(cnp_bwd_sigq_kernel<3>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, b);
-    });
+    }, true);
 }
 
 hipError_t cnp_bwd_block(const float* dG, const void* S, const void* T, const void* Q, void* dGh, float* dq,
