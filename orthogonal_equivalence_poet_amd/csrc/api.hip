@@ -303,7 +303,7 @@ constexpr int64_t kBlockFwdMinBlocks = 96;
 // correction term; the leading terms are added in float32 by the epilogue.
 int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void* G, bool gbf16, CnpBufs& B,
                 bool save, hipStream_t s) {
-    if (cbf16 && gbf16 && k == 3 && b == 256 && nblk >= kBlockFwdMinBlocks && (reinterpret_cast<uintptr_t>(G) & 15) == 0) {
+    if (cbf16 && gbf16 && k == 3 && b == 256 && nblk >= kBlockFwdMinBlocks && all_al16(G, B.Sc, B.Tc, B.Qc)) {
         // one block per workgroup: Q built once per block, S and T through memory
         // (the saving forward keeps them; otherwise the workspace holds them)
         HIP_TRY(cnp_fwd_block(q, G, save ? B.Qc : nullptr, B.Sc, B.Tc, nblk, (int)b, s));
@@ -358,7 +358,7 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
     if (!saved) POETX_TRY(cnp_prologue(q, nblk, b, k, cbf16, B, s));
     const int ib = (int)b;
     const int64_t bb = b * b;
-    if (cbf16 && k == 3 && b == 256 && nblk >= kBlockBwdMinBlocks) {
+    if (cbf16 && k == 3 && b == 256 && nblk >= kBlockBwdMinBlocks && all_al16(dG, B.Sc, B.Tc, B.Qc, B.dGc)) {
         // one block per workgroup: every intermediate on chip, dG read as float32
         // and kept as bf16 in the scratch of its compute copy
         HIP_TRY(cnp_bwd_block(dG, B.Sc, B.Tc, B.Qc, B.dGc, dq, nblk, ib, s));
