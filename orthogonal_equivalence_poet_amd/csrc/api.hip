@@ -364,6 +364,20 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
         HIP_TRY(cnp_bwd_block(dG, B.Sc, B.Tc, B.Qc, B.dGc, dq, nblk, ib, s));
         return POETX_OK;
     }
+    const bool dual = cbf16 && b % 64 == 0 && pipe_gemm_supported(false, false, b, b, b, b, b, bb, bb) &&
+                      pipe_gemm_supported(true, true, b, b, b, b, b, bb, bb);
+    if (k == 3 && dual && al16(dG)) {
+        // Only the skew part of dQ reaches dq: with X1 = dG S, X2 = T^T dG,
+        // dS = 2 dG + X1 + X2 and Sigma = dS + dS^T (symmetric),
+        // dQ - dQ^T = 2 (dA - dA^T) - (P - P^T) with dA = dG + X1, P = Sigma Q,
+        // since Q Sigma = -(Sigma Q)^T.  Pass 1 (which rounds dG to bf16 on
+        // chip) writes Sigma and the packed 2 (dA - dA^T); pass 2 adds the
+        // packed -(P - P^T).  Three products instead of four; the pack rides on
+        // both passes.
+        HIP_TRY(cnp_bwd_sym(dG, B.Sc, B.Tc, B.c_c, dq, nblk, ib, s));
+        HIP_TRY(cnp_bwd_sigq(B.c_c, B.Qc, dq, nblk, ib, s));
+        return POETX_OK;
+    }
     const void* dGc = dG;
     if (cbf16) {
         HIP_TRY(combine(nblk, ib, dG, 1.f, nullptr, 0, nullptr, 0, 0, nullptr, B.dGc, true, s));
@@ -371,19 +385,7 @@ int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k
     }
     float* dQ = B.g32;
     bool packed = false;   // dq already written by the last product pair
-    const bool dual = cbf16 && b % 64 == 0 && pipe_gemm_supported(false, false, b, b, b, b, b, bb, bb) &&
-                      pipe_gemm_supported(true, true, b, b, b, b, b, bb, bb);
-    if (k == 3 && dual) {
-        // Only the skew part of dQ reaches dq: with X1 = dG S, X2 = T^T dG,
-        // dS = 2 dG + X1 + X2 and Sigma = dS + dS^T (symmetric),
-        // dQ - dQ^T = 2 (dA - dA^T) - (P - P^T) with dA = dG + X1, P = Sigma Q,
-        // since Q Sigma = -(Sigma Q)^T.  Pass 1 writes Sigma and the packed
-        // 2 (dA - dA^T); pass 2 adds the packed -(P - P^T).  Three products
-        // instead of four; the pack rides on both passes.
-        HIP_TRY(cnp_bwd_sym(dGc, dG, B.Sc, B.Tc, B.c_c, dq, nblk, ib, s));
-        HIP_TRY(cnp_bwd_sigq(B.c_c, B.Qc, dq, nblk, ib, s));
-        packed = true;
-    } else if (k == 3) {
+    if (k == 3) {
         // G = A B with A = I + T, B = I + S (T = 2Q + S, S symmetric):
         // dA = dG + dG S ;  dS = dA + dB with dB = dG + T^T dG ;  dQ = 2 dA + dS Q^T + Q^T dS
         HIP_TRY(gemm(GemmLayout::NT, cbf16, false, b, b, b, nblk, sq(dGc, b), sq(B.Sc, b), B.a32, b, bb, s, 1.f, dG,

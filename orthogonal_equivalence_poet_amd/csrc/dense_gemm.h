@@ -102,14 +102,15 @@ int pipe_tile_cols(PipeTile t);
 // dq[idx(r, c)] = dQ[r][c] - dQ[c][r] for r < c (row-major upper triangle).
 hipError_t cnp_pack_pair(const PipeArgs& p, float* dq, int b, hipStream_t stream);
 
-// The k = 3 Cayley-Neumann backward in two passes over mirrored tile pairs (bf16
+// The k = 3 Cayley-Neumann backward in two passes over units of two tiles (bf16
 // operands, b % 64 == 0, all [nblk, b, b] row-major): with X1 = dG S,
 // X2 = T^T dG, dS = 2 dG + X1 + X2, Sigma = dS + dS^T,
 //   cnp_bwd_sym:  sigma = Sigma (bf16), dq = 2 (dA - dA^T) packed (dA = dG + X1);
 //   cnp_bwd_sigq: dq += pack(-(P - P^T)), P = Sigma Q.
-// dGc is dG in bf16, dG the float32 original (the exact leading terms).
-hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const void* T, void* sigma, float* dq,
-                       int64_t nblk, int b, hipStream_t stream);
+// dG is float32 (16-byte aligned): the products take it rounded to bf16 on chip,
+// the leading terms exactly.
+hipError_t cnp_bwd_sym(const float* dG, const void* S, const void* T, void* sigma, float* dq, int64_t nblk, int b,
+                       hipStream_t stream);
 hipError_t cnp_bwd_sigq(const void* sigma, const void* Q, float* dq, int64_t nblk, int b, hipStream_t stream);
 // The same k = 3 backward with one b = 256 block per workgroup (every
 // intermediate on chip, no Sigma or partial dq in memory): dq [nblk, b(b-1)/2]

@@ -1399,18 +1399,103 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     const int m0 = 64 * (grp ? tj : ti), n0 = diag ? m0 : 64 * (grp ? ti : tj);
     const bool keep = !(diag && ti == tj && grp == 1);   // a lone diagonal tile: group 0's
     const int64_t bb = (int64_t)b * b;
-    // A = dG (bf16, k-major), B = S (k-major, S = S^T), A2 = T ([K][M]), B2 = dG ([K][N])
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + z * bb;
+    // X1 = dG S: A = dG rows (k-major), B = S rows (S = S^T); X2 = T^T dG:
+    // A2 = T ([K][M], m-major), B2 = dG ([K][N], n-major).  S and T come by DMA;
+    // dG's tiles come from its float32 copy (Cin1) through registers, rounded to
+    // bf16 into the stage (the rounding the bf16 copy of dG would get).
     const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + z * bb;
     const uint16_t* A2 = reinterpret_cast<const uint16_t*>(p.A2) + z * bb;
-    const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.B2) + z * bb;
+    const float* dGz = p.Cin1 + z * p.strideCin1;
     unsigned char* ring = lds + grp * kRing;
+    const uint32_t rbase = lds_offset(ring);
+    const int gw = __builtin_amdgcn_readfirstlane(w4);   // wave within the group
+    constexpr int NB = OperandLoads<64, false, G::NW>::n;   // DMA loads of a 64 x 64 tile per thread
+    static_assert(NB == OperandLoads<64, true, G::NW>::n, "tile loads");
+    const int nk = b / 64;
     EpiAddends<64, 64, 256> pre;   // dG (float32) of this group's tile, Cin1
     load_addends(p, m0, n0, z, gtid, pre);
+    // 16 consecutive floats of dG row `row` at column `col` (this thread's part
+    // of a 64 x 64 tile: row gtid / 4, columns 16 (gtid % 4) ..)
+    float4 st[4];
+    auto load_dg = [&](int row, int col) __attribute__((always_inline)) {
+        const float4* src = reinterpret_cast<const float4*>(dGz + (int64_t)row * b + col);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] = src[i];
+    };
+    // ... as two 16-byte chunks of row gtid / 4 of a 128-byte-row image whose
+    // chunk c sits in slot c ^ swz(row)
+    auto put_dg = [&](unsigned char* img, int swz) __attribute__((always_inline)) {
+        const int r = gtid >> 2, sg = gtid & 3;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float4 u = st[2 * h], v = st[2 * h + 1];
+            *reinterpret_cast<uint4*>(img + r * 128 + (((2 * sg + h) ^ swz) << 4)) =
+                make_uint4(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                           pack_bf16x2(v.z, v.w));
+        }
+    };
+    auto compute = [&](auto amn_c, auto bmn_c, const unsigned char* stage, f32x16_t& acc)
+                       __attribute__((always_inline)) {
+        constexpr bool AMN = decltype(amn_c)::value, BMN = decltype(bmn_c)::value;
+        uint4 af[2][1], bfr[2][1];
+        load_frags<G, AMN, BMN>(stage, wm, wn, 0, lane, af[0], bfr[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 16) load_frags<G, AMN, BMN>(stage, wm, wn, ks + 1, lane, af[cur ^ 1], bfr[cur ^ 1]);
+            asm volatile("" ::: "memory");
+            Mfma32<bf16_t>::run(af[cur][0], bfr[cur][0], acc);
+        }
+    };
+    // One product over the nk k-tiles in a two-stage ring: the dG tile through
+    // registers (its loads issued before the DMA of the other operand, so a wait
+    // for them leaves the DMA in flight), tile kt + 1 into the stage tile kt - 1
+    // used once every wave has passed the barrier that opens tile kt.
+    // X1: dG rows m0.. as the k-major A, S rows n0.. as the k-major B
+    // X2: T rows (columns m0..) as the m-major A, dG rows (columns n0..) as the n-major B
+    auto product = [&](auto x2_c, f32x16_t& acc) __attribute__((always_inline)) {
+        constexpr bool X2 = decltype(x2_c)::value;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const int r = gtid >> 2, c16 = 16 * (gtid & 3);
+        auto issue = [&](int kt) __attribute__((always_inline)) {
+            const uint32_t dst = rbase + (kt & 1) * G::kStageBytes;
+            if constexpr (!X2) {
+                load_dg(m0 + r, 64 * kt + c16);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) dma_one<64, false, G::NW>(j, dst + G::kABytes, B, b, n0, b, 64 * kt, b, gw, lane);
+            } else {
+                load_dg(64 * kt + r, n0 + c16);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) dma_one<64, true, G::NW>(j, dst, A2, b, m0, b, 64 * kt, b, gw, lane);
+            }
+        };
+        auto put = [&](int kt) __attribute__((always_inline)) {
+            unsigned char* stage = ring + (kt & 1) * G::kStageBytes;
+            if constexpr (!X2) put_dg(stage, swz_k(r));
+            else put_dg(stage + G::kABytes, swz_mn<64>(r));
+        };
+        issue(0);
+        wait_vmcnt<NB>();
+        put(0);
+#pragma unroll 1
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_vmcnt<0>();
+            wait_lgkm0();
+            block_barrier();   // tile kt complete in every wave
+            if (kt + 1 < nk) issue(kt + 1);
+            compute(std::integral_constant<bool, X2>{}, std::integral_constant<bool, X2>{},
+                    ring + (kt & 1) * G::kStageBytes, acc);
+            if (kt + 1 < nk) {
+                wait_vmcnt<NB>();
+                put(kt + 1);
+            }
+        }
+    };
     f32x16_t x1[1][1], x2[1][1];
-    main_loop<G, false, false, S>(ring, A, b, B, b, m0, n0, b, b, 0, b, gtid, x1);
+    product(std::false_type{}, x1[0][0]);
     block_barrier();   // the second product reuses the LDS ring
-    main_loop<G, true, true, S>(ring, A2, b, B2, b, m0, n0, b, b, 0, b, gtid, x2);
+    product(std::true_type{}, x2[0][0]);
     block_barrier();   // every wave is done reading the operand stages
     float* E = reinterpret_cast<float*>(ring);   // 2 dG + X1 + X2 (= dS)
     float* F = E + 64 * 64;                      // dG + X1 (= dA)
@@ -2701,20 +2786,19 @@ hipError_t launch_pairs(int64_t nblk, int b, Fn&& fn, bool units = false) {
     return hipSuccess;
 }
 
-hipError_t cnp_bwd_sym(const void* dGc, const float* dG, const void* S, const void* T, void* sigma, float* dq,
-                       int64_t nblk, int b, hipStream_t stream) {
+hipError_t cnp_bwd_sym(const float* dG, const void* S, const void* T, void* sigma, float* dq, int64_t nblk, int b,
+                       hipStream_t stream) {
     if (nblk <= 0) return hipSuccess;
     if (b % 64 != 0 || b > 1024) return hipErrorInvalidValue;
+    if (reinterpret_cast<uintptr_t>(dG) & 15) return hipErrorInvalidValue;   // 16-byte loads of dG
     const int64_t bb = (int64_t)b * b, ntri = (int64_t)b * (b - 1) / 2;
     return launch_pairs(nblk, b, [&](int64_t y0, dim3 grid) {
         PipeArgs p;
-        p.A = static_cast<const uint16_t*>(dGc) + y0 * bb;
         p.B = static_cast<const uint16_t*>(S) + y0 * bb;
         p.A2 = static_cast<const uint16_t*>(T) + y0 * bb;
-        p.B2 = static_cast<const uint16_t*>(dGc) + y0 * bb;
         p.Cin1 = dG + y0 * bb; p.ldcin1 = b; p.strideCin1 = bb;
         p.M = p.N = p.K = b;
-        p.epi_vec = (reinterpret_cast<uintptr_t>(dG) & 15) == 0;   // 16-byte addend loads
+        p.epi_vec = true;   // 16-byte addend loads
         uint16_t* sg = static_cast<uint16_t*>(sigma) + y0 * bb;
         if (b <= 256)
             hipLaunchKernelGGL(cnp_bwd_sym_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
