@@ -345,12 +345,12 @@ int cnp_forward(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, void
 }
 
 // Batches from which the k = 3, b = 256 backward takes one block per workgroup
-// instead of the two passes over tile pairs.  A lone workgroup takes about
-// 54 us on its block, the pair passes spread a few blocks over the whole chip
-// (32 blocks: 28 us, 96: 53 against 59 us); from about 128 blocks on, the
-// per-block kernel moves fewer bytes and is ahead (128: 63 against 66 us; 256:
-// 84 against 116 us; 15280: 4.8 against 7.7 ms).
-constexpr int64_t kBlockBwdMinBlocks = 128;
+// instead of the two passes over tile units.  A lone workgroup takes about
+// 54 us on its block, the passes spread a few blocks over the whole chip
+// (32 blocks: 23 us; 128: 61 against 63 us); from about 150 blocks on, the
+// per-block kernel moves fewer bytes and is ahead (160: 67 against 74 us; 256:
+// 84 against 108 us; 15280: 4.8 against 7.7 ms).
+constexpr int64_t kBlockBwdMinBlocks = 144;
 
 // Adjoint schedules (reverse of the forward ones), ending with the skew pack.
 int cnp_backward(const float* q, const float* dG, int64_t nblk, int64_t b, int k, bool cbf16, float* dq,
