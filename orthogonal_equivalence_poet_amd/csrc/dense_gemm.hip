@@ -1910,8 +1910,11 @@ cnp_bwd_block_kernel(const float* __restrict__ dG, const uint16_t* __restrict__ 
     // (r, c) steps by b - r - 2 from row r to row r + 1; the stores go through a
     // buffer resource spanning the block's dq, where an entry on or below the
     // diagonal takes an offset past its end and the store is dropped (no branch).
+    // (stride 0: a raw byte range of num_records bytes; the last word selects the
+    // 32-bit data format, the one the untyped buffer accesses of gfx9 parts use)
+    constexpr int kFmt32 = 0x00020000;
     const __amdgpu_buffer_rsrc_t out =
-        __builtin_amdgcn_make_buffer_rsrc(dq + z * (kBlkB * (kBlkB - 1) / 2), 0, kBlkB * (kBlkB - 1) / 2 * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(dq + z * (kBlkB * (kBlkB - 1) / 2), 0, kBlkB * (kBlkB - 1) / 2 * 4, kFmt32);
     constexpr uint32_t kDrop = 0x80000000u;   // past the resource's end
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
