@@ -1412,8 +1412,6 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     constexpr int NB = OperandLoads<64, false, G::NW>::n;   // DMA loads of a 64 x 64 tile per thread
     static_assert(NB == OperandLoads<64, true, G::NW>::n, "tile loads");
     const int nk = b / 64;
-    EpiAddends<64, 64, 256> pre;   // dG (float32) of this group's tile, Cin1
-    load_addends(p, m0, n0, z, gtid, pre);
     // 16 consecutive floats of dG row `row` at column `col` (this thread's part
     // of a 64 x 64 tile: row gtid / 4, columns 16 (gtid % 4) ..)
     float4 st[4];
@@ -1453,10 +1451,16 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
     // used once every wave has passed the barrier that opens tile kt.
     // X1: dG rows m0.. as the k-major A, S rows n0.. as the k-major B
     // X2: T rows (columns m0..) as the m-major A, dG rows (columns n0..) as the n-major B
+    // Both products start from dG's float32 values of the group's tile (the lane's
+    // accumulator entries, loaded straight into the accumulators): X1's gives
+    // dA = dG + X1, and the two together dS = 2 dG + X1 + X2.
     auto product = [&](auto x2_c, f32x16_t& acc) __attribute__((always_inline)) {
         constexpr bool X2 = decltype(x2_c)::value;
+        {
+            const float* t0 = dGz + (int64_t)(m0 + wm * 32 + 4 * (lane >> 5)) * b + n0 + wn * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            for (int q = 0; q < 16; ++q) acc[q] = t0[(8 * (q >> 2) + (q & 3)) * b];
+        }
         const int r = gtid >> 2, c16 = 16 * (gtid & 3);
         auto issue = [&](int kt) __attribute__((always_inline)) {
             const uint32_t dst = rbase + (kt & 1) * G::kStageBytes;
@@ -1503,19 +1507,6 @@ cnp_bwd_sym_kernel(const PipeArgs p, float* __restrict__ dq, uint16_t* __restric
         f32x16_t e = x1[0][0] + x2[0][0];
         stage_acc(E, e, wm, wn, lane);
         stage_acc(F, x1[0][0], wm, wn, lane);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < EpiAddends<64, 64, 256>::kPer; ++k) {
-        const int u = k * 256 + gtid;
-        const int row = u >> 4, c = (u & 15) * 4;
-        float4 e = *reinterpret_cast<const float4*>(E + t64(row, c));
-        float4 f = *reinterpret_cast<const float4*>(F + t64(row, c));
-        const float4 a = pre.a1[k];
-        e.x += 2.f * a.x; e.y += 2.f * a.y; e.z += 2.f * a.z; e.w += 2.f * a.w;
-        f.x += a.x; f.y += a.y; f.z += a.z; f.w += a.w;
-        *reinterpret_cast<float4*>(E + t64(row, c)) = e;
-        *reinterpret_cast<float4*>(F + t64(row, c)) = f;
     }
     __syncthreads();
     const float* E0 = reinterpret_cast<const float*>(lds);
@@ -2801,7 +2792,6 @@ hipError_t cnp_bwd_sym(const float* dG, const void* S, const void* T, void* sigm
         p.A2 = static_cast<const uint16_t*>(T) + y0 * bb;
         p.Cin1 = dG + y0 * bb; p.ldcin1 = b; p.strideCin1 = bb;
         p.M = p.N = p.K = b;
-        p.epi_vec = true;   // 16-byte addend loads
         uint16_t* sg = static_cast<uint16_t*>(sigma) + y0 * bb;
         if (b <= 256)
             hipLaunchKernelGGL(cnp_bwd_sym_kernel<2>, grid, dim3(512), 0, stream, p, dq + y0 * ntri, sg, b);
