@@ -177,6 +177,29 @@ def test_cnp_bwd_many_blocks(nblk, std, norm):
     assert rel_fro(dq, ref) <= tol("bf16")    # every sampled block on its own, too
 
 
+# dG and G off 16-byte alignment (a view at an odd element offset): the fused
+# and per-block kernels need 16-byte rows, so these calls take the general
+# b x b products; their results must be the same transform
+@pytest.mark.parametrize("nblk", [32, 150])
+def test_cnp_unaligned_buffers_take_general_path(nblk):
+    b, k = 256, 3
+    q = _q(nblk, b, 1e-2, 700 + nblk)
+    js = [0, nblk // 2, nblk - 1]
+    dG = I.gaussian((nblk, b, b), 1.0, "f32", 701, nblk)
+    dG_buf = torch.empty(nblk * b * b + 1, dtype=torch.float32, device=DEV)
+    dG_view = dG_buf[1:].view(nblk, b, b)              # 4 bytes past a 16-byte boundary
+    dG_view.copy_(dev(dG))
+    dq = host(cnp_bwd(dev(q), dG_view, nblk, b, k, "bf16")[js])
+    ref = O.params_grad_from_skew_grad(O.cnp_vjp(O.skew_from_params(q[js], b), dG[js], k))
+    assert rel_fro(dq, ref) <= tol("bf16")
+    G_buf = torch.empty(nblk * b * b + 1, dtype=torch.bfloat16, device=DEV)
+    G = G_buf[1:].view(nblk, b, b)                      # 2 bytes past a 16-byte boundary
+    ws = B.workspace(B.poetx_cnp_fwd_workspace_bytes(nblk, b, k, B.POETX_BF16))
+    B.poetx_cnp_fwd(dev(q), nblk, b, k, G, ws)
+    ref_G = O.neumann_cayley(O.skew_from_params(q[js], b), k)
+    assert rel_fro(host(G[js]), ref_G) <= tol("bf16")
+
+
 # bf16 blocks of 128 or 256 take the fused per-panel forward (32-row panels for
 # a few blocks, as in the cases above; 64-row panels once there are 256 or more
 # of those), except k = 3 at b = 256 from 96 blocks on, which takes one block
