@@ -293,8 +293,9 @@ int cnp_prologue(const float* q, int64_t nblk, int64_t b, int k, bool cbf16, Cnp
 // Batches from which the k = 3, b = 256 forward (bf16) takes one block per
 // workgroup instead of one 32- or 64-row panel per workgroup: one workgroup
 // takes about 24 us on its block, the panels spread a few blocks over more CUs
-// (64 blocks: 20 us against 27); from about a hundred blocks on, building each
-// block's Q image once wins (96: 28 against 33 us; 15280: 2.5 against 4.2 ms).
+// (64 blocks: 17 us against 27); from about a hundred blocks on the two are even
+// (96 to 128: 28 to 31 us both) and building each block's Q image once then
+// pulls ahead (160: 34 against 40 us; 15280: 2.5 against 4.2 ms).
 constexpr int64_t kBlockFwdMinBlocks = 96;
 
 // Forward Cayley-Neumann schedules.  k = 3: G = I + 2Q + 2S + (2Q + S) S.

@@ -2171,14 +2171,17 @@ __device__ __forceinline__ int opaque_zero() {
 //     X buffer and stored as whole rows.
 // With Qc given the panel rows of Q are stored as well; with S / T (k >= 2)
 // S_p = X_2 and T_p = 2 Q_p + S_p (what the saving forward keeps for k = 3).
-template <int B, int PH>
+// b = 256 runs eight waves (NT = 512): the image build, the same work for
+// every panel of a block, is then split over twice the lanes (32 blocks:
+// 11 us against 13 with four waves), and each wave's share of C is 32 rows.
+template <int B, int PH, int NW = 4>
 struct FusedCnp {
     static constexpr int KT = B / 64;         // k-tiles of one product
     static constexpr int NP = B / PH;         // panels per block
     static constexpr int QB = B * 128;        // bytes of one Q k-tile ([B rows][64 k])
     static constexpr int XB = PH * 128;       // bytes of one X k-tile ([PH rows][64 k])
     static constexpr int LDS = KT * (QB + XB);
-    static constexpr int MI = B / 128;        // wave w: rows n in [w B/4, (w+1) B/4) of C
+    static constexpr int MI = B / (32 * NW);  // wave w of NW: rows n in [w B/NW, (w+1) B/NW) of C
     static constexpr int NJ = PH / 32;        //         and all PH columns m
     static constexpr int NPAR = B * (B - 1) / 2;
     static constexpr int NB8 = B / 8;         // 8 x 8 sub-blocks per side
@@ -2281,11 +2284,12 @@ __device__ __forceinline__ void build_q_image(const float* __restrict__ qz, unsi
     }
 }
 
-template <int B, int PH>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, B == 256 ? 1 : 2)))
+template <int B, int PH, int NT = 256>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 256, B == 256 ? NT / 256 : 2)))
 cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t* __restrict__ Qc,
                  uint16_t* __restrict__ Sv, uint16_t* __restrict__ Tv, int k, int total) {
-    using F = FusedCnp<B, PH>;
+    using F = FusedCnp<B, PH, NT / 64>;
+    static_assert(F::MI >= 1, "a wave owns at least 32 rows");
     constexpr int KT = F::KT, QB = F::QB, XB = F::XB, MI = F::MI, NJ = F::NJ, NB8 = F::NB8;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS];
     unsigned char* qs = lds;
@@ -2299,12 +2303,12 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
     const int r0 = PH * p;   // first row of the panel
 
     // 1. the Q image
-    build_q_image<B, 256>(qz, qs, tid);
+    build_q_image<B, NT>(qz, qs, tid);
     __syncthreads();
 
     // rows of an image as 16-byte chunks: PH rows x B/8 chunks over the workgroup
     auto copy_rows = [&](uint16_t* __restrict__ dst, auto chunk_value) {
-        for (int u = tid; u < PH * (B / 8); u += 256) {
+        for (int u = tid; u < PH * (B / 8); u += NT) {
             const int m = u / (B / 8), c8 = u - m * (B / 8);
             *reinterpret_cast<uint4*>(dst + zoff + (int64_t)(r0 + m) * B + 8 * c8) = chunk_value(m, 8 * c8);
         }
@@ -2320,7 +2324,7 @@ cnp_fused_kernel(const float* __restrict__ q, uint16_t* __restrict__ G, uint16_t
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sum[i][j][r] = 0.f;
-    const int n_base = wave * (B / 4);
+    const int n_base = wave * (B / (NT / 64));
     for (int it = 1; it <= k; ++it) {
         // B operand: X_1 = rows r0.. of the Q image, later X_it in the X buffer
         const unsigned char* xb = it == 1 ? qs : xs;
@@ -2969,9 +2973,9 @@ hipError_t cnp_fused_fwd(const float* q, void* G, void* Qc, void* S, void* T, in
     const auto tv = static_cast<uint16_t*>(T);
     const dim3 grid((unsigned)panels);
     if (b == 256 && tall)
-        hipLaunchKernelGGL((cnp_fused_kernel<256, 64>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
+        hipLaunchKernelGGL((cnp_fused_kernel<256, 64, 512>), grid, dim3(512), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     else if (b == 256)
-        hipLaunchKernelGGL((cnp_fused_kernel<256, 32>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
+        hipLaunchKernelGGL((cnp_fused_kernel<256, 32, 512>), grid, dim3(512), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     else if (tall)
         hipLaunchKernelGGL((cnp_fused_kernel<128, 64>), grid, dim3(256), 0, stream, q, g, qc, sv, tv, k, (int)panels);
     else
