@@ -4,6 +4,7 @@
 // products, fills, permutation helpers and the dense block-diagonal transforms
 // of the weight-centric variant.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "elementwise.h"
@@ -125,11 +126,15 @@ __global__ void skew_pack_simple(const float* __restrict__ dQ, float* __restrict
 // A workgroup owns `rows_per_wg` full rows, staged in LDS: gathers read the
 // row contiguously and pick from LDS; scatters place into LDS and write the
 // row contiguously.  Both global streams are 16-byte vectors.  Every thread
-// issues kBatch loads (data and indices) before it uses any of them, so a
-// workgroup waits for memory a few times, not once per vector.
-constexpr int kPermBatch = 8;
-
-template <typename T>
+// issues NB loads (data and indices) before it uses any of them, so a
+// workgroup waits for memory a few times, not once per vector.  NB is the
+// thread's share of the workgroup's vectors, up to 8: registers beyond it would
+// cost resident workgroups (at 2 vectors a thread, 46 registers keep eight
+// workgroups of 256 threads on a CU, 120 kept four).  When the share fits one
+// batch of at most 4, a gather loads its column indices together with the row,
+// so that the two latencies overlap (for 8 the indices would stay live across
+// the barrier, at a cost in resident workgroups).
+template <typename T, int NB>
 __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ src, T* __restrict__ dst,
                                                         int64_t rows, int cols, const int* __restrict__ row_idx,
                                                         const int* __restrict__ col_idx, int scatter,
@@ -137,15 +142,16 @@ __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ sr
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     T* buf = reinterpret_cast<T*>(smem_raw);
     constexpr int V = ElemTraits<T>::kVec;
-    constexpr int NB = kPermBatch;
     const int chunks = cols / V;
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     const int nrows = (int)min<int64_t>(rows_per_wg, rows - row0);
     const int total = nrows * chunks;
     const bool scat = scatter && col_idx;
+    const bool gath = !scatter && col_idx;
+    const bool one = NB <= 4 && total <= 256 * NB;   // one batch: a gather's indices load with the row
+    int ci[NB][V];
     for (int u0 = threadIdx.x; u0 < total; u0 += 256 * NB) {
         uint4 v[NB];
-        int ci[NB][V];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int u = u0 + k * 256;
@@ -155,7 +161,7 @@ __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ sr
                 const int64_t gr = row0 + r;
                 const int64_t sr = row_idx ? row_idx[gr] : gr;
                 v[k] = *reinterpret_cast<const uint4*>(src + sr * cols + c);
-                if (scat) {
+                if (scat || (gath && one)) {
 #pragma unroll
                     for (int i = 0; i < V; ++i) ci[k][i] = col_idx[c + i];
                 }
@@ -178,10 +184,8 @@ __global__ void __launch_bounds__(256) permute_rows_lds(const T* __restrict__ sr
         }
     }
     __syncthreads();
-    const bool gath = !scatter && col_idx;
     for (int u0 = threadIdx.x; u0 < total; u0 += 256 * NB) {
-        int ci[NB][V];
-        if (gath) {
+        if (gath && !one) {
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int u = u0 + k * 256;
@@ -570,12 +574,20 @@ hipError_t permute_2d(const void* src, void* dst, bool bf16, int64_t rows, int64
         rpw = (int)std::min<int64_t>(rpw, rows);
         const size_t smem = (size_t)rpw * row_bytes;
         const unsigned grid = (unsigned)((rows + rpw - 1) / rpw);
-        if (bf16)
-            hipLaunchKernelGGL(permute_rows_lds<bf16_t>, dim3(grid), dim3(256), smem, s, (const bf16_t*)src,
-                               (bf16_t*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
-        else
-            hipLaunchKernelGGL(permute_rows_lds<float>, dim3(grid), dim3(256), smem, s, (const float*)src,
-                               (float*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
+        // 16-byte vectors per thread of one workgroup
+        const int64_t per = (rpw * row_bytes / 16 + 255) / 256;
+        auto go = [&](auto nb_c) {
+            constexpr int NB = decltype(nb_c)::value;
+            if (bf16)
+                hipLaunchKernelGGL((permute_rows_lds<bf16_t, NB>), dim3(grid), dim3(256), smem, s, (const bf16_t*)src,
+                                   (bf16_t*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
+            else
+                hipLaunchKernelGGL((permute_rows_lds<float, NB>), dim3(grid), dim3(256), smem, s, (const float*)src,
+                                   (float*)dst, rows, (int)cols, row_idx, col_idx, scatter ? 1 : 0, rpw);
+        };
+        if (per <= 2) go(std::integral_constant<int, 2>{});
+        else if (per <= 4) go(std::integral_constant<int, 4>{});
+        else go(std::integral_constant<int, 8>{});
     } else {
         const int64_t total = rows * cols;
         if (bf16)
