@@ -51,7 +51,9 @@ def test_skew_pack_bitexact(b):
 
 # ------------------------------------------------------------ permutations
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,cols", [(37, 4096), (3, 16), (300, 512), (2, 40960)])
+# rows of 16 B to 57 KB in LDS (each thread's share of a row's 16-byte vectors
+# 1 to 14: batches of 2, 4 and 8, one or several per row) and rows past LDS
+@pytest.mark.parametrize("rows,cols", [(37, 4096), (3, 16), (300, 512), (9, 6144), (5, 14336), (2, 40960)])
 @pytest.mark.parametrize("mode", ["gather", "scatter", "rows_and_cols"])
 def test_permute_bitexact(dtype, rows, cols, mode):
     src = I.gaussian((rows, cols), 1.0, dtype, 92, rows, cols)
